@@ -1,0 +1,145 @@
+"""fp64 CPU oracle of the selective state-space scan (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product library never touches it, and it shares no
+code with the HIP path: the arithmetic lives in ``oracle.c`` (plain C, double
+precision, host libm), and this module only widens inputs to float64,
+allocates outputs and calls it.
+
+What the scan computes, and where the pages define it, is documented at the
+top of ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no
+    FMA contraction, OpenMP over independent rows)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+             "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"],
+            check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = os.environ.get("SELSCAN_ORACLE_LIB")  # a deliberately broken copy, in tests
+            if not path:
+                if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                    build(force=True)
+                path = _LIB
+            lib = ctypes.CDLL(path)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i64 = ctypes.c_int64
+            lib.oracle_m1_f64.argtypes = [i64, i64, i64, i64] + [dp] * 8 + [ctypes.c_int, dp, dp, dp]
+            lib.oracle_m1_f64.restype = ctypes.c_int
+            lib.oracle_m2_f64.argtypes = [i64] * 6 + [dp] * 8 + [ctypes.c_int, dp, dp, dp]
+            lib.oracle_m2_f64.restype = ctypes.c_int
+            lib.oracle_version.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _f64(a, shape=None):
+    """Widen to a C-contiguous float64 array (exact for bf16/fp16/fp32)."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # a torch tensor: widen on the CPU
+        a = a.detach().to("cpu").double().numpy()
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def set_threads(n: int | None) -> None:
+    """Set the OpenMP thread count used by later oracle calls."""
+    if n is not None:
+        os.environ["OMP_NUM_THREADS"] = str(int(n))
+
+
+def m1(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None):
+    """Mamba-1 selective scan in fp64.
+
+    Shapes: u, delta, z [batch, dim, L]; A [dim, N]; B, C [batch, N, L];
+    D, delta_bias [dim]; h0 [batch, dim, N].
+    Returns (y [batch, dim, L] float64, last_state [batch, dim, N] float64).
+    """
+    u = _f64(u)
+    nb, nd, nl = u.shape
+    A = _f64(A)
+    nn = A.shape[1]
+    delta = _f64(delta, (nb, nd, nl))
+    A = _f64(A, (nd, nn))
+    B = _f64(B, (nb, nn, nl))
+    C = _f64(C, (nb, nn, nl))
+    D = _f64(D, (nd,))
+    z = _f64(z, (nb, nd, nl))
+    delta_bias = _f64(delta_bias, (nd,))
+    h0 = _f64(h0, (nb, nd, nn))
+    y = np.empty((nb, nd, nl), np.float64)
+    last = np.empty((nb, nd, nn), np.float64)
+    rc = _load().oracle_m1_f64(nb, nd, nn, nl, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                               _ptr(h0), _ptr(y), _ptr(last))
+    if rc != 0:
+        raise RuntimeError(f"oracle_m1_f64 failed with status {rc}")
+    return y, last
+
+
+def m2(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, h0=None):
+    """Mamba-2 multi-head selective scan in fp64.
+
+    Shapes: x, z [batch, L, H, P]; dt [batch, L, H]; A, D, dt_bias [H];
+    B, C [batch, L, G, N]; h0 [batch, H, P, N].
+    Returns (y [batch, L, H, P], last_state [batch, H, P, N]), float64.
+    """
+    x = _f64(x)
+    nb, nl, nh, npd = x.shape
+    B = _f64(B)
+    ng, nn = B.shape[2], B.shape[3]
+    B = _f64(B, (nb, nl, ng, nn))
+    C = _f64(C, (nb, nl, ng, nn))
+    dt = _f64(dt, (nb, nl, nh))
+    A = _f64(A, (nh,))
+    D = _f64(D, (nh,))
+    z = _f64(z, (nb, nl, nh, npd))
+    dt_bias = _f64(dt_bias, (nh,))
+    h0 = _f64(h0, (nb, nh, npd, nn))
+    y = np.empty((nb, nl, nh, npd), np.float64)
+    last = np.empty((nb, nh, npd, nn), np.float64)
+    rc = _load().oracle_m2_f64(nb, nl, nh, npd, ng, nn, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), int(bool(softplus)),
+                               _ptr(h0), _ptr(y), _ptr(last))
+    if rc != 0:
+        raise RuntimeError(f"oracle_m2_f64 failed with status {rc}")
+    return y, last
+
+
+def version() -> str:
+    return _load().oracle_version().decode()

@@ -1,0 +1,179 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference of the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg do.  It shares no code, header, table or
+ * helper with the HIP library.
+ *
+ * Every input arrives widened to double (bf16 and fp32 widen exactly), every
+ * operation runs in double with the host libm, one (batch, channel) row at a
+ * time, token by token, in the order the method defines.  No blocking, no
+ * reassociation, no vector tricks.  Rows are independent, so OpenMP splits
+ * the row loop (static schedule); that changes no arithmetic.
+ *
+ * Sources for what is computed (all are web pages about Mamba):
+ *  - "Understanding Mamba and Selective State Space Models (SSMs)" (bqwf.cn
+ *    practitioner blog), section 2.2 "first cut: selectivity": the state
+ *    update h_n = exp(Delta_n A) h_{n-1} + Delta_n B_n x_n, with Delta, B, C
+ *    depending on the token; section 2.2 "second cut": the recurrent scan
+ *    starting from a zero state; the tip closing section 2.2: Delta passes
+ *    through softplus log(1+exp(x)) to stay positive; section 2.1: the
+ *    read-out y = C h + D x; section 4.3: A = -exp(A_log), diagonal.
+ *  - The Mamba README embedded in the gittoolsai tool page for
+ *    state-spaces/mamba, sections "Selective SSM", "Mamba-2" and
+ *    "Initialization": the selective SSM layer, the Mamba-2 variant, and the
+ *    Delta bias that places Delta in a target range.
+ *  - The "model-architecture-mamba" skill page: Mamba-2 uses multiple heads,
+ *    d_state 128 and headdim 64.
+ * Readings where the pages are silent or garbled (sign of the exponent, the
+ * sum over the state index in the read-out, the gate multiplying the D term,
+ * the zero initial state) are the plainest ones consistent with those pages:
+ *   y_t = (sum_n C_t[n] h_t[n] + D_d u_t) * silu(z_t),  h_{-1} = 0 (or h0).
+ *
+ * Parity pins: see tests/test_oracle_pins.py (closed forms, brute force,
+ * invariants).  Every function here is pinned there.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEM 2
+
+/* softplus(x) = log(1 + e^x), written so that e^x never overflows. */
+static double sp64(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^-z). */
+static double silu64(double z) { return z / (1.0 + exp(-z)); }
+
+const char* oracle_version(void) { return "selscan-oracle fp64 1"; }
+
+/*
+ * Mamba-1 selective scan, one channel row at a time.
+ *   u, delta, z : [nb, nd, nl]   (z may be NULL: no gate)
+ *   A           : [nd, nn]
+ *   Bm, Cm      : [nb, nn, nl]
+ *   Dv, bias    : [nd]           (either may be NULL: treated as 0)
+ *   h0          : [nb, nd, nn]   (NULL: zero initial state)
+ *   y           : [nb, nd, nl]   out
+ *   last        : [nb, nd, nn]   out (may be NULL)
+ */
+int oracle_m1_f64(int64_t nb, int64_t nd, int64_t nn, int64_t nl,
+                  const double* u, const double* delta, const double* A,
+                  const double* Bm, const double* Cm, const double* Dv,
+                  const double* z, const double* bias, int softplus,
+                  const double* h0, double* y, double* last)
+{
+    if (nb < 0 || nd < 0 || nn < 1 || nl < 0) return ORACLE_BAD_ARG;
+    if (!u || !delta || !A || !Bm || !Cm || !y) return ORACLE_BAD_ARG;
+    const int64_t rows = nb * nd;
+    int status = ORACLE_OK;
+
+#pragma omp parallel
+    {
+        double* h = (double*)malloc((size_t)nn * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            status = ORACLE_NO_MEM;
+        }
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < rows; ++row) {
+            if (!h) continue;
+            const int64_t b = row / nd;
+            const int64_t d = row % nd;
+            const double* urow = u + row * nl;
+            const double* drow = delta + row * nl;
+            const double* zrow = z ? z + row * nl : NULL;
+            const double* Arow = A + d * nn;
+            const double* Bb = Bm + b * nn * nl;   /* B[b, n, t] = Bb[n*nl + t] */
+            const double* Cb = Cm + b * nn * nl;
+            double* yrow = y + row * nl;
+            for (int64_t n = 0; n < nn; ++n) h[n] = h0 ? h0[row * nn + n] : 0.0;
+            for (int64_t t = 0; t < nl; ++t) {
+                double xv = drow[t] + (bias ? bias[d] : 0.0);
+                double dt = softplus ? sp64(xv) : xv;        /* Delta_t */
+                double ut = urow[t];
+                double acc = 0.0;
+                for (int64_t n = 0; n < nn; ++n) {
+                    double dA = exp(dt * Arow[n]);            /* exp(Delta A) */
+                    h[n] = dA * h[n] + dt * Bb[n * nl + t] * ut;
+                    acc += Cb[n * nl + t] * h[n];
+                }
+                double yv = acc + (Dv ? Dv[d] * ut : 0.0);
+                if (zrow) yv *= silu64(zrow[t]);
+                yrow[t] = yv;
+            }
+            if (last)
+                for (int64_t n = 0; n < nn; ++n) last[row * nn + n] = h[n];
+        }
+        free(h);
+    }
+    return status;
+}
+
+/*
+ * Mamba-2 multi-head selective scan: a scalar A per head, one Delta per
+ * (batch, token, head) shared by the head's channels, B and C shared by the
+ * heads of a group (head h belongs to group h / (nh / ng)).
+ *   x, z        : [nb, nl, nh, np]   (z may be NULL)
+ *   dt          : [nb, nl, nh]
+ *   A, Dv, dtb  : [nh]               (Dv, dtb may be NULL: treated as 0)
+ *   Bm, Cm      : [nb, nl, ng, nn]
+ *   h0, last    : [nb, nh, np, nn]   (h0 NULL: zero state; last may be NULL)
+ *   y           : [nb, nl, nh, np]
+ */
+int oracle_m2_f64(int64_t nb, int64_t nl, int64_t nh, int64_t np, int64_t ng,
+                  int64_t nn, const double* x, const double* dt, const double* A,
+                  const double* Bm, const double* Cm, const double* Dv,
+                  const double* z, const double* dtb, int softplus,
+                  const double* h0, double* y, double* last)
+{
+    if (nb < 0 || nl < 0 || nh < 1 || np < 1 || ng < 1 || nn < 1) return ORACLE_BAD_ARG;
+    if (nh % ng != 0) return ORACLE_BAD_ARG;
+    if (!x || !dt || !A || !Bm || !Cm || !y) return ORACLE_BAD_ARG;
+    const int64_t units = nb * nh * np;   /* one (batch, head, channel) each */
+    const int64_t heads_per_group = nh / ng;
+    int status = ORACLE_OK;
+
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)nn * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            status = ORACLE_NO_MEM;
+        }
+#pragma omp for schedule(static)
+        for (int64_t unit = 0; unit < units; ++unit) {
+            if (!s) continue;
+            const int64_t b = unit / (nh * np);
+            const int64_t hh = (unit / np) % nh;
+            const int64_t p = unit % np;
+            const int64_t g = hh / heads_per_group;
+            for (int64_t n = 0; n < nn; ++n) s[n] = h0 ? h0[unit * nn + n] : 0.0;
+            for (int64_t t = 0; t < nl; ++t) {
+                const int64_t bt = b * nl + t;
+                double xv = dt[bt * nh + hh] + (dtb ? dtb[hh] : 0.0);
+                double delt = softplus ? sp64(xv) : xv;
+                double dA = exp(delt * A[hh]);
+                double xt = x[(bt * nh + hh) * np + p];
+                const double* Bt = Bm + (bt * ng + g) * nn;
+                const double* Ct = Cm + (bt * ng + g) * nn;
+                double acc = 0.0;
+                for (int64_t n = 0; n < nn; ++n) {
+                    s[n] = dA * s[n] + delt * Bt[n] * xt;
+                    acc += Ct[n] * s[n];
+                }
+                double yv = acc + (Dv ? Dv[hh] * xt : 0.0);
+                if (z) yv *= silu64(z[(bt * nh + hh) * np + p]);
+                y[(bt * nh + hh) * np + p] = yv;
+            }
+            if (last)
+                for (int64_t n = 0; n < nn; ++n) last[unit * nn + n] = s[n];
+        }
+        free(s);
+    }
+    return status;
+}

@@ -1,0 +1,186 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module only draws random numbers with the distributions, shapes and
+dtypes of the five workloads; it performs none of the scan's arithmetic.  The
+same tensors (the same bytes) feed the HIP library and the fp64 oracle.
+
+Every tensor gets its own generator stream, seeded from (seed, tensor id), so
+adding or resizing one tensor never shifts another.  Large tensors are drawn on
+the device they will live on (torch's counter-based generator on the GPU);
+small parameter vectors are always drawn on the CPU so they are identical
+whatever the device.
+
+Distributions (the workloads' definitions):
+  u, z, B, C, delta ~ N(0, 1), rounded to the input dtype (bf16: RNE);
+  delta_bias[d] = log(expm1(U_d)), U_d ~ Uniform[1e-3, 1e-1] per channel,
+      so softplus(delta + bias) equals U_d where delta = 0;
+  D[d] ~ N(0, 1) per channel;
+  A[d, n] = -(n + 1)                              ("s4d", S4D-real);
+  A[d, n] = -(n + 1) * exp(eps_d), eps_d ~ N(0, 0.1) per row ("s4d_jitter");
+  Mamba-2: A[h] = -U[1, 16], D[h] ~ N(0, 1), dt_bias as above, all per head.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+# tensor ids of the per-tensor streams
+_TID = {"u": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "A": 6, "D": 7, "bias": 8}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "m1" or "m2"
+    batch: int
+    seqlen: int
+    dstate: int
+    dtype: torch.dtype   # u/delta/z/B/C (M2: x/dt/z/B/C) and y
+    dim: int = 0         # M1 channels (d_inner)
+    a_kind: str = "s4d"  # M1 A initialisation
+    nheads: int = 0      # M2
+    headdim: int = 0     # M2
+    ngroups: int = 0     # M2
+    note: str = field(default="", compare=False)
+
+    @property
+    def updates(self) -> int:
+        """State updates per scan: batch * L * channels * d_state."""
+        ch = self.dim if self.kind == "m1" else self.nheads * self.headdim
+        return self.batch * self.seqlen * ch * self.dstate
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", "m1", batch=1, seqlen=64, dstate=16, dtype=torch.float32,
+                          dim=32, a_kind="s4d",
+                          note="tiny fp32 scan: batch 1, d_inner 32, d_state 16, L 64"),
+    "mamba130m_l2k": Workload("mamba130m_l2k", "m1", batch=8, seqlen=2048, dstate=16,
+                              dtype=torch.bfloat16, dim=1536, a_kind="s4d",
+                              note="Mamba-130m-shaped layer: d_inner 1536, d_state 16, batch 8, L 2048"),
+    "mamba2p8b_l8k": Workload("mamba2p8b_l8k", "m1", batch=4, seqlen=8192, dstate=16,
+                              dtype=torch.bfloat16, dim=5120, a_kind="s4d_jitter",
+                              note="Mamba-2.8b-shaped layer: d_inner 5120, d_state 16, batch 4, L 8192"),
+    "long_1m": Workload("long_1m", "m1", batch=1, seqlen=1 << 20, dstate=16, dtype=torch.bfloat16,
+                        dim=2048, a_kind="s4d_jitter",
+                        note="million-token scan: d_inner 2048, d_state 16, batch 1, L 2^20"),
+    "mamba2_mh": Workload("mamba2_mh", "m2", batch=8, seqlen=4096, dstate=128, dtype=torch.bfloat16,
+                          nheads=32, headdim=64, ngroups=1,
+                          note="Mamba-2 multi-head: 32 heads x headdim 64, d_state 128, ngroups 1, "
+                               "batch 8, L 4096"),
+}
+
+
+def _gen(seed: int, name: str, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + _TID[name] * 7919) & 0x7FFF_FFFF_FFFF_FFFF)
+    return g
+
+
+def _normal(shape, seed, name, dtype, device):
+    dev = torch.device(device)
+    out = torch.empty(shape, dtype=dtype, device=dev)
+    g = _gen(seed, name, dev)
+    # draw in fp32 and round once (RNE) to the storage dtype; chunked so the
+    # fp32 temporary stays bounded for the multi-GB tensors
+    flat = out.view(-1)
+    step = 1 << 28
+    for s in range(0, flat.numel(), step):
+        e = min(flat.numel(), s + step)
+        flat[s:e] = torch.randn(e - s, generator=g, device=dev, dtype=torch.float32).to(dtype)
+    return out
+
+
+def _cpu_uniform(n, lo, hi, seed, name):
+    g = _gen(seed, name, "cpu")
+    return torch.rand(n, generator=g, dtype=torch.float64) * (hi - lo) + lo
+
+
+def delta_bias(n: int, seed: int) -> torch.Tensor:
+    """bias = log(expm1(U)), U ~ Uniform[1e-3, 1e-1]; fp32 [n] on the CPU."""
+    U = _cpu_uniform(n, 1e-3, 1e-1, seed, "bias")
+    return torch.log(torch.expm1(U)).to(torch.float32)
+
+
+def a_matrix(dim: int, dstate: int, kind: str, seed: int) -> torch.Tensor:
+    n1 = torch.arange(1, dstate + 1, dtype=torch.float32)
+    if kind == "s4d":
+        return (-n1).repeat(dim, 1).contiguous()
+    if kind == "s4d_jitter":
+        g = _gen(seed, "A", "cpu")
+        scale = torch.exp(torch.randn(dim, generator=g, dtype=torch.float32) * 0.1)
+        return (-(n1[None, :] * scale[:, None])).contiguous()
+    if kind == "random":  # unstructured negative A, for the general decay path
+        g = _gen(seed, "A", "cpu")
+        return (-torch.rand(dim, dstate, generator=g, dtype=torch.float32) * 15.9 - 0.1).contiguous()
+    raise ValueError(kind)
+
+
+def m1_inputs(batch, dim, dstate, seqlen, dtype=torch.bfloat16, a_kind="s4d", seed=0,
+              device="cpu", gate=True, skip=True, bias=True):
+    """Inputs of one Mamba-1 scan as a dict of tensors.
+
+    u, delta, z: [batch, dim, seqlen]; B, C: [batch, dstate, seqlen] (dtype);
+    A: [dim, dstate], D, delta_bias: [dim] (fp32).
+    """
+    dev = torch.device(device)
+    out = {
+        "u": _normal((batch, dim, seqlen), seed, "u", dtype, dev),
+        "delta": _normal((batch, dim, seqlen), seed, "delta", dtype, dev),
+        "B": _normal((batch, dstate, seqlen), seed, "B", dtype, dev),
+        "C": _normal((batch, dstate, seqlen), seed, "C", dtype, dev),
+        "A": a_matrix(dim, dstate, a_kind, seed).to(dev),
+        "z": _normal((batch, dim, seqlen), seed, "z", dtype, dev) if gate else None,
+        "D": torch.randn(dim, generator=_gen(seed, "D", "cpu")).to(dev) if skip else None,
+        "delta_bias": delta_bias(dim, seed).to(dev) if bias else None,
+    }
+    return out
+
+
+def m2_inputs(batch, seqlen, nheads, headdim, ngroups, dstate, dtype=torch.bfloat16, seed=0,
+              device="cpu", gate=True, skip=True, bias=True):
+    """Inputs of one Mamba-2 scan as a dict of tensors.
+
+    x, z: [batch, seqlen, nheads, headdim]; dt: [batch, seqlen, nheads];
+    B, C: [batch, seqlen, ngroups, dstate] (dtype); A, D, dt_bias: [nheads] fp32.
+    """
+    dev = torch.device(device)
+    gA = _gen(seed, "A", "cpu")
+    out = {
+        "x": _normal((batch, seqlen, nheads, headdim), seed, "u", dtype, dev),
+        "dt": _normal((batch, seqlen, nheads), seed, "delta", dtype, dev),
+        "B": _normal((batch, seqlen, ngroups, dstate), seed, "B", dtype, dev),
+        "C": _normal((batch, seqlen, ngroups, dstate), seed, "C", dtype, dev),
+        "A": (-(torch.rand(nheads, generator=gA, dtype=torch.float32) * 15.0 + 1.0)).to(dev),
+        "z": _normal((batch, seqlen, nheads, headdim), seed, "z", dtype, dev) if gate else None,
+        "D": torch.randn(nheads, generator=_gen(seed, "D", "cpu")).to(dev) if skip else None,
+        "dt_bias": delta_bias(nheads, seed).to(dev) if bias else None,
+    }
+    return out
+
+
+def workload_inputs(w: Workload | str, seed: int = 0, device="cpu"):
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if w.kind == "m1":
+        return m1_inputs(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.a_kind, seed, device)
+    return m2_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.dtype, seed,
+                     device)
+
+
+def algorithmic_bytes(w: Workload) -> int:
+    """Bytes the scan must move: every input read once, y and the final state
+    written once, no intermediate state."""
+    s = torch.tensor([], dtype=w.dtype).element_size()
+    if w.kind == "m1":
+        elem = w.batch * w.dim * w.seqlen
+        return (elem * 4 * s + 2 * w.batch * w.dstate * w.seqlen * s
+                + (w.dim * w.dstate + 2 * w.dim) * 4 + w.batch * w.dim * w.dstate * 4)
+    elem = w.batch * w.seqlen * w.nheads * w.headdim
+    return (elem * 3 * s + w.batch * w.seqlen * w.nheads * s
+            + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * s + 3 * w.nheads * 4
+            + w.batch * w.nheads * w.headdim * w.dstate * 4)
+
+
+__all__ = ["WORKLOADS", "Workload", "m1_inputs", "m2_inputs", "workload_inputs",
+           "algorithmic_bytes", "a_matrix", "delta_bias"]
