@@ -1,0 +1,156 @@
+/*
+ * selscan.h -- C ABI of libselscan, the selective state-space scan of Mamba
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch b, channel d, state index n and token t
+ * (Mamba-1 form):
+ *
+ *     Delta_t  = softplus(delta_t + delta_bias_d)      (or delta_t + bias if softplus == 0)
+ *     h_t[n]   = exp(Delta_t * A[d,n]) * h_{t-1}[n] + Delta_t * B_t[n] * u_t,   h_{-1} = 0
+ *     y_t      = (sum_n C_t[n] * h_t[n] + D_d * u_t) * silu(z_t)             (gate optional)
+ *
+ * Sources: the "Understanding Mamba and Selective State Space Models (SSMs)"
+ * blog, section 2.2 (the selective update with exp(Delta A), the recurrent
+ * scan from a zero state, softplus keeping Delta positive) and section 2.1
+ * (the read-out y = C h + D x); the Mamba README on the gittoolsai page for
+ * state-spaces/mamba, sections "Selective SSM" (the layer), "Mamba-2" and
+ * "Initialization" (the Delta bias); the "model-architecture-mamba" skill
+ * page (Mamba-2: multi-head, d_state 128, headdim 64).  Where the pages are
+ * silent the plainest reading is taken: the read-out sums over n, the gate
+ * multiplies the D term too, the initial state is zero, A is stored negative.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    row-major in the layouts given below.  The library keeps no pointer after
+ *    a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued on it and the call returns without synchronising.  Faults
+ *    inside a kernel surface at the caller's next synchronisation.
+ *  - Argument errors are detected on the host before any device work and
+ *    return SELSCAN_ERR_INVALID_ARG / SELSCAN_ERR_UNSUPPORTED with a message
+ *    available from selscan_last_error() on the calling thread.  No C++
+ *    exception crosses this interface; the library never aborts the process.
+ *  - NaN and Inf in the inputs propagate to the outputs; nothing is clamped.
+ *  - Calls on distinct streams may run concurrently.
+ */
+#ifndef SELSCAN_H
+#define SELSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SELSCAN_OK = 0,
+    SELSCAN_ERR_INVALID_ARG = 1,  /* null required pointer, bad size, overflow */
+    SELSCAN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype, d_state) */
+    SELSCAN_ERR_NO_DEVICE = 3,    /* no usable gfx950 device */
+    SELSCAN_ERR_LAUNCH = 4,       /* the HIP runtime refused a launch or an allocation */
+    SELSCAN_ERR_WORKSPACE = 5     /* caller workspace smaller than selscan_*_workspace_bytes */
+} selscan_status_t;
+
+typedef enum {
+    SELSCAN_F32 = 0,   /* IEEE binary32 */
+    SELSCAN_BF16 = 1   /* bfloat16 (upper half of a binary32); stores round to nearest even */
+} selscan_dtype_t;
+
+/*
+ * Mamba-1 problem description.
+ *   batch  B >= 1, dim D >= 1 (channels, d_inner), dstate N in {1..16},
+ *   seqlen L >= 1.
+ *   in_dtype : dtype of u, delta, z, B, C.
+ *   out_dtype: dtype of y.
+ *   workspace: optional device scratch of at least selscan_workspace_bytes()
+ *              bytes, 256-byte aligned.  NULL: the library allocates what it
+ *              needs with stream-ordered hipMallocAsync / hipFreeAsync on the
+ *              call's stream.
+ */
+typedef struct {
+    int64_t batch, dim, dstate, seqlen;
+    int32_t in_dtype;
+    int32_t out_dtype;
+    void* workspace;
+    size_t workspace_bytes;
+} selscan_shape_t;
+
+/* Bytes of workspace selscan_fwd needs for `shape` (0 if none). */
+size_t selscan_workspace_bytes(const selscan_shape_t* shape);
+
+/*
+ * Mamba-1 selective scan (the selective SSM layer of the Mamba README; the
+ * update of section 2.2 of the "Understanding Mamba ..." blog).
+ *
+ *   u          [B, D, L]  in_dtype   input x_t of each channel
+ *   delta      [B, D, L]  in_dtype   Delta pre-activation
+ *   A          [D, N]     fp32       state matrix diagonal (normally < 0)
+ *   B          [B, N, L]  in_dtype   input projection, shared by all channels
+ *   C          [B, N, L]  in_dtype   output projection, shared by all channels
+ *   D          [D]        fp32       skip weight; NULL = no skip term
+ *   z          [B, D, L]  in_dtype   gate; NULL = no silu(z) gating
+ *   delta_bias [D]        fp32       added to delta before softplus; NULL = 0
+ *   softplus   0 or 1     apply softplus to delta + bias
+ *   y          [B, D, L]  out_dtype  output (written)
+ *   last_state [B, D, N]  fp32       h after the last token (written); NULL = skip
+ *
+ * Returns SELSCAN_OK once the work is enqueued.
+ */
+selscan_status_t selscan_fwd(const selscan_shape_t* shape,
+                             const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D,
+                             const void* z, const float* delta_bias, int softplus,
+                             void* y, float* last_state, void* stream);
+
+/*
+ * Mamba-2 problem description.
+ *   batch >= 1, seqlen >= 1, nheads H >= 1, headdim P >= 1, ngroups G >= 1
+ *   with H % G == 0, dstate N in {16, 32, 64, 128}.
+ *   in_dtype: dtype of x, dt, z, B, C; out_dtype: dtype of y.
+ *   workspace: as for selscan_shape_t.
+ */
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
+    int32_t in_dtype;
+    int32_t out_dtype;
+    void* workspace;
+    size_t workspace_bytes;
+} selscan_m2_shape_t;
+
+size_t selscan_mamba2_workspace_bytes(const selscan_m2_shape_t* shape);
+
+/*
+ * Mamba-2 multi-head selective scan (the Mamba-2 block of the Mamba README;
+ * the "model-architecture-mamba" page's multi-head Mamba-2): a scalar A per
+ * head, one Delta per (batch, token, head) shared by the head's P channels,
+ * B and C shared by the heads of a group; head h reads group h / (H / G).
+ *
+ *   x          [B, L, H, P]  in_dtype
+ *   dt         [B, L, H]     in_dtype   Delta pre-activation
+ *   A          [H]           fp32
+ *   B, C       [B, L, G, N]  in_dtype
+ *   D          [H]           fp32       NULL = no skip
+ *   z          [B, L, H, P]  in_dtype   NULL = no gate
+ *   dt_bias    [H]           fp32       NULL = 0
+ *   y          [B, L, H, P]  out_dtype  (written)
+ *   last_state [B, H, P, N]  fp32       (written); NULL = skip
+ */
+selscan_status_t selscan_mamba2_fwd(const selscan_m2_shape_t* shape,
+                                    const void* x, const void* dt, const float* A,
+                                    const void* B, const void* C, const float* D,
+                                    const void* z, const float* dt_bias, int softplus,
+                                    void* y, float* last_state, void* stream);
+
+/* Message for the last failed call on this thread ("" after a success).
+ * The string stays valid until the next call on the same thread. */
+const char* selscan_last_error(void);
+
+/* Library version string, e.g. "libselscan 0.1 gfx950". */
+const char* selscan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SELSCAN_H */

@@ -1,0 +1,213 @@
+"""libselscan: the selective state-space scan of Mamba on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/selscan.h``.  It only
+marshals arguments: torch tensors provide device memory and the current HIP
+stream; every step of the scan runs in the HIP kernels of ``libselscan.so``.
+There is no fallback: if the library is missing the import of a kernel entry
+point raises.
+
+    y, last_state = selscan.fwd(u, delta, A, B, C, D, z, delta_bias, softplus=True)
+    y, last_state = selscan.mamba2_fwd(x, dt, A, B, C, D, z, dt_bias, softplus=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libselscan.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_LAUNCH, ERR_WORKSPACE = range(6)
+F32, BF16 = 0, 1
+
+_STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "NO_DEVICE", 4: "LAUNCH", 5: "WORKSPACE"}
+
+
+class SelscanError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libselscan {_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    """selscan_shape_t (Mamba-1)."""
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class M2Shape(ctypes.Structure):
+    """selscan_m2_shape_t (Mamba-2)."""
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+EXPORTED = ("selscan_fwd", "selscan_mamba2_fwd", "selscan_workspace_bytes", "selscan_mamba2_workspace_bytes",
+            "selscan_last_error", "selscan_version")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libselscan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m selective_state_space_25_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, fp, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+        L.selscan_fwd.argtypes = [ctypes.POINTER(Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, fp, vp]
+        L.selscan_fwd.restype = i32
+        L.selscan_mamba2_fwd.argtypes = [ctypes.POINTER(M2Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, fp, vp]
+        L.selscan_mamba2_fwd.restype = i32
+        L.selscan_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
+        L.selscan_workspace_bytes.restype = ctypes.c_size_t
+        L.selscan_mamba2_workspace_bytes.argtypes = [ctypes.POINTER(M2Shape)]
+        L.selscan_mamba2_workspace_bytes.restype = ctypes.c_size_t
+        L.selscan_last_error.restype = ctypes.c_char_p
+        L.selscan_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().selscan_version().decode()
+
+
+def last_error() -> str:
+    return lib().selscan_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise SelscanError(status, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _ptr(t, name, shape=None, dtype=None, device=None):
+    """Device pointer of a dense tensor after checking shape/dtype/device."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.data_ptr()
+
+
+def _stream_handle(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def m1_shape(batch, dim, dstate, seqlen, in_dtype=BF16, out_dtype=None, workspace=None, workspace_bytes=0):
+    return Shape(batch, dim, dstate, seqlen, in_dtype, in_dtype if out_dtype is None else out_dtype,
+                 workspace, workspace_bytes)
+
+
+def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, out=None, last_state=None,
+        return_last_state=True, workspace=None, out_dtype=None):
+    """Mamba-1 selective scan on the GPU.
+
+    u, delta, z: [batch, dim, L]; B, C: [batch, N, L] (float32 or bfloat16, one
+    dtype for all five); A: [dim, N], D, delta_bias: [dim] float32.
+    Returns (y [batch, dim, L] float32 unless out_dtype says otherwise,
+    last_state [batch, dim, N] float32 or None).  y defaults to float32, the
+    precision of the state: a bfloat16 y carries up to 2^-8 relative rounding.
+    """
+    torch = _torch()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.fwd needs tensors on a GPU device")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    dt = u.dtype
+    code = _dtype_code(u)
+    odt = (out.dtype if out is not None else torch.float32) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=odt, device=dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    s = Shape(batch, dim, N, L, code, _dtype_code(out), ws_ptr, ws_bytes)
+    args = (
+        _ptr(u, "u", (batch, dim, L), dt, dev), _ptr(delta, "delta", (batch, dim, L), dt, dev),
+        _ptr(A, "A", (dim, N), torch.float32, dev), _ptr(B, "B", (batch, N, L), dt, dev),
+        _ptr(C, "C", (batch, N, L), dt, dev), _ptr(D, "D", (dim,), torch.float32, dev),
+        _ptr(z, "z", (batch, dim, L), dt, dev), _ptr(delta_bias, "delta_bias", (dim,), torch.float32, dev),
+        int(bool(softplus)), _ptr(out, "out", (batch, dim, L), odt, dev),
+        _ptr(last_state, "last_state", (batch, dim, N), torch.float32, dev), _stream_handle(dev))
+    _check(lib().selscan_fwd(ctypes.byref(s), *args))
+    return out, last_state
+
+
+def workspace_bytes(batch, dim, dstate, seqlen, in_dtype=BF16, out_dtype=None) -> int:
+    s = m1_shape(batch, dim, dstate, seqlen, in_dtype, out_dtype)
+    return int(lib().selscan_workspace_bytes(ctypes.byref(s)))
+
+
+def mamba2_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, out=None, last_state=None,
+               return_last_state=True, workspace=None, out_dtype=None):
+    """Mamba-2 multi-head selective scan on the GPU.
+
+    x, z: [batch, L, H, P]; dt: [batch, L, H]; B, C: [batch, L, G, N]
+    (float32 or bfloat16); A, D, dt_bias: [H] float32.
+    Returns (y [batch, L, H, P] float32 unless out_dtype says otherwise,
+    last_state [batch, H, P, N] float32 or None).
+    """
+    torch = _torch()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.mamba2_fwd needs tensors on a GPU device")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dtp = x.dtype
+    odt = (out.dtype if out is not None else torch.float32) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((batch, L, H, P), dtype=odt, device=dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    s = M2Shape(batch, L, H, P, G, N, _dtype_code(x), _dtype_code(out), ws_ptr, ws_bytes)
+    args = (
+        _ptr(x, "x", (batch, L, H, P), dtp, dev), _ptr(dt, "dt", (batch, L, H), dtp, dev),
+        _ptr(A, "A", (H,), torch.float32, dev), _ptr(B, "B", (batch, L, G, N), dtp, dev),
+        _ptr(C, "C", (batch, L, G, N), dtp, dev), _ptr(D, "D", (H,), torch.float32, dev),
+        _ptr(z, "z", (batch, L, H, P), dtp, dev), _ptr(dt_bias, "dt_bias", (H,), torch.float32, dev),
+        int(bool(softplus)), _ptr(out, "out", (batch, L, H, P), odt, dev),
+        _ptr(last_state, "last_state", (batch, H, P, N), torch.float32, dev), _stream_handle(dev))
+    _check(lib().selscan_mamba2_fwd(ctypes.byref(s), *args))
+    return out, last_state
+
+
+def mamba2_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype=BF16, out_dtype=None) -> int:
+    s = M2Shape(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype,
+                in_dtype if out_dtype is None else out_dtype, None, 0)
+    return int(lib().selscan_mamba2_workspace_bytes(ctypes.byref(s)))
+
+
+__all__ = ["fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
+           "SelscanError", "Shape", "M2Shape", "m1_shape", "EXPORTED", "LIB_PATH"]

@@ -1,0 +1,59 @@
+// kernels.hpp -- argument blocks and launchers shared by the host entry
+// points and the HIP kernels (internal to libselscan; not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace selscan {
+
+// Mamba-1.  Tensors as in selscan.h; ws_* point into the workspace.
+struct M1Args {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* bias;
+    void* y;
+    float* last;
+    float* ws_state;  // [rows, G, NS] chunk end states, then carries-in
+    float* ws_w;      // [rows, G] chunk sums of Delta / ln2
+    int64_t batch, dim, L;
+    int64_t chunk;    // tokens per chunk (a multiple of 16); the last may be short
+    int N;            // d_state
+    int G;            // chunks per row
+    int softplus;
+    int vec_ok;       // every row starts 16-byte aligned (L a multiple of 16 bytes / elem)
+    int force_general;
+};
+
+int m1_padded_states(int N);
+hipError_t launch_m1(const M1Args& a, int in_bf16, int out_bf16, hipStream_t stream);
+
+// Mamba-2.
+struct M2Args {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* dt_bias;
+    void* y;
+    float* last;
+    float* ws_bc;     // [batch, L, G, 2, N] fp32 copy of B and C (interleaved per token)
+    float* ws_state;  // [batch, H, P, chunks, N] chunk end states, then carries-in
+    float* ws_w;      // [batch, H, chunks] chunk sums of Delta / ln2
+    int64_t batch, L, H, P, G, N;
+    int64_t chunk;
+    int chunks;
+    int softplus;
+};
+
+hipError_t launch_m2(const M2Args& a, int in_bf16, int out_bf16, hipStream_t stream);
+
+}  // namespace selscan

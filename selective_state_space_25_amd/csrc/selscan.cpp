@@ -1,0 +1,320 @@
+// selscan.cpp -- host side of libselscan: argument checks, launch plans,
+// workspace and error reporting behind the C ABI declared in selscan.h.
+#include "selscan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+selscan_status_t fail(selscan_status_t s, const std::string& msg) {
+    g_error = msg;
+    return s;
+}
+
+selscan_status_t ok() {
+    g_error.clear();
+    return SELSCAN_OK;
+}
+
+int64_t env_int(const char* name, int64_t dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::strtoll(v, nullptr, 10);
+}
+
+bool log_plans() { return env_int("SELSCAN_LOG", 0) != 0; }
+
+// Compute units of the current device (256 on MI355X); cached per device.
+int device_cus() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!cache[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+// Overflow-checked product of non-negative sizes; -1 on overflow.
+int64_t mul_checked(std::initializer_list<int64_t> xs) {
+    int64_t r = 1;
+    for (int64_t x : xs) {
+        if (x < 0) return -1;
+        if (x != 0 && r > INT64_MAX / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+selscan_status_t device_check() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SELSCAN_ERR_NO_DEVICE, "no HIP device available");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(SELSCAN_ERR_NO_DEVICE, "cannot query the HIP device");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(SELSCAN_ERR_NO_DEVICE, std::string("libselscan is built for gfx950, device is ") +
+                                               prop.gcnArchName);
+    return SELSCAN_OK;
+}
+
+// ----------------------------------------------------------------- Mamba-1
+struct M1Plan {
+    int G;
+    int64_t chunk;
+    int NS;
+    size_t ws_bytes;
+};
+
+selscan_status_t check_m1_shape(const selscan_shape_t* s) {
+    if (!s) return fail(SELSCAN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->batch < 1 || s->dim < 1 || s->seqlen < 1 || s->dstate < 1)
+        return fail(SELSCAN_ERR_INVALID_ARG, "batch, dim, dstate and seqlen must all be >= 1");
+    if (s->dstate > 16) return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-1 scan supports dstate <= 16");
+    if ((s->in_dtype != SELSCAN_F32 && s->in_dtype != SELSCAN_BF16) ||
+        (s->out_dtype != SELSCAN_F32 && s->out_dtype != SELSCAN_BF16))
+        return fail(SELSCAN_ERR_UNSUPPORTED, "dtypes must be SELSCAN_F32 or SELSCAN_BF16");
+    if (mul_checked({s->batch, s->dim, s->seqlen, 4}) < 0 || mul_checked({s->batch, s->dstate, s->seqlen, 4}) < 0 ||
+        mul_checked({s->batch, s->dim, 64, 4}) < 0)
+        return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
+    if (s->batch * ((s->dim + 255) / 256) > 0x7fffffff)
+        return fail(SELSCAN_ERR_UNSUPPORTED, "too many channel blocks for one launch");
+    return SELSCAN_OK;
+}
+
+M1Plan plan_m1(const selscan_shape_t* s) {
+    M1Plan p;
+    p.NS = selscan::m1_padded_states((int)s->dstate);
+    const int64_t wgs = s->batch * ((s->dim + 255) / 256);
+    int64_t G = env_int("SELSCAN_M1_CHUNKS", 0);
+    if (G <= 0) {
+        const int64_t target = (int64_t)device_cus() * 4;  // workgroups of 4 waves
+        G = (target + wgs - 1) / wgs;
+        G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 64));
+    }
+    G = std::max<int64_t>(1, std::min<int64_t>(G, (s->seqlen + 15) / 16));
+    G = std::min<int64_t>(G, 65535);
+    int64_t chunk = (s->seqlen + G - 1) / G;
+    chunk = (chunk + 15) / 16 * 16;
+    G = (s->seqlen + chunk - 1) / chunk;
+    p.G = (int)G;
+    p.chunk = chunk;
+    if (G > 1) {
+        const int64_t rows = s->batch * s->dim;
+        p.ws_bytes = align256((size_t)rows * G * p.NS * 4) + align256((size_t)rows * G * 4);
+    } else {
+        p.ws_bytes = 0;
+    }
+    return p;
+}
+
+// ----------------------------------------------------------------- Mamba-2
+struct M2Plan {
+    int chunks;
+    int64_t chunk;
+    size_t bc_bytes, state_bytes, w_bytes, ws_bytes;
+};
+
+selscan_status_t check_m2_shape(const selscan_m2_shape_t* s) {
+    if (!s) return fail(SELSCAN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->batch < 1 || s->seqlen < 1 || s->nheads < 1 || s->headdim < 1 || s->ngroups < 1 || s->dstate < 1)
+        return fail(SELSCAN_ERR_INVALID_ARG, "batch, seqlen, nheads, headdim, ngroups, dstate must be >= 1");
+    if (s->nheads % s->ngroups != 0) return fail(SELSCAN_ERR_INVALID_ARG, "nheads must be a multiple of ngroups");
+    if (s->dstate != 16 && s->dstate != 32 && s->dstate != 64 && s->dstate != 128)
+        return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-2 scan supports dstate 16, 32, 64, 128");
+    if ((s->in_dtype != SELSCAN_F32 && s->in_dtype != SELSCAN_BF16) ||
+        (s->out_dtype != SELSCAN_F32 && s->out_dtype != SELSCAN_BF16))
+        return fail(SELSCAN_ERR_UNSUPPORTED, "dtypes must be SELSCAN_F32 or SELSCAN_BF16");
+    if (mul_checked({s->batch, s->seqlen, s->nheads, s->headdim, 4}) < 0 ||
+        mul_checked({s->batch, s->seqlen, s->ngroups, s->dstate, 8}) < 0 ||
+        mul_checked({s->batch, s->nheads, s->headdim, s->dstate, 4, 1024}) < 0)
+        return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
+    if (s->batch * s->nheads * ((s->headdim + 63) / 64) > 0x7fffffff)
+        return fail(SELSCAN_ERR_UNSUPPORTED, "too many (batch, head) units for one launch");
+    return SELSCAN_OK;
+}
+
+M2Plan plan_m2(const selscan_m2_shape_t* s) {
+    M2Plan p;
+    const int64_t waves = s->batch * s->nheads * ((s->headdim + 63) / 64);
+    int64_t G = env_int("SELSCAN_M2_CHUNKS", 0);
+    if (G <= 0) {
+        const int64_t target = (int64_t)device_cus() * 8;
+        G = (target + waves - 1) / waves;
+        G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 64));
+    }
+    G = std::max<int64_t>(1, std::min<int64_t>(G, s->seqlen));
+    G = std::min<int64_t>(G, 65535);
+    int64_t chunk = (s->seqlen + G - 1) / G;
+    G = (s->seqlen + chunk - 1) / chunk;
+    p.chunks = (int)G;
+    p.chunk = chunk;
+    p.bc_bytes = align256((size_t)s->batch * s->seqlen * s->ngroups * 2 * s->dstate * 4);
+    if (G > 1) {
+        p.state_bytes = align256((size_t)s->batch * s->nheads * s->headdim * G * s->dstate * 4);
+        p.w_bytes = align256((size_t)s->batch * s->nheads * G * 4);
+    } else {
+        p.state_bytes = p.w_bytes = 0;
+    }
+    p.ws_bytes = p.bc_bytes + p.state_bytes + p.w_bytes;
+    return p;
+}
+
+// Stream-ordered scratch: the caller's workspace when given, else an
+// allocation freed on the same stream after the launches.
+struct Scratch {
+    void* ptr = nullptr;
+    bool owned = false;
+    hipStream_t stream = nullptr;
+    selscan_status_t get(void* user, size_t user_bytes, size_t need, hipStream_t st) {
+        stream = st;
+        if (need == 0) return SELSCAN_OK;
+        if (user) {
+            if (user_bytes < need)
+                return fail(SELSCAN_ERR_WORKSPACE, "workspace is smaller than the required " + std::to_string(need) +
+                                                       " bytes");
+            if ((reinterpret_cast<uintptr_t>(user) & 255) != 0)
+                return fail(SELSCAN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+            ptr = user;
+            return SELSCAN_OK;
+        }
+        if (hipMallocAsync(&ptr, need, st) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(SELSCAN_ERR_LAUNCH, "hipMallocAsync of " + std::to_string(need) + " workspace bytes failed");
+        }
+        owned = true;
+        return SELSCAN_OK;
+    }
+    void release() {
+        if (owned && ptr) (void)hipFreeAsync(ptr, stream);
+        ptr = nullptr;
+        owned = false;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* selscan_last_error(void) { return g_error.c_str(); }
+
+const char* selscan_version(void) { return "libselscan 0.1 gfx950"; }
+
+size_t selscan_workspace_bytes(const selscan_shape_t* shape) {
+    if (check_m1_shape(shape) != SELSCAN_OK) return 0;
+    return plan_m1(shape).ws_bytes;
+}
+
+size_t selscan_mamba2_workspace_bytes(const selscan_m2_shape_t* shape) {
+    if (check_m2_shape(shape) != SELSCAN_OK) return 0;
+    return plan_m2(shape).ws_bytes;
+}
+
+selscan_status_t selscan_fwd(const selscan_shape_t* s, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, int softplus, void* y, float* last_state, void* stream) {
+    try {
+        selscan_status_t st = check_m1_shape(s);
+        if (st != SELSCAN_OK) return st;
+        if (!u || !delta || !A || !B || !C || !y)
+            return fail(SELSCAN_ERR_INVALID_ARG, "u, delta, A, B, C and y must be non-NULL");
+        if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        st = device_check();
+        if (st != SELSCAN_OK) return st;
+        const M1Plan plan = plan_m1(s);
+        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        Scratch ws;
+        st = ws.get(s->workspace, s->workspace_bytes, plan.ws_bytes, hs);
+        if (st != SELSCAN_OK) return st;
+
+        const int in_bf16 = s->in_dtype == SELSCAN_BF16;
+        const int out_bf16 = s->out_dtype == SELSCAN_BF16;
+        const int64_t in_es = in_bf16 ? 2 : 4, out_es = out_bf16 ? 2 : 4;
+        selscan::M1Args a{};
+        a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+        a.y = y; a.last = last_state;
+        a.batch = s->batch; a.dim = s->dim; a.L = s->seqlen; a.N = (int)s->dstate;
+        a.G = plan.G; a.chunk = plan.chunk; a.softplus = softplus;
+        a.force_general = env_int("SELSCAN_FORCE_GENERAL", 0) != 0;
+        a.vec_ok = (s->seqlen * in_es) % 16 == 0 && (s->seqlen * out_es) % 16 == 0 && aligned16(u) &&
+                   aligned16(delta) && aligned16(y) && (!z || aligned16(z));
+        if (plan.G > 1) {
+            const int64_t rows = s->batch * s->dim;
+            a.ws_state = static_cast<float*>(ws.ptr);
+            a.ws_w = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + align256((size_t)rows * plan.G * plan.NS * 4));
+        }
+        if (log_plans())
+            std::fprintf(stderr, "[selscan] m1 B=%lld D=%lld N=%lld L=%lld chunks=%d chunk=%lld ws=%zu vec=%d\n",
+                         (long long)s->batch, (long long)s->dim, (long long)s->dstate, (long long)s->seqlen, plan.G,
+                         (long long)plan.chunk, plan.ws_bytes, a.vec_ok);
+        hipError_t e = selscan::launch_m1(a, in_bf16, out_bf16, hs);
+        ws.release();
+        if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(SELSCAN_ERR_LAUNCH, "unexpected host exception");
+    }
+}
+
+selscan_status_t selscan_mamba2_fwd(const selscan_m2_shape_t* s, const void* x, const void* dt, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    const float* dt_bias, int softplus, void* y, float* last_state, void* stream) {
+    try {
+        selscan_status_t st = check_m2_shape(s);
+        if (st != SELSCAN_OK) return st;
+        if (!x || !dt || !A || !B || !C || !y)
+            return fail(SELSCAN_ERR_INVALID_ARG, "x, dt, A, B, C and y must be non-NULL");
+        if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        st = device_check();
+        if (st != SELSCAN_OK) return st;
+        const M2Plan plan = plan_m2(s);
+        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        Scratch ws;
+        st = ws.get(s->workspace, s->workspace_bytes, plan.ws_bytes, hs);
+        if (st != SELSCAN_OK) return st;
+        selscan::M2Args a{};
+        a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.dt_bias = dt_bias;
+        a.y = y; a.last = last_state;
+        a.batch = s->batch; a.L = s->seqlen; a.H = s->nheads; a.P = s->headdim; a.G = s->ngroups; a.N = s->dstate;
+        a.chunks = plan.chunks; a.chunk = plan.chunk; a.softplus = softplus;
+        char* base = static_cast<char*>(ws.ptr);
+        a.ws_bc = reinterpret_cast<float*>(base);
+        if (plan.chunks > 1) {
+            a.ws_state = reinterpret_cast<float*>(base + plan.bc_bytes);
+            a.ws_w = reinterpret_cast<float*>(base + plan.bc_bytes + plan.state_bytes);
+        }
+        if (log_plans())
+            std::fprintf(stderr, "[selscan] m2 B=%lld L=%lld H=%lld P=%lld G=%lld N=%lld chunks=%d chunk=%lld ws=%zu\n",
+                         (long long)s->batch, (long long)s->seqlen, (long long)s->nheads, (long long)s->headdim,
+                         (long long)s->ngroups, (long long)s->dstate, plan.chunks, (long long)plan.chunk,
+                         plan.ws_bytes);
+        hipError_t e = selscan::launch_m2(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, hs);
+        ws.release();
+        if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(SELSCAN_ERR_LAUNCH, "unexpected host exception");
+    }
+}
+
+}  // extern "C"

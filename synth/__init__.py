@@ -36,13 +36,14 @@ class Workload:
     batch: int
     seqlen: int
     dstate: int
-    dtype: torch.dtype   # u/delta/z/B/C (M2: x/dt/z/B/C) and y
+    dtype: torch.dtype   # u/delta/z/B/C (M2: x/dt/z/B/C)
     dim: int = 0         # M1 channels (d_inner)
     a_kind: str = "s4d"  # M1 A initialisation
     nheads: int = 0      # M2
     headdim: int = 0     # M2
     ngroups: int = 0     # M2
     note: str = field(default="", compare=False)
+    out_dtype: torch.dtype = torch.float32   # y: fp32 (the state's precision)
 
     @property
     def updates(self) -> int:
@@ -172,12 +173,13 @@ def algorithmic_bytes(w: Workload) -> int:
     """Bytes the scan must move: every input read once, y and the final state
     written once, no intermediate state."""
     s = torch.tensor([], dtype=w.dtype).element_size()
+    so = torch.tensor([], dtype=w.out_dtype).element_size()
     if w.kind == "m1":
         elem = w.batch * w.dim * w.seqlen
-        return (elem * 4 * s + 2 * w.batch * w.dstate * w.seqlen * s
+        return (elem * (3 * s + so) + 2 * w.batch * w.dstate * w.seqlen * s
                 + (w.dim * w.dstate + 2 * w.dim) * 4 + w.batch * w.dim * w.dstate * 4)
     elem = w.batch * w.seqlen * w.nheads * w.headdim
-    return (elem * 3 * s + w.batch * w.seqlen * w.nheads * s
+    return (elem * (2 * s + so) + w.batch * w.seqlen * w.nheads * s
             + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * s + 3 * w.nheads * 4
             + w.batch * w.nheads * w.headdim * w.dstate * 4)
 

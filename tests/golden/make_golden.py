@@ -37,7 +37,7 @@ def m1_case():
 
 def m2_case():
     rng = np.random.default_rng(2025)
-    nb, nl, nh, npd, ng, nn = 1, 9, 4, 2, 2, 8
+    nb, nl, nh, npd, ng, nn = 1, 9, 4, 2, 2, 16
     x = dict(x=_f32(rng.standard_normal((nb, nl, nh, npd))), dt=_f32(rng.standard_normal((nb, nl, nh))),
              A=_f32(-rng.uniform(1, 16, nh)), B=_f32(rng.standard_normal((nb, nl, ng, nn))),
              C=_f32(rng.standard_normal((nb, nl, ng, nn))), D=_f32(rng.standard_normal(nh)),

@@ -1,0 +1,110 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/selscan.h declares, and rejects bad arguments on the host before any
+device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_25_amd as ss
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            for m in re.finditer(r"\b(selscan_[a-z0-9_]+)\s*\(", text):
+                names.add(m.group(1))
+    return names
+
+
+def test_library_is_built():
+    assert os.path.exists(ss.LIB_PATH), "run python -m selective_state_space_25_amd.build"
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared_functions()
+    assert {"selscan_fwd", "selscan_mamba2_fwd", "selscan_last_error", "selscan_version"} <= declared
+    L = ctypes.CDLL(ss.LIB_PATH)
+    missing = [n for n in sorted(declared) if not hasattr(L, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(ss.EXPORTED) <= declared
+
+
+def test_version():
+    assert "gfx950" in ss.version()
+
+
+def _m1(**kw):
+    base = dict(batch=2, dim=8, dstate=16, seqlen=32, in_dtype=ss.BF16, out_dtype=ss.BF16)
+    base.update(kw)
+    return ss.Shape(base["batch"], base["dim"], base["dstate"], base["seqlen"], base["in_dtype"],
+                    base["out_dtype"], None, 0)
+
+
+FAKE = 4096  # a non-null pointer value; never dereferenced because validation fails first
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, ss.ERR_INVALID_ARG), ("dim", -1, ss.ERR_INVALID_ARG), ("seqlen", 0, ss.ERR_INVALID_ARG),
+    ("dstate", 0, ss.ERR_INVALID_ARG), ("dstate", 17, ss.ERR_UNSUPPORTED), ("in_dtype", 7, ss.ERR_UNSUPPORTED),
+    ("seqlen", 1 << 62, ss.ERR_INVALID_ARG)])
+def test_m1_bad_shape_rejected(field, value, status):
+    s = _m1(**{field: value})
+    r = ss.lib().selscan_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE, None, None)
+    assert r == status
+    assert ss.last_error()
+
+
+def test_m1_null_pointer_rejected():
+    s = _m1()
+    r = ss.lib().selscan_fwd(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE, None, None)
+    assert r == ss.ERR_INVALID_ARG
+    assert "non-NULL" in ss.last_error()
+    r = ss.lib().selscan_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE, None, None)
+    assert r == ss.ERR_INVALID_ARG
+
+
+def test_m1_bad_softplus_flag():
+    s = _m1()
+    r = ss.lib().selscan_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 2, FAKE, None, None)
+    assert r == ss.ERR_INVALID_ARG
+
+
+def _m2(**kw):
+    base = dict(batch=1, seqlen=16, nheads=4, headdim=8, ngroups=2, dstate=16, in_dtype=ss.BF16, out_dtype=ss.BF16)
+    base.update(kw)
+    return ss.M2Shape(base["batch"], base["seqlen"], base["nheads"], base["headdim"], base["ngroups"],
+                      base["dstate"], base["in_dtype"], base["out_dtype"], None, 0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("ngroups", 3, ss.ERR_INVALID_ARG), ("nheads", 0, ss.ERR_INVALID_ARG), ("dstate", 48, ss.ERR_UNSUPPORTED),
+    ("out_dtype", 9, ss.ERR_UNSUPPORTED), ("headdim", 0, ss.ERR_INVALID_ARG)])
+def test_m2_bad_shape_rejected(field, value, status):
+    s = _m2(**{field: value})
+    r = ss.lib().selscan_mamba2_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE,
+                                    None, None)
+    assert r == status
+
+
+def test_workspace_sizes_are_consistent():
+    # a single chunk needs no workspace; a long sequence is split and needs some
+    assert ss.workspace_bytes(1, 32, 16, 64, ss.F32) == 0
+    big = ss.workspace_bytes(1, 2048, 16, 1 << 20)
+    assert big > 0 and big % 256 == 0
+    assert ss.mamba2_workspace_bytes(8, 4096, 32, 64, 1, 128) > 0
+    bad = ss.M2Shape(1, 1, 3, 1, 2, 16, 1, 1, None, 0)
+    assert ss.lib().selscan_mamba2_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    u = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        ss.fwd(u, u, torch.zeros(4, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
