@@ -19,18 +19,22 @@ struct M1Args {
     const float* bias;
     void* y;
     float* last;
-    float* ws_state;  // [rows, G, NS] chunk end states, then carries-in
+    float* ws_state;  // [rows, G, 16] chunk end states, then carries-in
     float* ws_w;      // [rows, G] chunk sums of Delta / ln2
+    float* bcq;       // [batch, 4, L, 8] fp32 copy of B and C, four states per wave
     int64_t batch, dim, L;
     int64_t chunk;    // tokens per chunk (a multiple of 16); the last may be short
     int N;            // d_state
     int G;            // chunks per row
     int softplus;
-    int vec_ok;       // every row starts 16-byte aligned (L a multiple of 16 bytes / elem)
+    int vec_ok;       // rows start aligned for 4-token vector accesses (L % 4 == 0)
     int force_general;
 };
 
 int m1_padded_states(int N);
+int m1_rows_per_block();
+int m1_waves_per_block();
+size_t m1_bc_bytes(int64_t batch, int64_t L);
 hipError_t launch_m1(const M1Args& a, int in_bf16, int out_bf16, hipStream_t stream);
 
 // Mamba-2.
@@ -54,6 +58,7 @@ struct M2Args {
     int softplus;
 };
 
+int m2_waves_per_block(int64_t N);
 hipError_t launch_m2(const M2Args& a, int in_bf16, int out_bf16, hipStream_t stream);
 
 }  // namespace selscan

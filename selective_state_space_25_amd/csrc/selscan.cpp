@@ -83,7 +83,7 @@ struct M1Plan {
     int G;
     int64_t chunk;
     int NS;
-    size_t ws_bytes;
+    size_t bc_bytes, state_bytes, w_bytes, ws_bytes;
 };
 
 selscan_status_t check_m1_shape(const selscan_shape_t* s) {
@@ -105,12 +105,15 @@ selscan_status_t check_m1_shape(const selscan_shape_t* s) {
 M1Plan plan_m1(const selscan_shape_t* s) {
     M1Plan p;
     p.NS = selscan::m1_padded_states((int)s->dstate);
-    const int64_t wgs = s->batch * ((s->dim + 255) / 256);
+    const int64_t rows_pb = selscan::m1_rows_per_block();
+    const int64_t wgs = s->batch * ((s->dim + rows_pb - 1) / rows_pb);
+    const int64_t waves_per_chunk = wgs * selscan::m1_waves_per_block();
     int64_t G = env_int("SELSCAN_M1_CHUNKS", 0);
     if (G <= 0) {
-        const int64_t target = (int64_t)device_cus() * 4;  // workgroups of 4 waves
-        G = (target + wgs - 1) / wgs;
-        G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 64));
+        // enough waves to give every SIMD of the device a few to interleave
+        const int64_t target = env_int("SELSCAN_M1_WAVES", (int64_t)device_cus() * 16);
+        G = (target + waves_per_chunk - 1) / waves_per_chunk;
+        G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 256));
     }
     G = std::max<int64_t>(1, std::min<int64_t>(G, (s->seqlen + 15) / 16));
     G = std::min<int64_t>(G, 65535);
@@ -119,12 +122,11 @@ M1Plan plan_m1(const selscan_shape_t* s) {
     G = (s->seqlen + chunk - 1) / chunk;
     p.G = (int)G;
     p.chunk = chunk;
-    if (G > 1) {
-        const int64_t rows = s->batch * s->dim;
-        p.ws_bytes = align256((size_t)rows * G * p.NS * 4) + align256((size_t)rows * G * 4);
-    } else {
-        p.ws_bytes = 0;
-    }
+    const int64_t rows = s->batch * s->dim;
+    p.bc_bytes = align256(selscan::m1_bc_bytes(s->batch, s->seqlen));
+    p.state_bytes = G > 1 ? align256((size_t)rows * G * p.NS * 4) : 0;
+    p.w_bytes = G > 1 ? align256((size_t)rows * G * 4) : 0;
+    p.ws_bytes = p.bc_bytes + p.state_bytes + p.w_bytes;
     return p;
 }
 
@@ -156,10 +158,10 @@ selscan_status_t check_m2_shape(const selscan_m2_shape_t* s) {
 
 M2Plan plan_m2(const selscan_m2_shape_t* s) {
     M2Plan p;
-    const int64_t waves = s->batch * s->nheads * ((s->headdim + 63) / 64);
+    const int64_t waves = s->batch * s->nheads * ((s->headdim + 63) / 64) * selscan::m2_waves_per_block(s->dstate);
     int64_t G = env_int("SELSCAN_M2_CHUNKS", 0);
     if (G <= 0) {
-        const int64_t target = (int64_t)device_cus() * 8;
+        const int64_t target = env_int("SELSCAN_M2_WAVES", (int64_t)device_cus() * 8);
         G = (target + waves - 1) / waves;
         G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 64));
     }
@@ -256,12 +258,14 @@ selscan_status_t selscan_fwd(const selscan_shape_t* s, const void* u, const void
         a.batch = s->batch; a.dim = s->dim; a.L = s->seqlen; a.N = (int)s->dstate;
         a.G = plan.G; a.chunk = plan.chunk; a.softplus = softplus;
         a.force_general = env_int("SELSCAN_FORCE_GENERAL", 0) != 0;
+        // 32-token runs of every row start on 16-byte boundaries
         a.vec_ok = (s->seqlen * in_es) % 16 == 0 && (s->seqlen * out_es) % 16 == 0 && aligned16(u) &&
                    aligned16(delta) && aligned16(y) && (!z || aligned16(z));
+        char* base = static_cast<char*>(ws.ptr);
+        a.bcq = reinterpret_cast<float*>(base);
         if (plan.G > 1) {
-            const int64_t rows = s->batch * s->dim;
-            a.ws_state = static_cast<float*>(ws.ptr);
-            a.ws_w = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + align256((size_t)rows * plan.G * plan.NS * 4));
+            a.ws_state = reinterpret_cast<float*>(base + plan.bc_bytes);
+            a.ws_w = reinterpret_cast<float*>(base + plan.bc_bytes + plan.state_bytes);
         }
         if (log_plans())
             std::fprintf(stderr, "[selscan] m1 B=%lld D=%lld N=%lld L=%lld chunks=%d chunk=%lld ws=%zu vec=%d\n",

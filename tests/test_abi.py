@@ -94,10 +94,12 @@ def test_m2_bad_shape_rejected(field, value, status):
 
 
 def test_workspace_sizes_are_consistent():
-    # a single chunk needs no workspace; a long sequence is split and needs some
-    assert ss.workspace_bytes(1, 32, 16, 64, ss.F32) == 0
+    # the fp32 copy of B and C is always needed; a long sequence is split
+    # into chunks and needs room for the chunk states too
+    small = ss.workspace_bytes(1, 32, 16, 64, ss.F32)
+    assert small > 0 and small % 256 == 0
     big = ss.workspace_bytes(1, 2048, 16, 1 << 20)
-    assert big > 0 and big % 256 == 0
+    assert big > 2 * (1 << 20) * 16 * 4 and big % 256 == 0
     assert ss.mamba2_workspace_bytes(8, 4096, 32, 64, 1, 128) > 0
     bad = ss.M2Shape(1, 1, 3, 1, 2, 16, 1, 1, None, 0)
     assert ss.lib().selscan_mamba2_workspace_bytes(ctypes.byref(bad)) == 0

@@ -121,7 +121,11 @@ def test_causality_bitwise(gpu, monkeypatch, name):
 
 
 @pytest.mark.parametrize("general", [False, True])
-def test_zero_delta_window_freezes_state_bitwise(gpu, monkeypatch, general):
+def test_zero_delta_window_freezes_state(gpu, monkeypatch, general):
+    """Delta = 0 on a window leaves the state unchanged.  Bitwise on the
+    general decay path (exp(0 A) = 1 and a zero input term are exact); the
+    structured path renormalises its state by sigma = Delta u / ln2 around
+    the window, which can round, so there it holds to a few ulp."""
     monkeypatch.setenv("SELSCAN_M1_CHUNKS", "1")
     if general:
         monkeypatch.setenv("SELSCAN_FORCE_GENERAL", "1")
@@ -132,7 +136,10 @@ def test_zero_delta_window_freezes_state_bitwise(gpu, monkeypatch, general):
     cut = lambda L: {k: (v[..., :L].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in inp.items()}
     _, l1 = _run(cut(t1), softplus=False)
     _, l2 = _run(cut(t2), softplus=False)
-    assert torch.equal(l1, l2)
+    if general:
+        assert torch.equal(l1, l2)
+    else:
+        check_close(host(l2).numpy(), host(l1).numpy(), (1e-7, 4e-7), "state across the window")
 
 
 def test_deterministic(gpu):
