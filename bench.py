@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--profile", action="store_true",
                    help="only warm up and run the timed steps of --workload (for rocprofv3)")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--copy-gib", type=float, default=0.0,
+                   help="with --profile: also run a plain copy of this many GiB and a half-line "
+                        "strided read of the same size (known bytes, to calibrate HBM byte counters)")
     return p.parse_args()
 
 
@@ -51,7 +54,41 @@ def _call(ss, w, inp, out):
                          softplus=True, out=out[0], last_state=out[1])
 
 
-def time_workload(name, steps, warmup, seed, device):
+def _outputs(w, device):
+    import torch
+    if w.kind == "m1":
+        y = torch.empty((w.batch, w.dim, w.seqlen), dtype=w.out_dtype, device=device)
+        last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=device)
+    else:
+        y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=w.out_dtype, device=device)
+        last = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=device)
+    return y, last
+
+
+def _timed(ss, w, inps, outs, steps, stream):
+    """Time `steps` calls back to back with events on the kernels' stream."""
+    import torch
+    copies = len(inps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        _call(ss, w, inps[i % copies], outs[i % copies])
+        ev[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end), sorted(a.elapsed_time(b) for a, b in ev), wall
+
+
+def time_workload(name, steps, warmup, seed, device, kernel_timing=True):
+    """Region 1: `steps` plain calls (throughput).  Region 2: the same number
+    of calls with every kernel bracketed by HIP events on the launch stream
+    (per-kernel durations for the roofline of the dominant kernel)."""
     import torch
     import selective_state_space_25_amd as ss
     import synth
@@ -60,36 +97,13 @@ def time_workload(name, steps, warmup, seed, device):
     nbytes = synth.algorithmic_bytes(w)
     copies = 1 if nbytes >= (1 << 30) else max(2, int((1 << 30) // max(nbytes, 1)) + 1)
     copies = min(copies, 8)
-    inps, outs = [], []
-    for c in range(copies):
-        inp = synth.workload_inputs(w, seed=seed + c, device=device)
-        inps.append(inp)
-        if w.kind == "m1":
-            y = torch.empty((w.batch, w.dim, w.seqlen), dtype=w.out_dtype, device=device)
-            last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=device)
-        else:
-            y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=w.out_dtype, device=device)
-            last = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=device)
-        outs.append((y, last))
+    inps = [synth.workload_inputs(w, seed=seed + c, device=device) for c in range(copies)]
+    outs = [_outputs(w, device) for _ in range(copies)]
     stream = torch.cuda.current_stream(device)
     for i in range(warmup):
         _call(ss, w, inps[i % copies], outs[i % copies])
     torch.cuda.synchronize(device)
-    # per-call events on the stream the kernels run on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        _call(ss, w, inps[i % copies], outs[i % copies])
-        ev[i][1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize(device)
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    per_call = sorted(a.elapsed_time(b) for a, b in ev)
+    total_ms, per_call, wall = _timed(ss, w, inps, outs, steps, stream)
     avg_call = sum(per_call) / len(per_call)
     ms_per_step = total_ms / steps
     res = {
@@ -98,44 +112,89 @@ def time_workload(name, steps, warmup, seed, device):
         "min_call_ms": per_call[0], "wall_s": wall, "steps": steps, "rotating_copies": copies,
         "updates_per_step": w.updates, "algorithmic_bytes": nbytes,
         "state_updates_per_s": w.updates / (ms_per_step * 1e-3),
-        "hbm_gbs": nbytes / (avg_call * 1e-3) / 1e9,
+        "hbm_gbs": nbytes / (ms_per_step * 1e-3) / 1e9,
     }
     res["hbm_frac_of_peak"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    if kernel_timing:
+        ss.timing_collect()
+        ss.timing_enable(True)
+        try:
+            _timed(ss, w, inps, outs, steps, stream)
+        finally:
+            ss.timing_enable(False)
+        res["kernels"] = ss.timing_collect()
     del inps, outs
     torch.cuda.empty_cache()
     return w, res
 
 
-def cpu_baseline(name, seed, budget_s=12.0):
-    """The fp64 oracle on this host's cores, on the same workload: whole
-    (batch, channel) rows of the workload's inputs, as many as fit in the time
-    budget (all of them for the small workloads)."""
+def dominant_kernel(res):
+    name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["total_ms"])
+    return name, k
+
+
+def read_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel's
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = kv.get("source")
+    if not src or "source_sha256" not in kv or "hbm_bytes_per_launch" not in kv:
+        return None
+    spath = os.path.join(os.path.dirname(os.path.abspath(__file__)), src)
+    if not os.path.exists(spath) or hashlib.sha256(open(spath, "rb").read()).hexdigest() != kv["source_sha256"]:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(name, seed, min_s=10.0, max_s=30.0):
+    """The fp64 oracle on this host's cores, on the same workload.  The
+    whole workload is repeated until at least `min_s` seconds of oracle time
+    have run; when one pass takes longer than `max_s`, a prefix of the
+    (batch, channel) rows is used instead."""
     import numpy as np
-    import torch
     import synth
     import oracle
 
     cores = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        cores = min(cores, int(env))
     oracle.set_threads(cores)
     w = synth.WORKLOADS[name]
     if w.kind != "m1":
         raise ValueError("cpu baseline implemented for Mamba-1 workloads")
-    # rows processed per batch element; grow until the budget is used
-    inp = synth.m1_inputs(1, w.dim, w.dstate, w.seqlen, w.dtype, w.a_kind, seed=seed, device="cpu")
-    rows_total = w.batch * w.dim
-    done_rows, elapsed, calls = 0, 0.0, 0
-    t_start = time.perf_counter()
-    while done_rows < rows_total and elapsed < budget_s:
+    inp = synth.m1_inputs(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.a_kind, seed=seed, device="cpu")
+    f64 = {k: (None if v is None else np.ascontiguousarray(v.double().numpy())) for k, v in inp.items()}
+
+    def one(rows_b):
         t = time.perf_counter()
-        oracle.m1(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"])
-        elapsed += time.perf_counter() - t
-        done_rows += w.dim
-        calls += 1
-    _ = np, torch, t_start
-    upd = done_rows * w.seqlen * w.dstate
+        oracle.m1(f64["u"][:rows_b], f64["delta"][:rows_b], f64["A"], f64["B"][:rows_b], f64["C"][:rows_b],
+                  f64["D"], f64["z"][:rows_b], f64["delta_bias"])
+        return time.perf_counter() - t
+
+    # probe with one batch element, then size the sample
+    t1 = one(1)
+    per_pass = t1 * w.batch
+    rows_b = w.batch if per_pass <= max_s else max(1, int(max_s / t1))
+    passes, elapsed = 0, 0.0
+    while elapsed < min_s or passes == 0:
+        elapsed += one(rows_b)
+        passes += 1
+    upd = passes * rows_b * w.dim * w.seqlen * w.dstate
     return {"value": upd / elapsed, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done_rows} of {rows_total} (batch, channel) rows of {name}, full L={w.seqlen}, "
-                      f"N={w.dstate}, fp64, {calls} oracle call(s), {elapsed:.2f} s",
+            "sample": f"{passes} pass(es) over {rows_b} of {w.batch} batch elements of {name} "
+                      f"({rows_b * w.dim} (batch, channel) rows, full L={w.seqlen}, N={w.dstate}), "
+                      f"fp64 with {cores} OpenMP threads, {elapsed:.1f} s of oracle time",
             "seconds": elapsed}
 
 
@@ -153,15 +212,42 @@ def main():
     import selective_state_space_25_amd as ss
     ss.lib()  # fail loudly if the HIP library is missing
 
-    w, head = time_workload(args.workload, args.steps, args.warmup, args.seed, device)
+    w, head = time_workload(args.workload, args.steps, args.warmup, args.seed, device,
+                            kernel_timing=not args.profile)
     if args.profile:
+        if args.copy_gib > 0:
+            # calibration of the HBM byte counters: a plain copy (torch.neg
+            # over fp32, reads and writes copy_gib GiB) and a read of the first
+            # 64 bytes of every 128-byte line of a copy_gib GiB bf16 buffer
+            n = int(args.copy_gib * (1 << 30)) // 4
+            src = torch.ones(n, dtype=torch.float32, device=device)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.neg(src, out=dst)
+            del src, dst
+            xb = torch.ones(n * 4 // 128, 64, dtype=torch.bfloat16, device=device)
+            for _ in range(3):
+                half = xb[:, :32].contiguous()
+            del xb, half
+            torch.cuda.synchronize(device)
+            head["copy_calibration_bytes_each_way"] = n * 4
         print(json.dumps(head))
         return
     extras = {}
     for name in [e for e in args.extra.split(",") if e and e != args.workload]:
         _, r = time_workload(name, max(3, min(args.steps, 20)), 2, args.seed, device)
+        kn, kk = dominant_kernel(r)
+        r["dominant_kernel"] = {"name": kn, "avg_ms": kk["avg_ms"],
+                                "gbs": r["algorithmic_bytes"] / (kk["avg_ms"] * 1e-3) / 1e9,
+                                "traffic": read_traffic(name, kn)}
         extras[name] = r
 
+    kname, k = dominant_kernel(head)
+    avg_ms = k["avg_ms"]
+    # the dominant (output) kernel reads every input once and writes y and
+    # the final state: its algorithmic bytes per launch are the method's
+    achieved = head["algorithmic_bytes"] / (avg_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload, kname)
     line = {
         "metric": "selective-scan state-updates/s (B*L*D*N)",
         "value": head["state_updates_per_s"],
@@ -181,10 +267,10 @@ def main():
                    "parallelism": "single GPU"},
         "hbm_gbs": head["hbm_gbs"],
         "hbm_frac_of_peak": head["hbm_frac_of_peak"],
-        "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["hbm_frac_of_peak"], "traffic": None,
-                     "kernel": "selscan_fwd (all kernels of one call)",
-                     "avg_launch_ms": head["avg_call_ms"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": kname, "avg_launch_ms": avg_ms, "launches": k["launches"],
+                     "bytes_per_launch": head["algorithmic_bytes"]},
         "workloads": {args.workload: head, **extras},
         "library": ss.version(),
     }

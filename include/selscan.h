@@ -149,6 +149,27 @@ const char* selscan_last_error(void);
 /* Library version string, e.g. "libselscan 0.1 gfx950". */
 const char* selscan_version(void);
 
+/* ---- Kernel timing (instrumentation for benchmarks) ---------------------
+ * selscan_timing_enable(1) makes every later kernel launch of the entry
+ * points, on any thread, record a HIP event before and after the kernel on
+ * the call's own stream.  selscan_timing_collect waits for all events
+ * recorded so far, writes at most max_entries per-kernel aggregates to `out`
+ * (host memory owned by the caller; `name` points to a static string of the
+ * library) in order of first launch, forgets those events and returns the
+ * number of distinct kernels (which may exceed max_entries), or a negative
+ * value on a bad argument (-1) or an event failure (-2).  Enabling adds two
+ * event records per launch to the stream; leave it off for end-to-end
+ * timing.  selscan_timing_enable returns SELSCAN_ERR_INVALID_ARG for values
+ * other than 0 and 1. */
+typedef struct {
+    const char* name;   /* e.g. "m1_scan_output" */
+    int64_t launches;
+    double total_ms, min_ms, max_ms;
+} selscan_kernel_time_t;
+
+selscan_status_t selscan_timing_enable(int on);
+int selscan_timing_collect(selscan_kernel_time_t* out, int max_entries);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,7 +47,12 @@ class M2Shape(ctypes.Structure):
 _lib = None
 
 EXPORTED = ("selscan_fwd", "selscan_mamba2_fwd", "selscan_workspace_bytes", "selscan_mamba2_workspace_bytes",
-            "selscan_last_error", "selscan_version")
+            "selscan_last_error", "selscan_version", "selscan_timing_enable", "selscan_timing_collect")
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("min_ms", ctypes.c_double), ("max_ms", ctypes.c_double)]
 
 
 def lib() -> ctypes.CDLL:
@@ -69,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.selscan_mamba2_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_last_error.restype = ctypes.c_char_p
         L.selscan_version.restype = ctypes.c_char_p
+        L.selscan_timing_enable.argtypes = [i32]
+        L.selscan_timing_enable.restype = i32
+        L.selscan_timing_collect.argtypes = [ctypes.POINTER(KernelTime), i32]
+        L.selscan_timing_collect.restype = i32
         _lib = L
     return _lib
 
@@ -209,5 +218,25 @@ def mamba2_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, in_d
     return int(lib().selscan_mamba2_workspace_bytes(ctypes.byref(s)))
 
 
-__all__ = ["fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
+def timing_enable(on: bool) -> None:
+    """Bracket every later kernel launch with HIP events on its own stream."""
+    _check(lib().selscan_timing_enable(int(bool(on))))
+
+
+def timing_collect() -> dict:
+    """Wait for the bracketed launches so far; {kernel: {launches, total_ms,
+    avg_ms, min_ms, max_ms}} in order of first launch."""
+    cap = 32
+    buf = (KernelTime * cap)()
+    n = lib().selscan_timing_collect(buf, cap)
+    if n < 0:
+        raise SelscanError(n, "selscan_timing_collect failed")
+    res = {}
+    for k in buf[:min(n, cap)]:
+        res[k.name.decode()] = {"launches": k.launches, "total_ms": k.total_ms,
+                                "avg_ms": k.total_ms / max(k.launches, 1), "min_ms": k.min_ms, "max_ms": k.max_ms}
+    return res
+
+
+__all__ = ["timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
            "SelscanError", "Shape", "M2Shape", "m1_shape", "EXPORTED", "LIB_PATH"]

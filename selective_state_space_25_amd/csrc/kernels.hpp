@@ -7,6 +7,15 @@
 
 namespace selscan {
 
+// Per-kernel timing bracket (no-op unless selscan_timing_enable(1)).
+void ktime_mark(const char* kernel, hipStream_t stream, bool begin);
+struct KTime {
+    const char* name;
+    hipStream_t stream;
+    KTime(const char* n, hipStream_t s) : name(n), stream(s) { ktime_mark(name, stream, true); }
+    ~KTime() { ktime_mark(name, stream, false); }
+};
+
 // Mamba-1.  Tensors as in selscan.h; ws_* point into the workspace.
 struct M1Args {
     const void* u;

@@ -363,15 +363,23 @@ __global__ __launch_bounds__(256) void m1_carry_kernel(M1Args a) {
 template <typename Tin, typename Tout>
 hipError_t launch_dt(const M1Args& a, hipStream_t stream) {
     const int64_t bc_blocks = std::min<int64_t>((a.batch * a.L + 255) / 256, 16384);
-    hipLaunchKernelGGL((m1_bc_kernel<Tin>), dim3((unsigned)bc_blocks), dim3(256), 0, stream, a);
+    {
+        KTime kt("m1_bc_convert", stream);
+        hipLaunchKernelGGL((m1_bc_kernel<Tin>), dim3((unsigned)bc_blocks), dim3(256), 0, stream, a);
+    }
     const int64_t blocks_per_batch = (a.dim + kRows - 1) / kRows;
     const unsigned gx = (unsigned)(blocks_per_batch * a.batch);
     if (a.G > 1) {
-        hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 1>), dim3(gx, (unsigned)(a.G - 1)), dim3(kRows), 0, stream,
-                           a);
+        {
+            KTime kt("m1_scan_summary", stream);
+            hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 1>), dim3(gx, (unsigned)(a.G - 1)), dim3(kRows), 0,
+                               stream, a);
+        }
         const int64_t threads = a.batch * a.dim * kNS;
+        KTime kt("m1_chunk_carry", stream);
         hipLaunchKernelGGL(m1_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
     }
+    KTime kt("m1_scan_output", stream);
     hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 0>), dim3(gx, (unsigned)a.G), dim3(kRows), 0, stream, a);
     return hipGetLastError();
 }

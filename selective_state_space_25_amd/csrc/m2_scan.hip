@@ -327,15 +327,23 @@ hipError_t launch_n(const M2Args& a, hipStream_t stream) {
     constexpr int threads = kP * (N / kSPW);
     const int64_t total = a.batch * a.L * a.G * a.N;
     const int64_t cblocks = std::min<int64_t>((total + 255) / 256, 65536);
-    hipLaunchKernelGGL((m2_bc_convert_kernel<Tin>), dim3((unsigned)cblocks), dim3(256), 0, stream, a);
+    {
+        KTime kt("m2_bc_convert", stream);
+        hipLaunchKernelGGL((m2_bc_convert_kernel<Tin>), dim3((unsigned)cblocks), dim3(256), 0, stream, a);
+    }
     const int64_t pblocks = (a.P + kP - 1) / kP;
     const unsigned gx = (unsigned)(a.batch * a.H * pblocks);
     if (a.chunks > 1) {
-        hipLaunchKernelGGL((m2_scan_kernel<Tin, Tout, N, 1>), dim3(gx, (unsigned)(a.chunks - 1)), dim3(threads), 0,
-                           stream, a);
+        {
+            KTime kt("m2_scan_summary", stream);
+            hipLaunchKernelGGL((m2_scan_kernel<Tin, Tout, N, 1>), dim3(gx, (unsigned)(a.chunks - 1)), dim3(threads),
+                               0, stream, a);
+        }
         const int64_t nthreads = a.batch * a.H * a.P * a.N;
+        KTime kt("m2_chunk_carry", stream);
         hipLaunchKernelGGL(m2_carry_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream, a);
     }
+    KTime kt("m2_scan_output", stream);
     hipLaunchKernelGGL((m2_scan_kernel<Tin, Tout, N, 0>), dim3(gx, (unsigned)a.chunks), dim3(threads), 0, stream, a);
     return hipGetLastError();
 }
