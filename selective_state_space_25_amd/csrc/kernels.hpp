@@ -30,17 +30,20 @@ struct M1Args {
     float* last;
     float* ws_state;  // [rows, G, 16] chunk end states, then carries-in
     float* ws_w;      // [rows, G] chunk sums of Delta / ln2
-    float* bcq;       // [batch, 4, L, 8] fp32 copy of B and C, four states per wave
+    float* bcq;       // [batch, L, 32] fp32 copy of B and C (B0..B15, C0..C15 per token)
     int64_t batch, dim, L;
-    int64_t chunk;    // tokens per chunk (a multiple of 16); the last may be short
+    int64_t chunk;    // tokens per chunk (a multiple of m1_chunk_align()); the last may be short
     int N;            // d_state
     int G;            // chunks per row
     int softplus;
-    int vec_ok;       // rows start aligned for 4-token vector accesses (L % 4 == 0)
+    int vec_ok;       // rows of u, delta, z, y start on 16-byte boundaries (tile path)
     int force_general;
+    int xcd_chunks;   // G is a multiple of 8 and chunk g runs on XCD g % 8 (1-D grid)
 };
 
 int m1_padded_states(int N);
+int m1_chunk_align();
+int m1_resident_waves_per_cu(int in_bf16);
 int m1_rows_per_block();
 int m1_waves_per_block();
 size_t m1_bc_bytes(int64_t batch, int64_t L);

@@ -13,11 +13,16 @@
 // order.  All lanes of the wave read the same B_t and C_t, so they come from
 // an fp32 copy laid out [batch][token][B0..B15, C0..C15] through scalar loads
 // (the next token's are requested while the current one is computed) and
-// enter the FMAs as SGPR operands: the sweep needs no LDS and no barrier.
-// u, delta and z arrive as 32-token runs per lane (64 contiguous bytes per
-// row for bf16, whole memory sectors), the next run requested before the
-// current one is processed and converted only when used.  y is written as
-// contiguous 16-byte pieces per lane.
+// enter the FMAs as SGPR operands.
+//
+// Memory traffic moves whole 128-byte lines.  u, delta and z arrive in tiles
+// of one line per row and tensor (64 bf16 or 32 fp32 tokens), copied by the
+// memory system straight into LDS (global_load_lds_dwordx4: every lane fetches
+// eight 16-byte pieces of its own row, all eight pieces of a line in one
+// burst).  The next tile is requested as soon as the last 8-token block of the
+// current one has been read out of LDS, so its latency overlaps that block's
+// arithmetic.  y collects 32 tokens per lane in registers (128 bytes of fp32
+// per row) and leaves as one burst of 16-byte stores covering whole lines.
 //
 // Long sequences are cut into G chunks so that enough waves exist to fill
 // the 256 CUs: a summary pass computes, per chunk, the end state from a zero
@@ -31,14 +36,13 @@
 //    S4D-real initialisation -(n+1), also when scaled per channel): then
 //    exp(Delta A[n]) = r^(n+1), r = 2^(w A[d,0]): one exp per token, one
 //    multiply per update.  This path also keeps the state divided by
-//    sigma_t = Delta_t u_t / ln2 (k = h / (ln2 sigma)), which makes the input
-//    term Delta B u equal to B itself:
-//        k_t[n] = (sigma_{t-1} / sigma_t) r^(n+1) k_{t-1}[n] + B_t[n]
-//        y_t    = (sigma_t sum_n C_t[n] k_t[n] + D u_t / ln2) * ln2 * silu(z_t)
-//    A token where some lane's sigma_t is zero, tiny, huge or not finite
-//    takes the general form of the update for that token (sigma kept from the
-//    previous token and B scaled by sigma_t / sigma_kept), so zeros, NaN and
-//    Inf behave as in the plain recurrence.
+//    Delta_t u_t = ln2 s_t (s = w u), which makes the input term equal to B:
+//        k_t[n] = (s_{t-1} / s_t) r^(n+1) k_{t-1}[n] + B_t[n]
+//        y_t    = (s_t sum_n C_t[n] k_t[n] + D u_t / ln2) * ln2 * silu(z_t)
+//    An 8-token block where some lane's s_t is zero, tiny, huge or not finite
+//    takes the general form of the update token by token (s kept from the
+//    last good token and B scaled by s_t / s_kept), so zeros, NaN and Inf
+//    behave as in the plain recurrence.
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -48,14 +52,22 @@ namespace {
 
 constexpr int kRows = 64;       // channels per workgroup = lanes of the wave
 constexpr int kNS = 16;         // states per channel (padded)
-constexpr int kT = 32;          // tokens per tile
+constexpr int kBlk = 8;         // tokens per block (one 16-byte piece of bf16)
+constexpr int kTile = 32;       // tokens per tile = tokens per y burst (128 bytes of fp32 y per row)
+constexpr int kChunkAlign = 32; // chunk starts are multiples of a tile
 constexpr float kSigLo = 8.673617379884035e-19f;   // 2^-60
 constexpr float kSigHi = 1.152921504606847e18f;    // 2^60
 
 typedef __attribute__((address_space(4))) const float* cfptr;
+typedef __attribute__((address_space(3))) void* ldsptr;
 
 // lgkmcnt(0), vmcnt and expcnt left at their maxima
-__device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// vmcnt(0), the others left at their maxima
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
 
@@ -67,45 +79,40 @@ __device__ __forceinline__ const float* uniform_ptr(const float* p) {
     return reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
 }
 
-template <typename T> struct Tok;
-template <> struct Tok<float> {
-    static constexpr int kWords = kT;        // 32-bit words per 32-token run
+// Input element types: tokens per tile (one line per row), words per block.
+template <typename T> struct In;
+template <> struct In<float> {
+    static constexpr int kPieces = 8;         // 16-byte pieces per row per tile
+    static constexpr int kWords = kBlk;       // 32-bit words per 8-token block
     static __device__ __forceinline__ float get(const uint32_t* w, int j) { return __uint_as_float(w[j]); }
     static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
 };
-template <> struct Tok<uint16_t> {
-    static constexpr int kWords = kT / 2;
+template <> struct In<uint16_t> {
+    static constexpr int kPieces = 4;
+    static constexpr int kWords = kBlk / 2;
     static __device__ __forceinline__ float get(const uint32_t* w, int j) {
         return (j & 1) ? bf16hi(w[j >> 1]) : bf16lo(w[j >> 1]);
     }
     static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 };
 
-// One 32-token run of one row as raw words.
-template <typename T>
-struct Run {
-    uint32_t w[Tok<T>::kWords];
-    __device__ __forceinline__ void load_vec(const T* p) {
-        const uint4* q = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-        for (int i = 0; i < Tok<T>::kWords / 4; ++i) {
-            const uint4 x = q[i];
-            w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
-        }
-    }
-    __device__ __forceinline__ float operator[](int j) const { return Tok<T>::get(w, j); }
-};
-
+// y stores: a whole 32-token burst, or one token.
 template <typename T> struct Out;
 template <> struct Out<float> {
-    static __device__ __forceinline__ void st4(float* p, const float* v) {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    static __device__ __forceinline__ void burst(float* p, const float* v) {
+        float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+        for (int i = 0; i < kTile / 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
     }
     static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
 };
 template <> struct Out<uint16_t> {
-    static __device__ __forceinline__ void st4(uint16_t* p, const float* v) {
-        *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    static __device__ __forceinline__ void burst(uint16_t* p, const float* v) {
+        uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+        for (int i = 0; i < kTile / 8; ++i)
+            q[i] = make_uint4(pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
+                              pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
     }
     static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
@@ -114,73 +121,181 @@ template <> struct Out<uint16_t> {
 struct Lane {
     float k[kNS];
     float Ar[kNS];
-    float A0, bias_l, Dv, Dp;
-    float sig_prev;   // structured path: h = ln2 * sig_prev * k
+    float A0, bias_l, Dp;
+    float s_prev;     // structured path: h = ln2 * s_prev * k
     float wsum;       // summary pass: sum of w over the chunk
 };
 
-// One token of the sweep.  bc holds the token's B (bc[0..16)) and C
-// (bc[16..32)).  Returns the read-out before the gate (output pass).
-template <int MODE, bool STRUCT>
-__device__ __forceinline__ float token(Lane& L, const float* bc, float uu, float dl, int softplus) {
+template <bool SP>
+__device__ __forceinline__ float delta_log2(const Lane& L, float dl) {
     const float vl = __builtin_fmaf(dl, kLog2e, L.bias_l);
-    const float w = softplus ? softplus_log2(vl) : vl;
-    if (MODE == 1) L.wsum += w;
+    return SP ? softplus_log2(vl) : vl;
+}
+
+__device__ __forceinline__ bool s_in_range(float s) { return fabsf(s) >= kSigLo && fabsf(s) <= kSigHi; }
+
+// Structured path, every lane's s in range.  Returns the read-out / ln2.
+template <int MODE>
+__device__ __forceinline__ float tok_fast(Lane& L, const float* bc, float w, float s, float uu) {
+    const float r = fast_exp2(w * L.A0);
+    float q = L.s_prev * fast_rcp(s) * r;
     float acc0 = 0.0f, acc1 = 0.0f;
-    if constexpr (STRUCT) {
-        const float sig = w * uu;
-        const float r = fast_exp2(w * L.A0);
-        const bool ok = fabsf(sig) >= kSigLo && fabsf(sig) <= kSigHi;
-        if (wave_all(ok)) {
-            float q = L.sig_prev * fast_rcp(sig) * r;
 #pragma unroll
-            for (int n = 0; n < kNS; n += 2) {
-                L.k[n] = __builtin_fmaf(q, L.k[n], bc[n]);
-                q *= r;
-                L.k[n + 1] = __builtin_fmaf(q, L.k[n + 1], bc[n + 1]);
-                q *= r;
-                if (MODE == 0) {
-                    acc0 = __builtin_fmaf(bc[kNS + n], L.k[n], acc0);
-                    acc1 = __builtin_fmaf(bc[kNS + n + 1], L.k[n + 1], acc1);
-                }
-            }
-            L.sig_prev = sig;
-        } else {
-            const float sig_new = ok ? sig : L.sig_prev;
-            const float c = sig / sig_new;
-            float q = (L.sig_prev / sig_new) * r;
-#pragma unroll
-            for (int n = 0; n < kNS; ++n) {
-                L.k[n] = __builtin_fmaf(q, L.k[n], c * bc[n]);
-                q *= r;
-                if (MODE == 0) acc0 = __builtin_fmaf(bc[kNS + n], L.k[n], acc0);
-            }
-            L.sig_prev = sig_new;
+    for (int n = 0; n < kNS; n += 2) {
+        L.k[n] = __builtin_fmaf(q, L.k[n], bc[n]);
+        q *= r;
+        L.k[n + 1] = __builtin_fmaf(q, L.k[n + 1], bc[n + 1]);
+        q *= r;
+        if (MODE == 0) {
+            acc0 = __builtin_fmaf(bc[kNS + n], L.k[n], acc0);
+            acc1 = __builtin_fmaf(bc[kNS + n + 1], L.k[n + 1], acc1);
         }
-        if (MODE == 0) return __builtin_fmaf(L.sig_prev, acc0 + acc1, L.Dp * uu);
-        return 0.0f;
+    }
+    L.s_prev = s;
+    if (MODE == 1) L.wsum += w;
+    return MODE == 0 ? __builtin_fmaf(s, acc0 + acc1, L.Dp * uu) : 0.0f;
+}
+
+// Structured path, any s: lanes with s out of range keep their scale.
+template <int MODE>
+__device__ __forceinline__ float tok_slow(Lane& L, const float* bc, float w, float s, float uu) {
+    const float r = fast_exp2(w * L.A0);
+    const float s_new = s_in_range(s) ? s : L.s_prev;
+    const float c = s / s_new;
+    float q = (L.s_prev / s_new) * r;
+    float acc = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kNS; ++n) {
+        L.k[n] = __builtin_fmaf(q, L.k[n], c * bc[n]);
+        q *= r;
+        if (MODE == 0) acc = __builtin_fmaf(bc[kNS + n], L.k[n], acc);
+    }
+    L.s_prev = s_new;
+    if (MODE == 1) L.wsum += w;
+    return MODE == 0 ? __builtin_fmaf(s_new, acc, L.Dp * uu) : 0.0f;
+}
+
+// General A: one exp per update; the state is h itself.
+template <int MODE>
+__device__ __forceinline__ float tok_general(Lane& L, const float* bc, float w, float uu) {
+    const float x = (w * kLn2) * uu;   // Delta u
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kNS; n += 2) {
+        const float dA0 = fast_exp2(w * L.Ar[n]);
+        const float dA1 = fast_exp2(w * L.Ar[n + 1]);
+        L.k[n] = __builtin_fmaf(dA0, L.k[n], x * bc[n]);
+        L.k[n + 1] = __builtin_fmaf(dA1, L.k[n + 1], x * bc[n + 1]);
+        if (MODE == 0) {
+            acc0 = __builtin_fmaf(bc[kNS + n], L.k[n], acc0);
+            acc1 = __builtin_fmaf(bc[kNS + n + 1], L.k[n + 1], acc1);
+        }
+    }
+    if (MODE == 1) L.wsum += w;
+    return MODE == 0 ? __builtin_fmaf(L.Dp, uu, acc0 + acc1) : 0.0f;
+}
+
+template <int MODE>
+__device__ __forceinline__ void load_bc(float* dst, cfptr p) {
+    constexpr int n = MODE == 0 ? 2 * kNS : kNS;
+#pragma unroll
+    for (int e = 0; e < n; ++e) dst[e] = p[e];
+}
+
+// LDS image of one 32-token tile: [tensor][piece][lane] 16-byte pieces (4 per
+// row for bf16, 8 for fp32).  Tensor 0 u, 1 delta, 2 z (output pass only).
+// The tile's B/C records follow at bc_base.  `lds_base` is the LDS byte address of the
+// image.  The instruction offset moves both the global and the LDS address,
+// so M0 is set 16 p bytes short of piece p's slot.
+template <int P>
+__device__ __forceinline__ void dma_piece(const void* g, uint32_t slot) {
+    __builtin_amdgcn_global_load_lds(g, (ldsptr)(uintptr_t)(slot - 16 * P), 16, 16 * P, 0);
+}
+
+// 16 bytes per lane from g + OFF into LDS at slot + 16 * lane.
+template <int OFF>
+__device__ __forceinline__ void dma_at(const void* g, uint32_t slot) {
+    __builtin_amdgcn_global_load_lds(g, (ldsptr)(uintptr_t)(slot - OFF), 16, OFF, 0);
+}
+
+// B/C records of a tile in LDS: record j (32 floats, output pass) or its B
+// half (16 floats, summary pass) at bc_base + j * kRec<MODE> bytes.
+template <int MODE> constexpr int kRec = MODE == 0 ? 128 : 64;
+
+template <typename Tin, int NT, int MODE>
+__device__ __forceinline__ void issue_tile(const Tin* const* rowp, const float* bcb, int64_t t0, uint32_t lds_base,
+                                           uint32_t bc_base) {
+    constexpr int NP = In<Tin>::kPieces;
+    constexpr uint32_t kPiece = kRows * 16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const void* g = rowp[t] + t0;
+        const uint32_t s0 = lds_base + (uint32_t)(t * NP) * kPiece;
+        dma_piece<0>(g, s0);
+        dma_piece<1>(g, s0 + 1 * kPiece);
+        dma_piece<2>(g, s0 + 2 * kPiece);
+        dma_piece<3>(g, s0 + 3 * kPiece);
+        if constexpr (NP == 8) {
+            dma_piece<4>(g, s0 + 4 * kPiece);
+            dma_piece<5>(g, s0 + 5 * kPiece);
+            dma_piece<6>(g, s0 + 6 * kPiece);
+            dma_piece<7>(g, s0 + 7 * kPiece);
+        }
+    }
+    // the tile's B/C records: 1 KB per instruction, contiguous in memory
+    const int lane = threadIdx.x;
+    if constexpr (MODE == 0) {
+        const float* g = bcb + (t0 + (lane >> 3)) * (2 * kNS) + (lane & 7) * 4;   // 8 records per KB
+        dma_at<0>(g, bc_base);
+        dma_at<1024>(g, bc_base + 1024);
+        dma_at<2048>(g, bc_base + 2048);
+        dma_at<3072>(g, bc_base + 3072);
     } else {
-        const float x = (w * kLn2) * uu;   // Delta u
-#pragma unroll
-        for (int n = 0; n < kNS; n += 2) {
-            const float dA0 = fast_exp2(w * L.Ar[n]);
-            const float dA1 = fast_exp2(w * L.Ar[n + 1]);
-            L.k[n] = __builtin_fmaf(dA0, L.k[n], x * bc[n]);
-            L.k[n + 1] = __builtin_fmaf(dA1, L.k[n + 1], x * bc[n + 1]);
-            if (MODE == 0) {
-                acc0 = __builtin_fmaf(bc[kNS + n], L.k[n], acc0);
-                acc1 = __builtin_fmaf(bc[kNS + n + 1], L.k[n + 1], acc1);
-            }
-        }
-        if (MODE == 0) return __builtin_fmaf(L.Dv, uu, acc0 + acc1);
-        return 0.0f;
+        const float* g = bcb + (t0 + (lane >> 2)) * (2 * kNS) + (lane & 3) * 4;   // B halves, 16 per KB
+        dma_at<0>(g, bc_base);
+        dma_at<2048>(g, bc_base + 1024);
     }
 }
 
-// The chunk [t_begin, t_end) of one wave's 64 rows.  MODE 0: output pass.
-// MODE 1: summary pass.
-template <typename Tin, typename Tout, int MODE, bool STRUCT>
-__device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0, int g) {
+// The 8-token block `blk` of the current tile for this lane, as raw words.
+template <typename Tin>
+struct Blk {
+    uint32_t u[In<Tin>::kWords], d[In<Tin>::kWords], z[In<Tin>::kWords];
+};
+
+template <typename Tin, int MODE>
+__device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int blk, int lane) {
+    constexpr int per = In<Tin>::kWords / 4;   // 16-byte pieces per block
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        const uint4 x = lds[(0 * In<Tin>::kPieces + blk * per + q) * kRows + lane];
+        b.u[4 * q] = x.x; b.u[4 * q + 1] = x.y; b.u[4 * q + 2] = x.z; b.u[4 * q + 3] = x.w;
+        const uint4 y = lds[(1 * In<Tin>::kPieces + blk * per + q) * kRows + lane];
+        b.d[4 * q] = y.x; b.d[4 * q + 1] = y.y; b.d[4 * q + 2] = y.z; b.d[4 * q + 3] = y.w;
+        if (MODE == 0) {
+            const uint4 v = lds[(2 * In<Tin>::kPieces + blk * per + q) * kRows + lane];
+            b.z[4 * q] = v.x; b.z[4 * q + 1] = v.y; b.z[4 * q + 2] = v.z; b.z[4 * q + 3] = v.w;
+        }
+    }
+}
+
+// One input element of token j of the tile in LDS (tensor t).
+template <typename Tin>
+__device__ __forceinline__ float lds_elem(const uint4* lds, int t, int j, int lane) {
+    constexpr int per = 16 / sizeof(Tin);
+    const char* p = reinterpret_cast<const char*>(lds + (t * In<Tin>::kPieces + j / per) * kRows + lane) +
+                    (j % per) * sizeof(Tin);
+    return In<Tin>::ld(reinterpret_cast<const Tin*>(p), 0);
+}
+
+// The chunk [t_begin, t_end) of one wave's 64 rows.  MODE 0: output pass,
+// MODE 1: summary pass.  STRUCT: structured-A path.  SP: softplus on.
+template <typename Tin, typename Tout, int MODE, bool STRUCT, bool SP>
+__device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0, int g, uint4* lds,
+                                          uint32_t lds_base) {
+    constexpr int NT = MODE == 0 ? 3 : 2;
+    constexpr int kBlocks = kTile / kBlk;         // blocks per tile
+    constexpr int kBC = MODE == 0 ? 2 * kNS : kNS;
     const int lane = threadIdx.x;
     const bool row_ok = d0 + lane < a.dim;
     const int64_t d = row_ok ? d0 + lane : a.dim - 1;
@@ -188,20 +303,20 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     const int64_t t_begin = (int64_t)g * a.chunk;
     const int64_t t_end = min<int64_t>(a.L, t_begin + a.chunk);
     const bool has_z = MODE == 0 && a.z != nullptr;
-    const bool vec = a.vec_ok != 0;
 
     const Tin* urow = reinterpret_cast<const Tin*>(a.u) + row * a.L;
     const Tin* drow = reinterpret_cast<const Tin*>(a.delta) + row * a.L;
     const Tin* zrow = has_z ? reinterpret_cast<const Tin*>(a.z) + row * a.L : urow;
     Tout* yrow = reinterpret_cast<Tout*>(a.y) + row * a.L;
+    const Tin* rowp[3] = {urow, drow, zrow};
 
     Lane L;
     L.bias_l = (a.bias ? a.bias[d] : 0.0f) * kLog2e;
 #pragma unroll
     for (int n = 0; n < kNS; ++n) L.Ar[n] = (n < a.N) ? a.A[d * a.N + n] : 0.0f;
     L.A0 = L.Ar[0];
-    L.Dv = (MODE == 0 && a.D) ? a.D[d] : 0.0f;
-    L.Dp = L.Dv * kInvLn2;
+    const float Dv = (MODE == 0 && a.D) ? a.D[d] : 0.0f;
+    L.Dp = STRUCT ? Dv * kInvLn2 : Dv;
     if (MODE == 0 && g > 0) {
         const float* cin = a.ws_state + (row * a.G + g) * kNS;
 #pragma unroll
@@ -210,78 +325,122 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
 #pragma unroll
         for (int n = 0; n < kNS; ++n) L.k[n] = 0.0f;
     }
-    L.sig_prev = kInvLn2;
+    L.s_prev = kInvLn2;
     L.wsum = 0.0f;
-    // gate factor: the structured path carries an extra ln2
+    // the structured path carries an extra 1/ln2 in its read-out
     const float gscale = STRUCT ? kInvLn2 : 1.0f;
     const float nogate = STRUCT ? kLn2 : 1.0f;
 
     // this batch's B/C, 32 floats per token; the address is wave-uniform
-    const float* bcb = a.bcq + (b * a.L) * (2 * kNS);
+    const float* bcb = uniform_ptr(a.bcq + (b * a.L) * (2 * kNS));
 
-    // Full 32-token tiles: raw words of the next tile are requested first.
-    const int64_t t_full_end = vec ? t_begin + ((t_end - t_begin) / kT) * kT : t_begin;
-    Run<Tin> ru, rd, rz;
+    const int64_t t_full_end = a.vec_ok ? t_begin + ((t_end - t_begin) / kTile) * kTile : t_begin;
     if (t_begin < t_full_end) {
-        ru.load_vec(urow + t_begin);
-        rd.load_vec(drow + t_begin);
-        if (MODE == 0) rz.load_vec(zrow + t_begin);
-    }
-    for (int64_t t0 = t_begin; t0 < t_full_end; t0 += kT) {
-        const int64_t tn = (t0 + kT < t_full_end) ? t0 + kT : t0;   // clamped, always in bounds
-        Run<Tin> nu, nd, nz;
-        nu.load_vec(urow + tn);
-        nd.load_vec(drow + tn);
-        if (MODE == 0) nz.load_vec(zrow + tn);
-        // B/C of token j + 1 are requested while token j is computed
-        const cfptr bct = (cfptr)uniform_ptr(bcb + t0 * (2 * kNS));
-        float bcur[2 * kNS];
+        constexpr int RS = kRec<MODE> / 4;   // floats per B/C record in LDS
+        const uint32_t bc_base = lds_base + (uint32_t)(NT * In<Tin>::kPieces * kRows * 16);
+        const float* bcl = reinterpret_cast<const float*>(lds + NT * In<Tin>::kPieces * kRows);
+        issue_tile<Tin, NT, MODE>(rowp, bcb, t_begin, lds_base, bc_base);
+        wait_vm();   // the first tile is in LDS
+#pragma nounroll
+        for (int64_t t0 = t_begin; t0 < t_full_end; t0 += kTile) {
+            const bool more = t0 + kTile < t_full_end;
+            if constexpr (STRUCT) {
+                Blk<Tin> cur;
+                read_blk<Tin, MODE>(cur, lds, 0, lane);
+                float yb[kTile];
 #pragma unroll
-        for (int e = 0; e < 2 * kNS; ++e) bcur[e] = bct[e];
-        float yv[4];
+                for (int blk = 0; blk < kBlocks; ++blk) {
+                    Blk<Tin> nxt;
+                    if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, lane);
+                    float w[kBlk], sg[kBlk];
+                    bool ok = true;
 #pragma unroll
-        for (int j = 0; j < kT; ++j) {
-            // keep each token's scalar loads where they are: hoisting them
-            // across tokens would exhaust the SGPRs and spill
-            __builtin_amdgcn_sched_barrier(0);
-            wait_scalar_loads();
-            float bnxt[2 * kNS];
-            if (j + 1 < kT) {
+                    for (int j = 0; j < kBlk; ++j) {
+                        w[j] = delta_log2<SP>(L, In<Tin>::get(cur.d, j));
+                        sg[j] = w[j] * In<Tin>::get(cur.u, j);
+                        ok = ok && s_in_range(sg[j]);
+                    }
+                    if (wave_all(ok)) {
 #pragma unroll
-                for (int e = 0; e < 2 * kNS; ++e) bnxt[e] = bct[(j + 1) * (2 * kNS) + e];
+                        for (int j = 0; j < kBlk; ++j) {
+                            const float* bc = bcl + (blk * kBlk + j) * RS;   // same address in every lane
+                            const float pre = tok_fast<MODE>(L, bc, w[j], sg[j], In<Tin>::get(cur.u, j));
+                            if (MODE == 0)
+                                yb[blk * kBlk + j] =
+                                    pre * (has_z ? silu_scaled(In<Tin>::get(cur.z, j), gscale) : nogate);
+                        }
+                    } else {
+                        // rare: token by token with the general form of the update
+                        float ys[kBlk];
+#pragma unroll
+                        for (int j = 0; j < kBlk; ++j) ys[j] = 0.0f;
+#pragma nounroll
+                        for (int j = 0; j < kBlk; ++j) {
+                            const float* bc = bcl + (blk * kBlk + j) * RS;
+                            const float uu = lds_elem<Tin>(lds, 0, blk * kBlk + j, lane);
+                            const float wj = delta_log2<SP>(L, lds_elem<Tin>(lds, 1, blk * kBlk + j, lane));
+                            const float pre = tok_slow<MODE>(L, bc, wj, wj * uu, uu);
+                            if (MODE == 0) {
+                                const float zz = has_z ? lds_elem<Tin>(lds, 2, blk * kBlk + j, lane) : 0.0f;
+                                const float yv = pre * (has_z ? silu_scaled(zz, gscale) : nogate);
+#pragma unroll
+                                for (int i = 0; i < kBlk; ++i) ys[i] = (i == j) ? yv : ys[i];
+                            }
+                        }
+                        if (MODE == 0) {
+#pragma unroll
+                            for (int j = 0; j < kBlk; ++j) yb[blk * kBlk + j] = ys[j];
+                        }
+                    }
+                    if (blk + 1 < kBlocks) cur = nxt;
+                }
+                if (more) {
+                    // every piece of this tile has left LDS: fetch the next one
+                    wait_lgkm();
+                    issue_tile<Tin, NT, MODE>(rowp, bcb, t0 + kTile, lds_base, bc_base);
+                }
+                if (MODE == 0 && row_ok) Out<Tout>::burst(yrow + t0, yb);
+            } else {
+                // general A: token by token out of the LDS tile
+#pragma nounroll
+                for (int j = 0; j < kTile; ++j) {
+                    const float uu = lds_elem<Tin>(lds, 0, j, lane);
+                    const float dl = lds_elem<Tin>(lds, 1, j, lane);
+                    const float zz = has_z ? lds_elem<Tin>(lds, 2, j, lane) : 0.0f;
+                    const float pre = tok_general<MODE>(L, bcl + j * RS, delta_log2<SP>(L, dl), uu);
+                    if (MODE == 0 && row_ok)
+                        Out<Tout>::st(yrow, t0 + j, pre * (has_z ? silu_scaled(zz, 1.0f) : 1.0f));
+                }
+                if (more) {
+                    wait_lgkm();
+                    issue_tile<Tin, NT, MODE>(rowp, bcb, t0 + kTile, lds_base, bc_base);
+                }
             }
-            const float pre = token<MODE, STRUCT>(L, bcur, ru[j], rd[j], a.softplus);
-            if (MODE == 0) {
-                yv[j & 3] = pre * (has_z ? silu_scaled(rz[j], gscale) : nogate);
-                if ((j & 3) == 3 && row_ok) Out<Tout>::st4(yrow + t0 + j - 3, yv);
-            }
-            if (j + 1 < kT) {
-#pragma unroll
-                for (int e = 0; e < 2 * kNS; ++e) bcur[e] = bnxt[e];
-            }
+            if (more) wait_vm();
         }
-        ru = nu;
-        rd = nd;
-        if (MODE == 0) rz = nz;
     }
     // Remaining tokens (a ragged tail, or every token when rows are not
     // 16-byte aligned), one at a time.
     for (int64_t t = t_full_end; t < t_end; ++t) {
-        const cfptr bc = (cfptr)(bcb + t * (2 * kNS));
-        float bcur[2 * kNS];
-#pragma unroll
-        for (int e = 0; e < 2 * kNS; ++e) bcur[e] = bc[e];
-        const float uu = Tok<Tin>::ld(urow, t);
-        const float dl = Tok<Tin>::ld(drow, t);
-        const float pre = token<MODE, STRUCT>(L, bcur, uu, dl, a.softplus);
+        float bt[kBC];
+        load_bc<MODE>(bt, (cfptr)(bcb + t * (2 * kNS)));
+        const float uu = In<Tin>::ld(urow, t);
+        const float w = delta_log2<SP>(L, In<Tin>::ld(drow, t));
+        float pre;
+        if constexpr (STRUCT) {
+            const float sg = w * uu;
+            pre = wave_all(s_in_range(sg)) ? tok_fast<MODE>(L, bt, w, sg, uu) : tok_slow<MODE>(L, bt, w, sg, uu);
+        } else {
+            pre = tok_general<MODE>(L, bt, w, uu);
+        }
         if (MODE == 0 && row_ok) {
-            const float yy = pre * (has_z ? silu_scaled(Tok<Tin>::ld(zrow, t), gscale) : nogate);
+            const float yy = pre * (has_z ? silu_scaled(In<Tin>::ld(zrow, t), gscale) : nogate);
             Out<Tout>::st(yrow, t, yy);
         }
     }
 
     if (!row_ok) return;
-    const float hs = STRUCT ? kLn2 * L.sig_prev : 1.0f;
+    const float hs = STRUCT ? kLn2 * L.s_prev : 1.0f;
     if (MODE == 1) {
         float* dst = a.ws_state + (row * a.G + g) * kNS;
 #pragma unroll
@@ -302,19 +461,38 @@ __device__ __forceinline__ bool row_is_structured(const M1Args& a, int64_t d) {
     return s;
 }
 
-template <typename Tin, typename Tout, int MODE>
-__global__ __launch_bounds__(kRows) void m1_scan_kernel(M1Args a) {
+template <typename Tin, typename Tout, int MODE, bool SP>
+__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 3 : 4)))
+void m1_scan_kernel(M1Args a) {
+    __shared__ uint4 lds[(MODE == 0 ? 3 : 2) * In<Tin>::kPieces * kRows + kTile * kRec<MODE> / 16];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(ldsptr)lds;
     const int64_t blocks_per_batch = (a.dim + kRows - 1) / kRows;
-    const int64_t b = blockIdx.x / blocks_per_batch;
-    const int64_t d0 = (blockIdx.x - b * blocks_per_batch) * kRows;
-    const int g = blockIdx.y;
+    int64_t rb;   // (batch, 64-channel block) index
+    int g;        // chunk
+    if (a.xcd_chunks) {
+        // Workgroups are dealt to the 8 XCDs round-robin by linear id; chunk g
+        // of every channel block goes to XCD g % 8, so the waves that share a
+        // chunk's B/C records share one L2.  The grid holds a multiple of 8
+        // chunks; ids past the last chunk of this pass exit.
+        const int64_t id = blockIdx.x;
+        const int64_t k = id >> 3;
+        const int64_t nrb = a.batch * blocks_per_batch;
+        g = (int)((k / nrb) * 8 + (id & 7));
+        rb = k % nrb;
+        if (g >= (MODE == 0 ? a.G : a.G - 1)) return;
+    } else {
+        rb = blockIdx.x;
+        g = blockIdx.y;
+    }
+    const int64_t b = rb / blocks_per_batch;
+    const int64_t d0 = (rb - b * blocks_per_batch) * kRows;
     const int64_t d = min<int64_t>(d0 + threadIdx.x, a.dim - 1);
     // the structured path needs every one of the 16 register states to be real
     const bool structured = !a.force_general && a.N == kNS && wave_all(row_is_structured(a, d));
     if (structured)
-        run_chunk<Tin, Tout, MODE, true>(a, b, d0, g);
+        run_chunk<Tin, Tout, MODE, true, SP>(a, b, d0, g, lds, lds_base);
     else
-        run_chunk<Tin, Tout, MODE, false>(a, b, d0, g);
+        run_chunk<Tin, Tout, MODE, false, SP>(a, b, d0, g, lds, lds_base);
 }
 
 // B, C [batch, N, L] -> fp32 [batch, L, (B0..B15, C0..C15)] (zeros past N)
@@ -330,8 +508,8 @@ __global__ __launch_bounds__(256) void m1_bc_kernel(M1Args a) {
         float v[2 * kNS];
 #pragma unroll
         for (int n = 0; n < kNS; ++n) {
-            v[n] = n < a.N ? Tok<Tin>::ld(B, (b * a.N + n) * a.L + t) : 0.0f;
-            v[kNS + n] = n < a.N ? Tok<Tin>::ld(C, (b * a.N + n) * a.L + t) : 0.0f;
+            v[n] = n < a.N ? In<Tin>::ld(B, (b * a.N + n) * a.L + t) : 0.0f;
+            v[kNS + n] = n < a.N ? In<Tin>::ld(C, (b * a.N + n) * a.L + t) : 0.0f;
         }
         float4* o = reinterpret_cast<float4*>(a.bcq + i * (2 * kNS));
 #pragma unroll
@@ -360,8 +538,8 @@ __global__ __launch_bounds__(256) void m1_carry_kernel(M1Args a) {
     }
 }
 
-template <typename Tin, typename Tout>
-hipError_t launch_dt(const M1Args& a, hipStream_t stream) {
+template <typename Tin, typename Tout, bool SP>
+hipError_t launch_sp(const M1Args& a, hipStream_t stream) {
     const int64_t bc_blocks = std::min<int64_t>((a.batch * a.L + 255) / 256, 16384);
     {
         KTime kt("m1_bc_convert", stream);
@@ -372,21 +550,41 @@ hipError_t launch_dt(const M1Args& a, hipStream_t stream) {
     if (a.G > 1) {
         {
             KTime kt("m1_scan_summary", stream);
-            hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 1>), dim3(gx, (unsigned)(a.G - 1)), dim3(kRows), 0,
-                               stream, a);
+            if (a.xcd_chunks)
+                hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 1, SP>), dim3(gx * (unsigned)a.G), dim3(kRows), 0,
+                                   stream, a);
+            else
+                hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 1, SP>), dim3(gx, (unsigned)(a.G - 1)), dim3(kRows), 0,
+                                   stream, a);
         }
         const int64_t threads = a.batch * a.dim * kNS;
         KTime kt("m1_chunk_carry", stream);
         hipLaunchKernelGGL(m1_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
     }
     KTime kt("m1_scan_output", stream);
-    hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 0>), dim3(gx, (unsigned)a.G), dim3(kRows), 0, stream, a);
+    if (a.xcd_chunks)
+        hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 0, SP>), dim3(gx * (unsigned)a.G), dim3(kRows), 0, stream, a);
+    else
+        hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 0, SP>), dim3(gx, (unsigned)a.G), dim3(kRows), 0, stream, a);
     return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_dt(const M1Args& a, hipStream_t stream) {
+    return a.softplus ? launch_sp<Tin, Tout, true>(a, stream) : launch_sp<Tin, Tout, false>(a, stream);
 }
 
 }  // namespace
 
 int m1_padded_states(int) { return kNS; }
+// Output-pass waves one CU holds at once: LDS-limited (160 KB per CU), at
+// most three waves per SIMD by registers.
+int m1_resident_waves_per_cu(int in_bf16) {
+    const int bytes = in_bf16 ? 3 * In<uint16_t>::kPieces * kRows * 16 + kTile * kRec<0>
+                              : 3 * In<float>::kPieces * kRows * 16 + kTile * kRec<0>;
+    return std::min(12, 160 * 1024 / bytes);
+}
+int m1_chunk_align() { return kChunkAlign; }
 int m1_rows_per_block() { return kRows; }
 int m1_waves_per_block() { return 1; }
 size_t m1_bc_bytes(int64_t batch, int64_t L) { return (size_t)batch * L * 2 * kNS * sizeof(float); }

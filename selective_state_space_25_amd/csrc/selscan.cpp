@@ -81,6 +81,7 @@ selscan_status_t device_check() {
 // ----------------------------------------------------------------- Mamba-1
 struct M1Plan {
     int G;
+    int xcd;   // chunk g on XCD g % 8 (G a multiple of 8)
     int64_t chunk;
     int NS;
     size_t bc_bytes, state_bytes, w_bytes, ws_bytes;
@@ -110,18 +111,25 @@ M1Plan plan_m1(const selscan_shape_t* s) {
     const int64_t waves_per_chunk = wgs * selscan::m1_waves_per_block();
     int64_t G = env_int("SELSCAN_M1_CHUNKS", 0);
     if (G <= 0) {
-        // enough waves to give every SIMD of the device a few to interleave
-        const int64_t target = env_int("SELSCAN_M1_WAVES", (int64_t)device_cus() * 16);
-        G = (target + waves_per_chunk - 1) / waves_per_chunk;
+        // one round of resident output-pass waves; rounding down avoids a
+        // ragged last round
+        const int64_t target = env_int(
+            "SELSCAN_M1_WAVES",
+            (int64_t)device_cus() * selscan::m1_resident_waves_per_cu(s->in_dtype == SELSCAN_BF16));
+        G = std::max<int64_t>(1, target / waves_per_chunk);
         G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 256));
+        // whole groups of 8 chunks let each XCD own the chunks it scans
+        if (G >= 8) G = G / 8 * 8;
     }
-    G = std::max<int64_t>(1, std::min<int64_t>(G, (s->seqlen + 15) / 16));
+    const int64_t align = selscan::m1_chunk_align();
+    G = std::max<int64_t>(1, std::min<int64_t>(G, (s->seqlen + align - 1) / align));
     G = std::min<int64_t>(G, 65535);
     int64_t chunk = (s->seqlen + G - 1) / G;
-    chunk = (chunk + 15) / 16 * 16;
+    chunk = (chunk + align - 1) / align * align;
     G = (s->seqlen + chunk - 1) / chunk;
     p.G = (int)G;
     p.chunk = chunk;
+    p.xcd = G % 8 == 0 && wgs * G < (int64_t(1) << 24) && env_int("SELSCAN_M1_XCD", 1) != 0;
     const int64_t rows = s->batch * s->dim;
     p.bc_bytes = align256(selscan::m1_bc_bytes(s->batch, s->seqlen));
     p.state_bytes = G > 1 ? align256((size_t)rows * G * p.NS * 4) : 0;
@@ -258,6 +266,7 @@ selscan_status_t selscan_fwd(const selscan_shape_t* s, const void* u, const void
         a.batch = s->batch; a.dim = s->dim; a.L = s->seqlen; a.N = (int)s->dstate;
         a.G = plan.G; a.chunk = plan.chunk; a.softplus = softplus;
         a.force_general = env_int("SELSCAN_FORCE_GENERAL", 0) != 0;
+        a.xcd_chunks = plan.xcd;
         // 32-token runs of every row start on 16-byte boundaries
         a.vec_ok = (s->seqlen * in_es) % 16 == 0 && (s->seqlen * out_es) % 16 == 0 && aligned16(u) &&
                    aligned16(delta) && aligned16(y) && (!z || aligned16(z));
@@ -268,9 +277,9 @@ selscan_status_t selscan_fwd(const selscan_shape_t* s, const void* u, const void
             a.ws_w = reinterpret_cast<float*>(base + plan.bc_bytes + plan.state_bytes);
         }
         if (log_plans())
-            std::fprintf(stderr, "[selscan] m1 B=%lld D=%lld N=%lld L=%lld chunks=%d chunk=%lld ws=%zu vec=%d\n",
+            std::fprintf(stderr, "[selscan] m1 B=%lld D=%lld N=%lld L=%lld chunks=%d chunk=%lld ws=%zu vec=%d xcd=%d\n",
                          (long long)s->batch, (long long)s->dim, (long long)s->dstate, (long long)s->seqlen, plan.G,
-                         (long long)plan.chunk, plan.ws_bytes, a.vec_ok);
+                         (long long)plan.chunk, plan.ws_bytes, a.vec_ok, a.xcd_chunks);
         hipError_t e = selscan::launch_m1(a, in_bf16, out_bf16, hs);
         ws.release();
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));

@@ -57,7 +57,7 @@ def test_state_sizes(gpu, N, a_kind):
     _full_compare(inp)
 
 
-@pytest.mark.parametrize("chunks", [1, 2, 3, 7, 40])
+@pytest.mark.parametrize("chunks", [1, 2, 3, 7, 8, 40])
 @pytest.mark.parametrize("general", [False, True])
 def test_chunk_carry_plans(gpu, monkeypatch, chunks, general):
     """Forced chunk counts (including chunks that end mid-sequence with a
@@ -67,6 +67,18 @@ def test_chunk_carry_plans(gpu, monkeypatch, chunks, general):
         monkeypatch.setenv("SELSCAN_FORCE_GENERAL", "1")
     inp = _inputs(3, 300, 16, 1250, torch.bfloat16, seed=chunks)
     _full_compare(inp)
+
+
+def test_xcd_chunk_mapping_is_bitwise_neutral(gpu, monkeypatch):
+    """Dealing chunks to XCDs by chunk index (a multiple of 8 chunks) only
+    moves workgroups: the results equal the plain 2-D grid bit for bit."""
+    monkeypatch.setenv("SELSCAN_M1_CHUNKS", "16")
+    inp = _inputs(3, 200, 16, 2500, torch.bfloat16, seed=31)
+    monkeypatch.setenv("SELSCAN_M1_XCD", "1")
+    y1, l1 = _run(inp)
+    monkeypatch.setenv("SELSCAN_M1_XCD", "0")
+    y0, l0 = _run(inp)
+    assert torch.equal(y0, y1) and torch.equal(l0, l1)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
