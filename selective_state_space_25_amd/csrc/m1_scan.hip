@@ -43,6 +43,9 @@
 //    takes the general form of the update token by token (s kept from the
 //    last good token and B scaled by s_t / s_kept), so zeros, NaN and Inf
 //    behave as in the plain recurrence.
+#include <cstdio>
+#include <cstdlib>
+
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -204,7 +207,8 @@ __device__ __forceinline__ void load_bc(float* dst, cfptr p) {
 
 // LDS image of one 32-token tile: [tensor][piece][lane] 16-byte pieces (4 per
 // row for bf16, 8 for fp32).  Tensor 0 u, 1 delta, 2 z (output pass only).
-// The tile's B/C records follow at bc_base.  `lds_base` is the LDS byte address of the
+// The B/C records of the tile follow, double-buffered so that the next
+// tile's can land while the last block of this one still reads its own.  `lds_base` is the LDS byte address of the
 // image.  The instruction offset moves both the global and the LDS address,
 // so M0 is set 16 p bytes short of piece p's slot.
 template <int P>
@@ -222,9 +226,8 @@ __device__ __forceinline__ void dma_at(const void* g, uint32_t slot) {
 // half (16 floats, summary pass) at bc_base + j * kRec<MODE> bytes.
 template <int MODE> constexpr int kRec = MODE == 0 ? 128 : 64;
 
-template <typename Tin, int NT, int MODE>
-__device__ __forceinline__ void issue_tile(const Tin* const* rowp, const float* bcb, int64_t t0, uint32_t lds_base,
-                                           uint32_t bc_base) {
+template <typename Tin, int NT>
+__device__ __forceinline__ void issue_rows(const Tin* const* rowp, int64_t t0, uint32_t lds_base) {
     constexpr int NP = In<Tin>::kPieces;
     constexpr uint32_t kPiece = kRows * 16;
 #pragma unroll
@@ -242,7 +245,11 @@ __device__ __forceinline__ void issue_tile(const Tin* const* rowp, const float* 
             dma_piece<7>(g, s0 + 7 * kPiece);
         }
     }
-    // the tile's B/C records: 1 KB per instruction, contiguous in memory
+}
+
+// The tile's B/C records: 1 KB per instruction, contiguous in memory.
+template <int MODE>
+__device__ __forceinline__ void issue_bc(const float* bcb, int64_t t0, uint32_t bc_base) {
     const int lane = threadIdx.x;
     if constexpr (MODE == 0) {
         const float* g = bcb + (t0 + (lane >> 3)) * (2 * kNS) + (lane & 7) * 4;   // 8 records per KB
@@ -337,13 +344,18 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     const int64_t t_full_end = a.vec_ok ? t_begin + ((t_end - t_begin) / kTile) * kTile : t_begin;
     if (t_begin < t_full_end) {
         constexpr int RS = kRec<MODE> / 4;   // floats per B/C record in LDS
-        const uint32_t bc_base = lds_base + (uint32_t)(NT * In<Tin>::kPieces * kRows * 16);
-        const float* bcl = reinterpret_cast<const float*>(lds + NT * In<Tin>::kPieces * kRows);
-        issue_tile<Tin, NT, MODE>(rowp, bcb, t_begin, lds_base, bc_base);
+        constexpr int kBCBytes = kTile * kRec<MODE>;
+        const uint32_t bc_base0 = lds_base + (uint32_t)(NT * In<Tin>::kPieces * kRows * 16);
+        const float* bcl0 = reinterpret_cast<const float*>(lds + NT * In<Tin>::kPieces * kRows);
+        issue_rows<Tin, NT>(rowp, t_begin, lds_base);
+        issue_bc<MODE>(bcb, t_begin, bc_base0);
         wait_vm();   // the first tile is in LDS
+        int par = 0;   // B/C buffer of the current tile
 #pragma nounroll
-        for (int64_t t0 = t_begin; t0 < t_full_end; t0 += kTile) {
+        for (int64_t t0 = t_begin; t0 < t_full_end; t0 += kTile, par ^= 1) {
             const bool more = t0 + kTile < t_full_end;
+            const float* bcl = bcl0 + par * (kBCBytes / 4);
+            const uint32_t bc_next = bc_base0 + (uint32_t)((par ^ 1) * kBCBytes);
             if constexpr (STRUCT) {
                 Blk<Tin> cur;
                 read_blk<Tin, MODE>(cur, lds, 0, lane);
@@ -351,7 +363,15 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
 #pragma unroll
                 for (int blk = 0; blk < kBlocks; ++blk) {
                     Blk<Tin> nxt;
-                    if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, lane);
+                    if (blk + 1 < kBlocks) {
+                        read_blk<Tin, MODE>(nxt, lds, blk + 1, lane);
+                    } else if (more) {
+                        // u, delta, z of this tile are all in registers now and
+                        // the other B/C buffer is free: fetch the next tile
+                        wait_lgkm();
+                        issue_rows<Tin, NT>(rowp, t0 + kTile, lds_base);
+                        issue_bc<MODE>(bcb, t0 + kTile, bc_next);
+                    }
                     float w[kBlk], sg[kBlk];
                     bool ok = true;
 #pragma unroll
@@ -370,18 +390,21 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                                     pre * (has_z ? silu_scaled(In<Tin>::get(cur.z, j), gscale) : nogate);
                         }
                     } else {
-                        // rare: token by token with the general form of the update
+                        // rare: token by token with the general form of the update.
+                        // u, delta, z come from memory: in the last block the LDS
+                        // tile already receives the next one.
+                        const int64_t tb = t0 + blk * kBlk;
                         float ys[kBlk];
 #pragma unroll
                         for (int j = 0; j < kBlk; ++j) ys[j] = 0.0f;
 #pragma nounroll
                         for (int j = 0; j < kBlk; ++j) {
                             const float* bc = bcl + (blk * kBlk + j) * RS;
-                            const float uu = lds_elem<Tin>(lds, 0, blk * kBlk + j, lane);
-                            const float wj = delta_log2<SP>(L, lds_elem<Tin>(lds, 1, blk * kBlk + j, lane));
+                            const float uu = In<Tin>::ld(urow, tb + j);
+                            const float wj = delta_log2<SP>(L, In<Tin>::ld(drow, tb + j));
                             const float pre = tok_slow<MODE>(L, bc, wj, wj * uu, uu);
                             if (MODE == 0) {
-                                const float zz = has_z ? lds_elem<Tin>(lds, 2, blk * kBlk + j, lane) : 0.0f;
+                                const float zz = has_z ? In<Tin>::ld(zrow, tb + j) : 0.0f;
                                 const float yv = pre * (has_z ? silu_scaled(zz, gscale) : nogate);
 #pragma unroll
                                 for (int i = 0; i < kBlk; ++i) ys[i] = (i == j) ? yv : ys[i];
@@ -394,11 +417,10 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                     }
                     if (blk + 1 < kBlocks) cur = nxt;
                 }
-                if (more) {
-                    // every piece of this tile has left LDS: fetch the next one
-                    wait_lgkm();
-                    issue_tile<Tin, NT, MODE>(rowp, bcb, t0 + kTile, lds_base, bc_base);
-                }
+                // the next tile has landed (its request left one block ago);
+                // waiting before the y stores keeps their write latency off
+                // this wait
+                if (more) wait_vm();
                 if (MODE == 0 && row_ok) Out<Tout>::burst(yrow + t0, yb);
             } else {
                 // general A: token by token out of the LDS tile
@@ -407,16 +429,17 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                     const float uu = lds_elem<Tin>(lds, 0, j, lane);
                     const float dl = lds_elem<Tin>(lds, 1, j, lane);
                     const float zz = has_z ? lds_elem<Tin>(lds, 2, j, lane) : 0.0f;
+                    if (j == kTile - 1 && more) {
+                        wait_lgkm();
+                        issue_rows<Tin, NT>(rowp, t0 + kTile, lds_base);
+                        issue_bc<MODE>(bcb, t0 + kTile, bc_next);
+                    }
                     const float pre = tok_general<MODE>(L, bcl + j * RS, delta_log2<SP>(L, dl), uu);
                     if (MODE == 0 && row_ok)
                         Out<Tout>::st(yrow, t0 + j, pre * (has_z ? silu_scaled(zz, 1.0f) : 1.0f));
                 }
-                if (more) {
-                    wait_lgkm();
-                    issue_tile<Tin, NT, MODE>(rowp, bcb, t0 + kTile, lds_base, bc_base);
-                }
+                if (more) wait_vm();
             }
-            if (more) wait_vm();
         }
     }
     // Remaining tokens (a ragged tail, or every token when rows are not
@@ -462,9 +485,9 @@ __device__ __forceinline__ bool row_is_structured(const M1Args& a, int64_t d) {
 }
 
 template <typename Tin, typename Tout, int MODE, bool SP>
-__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 3 : 4)))
+__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 2 : 4)))
 void m1_scan_kernel(M1Args a) {
-    __shared__ uint4 lds[(MODE == 0 ? 3 : 2) * In<Tin>::kPieces * kRows + kTile * kRec<MODE> / 16];
+    __shared__ uint4 lds[(MODE == 0 ? 3 : 2) * In<Tin>::kPieces * kRows + 2 * kTile * kRec<MODE> / 16];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(ldsptr)lds;
     const int64_t blocks_per_batch = (a.dim + kRows - 1) / kRows;
     int64_t rb;   // (batch, 64-channel block) index
@@ -570,7 +593,24 @@ hipError_t launch_sp(const M1Args& a, hipStream_t stream) {
 }
 
 template <typename Tin, typename Tout>
+void log_occupancy() {
+    int out = 0, sum = 0;
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&out, m1_scan_kernel<Tin, Tout, 0, true>, kRows, 0);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&sum, m1_scan_kernel<Tin, Tout, 1, true>, kRows, 0);
+    int lds = 0, dev = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    std::fprintf(stderr, "[selscan] m1 occupancy: output %d, summary %d workgroups per CU; LDS per CU %d bytes\n",
+                 out, sum, lds);
+}
+
+template <typename Tin, typename Tout>
 hipError_t launch_dt(const M1Args& a, hipStream_t stream) {
+    static bool logged = false;
+    if (!logged && std::getenv("SELSCAN_LOG")) {
+        logged = true;
+        log_occupancy<Tin, Tout>();
+    }
     return a.softplus ? launch_sp<Tin, Tout, true>(a, stream) : launch_sp<Tin, Tout, false>(a, stream);
 }
 
@@ -578,11 +618,11 @@ hipError_t launch_dt(const M1Args& a, hipStream_t stream) {
 
 int m1_padded_states(int) { return kNS; }
 // Output-pass waves one CU holds at once: LDS-limited (160 KB per CU), at
-// most three waves per SIMD by registers.
+// most two waves per SIMD by registers.
 int m1_resident_waves_per_cu(int in_bf16) {
-    const int bytes = in_bf16 ? 3 * In<uint16_t>::kPieces * kRows * 16 + kTile * kRec<0>
-                              : 3 * In<float>::kPieces * kRows * 16 + kTile * kRec<0>;
-    return std::min(12, 160 * 1024 / bytes);
+    const int bytes = in_bf16 ? 3 * In<uint16_t>::kPieces * kRows * 16 + 2 * kTile * kRec<0>
+                              : 3 * In<float>::kPieces * kRows * 16 + 2 * kTile * kRec<0>;
+    return std::min(8, 160 * 1024 / bytes);
 }
 int m1_chunk_align() { return kChunkAlign; }
 int m1_rows_per_block() { return kRows; }

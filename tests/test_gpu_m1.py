@@ -190,6 +190,19 @@ def test_zero_input_prefix(gpu):
     _full_compare(inp)
 
 
+@pytest.mark.parametrize("chunks", [1, 3])
+def test_isolated_zero_inputs(gpu, monkeypatch, chunks):
+    """A single u = 0 in one channel sends its whole 8-token block down the
+    token-by-token path; placed in every block position of a tile (the last
+    block of a tile overlaps the fetch of the next tile), the other channels
+    of the wave must be unaffected."""
+    monkeypatch.setenv("SELSCAN_M1_CHUNKS", str(chunks))
+    inp = _inputs(2, 130, 16, 700, torch.bfloat16, seed=41)
+    for i, t in enumerate([3, 27, 30, 58, 95, 190, 223, 350, 511, 640]):
+        inp["u"][i % 2, (7 * i) % 130, t] = 0.0
+    _full_compare(inp)
+
+
 @pytest.mark.parametrize("workload,nrows", [("mamba130m_l2k", 48), ("mamba2p8b_l8k", 48), ("long_1m", 6)])
 def test_full_size_workloads_sampled(gpu, workload, nrows):
     """The benchmark's workloads at full size, in the launch plan the
