@@ -128,6 +128,61 @@ def time_workload(name, steps, warmup, seed, device, kernel_timing=True):
     return w, res
 
 
+def time_decode(name, steps, device):
+    """One-token update (selscan_step / selscan_mamba2_step) at the batch and
+    channel shape of a workload: HBM-bound on reading and writing the state."""
+    import torch
+    import selective_state_space_25_amd as ss
+    import synth
+
+    w = synth.WORKLOADS[name]
+    if w.kind == "m1":
+        inp = synth.m1_inputs(w.batch, w.dim, w.dstate, 1, w.dtype, w.a_kind, seed=0, device=device)
+        state = torch.zeros((w.batch, w.dim, w.dstate), dtype=torch.float32, device=device)
+        args = [inp[k][..., 0].contiguous() if inp[k] is not None and inp[k].dim() == 3 else inp[k]
+                for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+        f = lambda: ss.step(state, *args)
+        es = torch.tensor([], dtype=w.dtype).element_size()
+        rows = w.batch * w.dim
+        nbytes = rows * w.dstate * 4 * 2 + rows * (3 * es + 4) + 2 * w.batch * w.dstate * es + w.dim * (w.dstate + 2) * 4
+    else:
+        inp = synth.m2_inputs(w.batch, 1, w.nheads, w.headdim, w.ngroups, w.dstate, w.dtype, seed=0, device=device)
+        state = torch.zeros((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=device)
+        args = [inp[k][:, 0].contiguous() if inp[k] is not None and inp[k].dim() >= 3 else inp[k]
+                for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")]
+        f = lambda: ss.mamba2_step(state, *args)
+        es = torch.tensor([], dtype=w.dtype).element_size()
+        rows = w.batch * w.nheads * w.headdim
+        nbytes = (rows * w.dstate * 4 * 2 + rows * (2 * es + 4) + w.batch * w.nheads * es
+                  + 2 * w.batch * w.ngroups * w.dstate * es + 3 * w.nheads * 4)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream(device)
+    e0.record(stream)
+    for _ in range(steps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_call = e0.elapsed_time(e1) * 1e3 / steps
+    # the kernel alone (a single small launch per token: the call above is
+    # bound by the host issuing it)
+    ss.timing_collect()
+    ss.timing_enable(True)
+    try:
+        for _ in range(steps):
+            f()
+        torch.cuda.synchronize()
+    finally:
+        ss.timing_enable(False)
+    k = list(ss.timing_collect().values())[0]
+    us = k["avg_ms"] * 1e3
+    return {"shape_of": name, "us_per_token_kernel": us,
+            "us_per_token_call": us_call, "bytes_per_token": nbytes, "kernel_gbs": nbytes / (us * 1e-6) / 1e9,
+            "kernel_state_updates_per_s": rows * w.dstate / (us * 1e-6)}
+
+
 def dominant_kernel(res):
     name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["total_ms"])
     return name, k
@@ -274,6 +329,7 @@ def main():
         "workloads": {args.workload: head, **extras},
         "library": ss.version(),
     }
+    line["decode"] = {n: time_decode(n, 200, device) for n in ("mamba2p8b_l8k", "mamba2_mh")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
     print(json.dumps(line))

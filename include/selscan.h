@@ -104,6 +104,44 @@ selscan_status_t selscan_fwd(const selscan_shape_t* shape,
                              void* y, float* last_state, void* stream);
 
 /*
+ * selscan_fwd from a given initial state instead of zero: the scan continues
+ * a sequence whose state after its previous part is h0 (the recurrence of
+ * section 2.2 of the "Understanding Mamba ..." blog, resumed; the streaming
+ * use on the tutorial and skill pages).
+ *   h0 [B, D, N] fp32 device memory, read only; NULL = zero state (then
+ *      identical to selscan_fwd).  h0 and last_state must not alias: chunks
+ *      of one channel run concurrently.
+ * Other arguments, errors and workspace as for selscan_fwd.
+ */
+selscan_status_t selscan_fwd_h0(const selscan_shape_t* shape,
+                                const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D,
+                                const void* z, const float* delta_bias, int softplus,
+                                const float* h0, void* y, float* last_state, void* stream);
+
+/*
+ * One-token state update (decoding; the recurrent view of section 2.2 of the
+ * "Understanding Mamba ..." blog, one token at a time as the tutorial and
+ * skill pages use it for generation).  shape: batch, dim, dstate N (1..16),
+ * in_dtype, out_dtype; seqlen, workspace and workspace_bytes are ignored.
+ *   state      [B, D, N] fp32  h before the token on entry, after it on
+ *                              return (updated in place); 16-byte aligned
+ *                              when N is a multiple of 4
+ *   u, delta   [B, D]    in_dtype
+ *   A          [D, N]    fp32
+ *   B, C       [B, N]    in_dtype   this token's projections
+ *   D, delta_bias [D]    fp32       NULL = 0
+ *   z          [B, D]    in_dtype   NULL = no gate
+ *   y          [B, D]    out_dtype  (written)
+ * No workspace.  Errors as for selscan_fwd; UNSUPPORTED for N > 16.
+ */
+selscan_status_t selscan_step(const selscan_shape_t* shape, float* state,
+                              const void* u, const void* delta, const float* A,
+                              const void* B, const void* C, const float* D,
+                              const void* z, const float* delta_bias, int softplus,
+                              void* y, void* stream);
+
+/*
  * Mamba-2 problem description.
  *   batch >= 1, seqlen >= 1, nheads H >= 1, headdim P >= 1, ngroups G >= 1
  *   with H % G == 0, dstate N in {16, 32, 64, 128}.
@@ -141,6 +179,30 @@ selscan_status_t selscan_mamba2_fwd(const selscan_m2_shape_t* shape,
                                     const void* B, const void* C, const float* D,
                                     const void* z, const float* dt_bias, int softplus,
                                     void* y, float* last_state, void* stream);
+
+/* selscan_mamba2_fwd from an initial state h0 [B, H, P, N] fp32 (NULL =
+ * zero); h0 and last_state must not alias. */
+selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* shape,
+                                       const void* x, const void* dt, const float* A,
+                                       const void* B, const void* C, const float* D,
+                                       const void* z, const float* dt_bias, int softplus,
+                                       const float* h0, void* y, float* last_state, void* stream);
+
+/*
+ * Mamba-2 one-token update.  shape: batch, nheads H, headdim P, ngroups G,
+ * dstate N in {16, 32, 64, 128}, dtypes; seqlen and workspace ignored.
+ *   state   [B, H, P, N] fp32  updated in place, 16-byte aligned
+ *   x, z    [B, H, P]    in_dtype (z NULL = no gate)
+ *   dt      [B, H]       in_dtype
+ *   A, D, dt_bias [H]    fp32 (D, dt_bias NULL = 0)
+ *   B, C    [B, G, N]    in_dtype
+ *   y       [B, H, P]    out_dtype (written)
+ */
+selscan_status_t selscan_mamba2_step(const selscan_m2_shape_t* shape, float* state,
+                                     const void* x, const void* dt, const float* A,
+                                     const void* B, const void* C, const float* D,
+                                     const void* z, const float* dt_bias, int softplus,
+                                     void* y, void* stream);
 
 /* Message for the last failed call on this thread ("" after a success).
  * The string stays valid until the next call on the same thread. */

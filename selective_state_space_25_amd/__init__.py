@@ -47,6 +47,7 @@ class M2Shape(ctypes.Structure):
 _lib = None
 
 EXPORTED = ("selscan_fwd", "selscan_mamba2_fwd", "selscan_workspace_bytes", "selscan_mamba2_workspace_bytes",
+            "selscan_fwd_h0", "selscan_mamba2_fwd_h0", "selscan_step", "selscan_mamba2_step",
             "selscan_last_error", "selscan_version", "selscan_timing_enable", "selscan_timing_collect")
 
 
@@ -68,6 +69,15 @@ def lib() -> ctypes.CDLL:
         L.selscan_fwd.restype = i32
         L.selscan_mamba2_fwd.argtypes = [ctypes.POINTER(M2Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, fp, vp]
         L.selscan_mamba2_fwd.restype = i32
+        L.selscan_fwd_h0.argtypes = [ctypes.POINTER(Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, vp]
+        L.selscan_fwd_h0.restype = i32
+        L.selscan_mamba2_fwd_h0.argtypes = [ctypes.POINTER(M2Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp,
+                                            vp]
+        L.selscan_mamba2_fwd_h0.restype = i32
+        L.selscan_step.argtypes = [ctypes.POINTER(Shape), fp, vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, vp]
+        L.selscan_step.restype = i32
+        L.selscan_mamba2_step.argtypes = [ctypes.POINTER(M2Shape), fp, vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, vp]
+        L.selscan_mamba2_step.restype = i32
         L.selscan_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
         L.selscan_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_mamba2_workspace_bytes.argtypes = [ctypes.POINTER(M2Shape)]
@@ -138,7 +148,7 @@ def m1_shape(batch, dim, dstate, seqlen, in_dtype=BF16, out_dtype=None, workspac
 
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, out=None, last_state=None,
-        return_last_state=True, workspace=None, out_dtype=None):
+        return_last_state=True, workspace=None, out_dtype=None, h0=None):
     """Mamba-1 selective scan on the GPU.
 
     u, delta, z: [batch, dim, L]; B, C: [batch, N, L] (float32 or bfloat16, one
@@ -146,6 +156,7 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, out=N
     Returns (y [batch, dim, L] float32 unless out_dtype says otherwise,
     last_state [batch, dim, N] float32 or None).  y defaults to float32, the
     precision of the state: a bfloat16 y carries up to 2^-8 relative rounding.
+    h0 [batch, dim, N] float32: initial state (None: zero).
     """
     torch = _torch()
     dev = u.device
@@ -169,8 +180,38 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, out=N
         _ptr(z, "z", (batch, dim, L), dt, dev), _ptr(delta_bias, "delta_bias", (dim,), torch.float32, dev),
         int(bool(softplus)), _ptr(out, "out", (batch, dim, L), odt, dev),
         _ptr(last_state, "last_state", (batch, dim, N), torch.float32, dev), _stream_handle(dev))
-    _check(lib().selscan_fwd(ctypes.byref(s), *args))
+    if h0 is None:
+        _check(lib().selscan_fwd(ctypes.byref(s), *args))
+    else:
+        h0p = _ptr(h0, "h0", (batch, dim, N), torch.float32, dev)
+        _check(lib().selscan_fwd_h0(ctypes.byref(s), *args[:9], h0p, *args[9:]))
     return out, last_state
+
+
+def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, out=None, out_dtype=None):
+    """One-token Mamba-1 update (decoding).  state [batch, dim, N] float32 is
+    updated in place; u, delta, z [batch, dim]; B, C [batch, N] (float32 or
+    bfloat16); A [dim, N], D, delta_bias [dim] float32.  Returns y [batch, dim]
+    (float32 unless out_dtype or out says otherwise)."""
+    torch = _torch()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.step needs tensors on a GPU device")
+    batch, dim = u.shape
+    N = A.shape[1]
+    dt = u.dtype
+    odt = (out.dtype if out is not None else torch.float32) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((batch, dim), dtype=odt, device=dev)
+    s = Shape(batch, dim, N, 1, _dtype_code(u), _dtype_code(out), None, 0)
+    _check(lib().selscan_step(
+        ctypes.byref(s), _ptr(state, "state", (batch, dim, N), torch.float32, dev),
+        _ptr(u, "u", (batch, dim), dt, dev), _ptr(delta, "delta", (batch, dim), dt, dev),
+        _ptr(A, "A", (dim, N), torch.float32, dev), _ptr(B, "B", (batch, N), dt, dev),
+        _ptr(C, "C", (batch, N), dt, dev), _ptr(D, "D", (dim,), torch.float32, dev),
+        _ptr(z, "z", (batch, dim), dt, dev), _ptr(delta_bias, "delta_bias", (dim,), torch.float32, dev),
+        int(bool(softplus)), _ptr(out, "out", (batch, dim), odt, dev), _stream_handle(dev)))
+    return out
 
 
 def workspace_bytes(batch, dim, dstate, seqlen, in_dtype=BF16, out_dtype=None) -> int:
@@ -179,13 +220,14 @@ def workspace_bytes(batch, dim, dstate, seqlen, in_dtype=BF16, out_dtype=None) -
 
 
 def mamba2_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, out=None, last_state=None,
-               return_last_state=True, workspace=None, out_dtype=None):
+               return_last_state=True, workspace=None, out_dtype=None, h0=None):
     """Mamba-2 multi-head selective scan on the GPU.
 
     x, z: [batch, L, H, P]; dt: [batch, L, H]; B, C: [batch, L, G, N]
     (float32 or bfloat16); A, D, dt_bias: [H] float32.
     Returns (y [batch, L, H, P] float32 unless out_dtype says otherwise,
-    last_state [batch, H, P, N] float32 or None).
+    last_state [batch, H, P, N] float32 or None).  h0 [batch, H, P, N]
+    float32: initial state (None: zero).
     """
     torch = _torch()
     dev = x.device
@@ -208,8 +250,37 @@ def mamba2_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, out=
         _ptr(z, "z", (batch, L, H, P), dtp, dev), _ptr(dt_bias, "dt_bias", (H,), torch.float32, dev),
         int(bool(softplus)), _ptr(out, "out", (batch, L, H, P), odt, dev),
         _ptr(last_state, "last_state", (batch, H, P, N), torch.float32, dev), _stream_handle(dev))
-    _check(lib().selscan_mamba2_fwd(ctypes.byref(s), *args))
+    if h0 is None:
+        _check(lib().selscan_mamba2_fwd(ctypes.byref(s), *args))
+    else:
+        h0p = _ptr(h0, "h0", (batch, H, P, N), torch.float32, dev)
+        _check(lib().selscan_mamba2_fwd_h0(ctypes.byref(s), *args[:9], h0p, *args[9:]))
     return out, last_state
+
+
+def mamba2_step(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, out=None, out_dtype=None):
+    """One-token Mamba-2 update (decoding).  state [batch, H, P, N] float32 is
+    updated in place; x, z [batch, H, P]; dt [batch, H]; B, C [batch, G, N]
+    (float32 or bfloat16); A, D, dt_bias [H] float32.  Returns y [batch, H, P]."""
+    torch = _torch()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.mamba2_step needs tensors on a GPU device")
+    batch, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dtp = x.dtype
+    odt = (out.dtype if out is not None else torch.float32) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((batch, H, P), dtype=odt, device=dev)
+    s = M2Shape(batch, 1, H, P, G, N, _dtype_code(x), _dtype_code(out), None, 0)
+    _check(lib().selscan_mamba2_step(
+        ctypes.byref(s), _ptr(state, "state", (batch, H, P, N), torch.float32, dev),
+        _ptr(x, "x", (batch, H, P), dtp, dev), _ptr(dt, "dt", (batch, H), dtp, dev),
+        _ptr(A, "A", (H,), torch.float32, dev), _ptr(B, "B", (batch, G, N), dtp, dev),
+        _ptr(C, "C", (batch, G, N), dtp, dev), _ptr(D, "D", (H,), torch.float32, dev),
+        _ptr(z, "z", (batch, H, P), dtp, dev), _ptr(dt_bias, "dt_bias", (H,), torch.float32, dev),
+        int(bool(softplus)), _ptr(out, "out", (batch, H, P), odt, dev), _stream_handle(dev)))
+    return out
 
 
 def mamba2_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype=BF16, out_dtype=None) -> int:
@@ -238,5 +309,5 @@ def timing_collect() -> dict:
     return res
 
 
-__all__ = ["timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
+__all__ = ["step", "mamba2_step", "timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
            "SelscanError", "Shape", "M2Shape", "m1_shape", "EXPORTED", "LIB_PATH"]

@@ -28,6 +28,7 @@ struct M1Args {
     const float* bias;
     void* y;
     float* last;
+    const float* h0;  // [batch, dim, N] initial state, or NULL for zero
     float* ws_state;  // [rows, G, 16] chunk end states, then carries-in
     float* ws_w;      // [rows, G] chunk sums of Delta / ln2
     float* bcq;       // [batch, L, 32] fp32 copy of B and C (B0..B15, C0..C15 per token)
@@ -61,6 +62,7 @@ struct M2Args {
     const float* dt_bias;
     void* y;
     float* last;
+    const float* h0;  // [batch, H, P, N] initial state, or NULL for zero
     float* ws_bc;     // [batch, L, G, 2, N] fp32 copy of B and C (interleaved per token)
     float* ws_state;  // [batch, H, P, chunks, N] chunk end states, then carries-in
     float* ws_w;      // [batch, H, chunks] chunk sums of Delta / ln2
@@ -71,6 +73,28 @@ struct M2Args {
 };
 
 int m2_waves_per_block(int64_t N);
+
+// One-token state update (decoding), both variants.  Mamba-1: u, delta, z, y
+// [batch, dim]; B, C [batch, N]; A [dim, N]; D, bias [dim]; state
+// [batch, dim, N].  Mamba-2: u = x, z, y [batch, H, P]; delta = dt
+// [batch, H]; B, C [batch, G, N]; A, D, bias [H]; state [batch, H, P, N].
+struct StepArgs {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* bias;
+    void* y;
+    float* state;
+    int64_t batch, dim;       // Mamba-1
+    int64_t H, P, G;          // Mamba-2
+    int N;
+    int softplus;
+};
+hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, int mamba2, hipStream_t stream);
 hipError_t launch_m2(const M2Args& a, int in_bf16, int out_bf16, hipStream_t stream);
 
 }  // namespace selscan

@@ -328,6 +328,10 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
         const float* cin = a.ws_state + (row * a.G + g) * kNS;
 #pragma unroll
         for (int n = 0; n < kNS; ++n) L.k[n] = cin[n];
+    } else if (MODE == 0 && a.h0) {
+        // chunk 0 starts from the caller's state (k = h while s_prev = 1/ln2)
+#pragma unroll
+        for (int n = 0; n < kNS; ++n) L.k[n] = (n < a.N) ? a.h0[row * a.N + n] : 0.0f;
     } else {
 #pragma unroll
         for (int n = 0; n < kNS; ++n) L.k[n] = 0.0f;
@@ -363,11 +367,11 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
 #pragma unroll
                 for (int blk = 0; blk < kBlocks; ++blk) {
                     Blk<Tin> nxt;
-                    if (blk + 1 < kBlocks) {
-                        read_blk<Tin, MODE>(nxt, lds, blk + 1, lane);
-                    } else if (more) {
-                        // u, delta, z of this tile are all in registers now and
-                        // the other B/C buffer is free: fetch the next tile
+                    if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, lane);
+                    if (blk == kBlocks - 2 && more) {
+                        // u, delta, z of this tile's last two blocks are in
+                        // registers now and the other B/C buffer is free:
+                        // fetch the next tile
                         wait_lgkm();
                         issue_rows<Tin, NT>(rowp, t0 + kTile, lds_base);
                         issue_bc<MODE>(bcb, t0 + kTile, bc_next);
@@ -485,7 +489,7 @@ __device__ __forceinline__ bool row_is_structured(const M1Args& a, int64_t d) {
 }
 
 template <typename Tin, typename Tout, int MODE, bool SP>
-__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 2 : 4)))
+__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(MODE == 0 || sizeof(Tin) == 4 ? 2 : 4)))
 void m1_scan_kernel(M1Args a) {
     __shared__ uint4 lds[(MODE == 0 ? 3 : 2) * In<Tin>::kPieces * kRows + 2 * kTile * kRec<MODE> / 16];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(ldsptr)lds;
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(256) void m1_bc_kernel(M1Args a) {
 
 // Carry pass: one thread per (row, n).  Turns the per-chunk end states b_g
 // (slot g) into carries-in h_in(g) (slot g), in chunk order:
-//   h_in(0) = 0,   h_in(g+1) = 2^(A[d,n] W_g) h_in(g) + b_g.
+//   h_in(0) = h0 (or 0),   h_in(g+1) = 2^(A[d,n] W_g) h_in(g) + b_g.
 __global__ __launch_bounds__(256) void m1_carry_kernel(M1Args a) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t rows = a.batch * a.dim;
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(256) void m1_carry_kernel(M1Args a) {
     const int n = (int)(idx - row * kNS);
     const int64_t d = row % a.dim;
     const float An = (n < a.N) ? a.A[d * a.N + n] : 0.0f;
-    float h = 0.0f;
+    float h = (a.h0 && n < a.N) ? a.h0[row * a.N + n] : 0.0f;
     float* st = a.ws_state + row * a.G * kNS + n;
     const float* W = a.ws_w + row * a.G;
     for (int g = 0; g < a.G; ++g) {

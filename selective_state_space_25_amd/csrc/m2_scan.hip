@@ -120,6 +120,11 @@ __global__ __launch_bounds__(kP * (N / kSPW)) void m2_scan_kernel(M2Args a) {
         const float* cin = a.ws_state + (unit * a.chunks + g) * N + wave * kSPW;
 #pragma unroll
         for (int i = 0; i < kSPW; ++i) k[i] = cin[i];
+    } else if (MODE == 0 && a.h0) {
+        // chunk 0 starts from the caller's state (k = h while sig_prev = 1/ln2)
+        const float* cin = a.h0 + unit * N + wave * kSPW;
+#pragma unroll
+        for (int i = 0; i < kSPW; ++i) k[i] = cin[i];
     } else {
 #pragma unroll
         for (int i = 0; i < kSPW; ++i) k[i] = 0.0f;
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(kP * (N / kSPW)) void m2_scan_kernel(M2Args a) {
 }
 
 // Carry pass, one thread per (batch, head, channel, n):
-//   h_in(0) = 0,  h_in(g+1) = 2^(A[h] W_g) h_in(g) + b_g   (in place).
+//   h_in(0) = h0 (or 0),  h_in(g+1) = 2^(A[h] W_g) h_in(g) + b_g   (in place).
 __global__ __launch_bounds__(256) void m2_carry_kernel(M2Args a) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = a.batch * a.H * a.P * a.N;
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(256) void m2_carry_kernel(M2Args a) {
     const float Ah = a.A[h];
     float* st = a.ws_state + unit * a.chunks * a.N + n;
     const float* W = a.ws_w + bh * a.chunks;
-    float hv = 0.0f;
+    float hv = a.h0 ? a.h0[unit * a.N + n] : 0.0f;
     for (int g = 0; g < a.chunks; ++g) {
         const float bg = (g < a.chunks - 1) ? st[(int64_t)g * a.N] : 0.0f;
         st[(int64_t)g * a.N] = hv;

@@ -243,6 +243,13 @@ size_t selscan_mamba2_workspace_bytes(const selscan_m2_shape_t* shape) {
 selscan_status_t selscan_fwd(const selscan_shape_t* s, const void* u, const void* delta, const float* A,
                              const void* B, const void* C, const float* D, const void* z,
                              const float* delta_bias, int softplus, void* y, float* last_state, void* stream) {
+    return selscan_fwd_h0(s, u, delta, A, B, C, D, z, delta_bias, softplus, nullptr, y, last_state, stream);
+}
+
+selscan_status_t selscan_fwd_h0(const selscan_shape_t* s, const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, int softplus, const float* h0, void* y, float* last_state,
+                                void* stream) {
     try {
         selscan_status_t st = check_m1_shape(s);
         if (st != SELSCAN_OK) return st;
@@ -262,7 +269,7 @@ selscan_status_t selscan_fwd(const selscan_shape_t* s, const void* u, const void
         const int64_t in_es = in_bf16 ? 2 : 4, out_es = out_bf16 ? 2 : 4;
         selscan::M1Args a{};
         a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-        a.y = y; a.last = last_state;
+        a.y = y; a.last = last_state; a.h0 = h0;
         a.batch = s->batch; a.dim = s->dim; a.L = s->seqlen; a.N = (int)s->dstate;
         a.G = plan.G; a.chunk = plan.chunk; a.softplus = softplus;
         a.force_general = env_int("SELSCAN_FORCE_GENERAL", 0) != 0;
@@ -292,6 +299,13 @@ selscan_status_t selscan_fwd(const selscan_shape_t* s, const void* u, const void
 selscan_status_t selscan_mamba2_fwd(const selscan_m2_shape_t* s, const void* x, const void* dt, const float* A,
                                     const void* B, const void* C, const float* D, const void* z,
                                     const float* dt_bias, int softplus, void* y, float* last_state, void* stream) {
+    return selscan_mamba2_fwd_h0(s, x, dt, A, B, C, D, z, dt_bias, softplus, nullptr, y, last_state, stream);
+}
+
+selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* s, const void* x, const void* dt, const float* A,
+                                       const void* B, const void* C, const float* D, const void* z,
+                                       const float* dt_bias, int softplus, const float* h0, void* y,
+                                       float* last_state, void* stream) {
     try {
         selscan_status_t st = check_m2_shape(s);
         if (st != SELSCAN_OK) return st;
@@ -307,7 +321,7 @@ selscan_status_t selscan_mamba2_fwd(const selscan_m2_shape_t* s, const void* x, 
         if (st != SELSCAN_OK) return st;
         selscan::M2Args a{};
         a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.dt_bias = dt_bias;
-        a.y = y; a.last = last_state;
+        a.y = y; a.last = last_state; a.h0 = h0;
         a.batch = s->batch; a.L = s->seqlen; a.H = s->nheads; a.P = s->headdim; a.G = s->ngroups; a.N = s->dstate;
         a.chunks = plan.chunks; a.chunk = plan.chunk; a.softplus = softplus;
         char* base = static_cast<char*>(ws.ptr);
@@ -323,6 +337,74 @@ selscan_status_t selscan_mamba2_fwd(const selscan_m2_shape_t* s, const void* x, 
                          plan.ws_bytes);
         hipError_t e = selscan::launch_m2(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, hs);
         ws.release();
+        if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(SELSCAN_ERR_LAUNCH, "unexpected host exception");
+    }
+}
+
+selscan_status_t selscan_step(const selscan_shape_t* s, float* state, const void* u, const void* delta,
+                              const float* A, const void* B, const void* C, const float* D, const void* z,
+                              const float* delta_bias, int softplus, void* y, void* stream) {
+    try {
+        if (!s) return fail(SELSCAN_ERR_INVALID_ARG, "shape is NULL");
+        if (s->batch < 1 || s->dim < 1 || s->dstate < 1)
+            return fail(SELSCAN_ERR_INVALID_ARG, "batch, dim and dstate must all be >= 1");
+        if (s->dstate > 16) return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-1 step supports dstate <= 16");
+        if ((s->in_dtype != SELSCAN_F32 && s->in_dtype != SELSCAN_BF16) ||
+            (s->out_dtype != SELSCAN_F32 && s->out_dtype != SELSCAN_BF16))
+            return fail(SELSCAN_ERR_UNSUPPORTED, "dtypes must be SELSCAN_F32 or SELSCAN_BF16");
+        if (mul_checked({s->batch, s->dim, s->dstate, 4}) < 0)
+            return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
+        if (!state || !u || !delta || !A || !B || !C || !y)
+            return fail(SELSCAN_ERR_INVALID_ARG, "state, u, delta, A, B, C and y must be non-NULL");
+        if (s->dstate % 4 == 0 && !aligned16(state))
+            return fail(SELSCAN_ERR_INVALID_ARG, "state must be 16-byte aligned");
+        if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        selscan_status_t st = device_check();
+        if (st != SELSCAN_OK) return st;
+        selscan::StepArgs a{};
+        a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+        a.y = y; a.state = state;
+        a.batch = s->batch; a.dim = s->dim; a.N = (int)s->dstate; a.softplus = softplus;
+        hipError_t e = selscan::launch_step(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, 0,
+                                            reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(SELSCAN_ERR_LAUNCH, "unexpected host exception");
+    }
+}
+
+selscan_status_t selscan_mamba2_step(const selscan_m2_shape_t* s, float* state, const void* x, const void* dt,
+                                     const float* A, const void* B, const void* C, const float* D, const void* z,
+                                     const float* dt_bias, int softplus, void* y, void* stream) {
+    try {
+        if (!s) return fail(SELSCAN_ERR_INVALID_ARG, "shape is NULL");
+        if (s->batch < 1 || s->nheads < 1 || s->headdim < 1 || s->ngroups < 1 || s->dstate < 1)
+            return fail(SELSCAN_ERR_INVALID_ARG, "batch, nheads, headdim, ngroups, dstate must be >= 1");
+        if (s->nheads % s->ngroups != 0) return fail(SELSCAN_ERR_INVALID_ARG, "nheads must be a multiple of ngroups");
+        if (s->dstate != 16 && s->dstate != 32 && s->dstate != 64 && s->dstate != 128)
+            return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-2 step supports dstate 16, 32, 64, 128");
+        if ((s->in_dtype != SELSCAN_F32 && s->in_dtype != SELSCAN_BF16) ||
+            (s->out_dtype != SELSCAN_F32 && s->out_dtype != SELSCAN_BF16))
+            return fail(SELSCAN_ERR_UNSUPPORTED, "dtypes must be SELSCAN_F32 or SELSCAN_BF16");
+        if (mul_checked({s->batch, s->nheads, s->headdim, s->dstate, 4}) < 0)
+            return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
+        if (!state || !x || !dt || !A || !B || !C || !y)
+            return fail(SELSCAN_ERR_INVALID_ARG, "state, x, dt, A, B, C and y must be non-NULL");
+        if (!aligned16(state)) return fail(SELSCAN_ERR_INVALID_ARG, "state must be 16-byte aligned");
+        if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        selscan_status_t st = device_check();
+        if (st != SELSCAN_OK) return st;
+        selscan::StepArgs a{};
+        a.u = x; a.delta = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = dt_bias;
+        a.y = y; a.state = state;
+        a.batch = s->batch; a.H = s->nheads; a.P = s->headdim; a.G = s->ngroups; a.N = (int)s->dstate;
+        a.softplus = softplus;
+        hipError_t e = selscan::launch_step(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, 1,
+                                            reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
         return ok();
     } catch (...) {

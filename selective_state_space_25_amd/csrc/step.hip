@@ -1,0 +1,207 @@
+// step.hip -- one-token state update (decoding) for gfx950.
+//
+// The recurrent view of the selective SSM (blog "Understanding Mamba and
+// Selective State Space Models (SSMs)" section 2.2, second cut; the
+// streaming use of the step function on the tutorial and skill pages):
+// given the state h after token t-1, token t updates it in place,
+//
+//   Delta   = softplus(delta + bias)
+//   h[n]    = exp(Delta A[n]) h[n] + Delta B[n] u
+//   y       = (sum_n C[n] h[n] + D u) * silu(z)
+//
+// This pass reads and writes the whole state once per token, so it is bound
+// by HBM bandwidth on the state; each thread owns four consecutive states
+// (one 16-byte access), the lanes of a row reduce y with cross-lane shuffles
+// (state sizes that are not a multiple of 4: one thread per row).
+#include "device_math.hpp"
+#include "kernels.hpp"
+
+namespace selscan {
+
+namespace {
+
+template <typename T> __device__ __forceinline__ float ld1(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ld1<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+}
+template <typename T> __device__ __forceinline__ void st1(T* p, int64_t i, float v);
+template <> __device__ __forceinline__ void st1<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void st1<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+template <bool SP>
+__device__ __forceinline__ float delta_log2(float dl, float bias) {
+    const float vl = __builtin_fmaf(dl, kLog2e, bias * kLog2e);
+    return SP ? softplus_log2(vl) : vl;
+}
+
+__device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
+
+// Sum over the Q lanes of an aligned group (Q a power of two, at most 64).
+template <int Q>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < Q; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Mamba-1: row = (batch, channel), N states, Q = N/4 threads per row.
+template <typename Tin, typename Tout, bool SP, int Q>
+__global__ __launch_bounds__(256) void m1_step_kernel(StepArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t rows = a.batch * a.dim;
+    const int64_t row_raw = gid / Q;
+    const bool ok = row_raw < rows;
+    const int64_t row = ok ? row_raw : rows - 1;
+    const int qi = (int)(gid % Q);
+    const int64_t b = row / a.dim;
+    const int64_t d = row - b * a.dim;
+    const int N = a.N;
+    const Tin* U = reinterpret_cast<const Tin*>(a.u);
+    const Tin* DL = reinterpret_cast<const Tin*>(a.delta);
+    const Tin* Bm = reinterpret_cast<const Tin*>(a.B);
+    const Tin* Cm = reinterpret_cast<const Tin*>(a.C);
+    const float uu = ld1(U, row);
+    const float w = SP ? delta_log2<true>(ld1(DL, row), a.bias ? a.bias[d] : 0.0f)
+                       : delta_log2<false>(ld1(DL, row), a.bias ? a.bias[d] : 0.0f);
+    const float x = (w * kLn2) * uu;   // Delta u
+    float acc = 0.0f;
+    float4* st = reinterpret_cast<float4*>(a.state + row * N) + qi;
+    float4 h = *st;
+    float* hv = reinterpret_cast<float*>(&h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = 4 * qi + i;
+        const float dA = fast_exp2(w * a.A[d * N + n]);
+        hv[i] = __builtin_fmaf(dA, hv[i], x * ld1(Bm, b * N + n));
+        acc = __builtin_fmaf(ld1(Cm, b * N + n), hv[i], acc);
+    }
+    acc = group_sum<Q>(acc);
+    if (!ok) return;
+    *st = h;
+    if (qi == 0) {
+        float yv = a.D ? __builtin_fmaf(a.D[d], uu, acc) : acc;
+        if (a.z) yv *= silu(ld1(reinterpret_cast<const Tin*>(a.z), row));
+        st1(reinterpret_cast<Tout*>(a.y), row, yv);
+    }
+}
+
+// Mamba-1 with N not a multiple of 4: one thread per row.
+template <typename Tin, typename Tout, bool SP>
+__global__ __launch_bounds__(256) void m1_step_rows_kernel(StepArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.batch * a.dim) return;
+    const int64_t b = row / a.dim;
+    const int64_t d = row - b * a.dim;
+    const int N = a.N;
+    const Tin* Bm = reinterpret_cast<const Tin*>(a.B) + b * N;
+    const Tin* Cm = reinterpret_cast<const Tin*>(a.C) + b * N;
+    const float uu = ld1(reinterpret_cast<const Tin*>(a.u), row);
+    const float dl = ld1(reinterpret_cast<const Tin*>(a.delta), row);
+    const float w = delta_log2<SP>(dl, a.bias ? a.bias[d] : 0.0f);
+    const float x = (w * kLn2) * uu;
+    float acc = 0.0f;
+    float* st = a.state + row * N;
+    for (int n = 0; n < N; ++n) {
+        const float hn = __builtin_fmaf(fast_exp2(w * a.A[d * N + n]), st[n], x * ld1(Bm, n));
+        st[n] = hn;
+        acc = __builtin_fmaf(ld1(Cm, n), hn, acc);
+    }
+    float yv = a.D ? __builtin_fmaf(a.D[d], uu, acc) : acc;
+    if (a.z) yv *= silu(ld1(reinterpret_cast<const Tin*>(a.z), row));
+    st1(reinterpret_cast<Tout*>(a.y), row, yv);
+}
+
+// Mamba-2: row = (batch, head, channel), scalar A per head, B/C per group.
+template <typename Tin, typename Tout, bool SP, int Q>
+__global__ __launch_bounds__(256) void m2_step_kernel(StepArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t rows = a.batch * a.H * a.P;
+    const int64_t row_raw = gid / Q;
+    const bool ok = row_raw < rows;
+    const int64_t row = ok ? row_raw : rows - 1;
+    const int qi = (int)(gid % Q);
+    const int64_t bh = row / a.P;
+    const int64_t b = bh / a.H;
+    const int64_t h = bh - b * a.H;
+    const int64_t grp = h / (a.H / a.G);
+    const int N = a.N;
+    const Tin* X = reinterpret_cast<const Tin*>(a.u);
+    const Tin* DT = reinterpret_cast<const Tin*>(a.delta);
+    const Tin* Bm = reinterpret_cast<const Tin*>(a.B) + (b * a.G + grp) * N;
+    const Tin* Cm = reinterpret_cast<const Tin*>(a.C) + (b * a.G + grp) * N;
+    const float xx = ld1(X, row);
+    const float w = SP ? delta_log2<true>(ld1(DT, bh), a.bias ? a.bias[h] : 0.0f)
+                       : delta_log2<false>(ld1(DT, bh), a.bias ? a.bias[h] : 0.0f);
+    const float dA = fast_exp2(w * a.A[h]);
+    const float x = (w * kLn2) * xx;
+    float acc = 0.0f;
+    float4* st = reinterpret_cast<float4*>(a.state + row * N) + qi;
+    float4 s = *st;
+    float* sv = reinterpret_cast<float*>(&s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = 4 * qi + i;
+        sv[i] = __builtin_fmaf(dA, sv[i], x * ld1(Bm, n));
+        acc = __builtin_fmaf(ld1(Cm, n), sv[i], acc);
+    }
+    acc = group_sum<Q>(acc);
+    if (!ok) return;
+    *st = s;
+    if (qi == 0) {
+        float yv = a.D ? __builtin_fmaf(a.D[h], xx, acc) : acc;
+        if (a.z) yv *= silu(ld1(reinterpret_cast<const Tin*>(a.z), row));
+        st1(reinterpret_cast<Tout*>(a.y), row, yv);
+    }
+}
+
+template <typename Tin, typename Tout, bool SP, int Q>
+hipError_t launch_q(const StepArgs& a, int64_t rows, hipStream_t stream, bool mamba2) {
+    const int64_t threads = rows * Q;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (mamba2) {
+        KTime kt("m2_step", stream);
+        hipLaunchKernelGGL((m2_step_kernel<Tin, Tout, SP, Q>), dim3(blocks), dim3(256), 0, stream, a);
+    } else {
+        KTime kt("m1_step", stream);
+        hipLaunchKernelGGL((m1_step_kernel<Tin, Tout, SP, Q>), dim3(blocks), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout, bool SP>
+hipError_t launch_sp(const StepArgs& a, hipStream_t stream, bool mamba2) {
+    const int64_t rows = mamba2 ? a.batch * a.H * a.P : a.batch * a.dim;
+    switch (a.N) {
+        case 4: return launch_q<Tin, Tout, SP, 1>(a, rows, stream, mamba2);
+        case 8: return launch_q<Tin, Tout, SP, 2>(a, rows, stream, mamba2);
+        case 16: return launch_q<Tin, Tout, SP, 4>(a, rows, stream, mamba2);
+        case 32: return launch_q<Tin, Tout, SP, 8>(a, rows, stream, mamba2);
+        case 64: return launch_q<Tin, Tout, SP, 16>(a, rows, stream, mamba2);
+        case 128: return launch_q<Tin, Tout, SP, 32>(a, rows, stream, mamba2);
+        default:
+            if (mamba2 || a.N < 1 || a.N > 16) return hipErrorInvalidValue;
+            {
+                KTime kt("m1_step", stream);
+                hipLaunchKernelGGL((m1_step_rows_kernel<Tin, Tout, SP>), dim3((unsigned)((rows + 255) / 256)),
+                                   dim3(256), 0, stream, a);
+            }
+            return hipGetLastError();
+    }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_dt(const StepArgs& a, hipStream_t stream, bool mamba2) {
+    return a.softplus ? launch_sp<Tin, Tout, true>(a, stream, mamba2) : launch_sp<Tin, Tout, false>(a, stream, mamba2);
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, int mamba2, hipStream_t stream) {
+    if (in_bf16 && out_bf16) return launch_dt<uint16_t, uint16_t>(a, stream, mamba2 != 0);
+    if (in_bf16) return launch_dt<uint16_t, float>(a, stream, mamba2 != 0);
+    if (out_bf16) return launch_dt<float, uint16_t>(a, stream, mamba2 != 0);
+    return launch_dt<float, float>(a, stream, mamba2 != 0);
+}
+
+}  // namespace selscan

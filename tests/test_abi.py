@@ -93,6 +93,46 @@ def test_m2_bad_shape_rejected(field, value, status):
     assert r == status
 
 
+@pytest.mark.parametrize("field,value,status", [
+    ("dim", 0, ss.ERR_INVALID_ARG), ("dstate", 17, ss.ERR_UNSUPPORTED), ("out_dtype", 5, ss.ERR_UNSUPPORTED)])
+def test_step_bad_shape_rejected(field, value, status):
+    s = _m1(**{field: value})
+    r = ss.lib().selscan_step(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE, None)
+    assert r == status and ss.last_error()
+
+
+def test_step_null_state_and_misaligned_state_rejected():
+    s = _m1()
+    assert ss.lib().selscan_step(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE,
+                                 None) == ss.ERR_INVALID_ARG
+    assert ss.lib().selscan_step(ctypes.byref(s), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE,
+                                 None) == ss.ERR_INVALID_ARG
+    m2 = _m2(dstate=64)
+    assert ss.lib().selscan_mamba2_step(ctypes.byref(m2), FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                        1, FAKE, None) == ss.ERR_INVALID_ARG
+    assert "aligned" in ss.last_error()
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dstate", 8, ss.ERR_UNSUPPORTED), ("ngroups", 3, ss.ERR_INVALID_ARG), ("headdim", 0, ss.ERR_INVALID_ARG)])
+def test_m2_step_bad_shape_rejected(field, value, status):
+    s = _m2(**{field: value})
+    r = ss.lib().selscan_mamba2_step(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1,
+                                     FAKE, None)
+    assert r == status
+
+
+def test_h0_entry_points_validate_like_fwd():
+    s = _m1(dstate=17)
+    r = ss.lib().selscan_fwd_h0(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, FAKE,
+                                None, None)
+    assert r == ss.ERR_UNSUPPORTED
+    m2 = _m2(ngroups=3)
+    r = ss.lib().selscan_mamba2_fwd_h0(ctypes.byref(m2), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None,
+                                       FAKE, None, None)
+    assert r == ss.ERR_INVALID_ARG
+
+
 def test_workspace_sizes_are_consistent():
     # the fp32 copy of B and C is always needed; a long sequence is split
     # into chunks and needs room for the chunk states too
