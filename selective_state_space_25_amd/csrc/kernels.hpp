@@ -96,5 +96,8 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, int mamba2, hipStream_t stream);
 hipError_t launch_m2(const M2Args& a, int in_bf16, int out_bf16, hipStream_t stream);
+// Chunked matrix (SSD) form on MFMA for bf16 inputs, P = 64, N in {64, 128}.
+bool m2_ssd_supported(const M2Args& a, int in_bf16);
+hipError_t launch_m2_ssd(const M2Args& a, int out_bf16, hipStream_t stream);
 
 }  // namespace selscan

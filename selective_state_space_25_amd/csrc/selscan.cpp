@@ -316,14 +316,27 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* s, const void* 
         if (st != SELSCAN_OK) return st;
         const M2Plan plan = plan_m2(s);
         hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-        Scratch ws;
-        st = ws.get(s->workspace, s->workspace_bytes, plan.ws_bytes, hs);
-        if (st != SELSCAN_OK) return st;
         selscan::M2Args a{};
         a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.dt_bias = dt_bias;
         a.y = y; a.last = last_state; a.h0 = h0;
         a.batch = s->batch; a.L = s->seqlen; a.H = s->nheads; a.P = s->headdim; a.G = s->ngroups; a.N = s->dstate;
         a.chunks = plan.chunks; a.chunk = plan.chunk; a.softplus = softplus;
+        const int in_bf16 = s->in_dtype == SELSCAN_BF16, out_bf16 = s->out_dtype == SELSCAN_BF16;
+        if (env_int("SELSCAN_M2_SSD", 1) != 0 && selscan::m2_ssd_supported(a, in_bf16) && aligned16(x) &&
+            aligned16(B) && aligned16(C)) {
+            // chunked matrix form on MFMA; needs no workspace
+            if (log_plans())
+                std::fprintf(stderr, "[selscan] m2 ssd B=%lld L=%lld H=%lld P=%lld G=%lld N=%lld\n",
+                             (long long)s->batch, (long long)s->seqlen, (long long)s->nheads, (long long)s->headdim,
+                             (long long)s->ngroups, (long long)s->dstate);
+            hipError_t e = selscan::launch_m2_ssd(a, out_bf16, hs);
+            if (e != hipSuccess)
+                return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+            return ok();
+        }
+        Scratch ws;
+        st = ws.get(s->workspace, s->workspace_bytes, plan.ws_bytes, hs);
+        if (st != SELSCAN_OK) return st;
         char* base = static_cast<char*>(ws.ptr);
         a.ws_bc = reinterpret_cast<float*>(base);
         if (plan.chunks > 1) {
@@ -335,7 +348,7 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* s, const void* 
                          (long long)s->batch, (long long)s->seqlen, (long long)s->nheads, (long long)s->headdim,
                          (long long)s->ngroups, (long long)s->dstate, plan.chunks, (long long)plan.chunk,
                          plan.ws_bytes);
-        hipError_t e = selscan::launch_m2(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, hs);
+        hipError_t e = selscan::launch_m2(a, in_bf16, out_bf16, hs);
         ws.release();
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
         return ok();

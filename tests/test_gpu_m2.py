@@ -109,6 +109,18 @@ def test_causality_bitwise(gpu, monkeypatch):
     assert not torch.equal(y0[:, t0:], y1[:, t0:])
 
 
+@pytest.mark.parametrize("N,G,L", [(64, 1, 200), (128, 2, 333), (128, 4, 64)])
+def test_chunked_mfma_form_matches_recurrent_form(gpu, monkeypatch, N, G, L):
+    """The chunked matrix form (bf16 inputs, headdim 64, N 64 or 128) and the
+    recurrent form agree with each other and with the oracle."""
+    inp = _inputs(2, L, 4, 64, G, N, torch.bfloat16, seed=N + G)
+    y_ssd, l_ssd = _full_compare(inp)
+    monkeypatch.setenv("SELSCAN_M2_SSD", "0")
+    y_rec, l_rec = _full_compare(inp)
+    check_close(host(y_ssd).double().numpy(), host(y_rec).double().numpy(), TOL_BF16, "y ssd vs recurrent")
+    check_close(host(l_ssd).double().numpy(), host(l_rec).double().numpy(), TOL_BF16, "state ssd vs recurrent")
+
+
 def test_full_size_workload_sampled(gpu):
     """Mamba-2 workload at full size: sampled (batch, head) units."""
     w = synth.WORKLOADS["mamba2_mh"]
