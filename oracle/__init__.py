@@ -54,6 +54,8 @@ def _load():
             lib.oracle_m1_f64.restype = ctypes.c_int
             lib.oracle_m2_f64.argtypes = [i64] * 6 + [dp] * 8 + [ctypes.c_int, dp, dp, dp]
             lib.oracle_m2_f64.restype = ctypes.c_int
+            lib.oracle_conv1d_f64.argtypes = [i64] * 4 + [dp] * 3 + [ctypes.c_int, dp]
+            lib.oracle_conv1d_f64.restype = ctypes.c_int
             lib.oracle_version.restype = ctypes.c_char_p
             _lib = lib
     return _lib
@@ -139,6 +141,23 @@ def m2(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, h0=None):
     if rc != 0:
         raise RuntimeError(f"oracle_m2_f64 failed with status {rc}")
     return y, last
+
+
+def conv1d(x, w, bias=None, silu=True):
+    """Causal depthwise convolution in fp64: x [batch, dim, L], w [dim, K],
+    bias [dim]; out[t] = act(bias + sum_k w[k] x[t - (K - 1) + k]), zero
+    before the first token.  Returns out [batch, dim, L] float64."""
+    x = _f64(x)
+    nb, nd, nl = x.shape
+    w = _f64(w)
+    nk = w.shape[1]
+    w = _f64(w, (nd, nk))
+    bias = _f64(bias, (nd,))
+    out = np.empty((nb, nd, nl), np.float64)
+    rc = _load().oracle_conv1d_f64(nb, nd, nl, nk, _ptr(x), _ptr(w), _ptr(bias), int(bool(silu)), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv1d_f64 failed with status {rc}")
+    return out
 
 
 def version() -> str:

@@ -177,3 +177,35 @@ int oracle_m2_f64(int64_t nb, int64_t nl, int64_t nh, int64_t np, int64_t ng,
     }
     return status;
 }
+
+/*
+ * Causal depthwise convolution ahead of the scan (blog "Understanding Mamba
+ * ..." section 3.3: a width-4 1-D convolution whose output at a position
+ * sees that token and the three before it; the README's causal-conv1d layer
+ * inside the Mamba block), one channel row at a time:
+ *
+ *   out[b,d,t] = act( bias[d] + sum_{k=0}^{nk-1} w[d,k] * x[b,d,t-(nk-1)+k] ),
+ *
+ * x before the first token taken as 0, act = silu when `silu` else identity.
+ *   x, out : [nb, nd, nl];  w : [nd, nk];  bias : [nd] or NULL.
+ */
+int oracle_conv1d_f64(int64_t nb, int64_t nd, int64_t nl, int64_t nk, const double* x, const double* w,
+                      const double* bias, int silu, double* out) {
+    if (nb < 1 || nd < 1 || nl < 1 || nk < 1 || !x || !w || !out) return ORACLE_BAD_ARG;
+    const int64_t rows = nb * nd;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t d = r % nd;
+        const double* xr = x + r * nl;
+        double* orow = out + r * nl;
+        for (int64_t t = 0; t < nl; ++t) {
+            double acc = bias ? bias[d] : 0.0;
+            for (int64_t k = 0; k < nk; ++k) {
+                const int64_t s = t - (nk - 1) + k;
+                if (s >= 0) acc += w[d * nk + k] * xr[s];
+            }
+            orow[t] = silu ? silu64(acc) : acc;
+        }
+    }
+    return ORACLE_OK;
+}

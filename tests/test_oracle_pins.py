@@ -406,3 +406,56 @@ def test_oracle_matches_stored_fixture(name):
     y, last = fn(**ins, softplus=fx["softplus"])
     np.testing.assert_allclose(y, np.array(fx["y"]), rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(last, np.array(fx["last_state"]), rtol=1e-14, atol=1e-15)
+
+
+# ---- causal depthwise convolution (blog section 3.3; README causal-conv1d) --
+#   term / mistake                 caught by
+#   kernel orientation (k order)   numpy.convolve, shift kernel
+#   causal offset / zero padding   shift kernel, numpy.convolve, causality
+#   [dim, K] layout of w, bias     numpy.convolve with distinct rows
+#   silu after the bias            numpy.convolve + scipy expit
+
+def _silu(v):
+    return v * expit(v)
+
+
+@pytest.mark.parametrize("K", [1, 2, 4, 7])
+@pytest.mark.parametrize("silu", [False, True])
+def test_conv1d_matches_numpy_convolve(K, silu):
+    rng = np.random.default_rng(100 + K)
+    x = rng.standard_normal((2, 5, 23))
+    w = rng.standard_normal((5, K))
+    bias = rng.standard_normal(5)
+    out = oracle.conv1d(x, w, bias, silu=silu)
+    for b in range(2):
+        for d in range(5):
+            ref = np.convolve(x[b, d], w[d, ::-1])[:23] + bias[d]
+            if silu:
+                ref = _silu(ref)
+            np.testing.assert_allclose(out[b, d], ref, rtol=RTOL, atol=1e-13)
+
+
+def test_conv1d_identity_and_shift_kernels():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 3, 12))
+    ident = np.zeros((3, 4))
+    ident[:, 3] = 1.0
+    assert np.array_equal(oracle.conv1d(x, ident, None, silu=False), x)
+    shift = np.zeros((3, 4))
+    shift[:, 0] = 1.0
+    out = oracle.conv1d(x, shift, None, silu=False)
+    assert np.array_equal(out[..., 3:], x[..., :-3])
+    assert np.array_equal(out[..., :3], np.zeros((1, 3, 3)))
+
+
+def test_conv1d_is_causal():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 4, 30))
+    w = rng.standard_normal((4, 4))
+    base = oracle.conv1d(x, w, None, silu=True)
+    x2 = x.copy()
+    x2[:, :, 17] += 3.0
+    pert = oracle.conv1d(x2, w, None, silu=True)
+    assert np.array_equal(base[..., :17], pert[..., :17])
+    assert not np.array_equal(base[..., 17:21], pert[..., 17:21])
+    assert np.array_equal(base[..., 21:], pert[..., 21:])
