@@ -183,6 +183,38 @@ def time_decode(name, steps, device):
             "kernel_state_updates_per_s": rows * w.dstate / (us * 1e-6)}
 
 
+def time_conv1d(name, steps, device, width=4):
+    """Causal depthwise conv (+ SiLU) over a workload's u-shaped input, bf16
+    in and out: an HBM stream (one read of x, one write of out)."""
+    import torch
+    import selective_state_space_25_amd as ss
+    import synth
+
+    w = synth.WORKLOADS[name]
+    g = torch.Generator(device=device).manual_seed(0)
+    x = torch.randn((w.batch, w.dim, w.seqlen), generator=g, device=device, dtype=torch.float32).to(w.dtype)
+    wt = torch.randn((w.dim, width), generator=g, device=device, dtype=torch.float32) * 0.5
+    bias = torch.randn((w.dim,), generator=g, device=device, dtype=torch.float32)
+    out = torch.empty_like(x)
+    f = lambda: ss.conv1d(x, wt, bias, silu=True, out=out)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    ss.timing_collect()
+    ss.timing_enable(True)
+    try:
+        for _ in range(steps):
+            f()
+        torch.cuda.synchronize()
+    finally:
+        ss.timing_enable(False)
+    k = list(ss.timing_collect().values())[0]
+    nbytes = 2 * x.numel() * x.element_size() + (w.dim * (width + 1)) * 4
+    return {"shape_of": name, "width": width, "dtype": str(w.dtype).replace("torch.", ""),
+            "kernel_ms": k["avg_ms"], "bytes": nbytes, "gbs": nbytes / (k["avg_ms"] * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (k["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def dominant_kernel(res):
     name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["total_ms"])
     return name, k
@@ -330,6 +362,7 @@ def main():
         "library": ss.version(),
     }
     line["decode"] = {n: time_decode(n, 200, device) for n in ("mamba2p8b_l8k", "mamba2_mh")}
+    line["conv1d"] = time_conv1d("mamba2p8b_l8k", 10, device)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
     print(json.dumps(line))

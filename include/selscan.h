@@ -204,6 +204,28 @@ selscan_status_t selscan_mamba2_step(const selscan_m2_shape_t* shape, float* sta
                                      const void* z, const float* dt_bias, int softplus,
                                      void* y, void* stream);
 
+/*
+ * Causal depthwise convolution ahead of the scan (section 3.3 of the
+ * "Understanding Mamba ..." blog: a width-4 convolution whose output at a
+ * token sees it and the three before it; the README's causal-conv1d layer):
+ *   out[b,d,t] = act(bias[d] + sum_{k<K} weight[d,k] x[b,d,t-(K-1)+k]),
+ * x before the first token taken as zero, act = silu when silu == 1, else
+ * identity.  weight[d, K-1] multiplies the current token.
+ *   x       [B, D, L]  in_dtype
+ *   weight  [D, K]     fp32
+ *   bias    [D]        fp32, NULL = 0
+ *   out     [B, D, L]  out_dtype (written; must not alias x)
+ * width K in 1..64 (UNSUPPORTED above); no workspace; asynchronous on stream.
+ */
+typedef struct {
+    int64_t batch, dim, seqlen, width;
+    int32_t in_dtype, out_dtype;
+} selscan_conv_shape_t;
+
+selscan_status_t selscan_conv1d(const selscan_conv_shape_t* shape, const void* x,
+                                const float* weight, const float* bias, int silu,
+                                void* out, void* stream);
+
 /* Message for the last failed call on this thread ("" after a success).
  * The string stays valid until the next call on the same thread. */
 const char* selscan_last_error(void);

@@ -47,8 +47,13 @@ class M2Shape(ctypes.Structure):
 _lib = None
 
 EXPORTED = ("selscan_fwd", "selscan_mamba2_fwd", "selscan_workspace_bytes", "selscan_mamba2_workspace_bytes",
-            "selscan_fwd_h0", "selscan_mamba2_fwd_h0", "selscan_step", "selscan_mamba2_step",
+            "selscan_fwd_h0", "selscan_mamba2_fwd_h0", "selscan_step", "selscan_mamba2_step", "selscan_conv1d",
             "selscan_last_error", "selscan_version", "selscan_timing_enable", "selscan_timing_collect")
+
+
+class ConvShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("width", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
 class KernelTime(ctypes.Structure):
@@ -78,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.selscan_step.restype = i32
         L.selscan_mamba2_step.argtypes = [ctypes.POINTER(M2Shape), fp, vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, vp]
         L.selscan_mamba2_step.restype = i32
+        L.selscan_conv1d.argtypes = [ctypes.POINTER(ConvShape), vp, fp, fp, i32, vp, vp]
+        L.selscan_conv1d.restype = i32
         L.selscan_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
         L.selscan_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_mamba2_workspace_bytes.argtypes = [ctypes.POINTER(M2Shape)]
@@ -289,6 +296,28 @@ def mamba2_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, in_d
     return int(lib().selscan_mamba2_workspace_bytes(ctypes.byref(s)))
 
 
+def conv1d(x, weight, bias=None, silu=True, out=None, out_dtype=None):
+    """Causal depthwise convolution: x [batch, dim, L] (float32 or bfloat16),
+    weight [dim, K] and bias [dim] float32.  out[t] = act(bias + sum_k
+    weight[k] x[t - (K - 1) + k]), act = silu or identity.  Returns out
+    [batch, dim, L] in x's dtype unless out_dtype or out says otherwise."""
+    torch = _torch()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.conv1d needs tensors on a GPU device")
+    batch, dim, L = x.shape
+    K = weight.shape[1]
+    odt = (out.dtype if out is not None else x.dtype) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=odt, device=dev)
+    s = ConvShape(batch, dim, L, K, _dtype_code(x), _dtype_code(out))
+    _check(lib().selscan_conv1d(
+        ctypes.byref(s), _ptr(x, "x", (batch, dim, L), x.dtype, dev),
+        _ptr(weight, "weight", (dim, K), torch.float32, dev), _ptr(bias, "bias", (dim,), torch.float32, dev),
+        int(bool(silu)), _ptr(out, "out", (batch, dim, L), odt, dev), _stream_handle(dev)))
+    return out
+
+
 def timing_enable(on: bool) -> None:
     """Bracket every later kernel launch with HIP events on its own stream."""
     _check(lib().selscan_timing_enable(int(bool(on))))
@@ -309,5 +338,5 @@ def timing_collect() -> dict:
     return res
 
 
-__all__ = ["step", "mamba2_step", "timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
+__all__ = ["conv1d", "ConvShape", "step", "mamba2_step", "timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
            "SelscanError", "Shape", "M2Shape", "m1_shape", "EXPORTED", "LIB_PATH"]

@@ -95,6 +95,19 @@ struct StepArgs {
     int softplus;
 };
 hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, int mamba2, hipStream_t stream);
+
+// Causal depthwise convolution: x, out [batch, dim, L]; w [dim, K]; bias [dim].
+struct ConvArgs {
+    const void* x;
+    const float* w;
+    const float* bias;
+    void* out;
+    int64_t batch, dim, L;
+    int K;
+    int silu;
+    int vec_ok;   // L % 8 == 0 and 16-byte aligned rows of x and out
+};
+hipError_t launch_conv1d(const ConvArgs& a, int in_bf16, int out_bf16, hipStream_t stream);
 hipError_t launch_m2(const M2Args& a, int in_bf16, int out_bf16, hipStream_t stream);
 // Chunked matrix (SSD) form on MFMA for bf16 inputs, P = 64, N in {64, 128}.
 bool m2_ssd_supported(const M2Args& a, int in_bf16);

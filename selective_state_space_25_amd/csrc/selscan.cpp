@@ -425,4 +425,34 @@ selscan_status_t selscan_mamba2_step(const selscan_m2_shape_t* s, float* state, 
     }
 }
 
+selscan_status_t selscan_conv1d(const selscan_conv_shape_t* s, const void* x, const float* weight,
+                                const float* bias, int silu, void* out, void* stream) {
+    try {
+        if (!s) return fail(SELSCAN_ERR_INVALID_ARG, "shape is NULL");
+        if (s->batch < 1 || s->dim < 1 || s->seqlen < 1 || s->width < 1)
+            return fail(SELSCAN_ERR_INVALID_ARG, "batch, dim, seqlen and width must all be >= 1");
+        if (s->width > 64) return fail(SELSCAN_ERR_UNSUPPORTED, "conv1d supports width <= 64");
+        if ((s->in_dtype != SELSCAN_F32 && s->in_dtype != SELSCAN_BF16) ||
+            (s->out_dtype != SELSCAN_F32 && s->out_dtype != SELSCAN_BF16))
+            return fail(SELSCAN_ERR_UNSUPPORTED, "dtypes must be SELSCAN_F32 or SELSCAN_BF16");
+        if (mul_checked({s->batch, s->dim, s->seqlen, 4}) < 0 || mul_checked({s->dim, s->width, 4}) < 0)
+            return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
+        if (!x || !weight || !out) return fail(SELSCAN_ERR_INVALID_ARG, "x, weight and out must be non-NULL");
+        if (silu != 0 && silu != 1) return fail(SELSCAN_ERR_INVALID_ARG, "silu must be 0 or 1");
+        if (x == out) return fail(SELSCAN_ERR_INVALID_ARG, "out must not alias x");
+        selscan_status_t st = device_check();
+        if (st != SELSCAN_OK) return st;
+        const int in_bf16 = s->in_dtype == SELSCAN_BF16, out_bf16 = s->out_dtype == SELSCAN_BF16;
+        selscan::ConvArgs a{};
+        a.x = x; a.w = weight; a.bias = bias; a.out = out;
+        a.batch = s->batch; a.dim = s->dim; a.L = s->seqlen; a.K = (int)s->width; a.silu = silu;
+        a.vec_ok = s->seqlen % 8 == 0 && aligned16(x) && aligned16(out);
+        hipError_t e = selscan::launch_conv1d(a, in_bf16, out_bf16, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(SELSCAN_ERR_LAUNCH, "unexpected host exception");
+    }
+}
+
 }  // extern "C"

@@ -150,3 +150,21 @@ def test_binding_refuses_cpu_tensors():
     u = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         ss.fwd(u, u, torch.zeros(4, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, ss.ERR_INVALID_ARG), ("width", 0, ss.ERR_INVALID_ARG), ("width", 65, ss.ERR_UNSUPPORTED),
+    ("in_dtype", 3, ss.ERR_UNSUPPORTED), ("seqlen", 1 << 62, ss.ERR_INVALID_ARG)])
+def test_conv1d_bad_shape_rejected(field, value, status):
+    base = dict(batch=1, dim=4, seqlen=16, width=4, in_dtype=ss.BF16, out_dtype=ss.BF16)
+    base[field] = value
+    s = ss.ConvShape(base["batch"], base["dim"], base["seqlen"], base["width"], base["in_dtype"], base["out_dtype"])
+    assert ss.lib().selscan_conv1d(ctypes.byref(s), FAKE, FAKE, None, 1, FAKE + 64, None) == status
+
+
+def test_conv1d_rejects_null_alias_and_bad_flag():
+    s = ss.ConvShape(1, 4, 16, 4, ss.BF16, ss.BF16)
+    assert ss.lib().selscan_conv1d(ctypes.byref(s), None, FAKE, None, 1, FAKE, None) == ss.ERR_INVALID_ARG
+    assert ss.lib().selscan_conv1d(ctypes.byref(s), FAKE, FAKE, None, 1, FAKE, None) == ss.ERR_INVALID_ARG
+    assert "alias" in ss.last_error()
+    assert ss.lib().selscan_conv1d(ctypes.byref(s), FAKE, FAKE, None, 3, FAKE + 64, None) == ss.ERR_INVALID_ARG
