@@ -522,31 +522,44 @@ void m1_scan_kernel(M1Args a) {
         run_chunk<Tin, Tout, MODE, false, SP>(a, b, d0, g, lds, lds_base);
 }
 
-// B, C [batch, N, L] -> fp32 [batch, L, (B0..B15, C0..C15)] (zeros past N)
+// B, C [batch, N, L] -> fp32 [batch, L, (B0..B15, C0..C15)] (zeros past N).
+// A workgroup converts 32 tokens of one batch: coalesced reads along L of
+// the 32 source rows, a transpose through LDS, coalesced 128-byte records.
 template <typename Tin>
 __global__ __launch_bounds__(256) void m1_bc_kernel(M1Args a) {
-    const int64_t total = a.batch * a.L;
+    __shared__ float tr[32][33];
+    const int64_t tiles = (a.L + 31) / 32;
+    const int64_t b = blockIdx.x / tiles;
+    const int64_t t0 = (blockIdx.x - b * tiles) * 32;
     const Tin* B = reinterpret_cast<const Tin*>(a.B);
     const Tin* C = reinterpret_cast<const Tin*>(a.C);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t b = i / a.L;
-        const int64_t t = i - b * a.L;
-        float v[2 * kNS];
+    {
+        const int e = threadIdx.x >> 3;          // source row: B_0..B_15, C_0..C_15
+        const int tt = (threadIdx.x & 7) * 4;    // four tokens
+        const int n = e & (kNS - 1);
+        const Tin* src = (e < kNS) ? B : C;
 #pragma unroll
-        for (int n = 0; n < kNS; ++n) {
-            v[n] = n < a.N ? In<Tin>::ld(B, (b * a.N + n) * a.L + t) : 0.0f;
-            v[kNS + n] = n < a.N ? In<Tin>::ld(C, (b * a.N + n) * a.L + t) : 0.0f;
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = t0 + tt + j;
+            tr[tt + j][e] = (n < a.N && t < a.L) ? In<Tin>::ld(src, (b * a.N + n) * a.L + t) : 0.0f;
         }
-        float4* o = reinterpret_cast<float4*>(a.bcq + i * (2 * kNS));
-#pragma unroll
-        for (int q = 0; q < 2 * kNS / 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+    __syncthreads();
+    {
+        const int tt = threadIdx.x >> 3;         // token of the record
+        const int e4 = (threadIdx.x & 7) * 4;    // four values of it
+        const int64_t t = t0 + tt;
+        if (t < a.L)
+            *reinterpret_cast<float4*>(a.bcq + (b * a.L + t) * (2 * kNS) + e4) =
+                make_float4(tr[tt][e4], tr[tt][e4 + 1], tr[tt][e4 + 2], tr[tt][e4 + 3]);
     }
 }
 
 // Carry pass: one thread per (row, n).  Turns the per-chunk end states b_g
 // (slot g) into carries-in h_in(g) (slot g), in chunk order:
 //   h_in(0) = h0 (or 0),   h_in(g+1) = 2^(A[d,n] W_g) h_in(g) + b_g.
+// The summaries are read sixteen chunks at a time before the dependent chain
+// runs over them, so their loads overlap.
 __global__ __launch_bounds__(256) void m1_carry_kernel(M1Args a) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t rows = a.batch * a.dim;
@@ -558,16 +571,28 @@ __global__ __launch_bounds__(256) void m1_carry_kernel(M1Args a) {
     float h = (a.h0 && n < a.N) ? a.h0[row * a.N + n] : 0.0f;
     float* st = a.ws_state + row * a.G * kNS + n;
     const float* W = a.ws_w + row * a.G;
-    for (int g = 0; g < a.G; ++g) {
-        const float bg = (g < a.G - 1) ? st[(int64_t)g * kNS] : 0.0f;
-        st[(int64_t)g * kNS] = h;
-        if (g < a.G - 1) h = __builtin_fmaf(fast_exp2(An * W[g]), h, bg);
+    for (int g0 = 0; g0 < a.G; g0 += 16) {
+        float bg[16], wg[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int g = g0 + j;
+            bg[j] = (g < a.G - 1) ? st[(int64_t)g * kNS] : 0.0f;
+            wg[j] = (g < a.G - 1) ? W[g] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int g = g0 + j;
+            if (g < a.G) {
+                st[(int64_t)g * kNS] = h;
+                h = __builtin_fmaf(fast_exp2(An * wg[j]), h, bg[j]);
+            }
+        }
     }
 }
 
 template <typename Tin, typename Tout, bool SP>
 hipError_t launch_sp(const M1Args& a, hipStream_t stream) {
-    const int64_t bc_blocks = std::min<int64_t>((a.batch * a.L + 255) / 256, 16384);
+    const int64_t bc_blocks = a.batch * ((a.L + 31) / 32);
     {
         KTime kt("m1_bc_convert", stream);
         hipLaunchKernelGGL((m1_bc_kernel<Tin>), dim3((unsigned)bc_blocks), dim3(256), 0, stream, a);

@@ -98,8 +98,8 @@ selscan_status_t check_m1_shape(const selscan_shape_t* s) {
     if (mul_checked({s->batch, s->dim, s->seqlen, 4}) < 0 || mul_checked({s->batch, s->dstate, s->seqlen, 4}) < 0 ||
         mul_checked({s->batch, s->dim, 64, 4}) < 0)
         return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
-    if (s->batch * ((s->dim + 255) / 256) > 0x7fffffff)
-        return fail(SELSCAN_ERR_UNSUPPORTED, "too many channel blocks for one launch");
+    if (s->batch * ((s->dim + 63) / 64) > 0x7fffffff || s->batch * ((s->seqlen + 31) / 32) > 0x7fffffff)
+        return fail(SELSCAN_ERR_UNSUPPORTED, "too many channel blocks or token tiles for one launch");
     return SELSCAN_OK;
 }
 
