@@ -209,3 +209,94 @@ int oracle_conv1d_f64(int64_t nb, int64_t nd, int64_t nl, int64_t nk, const doub
     }
     return ORACLE_OK;
 }
+
+/*
+ * Gradients of the Mamba-1 scan (reverse-mode, fp64), for
+ *   out_t = y_t * silu(z_t),  y_t = sum_n C_t[n] h_t[n] + D u_t,
+ *   h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t u_t,  Delta_t = sp(delta_t + bias),
+ * given dout = d loss / d out.  The adjoint of the state runs backward in
+ * time: lam_t = dy_t C_t + exp(Delta_{t+1} A) lam_{t+1}, and each input's
+ * gradient collects lam_t times the partial derivative of h_t's update
+ * (the chain rule through the recurrence, no shortcut).  h0 = 0.
+ * Outputs (all written, all fp64): du, ddelta, dz [nb,nd,nl]; dA [nd,nn];
+ * dB, dC [nb,nn,nl]; dD, dbias [nd].  z, D, bias may be NULL (then their
+ * gradients are written as 0 and the corresponding terms vanish).
+ * Rows are processed one after another so that the sums over channels of
+ * dB, dC, dA, dD, dbias are plain sequential sums.
+ */
+int oracle_m1_bwd_f64(int64_t nb, int64_t nd, int64_t nn, int64_t nl, const double* u, const double* delta,
+                      const double* A, const double* Bm, const double* Cm, const double* Dv, const double* z,
+                      const double* bias, int softplus, const double* dout, double* du, double* ddelta,
+                      double* dA, double* dBm, double* dCm, double* dD, double* dz, double* dbias) {
+    if (nb < 1 || nd < 1 || nn < 1 || nl < 1 || !u || !delta || !A || !Bm || !Cm || !dout || !du || !ddelta ||
+        !dA || !dBm || !dCm || !dD || !dz || !dbias)
+        return ORACLE_BAD_ARG;
+    double* h = (double*)malloc(sizeof(double) * (size_t)(nl + 1) * (size_t)nn);   /* h_{-1} .. h_{L-1} */
+    double* lam = (double*)malloc(sizeof(double) * (size_t)nn);
+    double* dl = (double*)malloc(sizeof(double) * (size_t)nl);
+    if (!h || !lam || !dl) {
+        free(h); free(lam); free(dl);
+        return ORACLE_NO_MEM;
+    }
+    for (int64_t i = 0; i < nd * nn; ++i) dA[i] = 0.0;
+    for (int64_t i = 0; i < nd; ++i) { dD[i] = 0.0; dbias[i] = 0.0; }
+    for (int64_t i = 0; i < nb * nn * nl; ++i) { dBm[i] = 0.0; dCm[i] = 0.0; }
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t d = 0; d < nd; ++d) {
+            const int64_t row = b * nd + d;
+            const double* ur = u + row * nl;
+            const double* xr = delta + row * nl;
+            const double* zr = z ? z + row * nl : NULL;
+            const double* gr = dout + row * nl;
+            /* forward, keeping every state */
+            for (int64_t n = 0; n < nn; ++n) h[n] = 0.0;
+            for (int64_t t = 0; t < nl; ++t) {
+                const double x = xr[t] + (bias ? bias[d] : 0.0);
+                dl[t] = softplus ? sp64(x) : x;
+                for (int64_t n = 0; n < nn; ++n) {
+                    const double a = exp(dl[t] * A[d * nn + n]);
+                    h[(t + 1) * nn + n] = a * h[t * nn + n] + dl[t] * Bm[(b * nn + n) * nl + t] * ur[t];
+                }
+            }
+            /* backward */
+            for (int64_t n = 0; n < nn; ++n) lam[n] = 0.0;
+            for (int64_t t = nl - 1; t >= 0; --t) {
+                double y = Dv ? Dv[d] * ur[t] : 0.0;
+                for (int64_t n = 0; n < nn; ++n) y += Cm[(b * nn + n) * nl + t] * h[(t + 1) * nn + n];
+                double dy = gr[t];
+                if (zr) {
+                    const double zz = zr[t];
+                    const double sg = 1.0 / (1.0 + exp(-zz));
+                    dz[row * nl + t] = gr[t] * y * sg * (1.0 + zz * (1.0 - sg));
+                    dy = gr[t] * zz * sg;
+                } else {
+                    dz[row * nl + t] = 0.0;
+                }
+                double dut = Dv ? dy * Dv[d] : 0.0;
+                if (Dv) dD[d] += dy * ur[t];
+                double ddl = 0.0;
+                for (int64_t n = 0; n < nn; ++n) {
+                    const double c = Cm[(b * nn + n) * nl + t];
+                    const double bb = Bm[(b * nn + n) * nl + t];
+                    /* lam_t = dy C_t + a_{t+1} lam_{t+1}; lam[] holds a_{t+1} lam_{t+1} */
+                    const double l = dy * c + lam[n];
+                    dCm[(b * nn + n) * nl + t] += dy * h[(t + 1) * nn + n];
+                    dBm[(b * nn + n) * nl + t] += l * dl[t] * ur[t];
+                    dut += l * dl[t] * bb;
+                    const double a = exp(dl[t] * A[d * nn + n]);
+                    const double hp = h[t * nn + n];
+                    ddl += l * (bb * ur[t] + A[d * nn + n] * a * hp);
+                    dA[d * nn + n] += l * dl[t] * a * hp;
+                    lam[n] = a * l;   /* a_t lam_t, carried to token t-1 */
+                }
+                du[row * nl + t] = dut;
+                const double x = xr[t] + (bias ? bias[d] : 0.0);
+                const double dx = softplus ? ddl / (1.0 + exp(-x)) : ddl;   /* sp'(x) = sigmoid(x) */
+                ddelta[row * nl + t] = dx;
+                if (bias) dbias[d] += dx;
+            }
+        }
+    }
+    free(h); free(lam); free(dl);
+    return ORACLE_OK;
+}

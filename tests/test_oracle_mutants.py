@@ -30,6 +30,13 @@ MUTANTS = {
     "m2_group": ("const int64_t g = hh / heads_per_group;", "const int64_t g = hh % ng;"),
     "m2_dt_head": ("double xv = dt[bt * nh + hh] + (dtb ? dtb[hh] : 0.0);", "double xv = dt[bt * nh + (hh % 1)] + (dtb ? dtb[hh] : 0.0);"),
     "m2_state_order": ("s[n] = dA * s[n] + delt * Bt[n] * xt;", "s[n] = dA * s[n] + delt * Bt[nn - 1 - n] * xt;"),
+    "bwd_adjoint_undecayed": ("lam[n] = a * l;", "lam[n] = l;"),
+    "bwd_no_state_path": ("ddl += l * (bb * ur[t] + A[d * nn + n] * a * hp);", "ddl += l * (bb * ur[t]);"),
+    "bwd_softplus_derivative": ("ddl / (1.0 + exp(-x))", "ddl / (1.0 + exp(x))"),
+    "bwd_dc_previous_state": ("dCm[(b * nn + n) * nl + t] += dy * h[(t + 1) * nn + n];",
+                              "dCm[(b * nn + n) * nl + t] += dy * h[t * nn + n];"),
+    "conv_kernel_reversed": ("if (s >= 0) acc += w[d * nk + k] * xr[s];", "if (s >= 0) acc += w[d * nk + (nk - 1 - k)] * xr[s];"),
+    "conv_offset": ("const int64_t s = t - (nk - 1) + k;", "const int64_t s = t - nk + k;"),
 }
 
 

@@ -459,3 +459,52 @@ def test_conv1d_is_causal():
     assert np.array_equal(base[..., :17], pert[..., :17])
     assert not np.array_equal(base[..., 17:21], pert[..., 17:21])
     assert np.array_equal(base[..., 21:], pert[..., 21:])
+
+
+# ---- gradients of the Mamba-1 scan ----------------------------------------
+# The hand-derived adjoint in oracle_m1_bwd_f64 is pinned to central finite
+# differences of the (already pinned) forward oracle: a different route to
+# every partial derivative.  A wrong time index of the adjoint's decay, a
+# dropped path through h_{t-1}, a wrong softplus derivative or a missing sum
+# over channels of dB/dC shows up as a mismatch.
+
+def _loss(inp, dout, softplus):
+    y, _ = oracle.m1(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                     inp["delta_bias"], softplus=softplus)
+    return float(np.sum(y * dout))
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("gate_skip_bias", [True, False])
+def test_backward_matches_finite_differences(softplus, gate_skip_bias):
+    rng = np.random.default_rng(31 + int(softplus) + 2 * int(gate_skip_bias))
+    nb, nd, nn, nl = 2, 2, 3, 7
+    inp = {
+        "u": rng.standard_normal((nb, nd, nl)),
+        "delta": rng.standard_normal((nb, nd, nl)) * 0.5 + (0.0 if softplus else 1.0),
+        "A": -rng.uniform(0.2, 2.0, (nd, nn)),
+        "B": rng.standard_normal((nb, nn, nl)),
+        "C": rng.standard_normal((nb, nn, nl)),
+        "D": rng.standard_normal(nd) if gate_skip_bias else None,
+        "z": rng.standard_normal((nb, nd, nl)) if gate_skip_bias else None,
+        "delta_bias": rng.standard_normal(nd) * 0.3 if gate_skip_bias else None,
+    }
+    dout = rng.standard_normal((nb, nd, nl))
+    g = oracle.m1_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                      inp["delta_bias"], dout, softplus=softplus)
+    names = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+             "delta_bias": "ddelta_bias"}
+    eps = 1e-6
+    for name, gname in names.items():
+        if inp[name] is None:
+            continue
+        fd = np.zeros_like(inp[name])
+        for idx in np.ndindex(*inp[name].shape):
+            plus = {k: (None if v is None else v.copy()) for k, v in inp.items()}
+            minus = {k: (None if v is None else v.copy()) for k, v in inp.items()}
+            plus[name][idx] += eps
+            minus[name][idx] -= eps
+            fd[idx] = (_loss(plus, dout, softplus) - _loss(minus, dout, softplus)) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=2e-6, atol=2e-7, err_msg=gname)
+    if not gate_skip_bias:
+        assert np.all(g["dD"] == 0) and np.all(g["dz"] == 0) and np.all(g["ddelta_bias"] == 0)
