@@ -54,7 +54,7 @@ def _load():
             lib.oracle_m1_f64.restype = ctypes.c_int
             lib.oracle_m2_f64.argtypes = [i64] * 6 + [dp] * 8 + [ctypes.c_int, dp, dp, dp]
             lib.oracle_m2_f64.restype = ctypes.c_int
-            lib.oracle_m1_bwd_f64.argtypes = [i64] * 4 + [dp] * 8 + [ctypes.c_int] + [dp] * 9
+            lib.oracle_m1_bwd_f64.argtypes = [i64] * 4 + [dp] * 8 + [ctypes.c_int] + [dp] * 11
             lib.oracle_m1_bwd_f64.restype = ctypes.c_int
             lib.oracle_conv1d_f64.argtypes = [i64] * 4 + [dp] * 3 + [ctypes.c_int, dp]
             lib.oracle_conv1d_f64.restype = ctypes.c_int
@@ -145,10 +145,11 @@ def m2(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, h0=None):
     return y, last
 
 
-def m1_bwd(u, delta, A, B, C, D, z, delta_bias, dout, softplus=True):
-    """Gradients of the Mamba-1 scan output (y gated by silu(z)) in fp64,
-    zero initial state.  Returns a dict: du, ddelta, dz [batch, dim, L];
-    dA [dim, N]; dB, dC [batch, N, L]; dD, ddelta_bias [dim]."""
+def m1_bwd(u, delta, A, B, C, D, z, delta_bias, dout, softplus=True, h0=None):
+    """Gradients of the Mamba-1 scan output (y gated by silu(z)) in fp64 from
+    the initial state h0 [batch, dim, N] (None = zero).  Returns a dict: du,
+    ddelta, dz [batch, dim, L]; dA [dim, N]; dB, dC [batch, N, L]; dD,
+    ddelta_bias [dim]; dh0 [batch, dim, N]."""
     u = _f64(u)
     nb, nd, nl = u.shape
     A = _f64(A)
@@ -159,14 +160,16 @@ def m1_bwd(u, delta, A, B, C, D, z, delta_bias, dout, softplus=True):
     D = _f64(D, (nd,))
     z = _f64(z, (nb, nd, nl))
     delta_bias = _f64(delta_bias, (nd,))
+    h0 = _f64(h0, (nb, nd, nn))
     dout = _f64(dout, (nb, nd, nl))
     g = {k: np.empty(s, np.float64) for k, s in (("du", (nb, nd, nl)), ("ddelta", (nb, nd, nl)), ("dA", (nd, nn)),
                                                   ("dB", (nb, nn, nl)), ("dC", (nb, nn, nl)), ("dD", (nd,)),
-                                                  ("dz", (nb, nd, nl)), ("ddelta_bias", (nd,)))}
+                                                  ("dz", (nb, nd, nl)), ("ddelta_bias", (nd,)),
+                                                  ("dh0", (nb, nd, nn)))}
     rc = _load().oracle_m1_bwd_f64(nb, nd, nn, nl, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                   _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(dout), _ptr(g["du"]),
-                                   _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
-                                   _ptr(g["dz"]), _ptr(g["ddelta_bias"]))
+                                   _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(dout),
+                                   _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                   _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]))
     if rc != 0:
         raise RuntimeError(f"oracle_m1_bwd_f64 failed with status {rc}")
     return g

@@ -217,7 +217,9 @@ int oracle_conv1d_f64(int64_t nb, int64_t nd, int64_t nl, int64_t nk, const doub
  * given dout = d loss / d out.  The adjoint of the state runs backward in
  * time: lam_t = dy_t C_t + exp(Delta_{t+1} A) lam_{t+1}, and each input's
  * gradient collects lam_t times the partial derivative of h_t's update
- * (the chain rule through the recurrence, no shortcut).  h0 = 0.
+ * (the chain rule through the recurrence, no shortcut).  h0 [nb,nd,nn] is
+ * the state before the first token (NULL = 0); its gradient dh0 =
+ * exp(Delta_0 A) lam_0 is written when dh0 is non-NULL.
  * Outputs (all written, all fp64): du, ddelta, dz [nb,nd,nl]; dA [nd,nn];
  * dB, dC [nb,nn,nl]; dD, dbias [nd].  z, D, bias may be NULL (then their
  * gradients are written as 0 and the corresponding terms vanish).
@@ -226,8 +228,9 @@ int oracle_conv1d_f64(int64_t nb, int64_t nd, int64_t nl, int64_t nk, const doub
  */
 int oracle_m1_bwd_f64(int64_t nb, int64_t nd, int64_t nn, int64_t nl, const double* u, const double* delta,
                       const double* A, const double* Bm, const double* Cm, const double* Dv, const double* z,
-                      const double* bias, int softplus, const double* dout, double* du, double* ddelta,
-                      double* dA, double* dBm, double* dCm, double* dD, double* dz, double* dbias) {
+                      const double* bias, int softplus, const double* h0, const double* dout, double* du,
+                      double* ddelta, double* dA, double* dBm, double* dCm, double* dD, double* dz, double* dbias,
+                      double* dh0) {
     if (nb < 1 || nd < 1 || nn < 1 || nl < 1 || !u || !delta || !A || !Bm || !Cm || !dout || !du || !ddelta ||
         !dA || !dBm || !dCm || !dD || !dz || !dbias)
         return ORACLE_BAD_ARG;
@@ -249,7 +252,7 @@ int oracle_m1_bwd_f64(int64_t nb, int64_t nd, int64_t nn, int64_t nl, const doub
             const double* zr = z ? z + row * nl : NULL;
             const double* gr = dout + row * nl;
             /* forward, keeping every state */
-            for (int64_t n = 0; n < nn; ++n) h[n] = 0.0;
+            for (int64_t n = 0; n < nn; ++n) h[n] = h0 ? h0[row * nn + n] : 0.0;
             for (int64_t t = 0; t < nl; ++t) {
                 const double x = xr[t] + (bias ? bias[d] : 0.0);
                 dl[t] = softplus ? sp64(x) : x;
@@ -295,6 +298,8 @@ int oracle_m1_bwd_f64(int64_t nb, int64_t nd, int64_t nn, int64_t nl, const doub
                 ddelta[row * nl + t] = dx;
                 if (bias) dbias[d] += dx;
             }
+            if (dh0)
+                for (int64_t n = 0; n < nn; ++n) dh0[row * nn + n] = lam[n];
         }
     }
     free(h); free(lam); free(dl);

@@ -35,6 +35,8 @@ MUTANTS = {
     "bwd_softplus_derivative": ("ddl / (1.0 + exp(-x))", "ddl / (1.0 + exp(x))"),
     "bwd_dc_previous_state": ("dCm[(b * nn + n) * nl + t] += dy * h[(t + 1) * nn + n];",
                               "dCm[(b * nn + n) * nl + t] += dy * h[t * nn + n];"),
+    "bwd_h0_ignored": ("/* forward, keeping every state */\n            for (int64_t n = 0; n < nn; ++n) h[n] = h0 ? h0[row * nn + n] : 0.0;",
+                       "/* forward, keeping every state */\n            for (int64_t n = 0; n < nn; ++n) h[n] = 0.0;"),
     "conv_kernel_reversed": ("if (s >= 0) acc += w[d * nk + k] * xr[s];", "if (s >= 0) acc += w[d * nk + (nk - 1 - k)] * xr[s];"),
     "conv_offset": ("const int64_t s = t - (nk - 1) + k;", "const int64_t s = t - nk + k;"),
 }

@@ -470,7 +470,7 @@ def test_conv1d_is_causal():
 
 def _loss(inp, dout, softplus):
     y, _ = oracle.m1(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                     inp["delta_bias"], softplus=softplus)
+                     inp["delta_bias"], softplus=softplus, h0=inp["h0"])
     return float(np.sum(y * dout))
 
 
@@ -488,12 +488,13 @@ def test_backward_matches_finite_differences(softplus, gate_skip_bias):
         "D": rng.standard_normal(nd) if gate_skip_bias else None,
         "z": rng.standard_normal((nb, nd, nl)) if gate_skip_bias else None,
         "delta_bias": rng.standard_normal(nd) * 0.3 if gate_skip_bias else None,
+        "h0": rng.standard_normal((nb, nd, nn)) if gate_skip_bias else None,
     }
     dout = rng.standard_normal((nb, nd, nl))
     g = oracle.m1_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                      inp["delta_bias"], dout, softplus=softplus)
+                      inp["delta_bias"], dout, softplus=softplus, h0=inp["h0"])
     names = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
-             "delta_bias": "ddelta_bias"}
+             "delta_bias": "ddelta_bias", "h0": "dh0"}
     eps = 1e-6
     for name, gname in names.items():
         if inp[name] is None:
