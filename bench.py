@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--profile", action="store_true",
                    help="only warm up and run the timed steps of --workload (for rocprofv3)")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--backward", action="store_true",
+                   help="with --profile: time the gradients (selscan_bwd) of --workload instead")
     p.add_argument("--copy-gib", type=float, default=0.0,
                    help="with --profile: also run a plain copy of this many GiB and a half-line "
                         "strided read of the same size (known bytes, to calibrate HBM byte counters)")
@@ -215,6 +217,51 @@ def time_conv1d(name, steps, device, width=4):
             "frac_of_hbm_peak": nbytes / (k["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def time_backward(name, steps, device, warmup=2, seed=0):
+    """Mamba-1 gradients (selscan_bwd: every input's gradient from dout) on a
+    workload's full shape, fp32 dout and gradients, workspace preallocated."""
+    import torch
+    import selective_state_space_25_amd as ss
+    import synth
+
+    w = synth.WORKLOADS[name]
+    inp = synth.workload_inputs(w, seed=seed, device=device)
+    dout = synth.m1_dout(w.batch, w.dim, w.seqlen, torch.float32, seed=seed, device=device)
+    code = ss.BF16 if w.dtype == torch.bfloat16 else ss.F32
+    ws = torch.empty(ss.bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, code, ss.F32),
+                     dtype=torch.uint8, device=device)
+    f = lambda: ss.bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                       inp["delta_bias"], dout, softplus=True, workspace=ws)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize(device)
+    stream = torch.cuda.current_stream(device)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        f()
+    end.record(stream)
+    torch.cuda.synchronize(device)
+    ms = start.elapsed_time(end) / steps
+    ss.timing_collect()
+    ss.timing_enable(True)
+    try:
+        for _ in range(steps):
+            f()
+        torch.cuda.synchronize(device)
+    finally:
+        ss.timing_enable(False)
+    kernels = ss.timing_collect()
+    nbytes = synth.bwd_algorithmic_bytes(w)
+    res = {"shape_of": name, "ms_per_call": ms, "steps": steps, "dout_dtype": "float32", "grad_dtype": "float32",
+           "state_updates_per_s": w.updates / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "kernels": kernels}
+    del inp, dout, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def dominant_kernel(res):
     name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["total_ms"])
     return name, k
@@ -299,6 +346,9 @@ def main():
     import selective_state_space_25_amd as ss
     ss.lib()  # fail loudly if the HIP library is missing
 
+    if args.profile and args.backward:
+        print(json.dumps(time_backward(args.workload, args.steps, device, warmup=args.warmup, seed=args.seed)))
+        return
     w, head = time_workload(args.workload, args.steps, args.warmup, args.seed, device,
                             kernel_timing=not args.profile)
     if args.profile:
@@ -363,6 +413,7 @@ def main():
     }
     line["decode"] = {n: time_decode(n, 200, device) for n in ("mamba2p8b_l8k", "mamba2_mh")}
     line["conv1d"] = time_conv1d("mamba2p8b_l8k", 10, device)
+    line["backward"] = {n: time_backward(n, 5, device) for n in ("mamba130m_l2k", "mamba2p8b_l8k")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
     print(json.dumps(line))

@@ -141,6 +141,42 @@ selscan_status_t selscan_step(const selscan_shape_t* shape, float* state,
                               const void* z, const float* delta_bias, int softplus,
                               void* y, void* stream);
 
+/* Bytes of workspace selscan_bwd needs for `shape` (0 on a bad shape). */
+size_t selscan_bwd_workspace_bytes(const selscan_shape_t* shape);
+
+/*
+ * Gradients of the Mamba-1 scan (training; reverse mode through the
+ * recurrence of section 2.2 of the "Understanding Mamba ..." blog, the layer
+ * the Mamba README trains end to end).  For out = selscan_fwd_h0(...) and
+ * dout = d loss / d out, writes the gradient of the loss with respect to
+ * every input.  The states are recomputed from the inputs (nothing from the
+ * forward call is needed).
+ *   u .. softplus, h0   as for selscan_fwd_h0 (h0 NULL = zero state)
+ *   dout        [B, D, L]  out_dtype   gradient of the output
+ *   du, ddelta  [B, D, L]  fp32        (written); ddelta is with respect to
+ *                                      delta itself (before bias/softplus)
+ *   dA          [D, N]     fp32        (written)
+ *   dB, dC      [B, N, L]  fp32        (written)
+ *   dD          [D]        fp32        (written; NULL = skip; 0 when D is NULL)
+ *   dz          [B, D, L]  fp32        (written; required when z is given,
+ *                                      ignored otherwise)
+ *   ddelta_bias [D]        fp32        (written; NULL = skip)
+ *   dh0         [B, D, N]  fp32        (written; NULL = skip)
+ * Gradients must not alias inputs or each other.  Sums over channels,
+ * batches and time are taken in a fixed order: results are reproducible
+ * bit for bit.  shape->workspace as for selscan_fwd, sized by
+ * selscan_bwd_workspace_bytes.  Errors as for selscan_fwd, plus
+ * SELSCAN_ERR_INVALID_ARG for a NULL required gradient.
+ */
+selscan_status_t selscan_bwd(const selscan_shape_t* shape,
+                             const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D,
+                             const void* z, const float* delta_bias, int softplus,
+                             const float* h0, const void* dout,
+                             float* du, float* ddelta, float* dA, float* dB, float* dC,
+                             float* dD, float* dz, float* ddelta_bias, float* dh0,
+                             void* stream);
+
 /*
  * Mamba-2 problem description.
  *   batch >= 1, seqlen >= 1, nheads H >= 1, headdim P >= 1, ngroups G >= 1

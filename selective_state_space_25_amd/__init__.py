@@ -48,6 +48,7 @@ _lib = None
 
 EXPORTED = ("selscan_fwd", "selscan_mamba2_fwd", "selscan_workspace_bytes", "selscan_mamba2_workspace_bytes",
             "selscan_fwd_h0", "selscan_mamba2_fwd_h0", "selscan_step", "selscan_mamba2_step", "selscan_conv1d",
+            "selscan_bwd", "selscan_bwd_workspace_bytes",
             "selscan_last_error", "selscan_version", "selscan_timing_enable", "selscan_timing_collect")
 
 
@@ -85,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.selscan_mamba2_step.restype = i32
         L.selscan_conv1d.argtypes = [ctypes.POINTER(ConvShape), vp, fp, fp, i32, vp, vp]
         L.selscan_conv1d.restype = i32
+        L.selscan_bwd.argtypes = [ctypes.POINTER(Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp] + [fp] * 9 + [vp]
+        L.selscan_bwd.restype = i32
+        L.selscan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
+        L.selscan_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
         L.selscan_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_mamba2_workspace_bytes.argtypes = [ctypes.POINTER(M2Shape)]
@@ -221,6 +226,57 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     return out
 
 
+def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, softplus=True, h0=None,
+        want_dh0=False, workspace=None):
+    """Gradients of the Mamba-1 scan on the GPU.
+
+    Inputs as for fwd; dout [batch, dim, L] (float32 or bfloat16: the dtype
+    of the forward's y) is the gradient of the loss with respect to y.
+    Returns a dict of float32 tensors: du, ddelta, dz (when z is given)
+    [batch, dim, L]; dA [dim, N]; dB, dC [batch, N, L]; dD (when D is given)
+    and ddelta_bias (when delta_bias is given) [dim]; dh0 [batch, dim, N]
+    (when h0 is given or want_dh0).
+    """
+    torch = _torch()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.bwd needs tensors on a GPU device")
+    if dout is None:
+        raise ValueError("dout is required")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    dt = u.dtype
+    f32 = torch.float32
+    new = lambda *shape: torch.empty(shape, dtype=f32, device=dev)
+    g = {"du": new(batch, dim, L), "ddelta": new(batch, dim, L), "dA": new(dim, N),
+         "dB": new(batch, N, L), "dC": new(batch, N, L)}
+    if z is not None:
+        g["dz"] = new(batch, dim, L)
+    if D is not None:
+        g["dD"] = new(dim)
+    if delta_bias is not None:
+        g["ddelta_bias"] = new(dim)
+    if h0 is not None or want_dh0:
+        g["dh0"] = new(batch, dim, N)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    s = Shape(batch, dim, N, L, _dtype_code(u), _dtype_code(dout), ws_ptr, ws_bytes)
+    gp = lambda k: g[k].data_ptr() if k in g else None
+    _check(lib().selscan_bwd(
+        ctypes.byref(s), _ptr(u, "u", (batch, dim, L), dt, dev), _ptr(delta, "delta", (batch, dim, L), dt, dev),
+        _ptr(A, "A", (dim, N), f32, dev), _ptr(B, "B", (batch, N, L), dt, dev), _ptr(C, "C", (batch, N, L), dt, dev),
+        _ptr(D, "D", (dim,), f32, dev), _ptr(z, "z", (batch, dim, L), dt, dev),
+        _ptr(delta_bias, "delta_bias", (dim,), f32, dev), int(bool(softplus)),
+        _ptr(h0, "h0", (batch, dim, N), f32, dev), _ptr(dout, "dout", (batch, dim, L), None, dev),
+        gp("du"), gp("ddelta"), gp("dA"), gp("dB"), gp("dC"), gp("dD"), gp("dz"), gp("ddelta_bias"), gp("dh0"),
+        _stream_handle(dev)))
+    return g
+
+
+def bwd_workspace_bytes(batch, dim, dstate, seqlen, in_dtype=BF16, out_dtype=None) -> int:
+    s = m1_shape(batch, dim, dstate, seqlen, in_dtype, out_dtype)
+    return int(lib().selscan_bwd_workspace_bytes(ctypes.byref(s)))
+
+
 def workspace_bytes(batch, dim, dstate, seqlen, in_dtype=BF16, out_dtype=None) -> int:
     s = m1_shape(batch, dim, dstate, seqlen, in_dtype, out_dtype)
     return int(lib().selscan_workspace_bytes(ctypes.byref(s)))
@@ -338,5 +394,5 @@ def timing_collect() -> dict:
     return res
 
 
-__all__ = ["conv1d", "ConvShape", "step", "mamba2_step", "timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
+__all__ = ["bwd", "bwd_workspace_bytes", "conv1d", "ConvShape", "step", "mamba2_step", "timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
            "SelscanError", "Shape", "M2Shape", "m1_shape", "EXPORTED", "LIB_PATH"]

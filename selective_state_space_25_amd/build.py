@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libselscan.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["selscan.cpp", "timing.cpp", "m1_scan.hip", "m2_scan.hip", "m2_ssd.hip", "step.hip", "conv1d.hip"]
+SOURCES = ["selscan.cpp", "timing.cpp", "m1_scan.hip", "m2_scan.hip", "m2_ssd.hip", "step.hip", "conv1d.hip", "m1_bwd.hip"]
 ARCH = os.environ.get("SELSCAN_ARCH", "gfx950")
 
 

@@ -50,6 +50,41 @@ int m1_waves_per_block();
 size_t m1_bc_bytes(int64_t batch, int64_t L);
 hipError_t launch_m1(const M1Args& a, int in_bf16, int out_bf16, hipStream_t stream);
 
+// Mamba-1 backward.  Inputs as for M1Args plus dout [batch, dim, L]
+// (out dtype); gradients fp32 in the layouts of their inputs.  hbuf .. part
+// point into the workspace (m1_bwd_carve).
+struct BwdArgs {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* bias;
+    const float* h0;
+    const void* dout;
+    float *du, *ddelta, *dA, *dB, *dC, *dD, *dz, *dbias, *dh0;
+    float* hbuf;    // [rows, G, 16] chunk-end states from zero, then states entering each chunk
+    float* mubuf;   // [rows, G, 16] adjoint leaving each chunk from zero, then the one entering it
+    float* wbuf;    // [rows, G] chunk sums of Delta
+    float* pA;      // [rows, G, 16] per-chunk dA terms
+    float* pD;      // [rows, G]
+    float* pbias;   // [rows, G]
+    float* part;    // [dim / 64, batch, 32, L] per-channel-block dB (16) and dC (16)
+    int64_t batch, dim, L;
+    int64_t chunk;  // tokens per chunk: a multiple of m1_bwd_tile(), at most m1_bwd_max_chunk()
+    int64_t G;      // chunks
+    int N;
+    int softplus;
+};
+int m1_bwd_tile();
+int m1_bwd_max_chunk();
+int m1_bwd_channels_per_block();
+size_t m1_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t G);
+void m1_bwd_carve(BwdArgs& a, void* ws);
+hipError_t launch_m1_bwd(const BwdArgs& a, int in_bf16, int out_bf16, hipStream_t stream);
+
 // Mamba-2.
 struct M2Args {
     const void* x;

@@ -222,6 +222,43 @@ struct Scratch {
     }
 };
 
+// ------------------------------------------------------- Mamba-1 backward
+struct BwdPlan {
+    int64_t chunk, G;
+    size_t ws_bytes;
+};
+
+BwdPlan plan_m1_bwd(const selscan_shape_t* s) {
+    BwdPlan p;
+    const int64_t tile = selscan::m1_bwd_tile();
+    const int64_t nbc = (s->dim + selscan::m1_bwd_channels_per_block() - 1) / selscan::m1_bwd_channels_per_block();
+    int64_t chunk = env_int("SELSCAN_BWD_CHUNK", 0);
+    if (chunk <= 0) {
+        // the longest chunk that still gives every compute unit several
+        // workgroups (one 1024-thread workgroup is resident per unit)
+        chunk = selscan::m1_bwd_max_chunk();
+        const int64_t want = 8 * (int64_t)device_cus();
+        while (chunk > 2 * tile && s->batch * nbc * ((s->seqlen + chunk - 1) / chunk) < want) chunk /= 2;
+    }
+    chunk = std::min<int64_t>(std::max<int64_t>(tile, (chunk + tile - 1) / tile * tile), selscan::m1_bwd_max_chunk());
+    p.chunk = chunk;
+    p.G = (s->seqlen + chunk - 1) / chunk;
+    p.ws_bytes = selscan::m1_bwd_workspace_bytes(s->batch, s->dim, s->seqlen, p.G);
+    return p;
+}
+
+selscan_status_t check_m1_bwd_shape(const selscan_shape_t* s) {
+    selscan_status_t st = check_m1_shape(s);
+    if (st != SELSCAN_OK) return st;
+    const int64_t nbc = (s->dim + 63) / 64;
+    if (mul_checked({nbc, s->batch, 32, s->seqlen, 4}) < 0 ||
+        mul_checked({s->batch, s->dim, (s->seqlen + 31) / 32, 16, 4}) < 0)
+        return fail(SELSCAN_ERR_INVALID_ARG, "workspace size overflows 64-bit byte counts");
+    if (s->batch * nbc * ((s->seqlen + 31) / 32) > 0x7fffffff)
+        return fail(SELSCAN_ERR_UNSUPPORTED, "too many workgroups for one launch");
+    return SELSCAN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,6 +270,11 @@ const char* selscan_version(void) { return "libselscan 0.1 gfx950"; }
 size_t selscan_workspace_bytes(const selscan_shape_t* shape) {
     if (check_m1_shape(shape) != SELSCAN_OK) return 0;
     return plan_m1(shape).ws_bytes;
+}
+
+size_t selscan_bwd_workspace_bytes(const selscan_shape_t* shape) {
+    if (check_m1_bwd_shape(shape) != SELSCAN_OK) return 0;
+    return plan_m1_bwd(shape).ws_bytes;
 }
 
 size_t selscan_mamba2_workspace_bytes(const selscan_m2_shape_t* shape) {
@@ -383,6 +425,48 @@ selscan_status_t selscan_step(const selscan_shape_t* s, float* state, const void
         a.batch = s->batch; a.dim = s->dim; a.N = (int)s->dstate; a.softplus = softplus;
         hipError_t e = selscan::launch_step(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, 0,
                                             reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(SELSCAN_ERR_LAUNCH, "unexpected host exception");
+    }
+}
+
+selscan_status_t selscan_bwd(const selscan_shape_t* s, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z, const float* delta_bias,
+                             int softplus, const float* h0, const void* dout, float* du, float* ddelta, float* dA,
+                             float* dB, float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
+                             void* stream) {
+    try {
+        selscan_status_t st = check_m1_bwd_shape(s);
+        if (st != SELSCAN_OK) return st;
+        if (!u || !delta || !A || !B || !C || !dout)
+            return fail(SELSCAN_ERR_INVALID_ARG, "u, delta, A, B, C and dout must be non-NULL");
+        if (!du || !ddelta || !dA || !dB || !dC)
+            return fail(SELSCAN_ERR_INVALID_ARG, "du, ddelta, dA, dB and dC must be non-NULL");
+        if (z && !dz) return fail(SELSCAN_ERR_INVALID_ARG, "dz must be non-NULL when z is given");
+        if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        st = device_check();
+        if (st != SELSCAN_OK) return st;
+        const BwdPlan plan = plan_m1_bwd(s);
+        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        Scratch ws;
+        st = ws.get(s->workspace, s->workspace_bytes, plan.ws_bytes, hs);
+        if (st != SELSCAN_OK) return st;
+        selscan::BwdArgs a{};
+        a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias; a.h0 = h0;
+        a.dout = dout;
+        a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz;
+        a.dbias = ddelta_bias; a.dh0 = dh0;
+        a.batch = s->batch; a.dim = s->dim; a.L = s->seqlen; a.N = (int)s->dstate; a.softplus = softplus;
+        a.chunk = plan.chunk; a.G = plan.G;
+        selscan::m1_bwd_carve(a, ws.ptr);
+        if (log_plans())
+            std::fprintf(stderr, "[selscan] m1 bwd B=%lld D=%lld N=%lld L=%lld chunks=%lld chunk=%lld ws=%zu\n",
+                         (long long)s->batch, (long long)s->dim, (long long)s->dstate, (long long)s->seqlen,
+                         (long long)plan.G, (long long)plan.chunk, plan.ws_bytes);
+        hipError_t e = selscan::launch_m1_bwd(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, hs);
+        ws.release();
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
         return ok();
     } catch (...) {

@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 import torch
 
 # tensor ids of the per-tensor streams
-_TID = {"u": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "A": 6, "D": 7, "bias": 8}
+_TID = {"u": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "A": 6, "D": 7, "bias": 8, "dout": 9, "h0": 10}
 
 
 @dataclass(frozen=True)
@@ -160,6 +160,28 @@ def m2_inputs(batch, seqlen, nheads, headdim, ngroups, dstate, dtype=torch.bfloa
     return out
 
 
+def m1_dout(batch, dim, seqlen, dtype=torch.bfloat16, seed=0, device="cpu"):
+    """Gradient of a loss with respect to a Mamba-1 scan's output: standard
+    normal [batch, dim, seqlen], drawn like the inputs."""
+    return _normal((batch, dim, seqlen), seed, "dout", dtype, torch.device(device))
+
+
+def m1_state(batch, dim, dstate, seed=0, device="cpu"):
+    """A Mamba-1 state [batch, dim, dstate] fp32, standard normal."""
+    return _normal((batch, dim, dstate), seed, "h0", torch.float32, torch.device(device))
+
+
+def bwd_algorithmic_bytes(w: Workload) -> int:
+    """Bytes the Mamba-1 backward must move: the forward's inputs and dout
+    read once, every fp32 gradient written once."""
+    s = torch.tensor([], dtype=w.dtype).element_size()
+    so = torch.tensor([], dtype=w.out_dtype).element_size()
+    elem = w.batch * w.dim * w.seqlen
+    bc = w.batch * w.dstate * w.seqlen
+    return (elem * (3 * s + so) + 2 * bc * s + (w.dim * w.dstate + 2 * w.dim) * 4
+            + elem * 3 * 4 + 2 * bc * 4 + (w.dim * w.dstate + 2 * w.dim) * 4)
+
+
 def workload_inputs(w: Workload | str, seed: int = 0, device="cpu"):
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -185,4 +207,4 @@ def algorithmic_bytes(w: Workload) -> int:
 
 
 __all__ = ["WORKLOADS", "Workload", "m1_inputs", "m2_inputs", "workload_inputs",
-           "algorithmic_bytes", "a_matrix", "delta_bias"]
+           "algorithmic_bytes", "bwd_algorithmic_bytes", "a_matrix", "delta_bias", "m1_dout", "m1_state"]

@@ -168,3 +168,38 @@ def test_conv1d_rejects_null_alias_and_bad_flag():
     assert ss.lib().selscan_conv1d(ctypes.byref(s), FAKE, FAKE, None, 1, FAKE, None) == ss.ERR_INVALID_ARG
     assert "alias" in ss.last_error()
     assert ss.lib().selscan_conv1d(ctypes.byref(s), FAKE, FAKE, None, 3, FAKE + 64, None) == ss.ERR_INVALID_ARG
+
+
+def _bwd(s, **over):
+    args = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1, h0=None,
+                dout=FAKE, du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dh0=None)
+    args.update(over)
+    return ss.lib().selscan_bwd(ctypes.byref(s), *args.values(), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, ss.ERR_INVALID_ARG), ("dstate", 17, ss.ERR_UNSUPPORTED), ("in_dtype", 5, ss.ERR_UNSUPPORTED),
+    ("seqlen", 1 << 62, ss.ERR_INVALID_ARG)])
+def test_bwd_bad_shape_rejected(field, value, status):
+    assert _bwd(_m1(**{field: value})) == status
+    assert ss.last_error()
+
+
+@pytest.mark.parametrize("missing", ["u", "dout", "du", "ddelta", "dA", "dB", "dC"])
+def test_bwd_null_required_pointer_rejected(missing):
+    assert _bwd(_m1(), **{missing: None}) == ss.ERR_INVALID_ARG
+    assert "non-NULL" in ss.last_error()
+
+
+def test_bwd_needs_dz_with_a_gate_and_a_valid_flag():
+    assert _bwd(_m1(), z=FAKE) == ss.ERR_INVALID_ARG
+    assert "dz" in ss.last_error()
+    assert _bwd(_m1(), softplus=2) == ss.ERR_INVALID_ARG
+
+
+def test_bwd_workspace_size():
+    # chunk states and adjoints, and per-channel-block partial sums of dB/dC
+    n = ss.bwd_workspace_bytes(2, 130, 16, 1000)
+    assert n % 256 == 0
+    assert n >= 3 * 2 * 32 * 1000 * 4
+    assert ss.lib().selscan_bwd_workspace_bytes(ctypes.byref(_m1(dstate=17))) == 0

@@ -1,0 +1,173 @@
+"""Mamba-1 backward on the GPU (through the C ABI) against the fp64 oracle's
+reverse-mode gradients (which are pinned to finite differences on the CPU).
+
+Tolerance: the kernels compute in fp32 from the same (bf16- or fp32-valued)
+inputs the oracle reads exactly, so the only error is fp32 arithmetic.  A
+gradient element is a sum of up to batch x L (dA, dD, dbias), dim (dB, dC)
+or N (du, ddelta) products carried through an adjoint recursion whose
+effective length is bounded by the decay; with unit roundoff 2^-24 ~ 6e-8
+and at most ~1e4 accumulated roundings the error stays below ~1e-3 of the
+typical size (rms) of that gradient even where its terms cancel, and below
+1e-4 relative where they do not.  Hence |gpu - ref| <= 1e-3 rms(ref) +
+1e-4 |ref| per element."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_25_amd as ss
+import synth
+from parity import check_close, host
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+RMS_TOL, REL_TOL = 1e-3, 1e-4
+GRADS = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias", "dh0")
+
+
+def _check_grads(got, ref, names=GRADS, rows=None, chans=None):
+    for k in names:
+        if k not in got:
+            continue
+        g = host(got[k]).double().numpy()
+        r = np.asarray(ref[k])
+        if rows is not None and k in ("du", "ddelta", "dz", "dh0"):
+            g = g[:, chans]
+        if chans is not None and k in ("dA", "dD", "ddelta_bias"):
+            g = g[chans]
+        scale = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+        check_close(g, r, (RMS_TOL * scale + 1e-30, REL_TOL), k)
+
+
+def _oracle(inp, dout, softplus=True, h0=None):
+    return oracle.m1_bwd(host(inp["u"]), host(inp["delta"]), host(inp["A"]), host(inp["B"]), host(inp["C"]),
+                         host(inp.get("D")), host(inp.get("z")), host(inp.get("delta_bias")), host(dout),
+                         softplus=softplus, h0=None if h0 is None else host(h0))
+
+
+def _gpu(inp, dout, softplus=True, h0=None, want_dh0=False):
+    g = ss.bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp.get("D"), inp.get("z"),
+               inp.get("delta_bias"), dout, softplus=softplus, h0=h0, want_dh0=want_dh0)
+    torch.cuda.synchronize()
+    return g
+
+
+def _case(batch, dim, N, L, dtype, a_kind="s4d_jitter", seed=0, dout_dtype=None, **kw):
+    inp = synth.m1_inputs(batch, dim, N, L, dtype, a_kind, seed=seed, device=DEV, **kw)
+    dout = synth.m1_dout(batch, dim, L, dout_dtype or torch.float32, seed=seed, device=DEV)
+    return inp, dout
+
+
+@pytest.mark.parametrize("L", [1, 17, 32, 33, 200, 1000])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_lengths(gpu, L, dtype):
+    inp, dout = _case(2, 70, 16, L, dtype, seed=L)
+    _check_grads(_gpu(inp, dout), _oracle(inp, dout))
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 96, 512])
+def test_chunked_time_matches_oracle(gpu, monkeypatch, chunk):
+    """Chunks of the sequence linked by the state and adjoint carries."""
+    monkeypatch.setenv("SELSCAN_BWD_CHUNK", str(chunk))
+    inp, dout = _case(2, 130, 16, 1000, torch.bfloat16, seed=chunk)
+    _check_grads(_gpu(inp, dout), _oracle(inp, dout))
+
+
+@pytest.mark.parametrize("N", [1, 3, 8, 16])
+@pytest.mark.parametrize("a_kind", ["s4d", "random"])
+def test_state_sizes(gpu, monkeypatch, N, a_kind):
+    monkeypatch.setenv("SELSCAN_BWD_CHUNK", "64")
+    inp, dout = _case(2, 40, N, 300, torch.bfloat16, a_kind, seed=N)
+    _check_grads(_gpu(inp, dout), _oracle(inp, dout))
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("gate,skip,bias", [(True, True, True), (False, False, False), (True, False, True),
+                                            (False, True, False)])
+def test_options(gpu, softplus, gate, skip, bias):
+    inp, dout = _case(2, 66, 16, 150, torch.float32, seed=3, gate=gate, skip=skip, bias=bias)
+    if not softplus:
+        # Delta = delta + bias must stay positive without softplus
+        inp["delta"] = inp["delta"].abs() * 0.05
+        if bias:
+            inp["delta_bias"] = inp["delta_bias"].abs() * 0.01
+    got = _gpu(inp, dout, softplus=softplus)
+    assert ("dz" in got) == gate and ("dD" in got) == skip and ("ddelta_bias" in got) == bias
+    _check_grads(got, _oracle(inp, dout, softplus=softplus))
+
+
+def test_bf16_dout(gpu):
+    inp, dout = _case(1, 64, 16, 257, torch.bfloat16, seed=8, dout_dtype=torch.bfloat16)
+    _check_grads(_gpu(inp, dout), _oracle(inp, dout))
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_initial_state_and_its_gradient(gpu, monkeypatch, chunk):
+    if chunk:
+        monkeypatch.setenv("SELSCAN_BWD_CHUNK", str(chunk))
+    inp, dout = _case(2, 70, 16, 400, torch.bfloat16, seed=11)
+    h0 = synth.m1_state(2, 70, 16, seed=11, device=DEV)
+    got = _gpu(inp, dout, h0=h0)
+    _check_grads(got, _oracle(inp, dout, h0=h0))
+    # without h0 the gradient of the (zero) initial state is still defined
+    got0 = _gpu(inp, dout, want_dh0=True)
+    ref0 = _oracle(inp, dout)
+    _check_grads(got0, ref0, names=("dh0", "du"))
+
+
+def test_gradients_are_reproducible_bit_for_bit(gpu):
+    inp, dout = _case(2, 200, 16, 3000, torch.bfloat16, seed=5)
+    a = _gpu(inp, dout)
+    b = _gpu(inp, dout)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_gradient_matches_the_forward_by_directional_derivative(gpu):
+    """<dout, d out/du . v> from the GPU forward (a central difference in
+    fp32 along a random direction v) equals <du, v> from the GPU backward:
+    the two entry points agree with each other as well as with the oracle."""
+    inp, dout = _case(1, 64, 16, 256, torch.float32, seed=21)
+    got = _gpu(inp, dout)
+    g = torch.Generator(device=DEV).manual_seed(4)
+    v = torch.randn(inp["u"].shape, generator=g, device=DEV)
+    eps = 0.5
+
+    def loss(u):
+        y, _ = ss.fwd(u, inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"])
+        return float((y.double() * dout.double()).sum())
+
+    fd = (loss(inp["u"] + eps * v) - loss(inp["u"] - eps * v)) / (2 * eps)
+    an = float((got["du"].double() * v.double()).sum())
+    # the scan is linear in u given delta, so the difference quotient is exact
+    # up to the forward's fp32 rounding of two large sums
+    assert abs(fd - an) <= 1e-3 * max(1.0, abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("name", ["mamba130m_l2k", "mamba2p8b_l8k"])
+def test_full_size_sampled(gpu, name):
+    """The workload's full shape, in the launch plan the benchmark times.
+    Per-row gradients and the per-channel sums (dA, dD, dbias) of a sample
+    of channels spread over the channel blocks are exact from the oracle
+    run on those channels alone.  dB and dC sum over all channels: with
+    dout zero outside the sample, the other channels' adjoints vanish, so the
+    oracle on the sample gives them exactly too."""
+    w = synth.WORKLOADS[name]
+    inp = synth.workload_inputs(w, seed=1, device=DEV)
+    dout = synth.m1_dout(w.batch, w.dim, w.seqlen, torch.float32, seed=1, device=DEV)
+    chans = torch.arange(3, w.dim, 197).tolist()
+    chans = sorted(set(chans + [0, w.dim - 1]))
+    idx = torch.tensor(chans, device=DEV)
+    sub = {k: (None if v is None else
+               v.index_select(1, idx).contiguous() if k in ("u", "delta", "z") else
+               v.index_select(0, idx).contiguous() if k in ("A", "D", "delta_bias") else v)
+           for k, v in inp.items()}
+    ref = _oracle(sub, dout.index_select(1, idx))
+    got = _gpu(inp, dout)
+    _check_grads(got, ref, names=("du", "ddelta", "dz", "dA", "dD", "ddelta_bias"), rows=True, chans=chans)
+    del got
+    masked = torch.zeros_like(dout)
+    masked[:, idx] = dout[:, idx]
+    got = _gpu(inp, masked)
+    _check_grads(got, ref, names=("dB", "dC"))
