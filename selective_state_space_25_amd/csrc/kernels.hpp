@@ -71,7 +71,9 @@ struct BwdArgs {
     float* pA;      // [rows, G, 16] per-chunk dA terms
     float* pD;      // [rows, G]
     float* pbias;   // [rows, G]
-    float* part;    // [dim / 64, batch, 32, L] per-channel-block dB (16) and dC (16)
+    float* part;    // [dim / 64, batch, L, 32] per-channel-block dB (16) and dC (16)
+    float* ckz;     // [rows, L / 8, 16] state before every 8th token from the chunk's zero start
+    float* wck;     // [rows, L / 8] sum of Delta from the chunk's start to the same tokens
     int64_t batch, dim, L;
     int64_t chunk;  // tokens per chunk: a multiple of m1_bwd_tile(), at most m1_bwd_max_chunk()
     int64_t G;      // chunks

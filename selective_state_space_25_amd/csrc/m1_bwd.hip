@@ -8,26 +8,35 @@
 //   dy_t     = dout_t silu(z_t)
 //   lam_t[n] = dy_t C_t[n] + a_{t+1}[n] lam_{t+1}[n]
 //   dC_t[n]  = sum_d dy_t h_t[n]        dB_t[n] = sum_d lam_t[n] Delta_t u_t
-//   du_t     = dy_t D + sum_n lam_t[n] Delta_t B_t[n]
+//   du_t     = dy_t D + Delta_t sum_n lam_t[n] B_t[n]
 //   dDelta_t = sum_n lam_t[n] (B_t[n] u_t + A[n] a_t[n] h_{t-1}[n])
-//   dA[n]    = sum_{b,t} lam_t[n] Delta_t a_t[n] h_{t-1}[n]
+//   dA[n]    = sum_{b,t} Delta_t lam_t[n] a_t[n] h_{t-1}[n]
 //
 // Time is cut into chunks so that the grid fills the chip:
-//   summary: per chunk, the state at its end from a zero start and the
-//            adjoint leaving its first token from a zero right boundary;
+//   summary: per chunk, a forward sweep from a zero state that stores the
+//            state (and the running sum of Delta) every 8 tokens and the
+//            state at the chunk's end; and a reverse sweep of the adjoint from
+//            a zero right boundary;
 //   carry:   the true state entering each chunk (forward over chunks, from
 //            h0) and the true adjoint entering it from the right (backward
-//            over chunks) -- both linear, so the chunk's decay exp(A sum Delta)
-//            is all that links neighbours;
-//   chunk:   per chunk, a forward sweep storing the state every 32 tokens in
-//            LDS, then tiles from the last: recompute the tile's 32 states in
-//            registers and run the adjoint back through them;
-//   reduce:  the sums over channel blocks, batches and chunks.
-// A workgroup is 1024 threads, one per (channel, state n) of 64 channels.
-// Sums over n use shuffles in the 16-lane group of a channel; dB and dC, sums
-// over channels, go over the wave's 4 channels by shuffles, over the 16
-// waves through LDS, and over channel blocks in the reduce pass from
-// per-block partials (no atomics: results do not depend on scheduling).
+//            over chunks); both are linear, so a chunk's decay
+//            exp(A sum Delta) is all that links neighbours;
+//   chunk:   per chunk, 8-token tiles from the last: the tile's first state
+//            is the stored zero-start state plus the decayed entering state;
+//            the tile's 8 states are recomputed into registers and the
+//            adjoint runs back through them;
+//   reduce:  sums of the per-block partials over channel blocks, batches and
+//            chunks (no atomics: results do not depend on scheduling).
+//
+// A workgroup is 256 threads for 64 channels of one batch.  A lane holds 4 of
+// a channel's 16 states (n = 4q .. 4q+3); lane = 16 dr + 4 q + rr, channel =
+// 16 wave + 4 dr + rr.  Per-channel, per-token values (Delta, Delta u, dy, ...)
+// are computed once per tile by a "producer" mapping (thread = channel x 2
+// tokens) into LDS.  Sums over n go over a lane's 4 states and then across
+// the 4 lanes of the channel (DPP row rotations by 4 and 8); dB and dC, sums
+// over channels, are reduce-scattered across the 4 channels of a DPP row
+// (quad permutes), then across the wave's 4 DPP rows (permlane32/16 swaps),
+// then across the 4 waves in LDS.
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -35,12 +44,12 @@ namespace selscan {
 
 namespace {
 
-constexpr int kCh = 64;        // channels per workgroup
-constexpr int kSt = 16;        // states per channel (padded)
-constexpr int kTile = 32;      // tokens per recomputed tile
-constexpr int kMaxTiles = 16;  // tiles per chunk (checkpoints held in LDS)
-constexpr int kThreads = kCh * kSt;
+constexpr int kCh = 64;          // channels per workgroup
+constexpr int kSt = 16;          // states per channel (padded)
+constexpr int kT = 8;            // tokens per tile
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kPad = kT + 1;     // LDS row pitch of per-channel tile values
 
 template <typename T> __device__ __forceinline__ float ld1(const T* p, int64_t i);
 template <> __device__ __forceinline__ float ld1<float>(const float* p, int64_t i) { return p[i]; }
@@ -48,133 +57,206 @@ template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p, in
     return bf16_to_f32(p[i]);
 }
 
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-    for (int o = 1; o < kSt; o <<= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// v + v of another lane, by a DPP control (row rotations, quad permutes)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kRor4 = 0x124, kRor8 = 0x128, kQuadX1 = 0xB1, kQuadX2 = 0x4E;
+
+// sum over the 4 lanes of a channel (lanes 4 apart in a DPP row)
+__device__ __forceinline__ float sum_q(float v) {
+    v += dpp<kRor4>(v);
+    return v + dpp<kRor8>(v);
 }
 
 __device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
 
-// One thread's (channel, state) view of the inputs.
-template <typename Tin, typename Tout, bool SP>
-struct Cell {
-    const Tin *u, *dl, *z, *bn, *cn;
-    const Tout* dout;
-    float A;       // A[d, n] log2(e)
-    float An;      // A[d, n]
-    float D, bias;
-    bool st_ok;    // n < N
-
-    __device__ Cell(const BwdArgs& a, int64_t b, int64_t d, int n) {
-        const int64_t row = b * a.dim + d;
-        const int nn = n < a.N ? n : 0;
-        st_ok = n < a.N;
-        u = reinterpret_cast<const Tin*>(a.u) + row * a.L;
-        dl = reinterpret_cast<const Tin*>(a.delta) + row * a.L;
-        z = a.z ? reinterpret_cast<const Tin*>(a.z) + row * a.L : nullptr;
-        bn = reinterpret_cast<const Tin*>(a.B) + (b * a.N + nn) * a.L;
-        cn = reinterpret_cast<const Tin*>(a.C) + (b * a.N + nn) * a.L;
-        dout = reinterpret_cast<const Tout*>(a.dout) + row * a.L;
-        An = st_ok ? a.A[d * a.N + n] : 0.0f;
-        A = An * kLog2e;
-        D = a.D ? a.D[d] : 0.0f;
-        bias = a.bias ? a.bias[d] : 0.0f;
-    }
-    // Delta_t (natural units) and dDelta/d(delta_t)
-    __device__ __forceinline__ float dt(int64_t t, float& deriv) const {
-        const float x = ld1(dl, t) + bias;
-        if (SP) {
-            deriv = sigmoid(x);
-            return softplus_log2(x * kLog2e) * kLn2;
-        }
+// Delta = softplus(x) (natural units) and its derivative sigmoid(x)
+template <bool SP>
+__device__ __forceinline__ float delta_of(float x, float& deriv) {
+    if (!SP) {
         deriv = 1.0f;
         return x;
     }
-    __device__ __forceinline__ float dt(int64_t t) const {
-        float dd;
-        return dt(t, dd);
-    }
-    __device__ __forceinline__ float bval(int64_t t) const { return st_ok ? ld1(bn, t) : 0.0f; }
-    __device__ __forceinline__ float cval(int64_t t) const { return st_ok ? ld1(cn, t) : 0.0f; }
-    // dL/dy_t = dout_t silu(z_t)
-    __device__ __forceinline__ float dy(int64_t t) const {
-        const float g = ld1(dout, t);
-        if (!z) return g;
-        const float zz = ld1(z, t);
-        return g * zz * sigmoid(zz);
-    }
-    // h_t from h_{t-1}; w accumulates Delta
-    __device__ __forceinline__ float advance(float h, int64_t t, float& w) const {
-        const float d = dt(t);
-        w += d;
-        return __builtin_fmaf(fast_exp2(d * A), h, d * bval(t) * ld1(u, t));
-    }
-};
-
-struct Place {
-    int tid, wave, n, ch;
-    int64_t b, cb, d, row, g, t0, len;
-    bool ch_ok;
-};
-
-__device__ __forceinline__ Place place(const BwdArgs& a) {
-    Place p;
-    p.tid = threadIdx.x;
-    p.wave = p.tid >> 6;
-    p.n = p.tid & (kSt - 1);
-    p.ch = p.tid >> 4;
-    const int64_t nbc = (a.dim + kCh - 1) / kCh;
-    // chunk fastest: neighbouring workgroups share rows of B and C
-    p.g = blockIdx.x % a.G;
-    const int64_t rb = blockIdx.x / a.G;
-    p.b = rb / nbc;
-    p.cb = rb - p.b * nbc;
-    const int64_t d_raw = p.cb * kCh + p.ch;
-    p.ch_ok = d_raw < a.dim;
-    p.d = p.ch_ok ? d_raw : a.dim - 1;
-    p.row = p.b * a.dim + p.d;
-    p.t0 = p.g * a.chunk;
-    p.len = min<int64_t>(a.chunk, a.L - p.t0);
-    return p;
+    const float e = fast_exp2(-fabsf(x) * kLog2e);       // exp(-|x|) in (0, 1]
+    const float r = fast_rcp(1.0f + e);
+    deriv = x >= 0.0f ? r : e * r;
+    return softplus_log2(x * kLog2e) * kLn2;
 }
 
-// Per chunk: state at the end from a zero start, sum of Delta, and the adjoint
-// leaving the first token (a_{t0} lam_{t0}) from a zero right boundary.
-template <typename Tin, typename Tout, bool SP>
-__global__ __launch_bounds__(kThreads) void m1_bwd_summary_kernel(BwdArgs a) {
-    const Place p = place(a);
-    const Cell<Tin, Tout, SP> c(a, p.b, p.d, p.n);
-    float h = 0.0f, w = 0.0f;
-    for (int64_t s = 0; s < p.len; s += kTile) {
-        const int cnt = (int)min<int64_t>(kTile, p.len - s);
-        if (cnt == kTile) {
+struct Blk {
+    int64_t b, cb, g, t0, t_end;
+    int tiles;
+};
+
+__device__ __forceinline__ Blk blk(const BwdArgs& a) {
+    Blk k;
+    const int64_t nbc = (a.dim + kCh - 1) / kCh;
+    k.g = blockIdx.x % a.G;          // chunk fastest: neighbours share rows of B and C
+    const int64_t rb = blockIdx.x / a.G;
+    k.b = rb / nbc;
+    k.cb = rb - k.b * nbc;
+    k.t0 = k.g * a.chunk;
+    k.t_end = min<int64_t>(a.L, k.t0 + a.chunk);
+    k.tiles = (int)((k.t_end - k.t0 + kT - 1) / kT);
+    return k;
+}
+
+// Consumer view: this lane's channel and its 4 states.
+struct Con {
+    int l, w, rr, q, r;
+    bool ok;          // channel < dim
+    int64_t row;      // b * dim + channel (clamped)
+    float Al2[4];     // A[n] log2(e), 0 for padded states
+    __device__ Con(const BwdArgs& a, const Blk& k) {
+        const int tid = threadIdx.x;
+        l = tid & 63;
+        w = tid >> 6;
+        rr = l & 3;
+        q = (l >> 2) & 3;
+        r = w * 16 + (l >> 4) * 4 + rr;
+        const int64_t d = k.cb * kCh + r;
+        ok = d < a.dim;
+        const int64_t dc = ok ? d : a.dim - 1;
+        row = k.b * a.dim + dc;
 #pragma unroll
-            for (int j = 0; j < kTile; ++j) h = c.advance(h, p.t0 + s + j, w);
-        } else {
-            for (int j = 0; j < cnt; ++j) h = c.advance(h, p.t0 + s + j, w);
+        for (int i = 0; i < 4; ++i) {
+            const int n = 4 * q + i;
+            Al2[i] = (n < a.N ? a.A[dc * a.N + n] : 0.0f) * kLog2e;
         }
     }
-    float mu = 0.0f;
-    for (int64_t s = p.len; s > 0; s -= kTile) {
-        const int cnt = (int)min<int64_t>(kTile, s);
-        for (int j = 1; j <= cnt; ++j) {
-            const int64_t t = p.t0 + s - j;
-            const float lam = __builtin_fmaf(c.dy(t), c.cval(t), mu);
-            mu = fast_exp2(c.dt(t) * c.A) * lam;
+};
+
+// Producer view: channel pr, tokens pj, pj + 1 of each tile.
+struct Pro {
+    int pr, pj;
+    bool ok;
+    int64_t row;
+    float bias, D;
+    __device__ Pro(const BwdArgs& a, const Blk& k) {
+        const int tid = threadIdx.x;
+        pr = tid >> 2;
+        pj = (tid & 3) * 2;
+        const int64_t d = k.cb * kCh + pr;
+        ok = d < a.dim;
+        const int64_t dc = ok ? d : a.dim - 1;
+        row = k.b * a.dim + dc;
+        bias = a.bias ? a.bias[dc] : 0.0f;
+        D = a.D ? a.D[dc] : 0.0f;
+    }
+};
+
+// B or C of one tile: [kT][16], zero past the sequence and for padded states.
+template <typename Tin>
+__device__ __forceinline__ void load_bc_tile(const BwdArgs& a, const void* src, int64_t b, int64_t tt0,
+                                             int64_t t_end, float (*dst)[kSt]) {
+    const int tid = threadIdx.x;
+    if (tid < kT * kSt) {
+        const int j = tid >> 4, n = tid & 15;
+        const int64_t t = tt0 + j;
+        float v = 0.0f;
+        if (n < a.N && t < t_end) v = ld1(reinterpret_cast<const Tin*>(src), (b * a.N + n) * a.L + t);
+        dst[j][n] = v;
+    }
+}
+
+struct SumSmem {
+    float dt[kCh][kPad];
+    float x2[kCh][kPad];     // Delta u (forward) or dy (reverse)
+    float bc[kT][kSt];       // B (forward) or C (reverse)
+};
+
+// Per chunk, from zero: state every 8 tokens and at the end, running sum of
+// Delta; and (when the sequence has several chunks) the adjoint leaving the
+// chunk's first token, a_{t0} lam_{t0}, from a zero right boundary.
+template <typename Tin, typename Tout, bool SP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void m1_bwd_summary_kernel(BwdArgs a) {
+    __shared__ SumSmem sm;
+    const Blk k = blk(a);
+    const Con c(a, k);
+    const Pro p(a, k);
+    const int64_t TL = (a.L + kT - 1) / kT;
+    const int64_t tile0 = k.t0 / kT;
+
+    float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float W = 0.0f;
+    for (int tile = 0; tile < k.tiles; ++tile) {
+        const int64_t tt0 = k.t0 + (int64_t)tile * kT;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int64_t t = tt0 + p.pj + jj;
+            float dt = 0.0f, dtu = 0.0f;
+            if (p.ok && t < k.t_end) {
+                float dd;
+                dt = delta_of<SP>(ld1(reinterpret_cast<const Tin*>(a.delta), p.row * a.L + t) + p.bias, dd);
+                dtu = dt * ld1(reinterpret_cast<const Tin*>(a.u), p.row * a.L + t);
+            }
+            sm.dt[p.pr][p.pj + jj] = dt;
+            sm.x2[p.pr][p.pj + jj] = dtu;
         }
+        load_bc_tile<Tin>(a, a.B, k.b, tt0, k.t_end, sm.bc);
+        if (c.ok) {
+            float* dst = a.ckz + ((c.row * TL + tile0 + tile) * kSt + 4 * c.q);
+            *reinterpret_cast<float4*>(dst) = make_float4(h[0], h[1], h[2], h[3]);
+            if (c.q == 0) a.wck[c.row * TL + tile0 + tile] = W;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kT; ++j) {
+            const float dt = sm.dt[c.r][j], dtu = sm.x2[c.r][j];
+            const float4 Bv = *reinterpret_cast<const float4*>(&sm.bc[j][4 * c.q]);
+            const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+            W += dt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * c.Al2[i]), h[i], dtu * bb[i]);
+        }
+        __syncthreads();
     }
-    if (p.ch_ok) {
-        const int64_t cell = (p.row * a.G + p.g) * kSt + p.n;
-        a.hbuf[cell] = h;
-        a.mubuf[cell] = mu;
-        if (p.n == 0) a.wbuf[p.row * a.G + p.g] = w;
+    const int64_t cell = (c.row * a.G + k.g) * kSt + 4 * c.q;
+    if (c.ok) {
+        *reinterpret_cast<float4*>(a.hbuf + cell) = make_float4(h[0], h[1], h[2], h[3]);
+        if (c.q == 0) a.wbuf[c.row * a.G + k.g] = W;
     }
+    if (a.G == 1) return;   // uniform over the grid
+
+    float mu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int tile = k.tiles - 1; tile >= 0; --tile) {
+        const int64_t tt0 = k.t0 + (int64_t)tile * kT;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int64_t t = tt0 + p.pj + jj;
+            float dt = 0.0f, dy = 0.0f;
+            if (p.ok && t < k.t_end) {
+                float dd;
+                dt = delta_of<SP>(ld1(reinterpret_cast<const Tin*>(a.delta), p.row * a.L + t) + p.bias, dd);
+                dy = ld1(reinterpret_cast<const Tout*>(a.dout), p.row * a.L + t);
+                if (a.z) {
+                    const float zz = ld1(reinterpret_cast<const Tin*>(a.z), p.row * a.L + t);
+                    dy *= zz * sigmoid(zz);
+                }
+            }
+            sm.dt[p.pr][p.pj + jj] = dt;
+            sm.x2[p.pr][p.pj + jj] = dy;
+        }
+        load_bc_tile<Tin>(a, a.C, k.b, tt0, k.t_end, sm.bc);
+        __syncthreads();
+#pragma unroll
+        for (int j = kT - 1; j >= 0; --j) {
+            const float dt = sm.dt[c.r][j], dy = sm.x2[c.r][j];
+            const float4 Cv = *reinterpret_cast<const float4*>(&sm.bc[j][4 * c.q]);
+            const float cc[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mu[i] = fast_exp2(dt * c.Al2[i]) * __builtin_fmaf(dy, cc[i], mu[i]);
+        }
+        __syncthreads();
+    }
+    if (c.ok) *reinterpret_cast<float4*>(a.mubuf + cell) = make_float4(mu[0], mu[1], mu[2], mu[3]);
 }
 
 // Per (row, n): the true state entering each chunk and the true adjoint
-// entering it from the right, in place of the summaries; dh0 = the adjoint
-// leaving the first chunk.
+// entering it from the right, in place of the summaries.
 __global__ __launch_bounds__(256) void m1_bwd_carry_kernel(BwdArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= a.batch * a.dim * kSt) return;
@@ -200,162 +282,269 @@ __global__ __launch_bounds__(256) void m1_bwd_carry_kernel(BwdArgs a) {
 }
 
 struct ChunkSmem {
-    float ck[kMaxTiles][kThreads];            // state before each tile
-    float red[kWaves][kTile][2 * kSt + 1];    // per wave and token: dB[16], dC[16]
-    float go[3][kCh][kTile + 1];              // per channel and token: du, ddelta, dz
+    float dt[kCh][kPad], dtu[kCh][kPad], dy[kCh][kPad];   // read by the adjoint lanes
+    float u[kCh][kPad], dd[kCh][kPad], zf[kCh][kPad];     // kept for the output pass
+    float B[kT][kSt], C[kT][kSt];
+    float sLB[kCh][kPad], sLAq[kCh][kPad], sCh[kCh][kPad];
+    float red[kWaves][kT][2 * kSt];                       // per wave: dB[16], dC[16] per token
 };
 
+// One lane's 8 values (dB of states 4q..4q+3, then dC) summed over the wave's
+// 16 channels.  Returns the lane's share: value k = 2 rr + (lane >= 32), i.e.
+// kind k >> 2 (0 = dB, 1 = dC) of state 4q + (k & 3); every value is held by
+// two lanes, one in DPP row 0 or 2 and one in DPP row 1 or 3.
+__device__ __forceinline__ float reduce_bc(const float* v, int rr) {
+    const bool hi2 = rr & 2, hi1 = rr & 1;
+    float u4[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float keep = hi2 ? v[m + 4] : v[m];
+        const float send = hi2 ? v[m] : v[m + 4];
+        u4[m] = keep + dpp<kQuadX2>(send);          // channels rr, rr ^ 2
+    }
+    float w2[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const float keep = hi1 ? u4[m + 2] : u4[m];
+        const float send = hi1 ? u4[m] : u4[m + 2];
+        w2[m] = keep + dpp<kQuadX1>(send);          // channels rr, rr ^ 1
+    }
+    // lanes 0..31 take w2[0] summed with lanes 32..63, lanes 32..63 take w2[1]
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(w2[0]), __float_as_uint(w2[1]), false, false);
+    const float x = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    // DPP rows 0 + 1 and 2 + 3
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
 template <typename Tin, typename Tout, bool SP>
-__global__ __launch_bounds__(kThreads) void m1_bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void m1_bwd_chunk_kernel(BwdArgs a) {
     __shared__ ChunkSmem sm;
-    const Place p = place(a);
-    const Cell<Tin, Tout, SP> c(a, p.b, p.d, p.n);
-    const int tiles = (int)((p.len + kTile - 1) / kTile);
-    const int64_t cell = (p.row * a.G + p.g) * kSt + p.n;
-    const float h_in = (a.h0 && p.n < a.N) ? a.h0[p.row * a.N + p.n] : 0.0f;
+    const Blk k = blk(a);
+    const Con c(a, k);
+    const Pro p(a, k);
+    const int tid = threadIdx.x;
+    const int64_t TL = (a.L + kT - 1) / kT;
+    const int64_t tile0 = k.t0 / kT;
+    const int64_t cell = (c.row * a.G + k.g) * kSt + 4 * c.q;
 
-    {   // forward: the state before each tile
-        float h = a.G > 1 ? a.hbuf[cell] : h_in;
-        float w = 0.0f;
-        for (int tl = 0; tl < tiles; ++tl) {
-            sm.ck[tl][p.tid] = h;
-            if (tl + 1 < tiles) {
+    // state entering the chunk and adjoint entering it from the right
+    float h_in[4] = {0.0f, 0.0f, 0.0f, 0.0f}, lamn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c.ok) {
+        if (a.G > 1) {
+            const float4 hv = *reinterpret_cast<const float4*>(a.hbuf + cell);
+            const float4 mv = *reinterpret_cast<const float4*>(a.mubuf + cell);
+            h_in[0] = hv.x; h_in[1] = hv.y; h_in[2] = hv.z; h_in[3] = hv.w;
+            lamn[0] = mv.x; lamn[1] = mv.y; lamn[2] = mv.z; lamn[3] = mv.w;
+        } else if (a.h0) {
 #pragma unroll
-                for (int j = 0; j < kTile; ++j) h = c.advance(h, p.t0 + tl * kTile + j, w);
+            for (int i = 0; i < 4; ++i) {
+                const int n = 4 * c.q + i;
+                h_in[i] = n < a.N ? a.h0[c.row * a.N + n] : 0.0f;
             }
         }
     }
+    float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float dD_acc = 0.0f, dbias_acc = 0.0f;
+    // identity of this lane's dB/dC share
+    const int kk = 2 * c.rr + (c.l >= 32 ? 1 : 0);
+    const int vidx = (kk >> 2) * kSt + 4 * c.q + (kk & 3);
+    const bool writer = (c.l & 16) == 0;
 
-    float lam_next = a.G > 1 ? a.mubuf[cell] : 0.0f;   // a_{t+1} lam_{t+1} past the chunk's end
-    float dA_acc = 0.0f, dD_acc = 0.0f, dbias_acc = 0.0f;
-    for (int tl = tiles - 1; tl >= 0; --tl) {
-        const int64_t t0 = p.t0 + tl * kTile;
-        const int cnt = (int)min<int64_t>(kTile, p.len - tl * kTile);
-        const float hprev = sm.ck[tl][p.tid];
-        float hs[kTile];
-        {
-            float h = hprev, w = 0.0f;
+    for (int tile = k.tiles - 1; tile >= 0; --tile) {
+        const int64_t tt0 = k.t0 + (int64_t)tile * kT;
+        // the tile's first state: zero-start checkpoint + decayed entering state
+        float ck[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (c.ok) {
+            const float4 z = *reinterpret_cast<const float4*>(a.ckz + ((c.row * TL + tile0 + tile) * kSt + 4 * c.q));
+            const float Wc = a.wck[c.row * TL + tile0 + tile];
+            const float zz[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
-            for (int j = 0; j < kTile; ++j) {
-                if (j < cnt) h = c.advance(h, t0 + j, w);
-                hs[j] = h;
-            }
+            for (int i = 0; i < 4; ++i) ck[i] = __builtin_fmaf(fast_exp2(Wc * c.Al2[i]), h_in[i], zz[i]);
         }
+        // per-channel tile values
 #pragma unroll
-        for (int j = kTile - 1; j >= 0; --j) {
-            float cB = 0.0f, cC = 0.0f;
-            if (j < cnt) {
-                const int64_t t = t0 + j;
-                const float uu = ld1(c.u, t);
-                float dd;
-                const float dt = c.dt(t, dd);
-                const float bv = c.bval(t);
-                const float cv = c.cval(t);
-                const float h = hs[j];
-                const float hp = j > 0 ? hs[j - 1] : hprev;
-                const float g = ld1(c.dout, t);
-                float dy = g, dz = 0.0f;
-                if (c.z) {
-                    const float zz = ld1(c.z, t);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = p.pj + jj;
+            const int64_t t = tt0 + j;
+            float dt = 0.0f, dd = 0.0f, uu = 0.0f, dy = 0.0f, zf = 0.0f;
+            if (p.ok && t < k.t_end) {
+                const int64_t o = p.row * a.L + t;
+                dt = delta_of<SP>(ld1(reinterpret_cast<const Tin*>(a.delta), o) + p.bias, dd);
+                uu = ld1(reinterpret_cast<const Tin*>(a.u), o);
+                const float g = ld1(reinterpret_cast<const Tout*>(a.dout), o);
+                dy = g;
+                if (a.z) {
+                    const float zz = ld1(reinterpret_cast<const Tin*>(a.z), o);
                     const float sg = sigmoid(zz);
-                    const float y = __builtin_fmaf(c.D, uu, sum16(cv * h));
                     dy = g * zz * sg;
-                    dz = g * y * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
-                }
-                const float lam = __builtin_fmaf(dy, cv, lam_next);
-                const float at = fast_exp2(dt * c.A);
-                cC = dy * h;
-                cB = lam * dt * uu;
-                const float du = __builtin_fmaf(dy, c.D, sum16(lam * dt * bv));
-                const float ddt = sum16(lam * __builtin_fmaf(c.An * at, hp, bv * uu));
-                dA_acc = __builtin_fmaf(lam * dt * at, hp, dA_acc);
-                lam_next = at * lam;
-                const float dx = ddt * dd;
-                if (p.n == 0) {
-                    dD_acc = __builtin_fmaf(dy, uu, dD_acc);
-                    dbias_acc += dx;
-                    sm.go[0][p.ch][j] = du;
-                    sm.go[1][p.ch][j] = dx;
-                    sm.go[2][p.ch][j] = dz;
+                    zf = g * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
                 }
             }
-            if (!p.ch_ok) cB = cC = 0.0f;
-            // sum over the wave's 4 channels (lanes 16 apart)
-            cB += __shfl_xor(cB, 16, 64);
-            cB += __shfl_xor(cB, 32, 64);
-            cC += __shfl_xor(cC, 16, 64);
-            cC += __shfl_xor(cC, 32, 64);
-            if ((p.tid & 63) < kSt) {
-                sm.red[p.wave][j][p.n] = cB;
-                sm.red[p.wave][j][kSt + p.n] = cC;
+            sm.dt[p.pr][j] = dt;
+            sm.dtu[p.pr][j] = dt * uu;
+            sm.dy[p.pr][j] = dy;
+            sm.u[p.pr][j] = uu;
+            sm.dd[p.pr][j] = dd;
+            sm.zf[p.pr][j] = zf;
+        }
+        load_bc_tile<Tin>(a, a.B, k.b, tt0, k.t_end, sm.B);
+        load_bc_tile<Tin>(a, a.C, k.b, tt0, k.t_end, sm.C);
+        __syncthreads();
+
+        // recompute the tile's states
+        float hs[kT][4];
+        {
+            float h[4] = {ck[0], ck[1], ck[2], ck[3]};
+#pragma unroll
+            for (int j = 0; j < kT; ++j) {
+                const float dt = sm.dt[c.r][j], dtu = sm.dtu[c.r][j];
+                const float4 Bv = *reinterpret_cast<const float4*>(&sm.B[j][4 * c.q]);
+                const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    h[i] = __builtin_fmaf(fast_exp2(dt * c.Al2[i]), h[i], dtu * bb[i]);
+                    hs[j][i] = h[i];
+                }
             }
+        }
+        // adjoint back through the tile
+#pragma unroll
+        for (int j = kT - 1; j >= 0; --j) {
+            const float dt = sm.dt[c.r][j], dtu = sm.dtu[c.r][j], dy = sm.dy[c.r][j];
+            const float4 Bv = *reinterpret_cast<const float4*>(&sm.B[j][4 * c.q]);
+            const float4 Cv = *reinterpret_cast<const float4*>(&sm.C[j][4 * c.q]);
+            const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+            const float cc[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
+            float sLB = 0.0f, sLAq = 0.0f, sCh = 0.0f;
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float hp = j > 0 ? hs[j - 1][i] : ck[i];
+                const float at = fast_exp2(dt * c.Al2[i]);
+                const float lam = __builtin_fmaf(dy, cc[i], lamn[i]);
+                const float tq = lam * at * hp;
+                sLB = __builtin_fmaf(lam, bb[i], sLB);
+                sLAq = __builtin_fmaf(c.Al2[i], tq, sLAq);   // log2(e) sum_n A lam a h_prev
+                dA[i] = __builtin_fmaf(dt, tq, dA[i]);
+                sCh = __builtin_fmaf(cc[i], hs[j][i], sCh);
+                v[i] = lam * dtu;
+                v[4 + i] = dy * hs[j][i];
+                lamn[i] = at * lam;
+            }
+            sLB = sum_q(sLB);
+            sLAq = sum_q(sLAq);
+            sCh = sum_q(sCh);
+            if (c.q == 0) {
+                sm.sLB[c.r][j] = sLB;
+                sm.sLAq[c.r][j] = sLAq;
+                sm.sCh[c.r][j] = sCh;
+            }
+            const float s = reduce_bc(v, c.rr);
+            if (writer) sm.red[c.w][j][vidx] = s;
         }
         __syncthreads();
-        {   // dB, dC partials of this channel block: thread = (value v, token j)
-            const int v = p.tid >> 5, j = p.tid & 31;
-            float s = 0.0f;
+
+        // per-channel outputs (producer mapping)
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) s += sm.red[w][j][v];
-            if (j < cnt) a.part[((p.cb * a.batch + p.b) * 2 * kSt + v) * a.L + t0 + j] = s;
-        }
-        {   // du, ddelta, dz: thread = (channel, token j), 32 channels at a time
-            const int j = p.tid & 31;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int ch = half * 32 + (p.tid >> 5);
-                const int64_t d = p.cb * kCh + ch;
-                if (j < cnt && d < a.dim) {
-                    const int64_t o = (p.b * a.dim + d) * a.L + t0 + j;
-                    a.du[o] = sm.go[0][ch][j];
-                    a.ddelta[o] = sm.go[1][ch][j];
-                    if (c.z) a.dz[o] = sm.go[2][ch][j];
-                }
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = p.pj + jj;
+            const int64_t t = tt0 + j;
+            if (p.ok && t < k.t_end) {
+                const float sLB = sm.sLB[p.pr][j], sLAq = sm.sLAq[p.pr][j], sCh = sm.sCh[p.pr][j];
+                const float dt = sm.dt[p.pr][j], dy = sm.dy[p.pr][j], uu = sm.u[p.pr][j];
+                const int64_t o = p.row * a.L + t;
+                a.du[o] = __builtin_fmaf(dt, sLB, p.D * dy);
+                const float dx = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd[p.pr][j];
+                a.ddelta[o] = dx;
+                if (a.z) a.dz[o] = __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j];
+                dD_acc = __builtin_fmaf(dy, uu, dD_acc);
+                dbias_acc += dx;
             }
         }
-        __syncthreads();
+        {   // dB, dC partials of this channel block: thread = (token j, value v)
+            const int j = tid >> 5, v = tid & 31;
+            const int64_t t = tt0 + j;
+            if (t < k.t_end) {
+                float s = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) s += sm.red[w][j][v];
+                a.part[((k.cb * a.batch + k.b) * a.L + t) * (2 * kSt) + v] = s;
+            }
+        }
+        // No barrier needed before the next tile: a producer thread rewrites
+        // only the entries it has just read itself, sm.B/C were last read
+        // before the barrier above, and sm.sLB/sLAq/sCh/red are rewritten only
+        // after the next tile's first barrier.
     }
-    if (p.ch_ok) {
-        a.pA[cell] = dA_acc;   // zero for padded states
-        if (p.n == 0) {
-            a.pD[p.row * a.G + p.g] = dD_acc;
-            a.pbias[p.row * a.G + p.g] = dbias_acc;
+
+    if (c.ok) {
+        *reinterpret_cast<float4*>(a.pA + cell) = make_float4(dA[0], dA[1], dA[2], dA[3]);
+        if (k.g == 0 && a.dh0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 4 * c.q + i;
+                if (n < a.N) a.dh0[c.row * a.N + n] = lamn[i];   // a_0 lam_0
+            }
         }
-        // the adjoint of h0 leaves the first chunk
-        if (p.g == 0 && a.dh0 && p.n < a.N) a.dh0[p.row * a.N + p.n] = lam_next;
+    }
+    // dD, dbias: sum over the 4 producer threads of a channel (a quad)
+    dD_acc += dpp<kQuadX1>(dD_acc);
+    dD_acc += dpp<kQuadX2>(dD_acc);
+    dbias_acc += dpp<kQuadX1>(dbias_acc);
+    dbias_acc += dpp<kQuadX2>(dbias_acc);
+    if (p.ok && (tid & 3) == 0) {
+        a.pD[p.row * a.G + k.g] = dD_acc;
+        a.pbias[p.row * a.G + k.g] = dbias_acc;
     }
 }
 
-// dB, dC: sums of the channel-block partials; dA, dD, dbias: sums over
-// batches and chunks.
-__global__ __launch_bounds__(256) void m1_bwd_reduce_kernel(BwdArgs a) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// dB, dC: sum of the channel-block partials for 64 tokens of one batch,
+// transposed through LDS to the [batch, N, L] layout.
+__global__ __launch_bounds__(256) void m1_bwd_bc_reduce_kernel(BwdArgs a) {
+    __shared__ float tr[2 * kSt][64 + 1];
     const int64_t nbc = (a.dim + kCh - 1) / kCh;
-    const int64_t tot_bc = a.batch * a.N * a.L;
-    if (gid < tot_bc) {
-        const int64_t t = gid % a.L;
-        const int64_t bn = gid / a.L;
-        const int64_t n = bn % a.N;
-        const int64_t b = bn / a.N;
-        float sb = 0.0f, sc = 0.0f;
-        for (int64_t cb = 0; cb < nbc; ++cb) {
-            const float* q = a.part + ((cb * a.batch + b) * 2 * kSt + n) * a.L + t;
-            sb += q[0];
-            sc += q[kSt * a.L];
-        }
-        a.dB[gid] = sb;
-        a.dC[gid] = sc;
-        return;
+    const int64_t tblocks = (a.L + 63) / 64;
+    const int64_t b = blockIdx.x / tblocks;
+    const int64_t t0 = (blockIdx.x - b * tblocks) * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int e = s * 256 + tid;          // 64 tokens x 32 values
+        const int j = e >> 5, v = e & 31;
+        const int64_t t = t0 + j;
+        float acc = 0.0f;
+        if (t < a.L)
+            for (int64_t cb = 0; cb < nbc; ++cb) acc += a.part[((cb * a.batch + b) * a.L + t) * (2 * kSt) + v];
+        tr[v][j] = acc;
     }
-    const int64_t i = gid - tot_bc;
-    if (i < a.dim * a.N) {
-        const int64_t d = i / a.N, n = i - d * a.N;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int e = s * 256 + tid;
+        const int v = e >> 6, j = e & 63;
+        const int64_t t = t0 + j;
+        const int n = v & (kSt - 1);
+        if (t < a.L && n < a.N) {
+            float* dst = v < kSt ? a.dB : a.dC;
+            dst[(b * a.N + n) * a.L + t] = tr[v][j];
+        }
+    }
+}
+
+// dA, dD, dbias: sums over batches and chunks.
+__global__ __launch_bounds__(256) void m1_bwd_param_reduce_kernel(BwdArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid < a.dim * a.N) {
+        const int64_t d = gid / a.N, n = gid - d * a.N;
         float s = 0.0f;
         for (int64_t b = 0; b < a.batch; ++b)
             for (int64_t g = 0; g < a.G; ++g) s += a.pA[((b * a.dim + d) * a.G + g) * kSt + n];
-        a.dA[i] = s;
+        a.dA[gid] = s;
         return;
     }
-    const int64_t d = i - a.dim * a.N;
+    const int64_t d = gid - a.dim * a.N;
     if (d < a.dim) {
         float sd = 0.0f, sbias = 0.0f;
         for (int64_t b = 0; b < a.batch; ++b)
@@ -372,11 +561,11 @@ template <typename Tin, typename Tout, bool SP>
 hipError_t launch_sp(const BwdArgs& a, hipStream_t stream) {
     const int64_t nbc = (a.dim + kCh - 1) / kCh;
     const unsigned blocks = (unsigned)(a.batch * nbc * a.G);
+    {
+        KTime kt("m1_bwd_summary", stream);
+        hipLaunchKernelGGL((m1_bwd_summary_kernel<Tin, Tout, SP>), dim3(blocks), dim3(kThreads), 0, stream, a);
+    }
     if (a.G > 1) {
-        {
-            KTime kt("m1_bwd_summary", stream);
-            hipLaunchKernelGGL((m1_bwd_summary_kernel<Tin, Tout, SP>), dim3(blocks), dim3(kThreads), 0, stream, a);
-        }
         KTime kt("m1_bwd_carry", stream);
         const int64_t cells = a.batch * a.dim * kSt;
         hipLaunchKernelGGL(m1_bwd_carry_kernel, dim3((unsigned)((cells + 255) / 256)), dim3(256), 0, stream, a);
@@ -385,9 +574,14 @@ hipError_t launch_sp(const BwdArgs& a, hipStream_t stream) {
         KTime kt("m1_bwd_chunk", stream);
         hipLaunchKernelGGL((m1_bwd_chunk_kernel<Tin, Tout, SP>), dim3(blocks), dim3(kThreads), 0, stream, a);
     }
-    const int64_t total = a.batch * a.N * a.L + a.dim * a.N + a.dim;
-    KTime kt("m1_bwd_reduce", stream);
-    hipLaunchKernelGGL(m1_bwd_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
+    {
+        KTime kt("m1_bwd_bc_reduce", stream);
+        const unsigned rb = (unsigned)(a.batch * ((a.L + 63) / 64));
+        hipLaunchKernelGGL(m1_bwd_bc_reduce_kernel, dim3(rb), dim3(256), 0, stream, a);
+    }
+    KTime kt("m1_bwd_param_reduce", stream);
+    const int64_t total = a.dim * a.N + a.dim;
+    hipLaunchKernelGGL(m1_bwd_param_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -400,19 +594,24 @@ size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-int m1_bwd_tile() { return kTile; }
-int m1_bwd_max_chunk() { return kTile * kMaxTiles; }
+int m1_bwd_tile() { return kT; }
+int m1_bwd_max_chunk() { return 4096; }
 int m1_bwd_channels_per_block() { return kCh; }
 
 size_t m1_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t G) {
     const int64_t nbc = (dim + kCh - 1) / kCh;
-    const size_t cells = (size_t)batch * dim * G;
-    return 3 * a256(cells * kSt * 4) + 3 * a256(cells * 4) + a256((size_t)nbc * batch * 2 * kSt * L * 4);
+    const size_t rows = (size_t)batch * dim;
+    const size_t cells = rows * G;
+    const size_t TL = (size_t)((L + kT - 1) / kT);
+    return 3 * a256(cells * kSt * 4) + 3 * a256(cells * 4) + a256((size_t)nbc * batch * 2 * kSt * L * 4) +
+           a256(rows * TL * kSt * 4) + a256(rows * TL * 4);
 }
 
 void m1_bwd_carve(BwdArgs& a, void* ws) {
     const int64_t nbc = (a.dim + kCh - 1) / kCh;
-    const size_t cells = (size_t)a.batch * a.dim * a.G;
+    const size_t rows = (size_t)a.batch * a.dim;
+    const size_t cells = rows * a.G;
+    const size_t TL = (size_t)((a.L + kT - 1) / kT);
     char* q = static_cast<char*>(ws);
     auto take = [&q](size_t bytes) {
         float* r = reinterpret_cast<float*>(q);
@@ -426,6 +625,8 @@ void m1_bwd_carve(BwdArgs& a, void* ws) {
     a.pD = take(cells * 4);
     a.pbias = take(cells * 4);
     a.part = take((size_t)nbc * a.batch * 2 * kSt * a.L * 4);
+    a.ckz = take(rows * TL * kSt * 4);
+    a.wck = take(rows * TL * 4);
 }
 
 hipError_t launch_m1_bwd(const BwdArgs& a, int in_bf16, int out_bf16, hipStream_t stream) {

@@ -250,11 +250,11 @@ BwdPlan plan_m1_bwd(const selscan_shape_t* s) {
 selscan_status_t check_m1_bwd_shape(const selscan_shape_t* s) {
     selscan_status_t st = check_m1_shape(s);
     if (st != SELSCAN_OK) return st;
-    const int64_t nbc = (s->dim + 63) / 64;
-    if (mul_checked({nbc, s->batch, 32, s->seqlen, 4}) < 0 ||
-        mul_checked({s->batch, s->dim, (s->seqlen + 31) / 32, 16, 4}) < 0)
+    const int64_t nbc = (s->dim + selscan::m1_bwd_channels_per_block() - 1) / selscan::m1_bwd_channels_per_block();
+    const int64_t tiles = (s->seqlen + selscan::m1_bwd_tile() - 1) / selscan::m1_bwd_tile();
+    if (mul_checked({nbc, s->batch, 32, s->seqlen, 4}) < 0 || mul_checked({s->batch, s->dim, tiles, 17, 4}) < 0)
         return fail(SELSCAN_ERR_INVALID_ARG, "workspace size overflows 64-bit byte counts");
-    if (s->batch * nbc * ((s->seqlen + 31) / 32) > 0x7fffffff)
+    if (s->batch * nbc * tiles > 0x7fffffff)
         return fail(SELSCAN_ERR_UNSUPPORTED, "too many workgroups for one launch");
     return SELSCAN_OK;
 }
