@@ -70,6 +70,16 @@ __device__ __forceinline__ float sum_q(float v) {
     return v + dpp<kRor8>(v);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, not for its global loads (prefetches stay in flight) or stores.
+// No data passes between threads through global memory inside a kernel here.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
 
 // Delta = softplus(x) (natural units) and its derivative sigmoid(x)
@@ -147,18 +157,49 @@ struct Pro {
     }
 };
 
-// B or C of one tile: [kT][16], zero past the sequence and for padded states.
-template <typename Tin>
-__device__ __forceinline__ void load_bc_tile(const BwdArgs& a, const void* src, int64_t b, int64_t tt0,
-                                             int64_t t_end, float (*dst)[kSt]) {
-    const int tid = threadIdx.x;
-    if (tid < kT * kSt) {
-        const int j = tid >> 4, n = tid & 15;
-        const int64_t t = tt0 + j;
-        float v = 0.0f;
-        if (n < a.N && t < t_end) v = ld1(reinterpret_cast<const Tin*>(src), (b * a.N + n) * a.L + t);
-        dst[j][n] = v;
+// A producer thread's raw inputs for its 2 tokens of one tile, and one entry
+// of the tile's B and C (threads 0..127), loaded a tile ahead of their use.
+// The loads are unconditional, from clamped in-bounds addresses, and the raw
+// bits are kept: the loads stay in flight until the values are used, where
+// tokens past the sequence and channels past dim are masked to zero.
+template <typename Tin, typename Tout>
+struct Raw {
+    Tin x[2], u[2], z[2];
+    Tout g[2];
+    Tin bv, cv;
+};
+
+__device__ __forceinline__ float f32_of(float v) { return v; }
+__device__ __forceinline__ float f32_of(uint16_t v) { return bf16_to_f32(v); }
+
+// U: u, Z: z and dout, BB: B, CC: C.
+template <typename Tin, typename Tout, bool U, bool Z, bool BB, bool CC>
+__device__ __forceinline__ void fetch_raw(const BwdArgs& a, const Blk& k, const Pro& p, int64_t tt0,
+                                          Raw<Tin, Tout>& r) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int64_t t = min<int64_t>(tt0 + p.pj + jj, a.L - 1);
+        const int64_t o = p.row * a.L + t;
+        r.x[jj] = reinterpret_cast<const Tin*>(a.delta)[o];
+        if (U) r.u[jj] = reinterpret_cast<const Tin*>(a.u)[o];
+        if (Z) {
+            r.g[jj] = reinterpret_cast<const Tout*>(a.dout)[o];
+            // without a gate: a valid address whose value is ignored
+            r.z[jj] = reinterpret_cast<const Tin*>(a.z ? a.z : a.delta)[o];
+        }
     }
+    {   // threads 0..127 hold entry (j, n); the others load a duplicate
+        const int j = (threadIdx.x >> 4) & (kT - 1), n = min<int>(threadIdx.x & 15, a.N - 1);
+        const int64_t o = (k.b * a.N + n) * a.L + min<int64_t>(tt0 + j, a.L - 1);
+        if (BB) r.bv = reinterpret_cast<const Tin*>(a.B)[o];
+        if (CC) r.cv = reinterpret_cast<const Tin*>(a.C)[o];
+    }
+}
+
+// whether entry (j, n) of a B/C tile is a real value
+__device__ __forceinline__ bool bc_valid(const BwdArgs& a, const Blk& k, int64_t tt0) {
+    const int j = threadIdx.x >> 4, n = threadIdx.x & 15;
+    return n < a.N && tt0 + j < k.t_end;
 }
 
 struct SumSmem {
@@ -177,32 +218,35 @@ void m1_bwd_summary_kernel(BwdArgs a) {
     const Blk k = blk(a);
     const Con c(a, k);
     const Pro p(a, k);
+    const int tid = threadIdx.x;
     const int64_t TL = (a.L + kT - 1) / kT;
     const int64_t tile0 = k.t0 / kT;
+    const bool bc_thread = tid < kT * kSt;
+    const int bj = (tid >> 4) & (kT - 1), bn = tid & 15;
 
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float W = 0.0f;
+    Raw<Tin, Tout> r;
+    fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, k.t0, r);
     for (int tile = 0; tile < k.tiles; ++tile) {
         const int64_t tt0 = k.t0 + (int64_t)tile * kT;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int64_t t = tt0 + p.pj + jj;
-            float dt = 0.0f, dtu = 0.0f;
-            if (p.ok && t < k.t_end) {
-                float dd;
-                dt = delta_of<SP>(ld1(reinterpret_cast<const Tin*>(a.delta), p.row * a.L + t) + p.bias, dd);
-                dtu = dt * ld1(reinterpret_cast<const Tin*>(a.u), p.row * a.L + t);
-            }
-            sm.dt[p.pr][p.pj + jj] = dt;
-            sm.x2[p.pr][p.pj + jj] = dtu;
+            float dd;
+            const float dt = delta_of<SP>(f32_of(r.x[jj]) + p.bias, dd);
+            const bool ok = p.ok && tt0 + p.pj + jj < k.t_end;
+            sm.dt[p.pr][p.pj + jj] = ok ? dt : 0.0f;
+            sm.x2[p.pr][p.pj + jj] = ok ? dt * f32_of(r.u[jj]) : 0.0f;
         }
-        load_bc_tile<Tin>(a, a.B, k.b, tt0, k.t_end, sm.bc);
+        if (bc_thread) sm.bc[bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.bv) : 0.0f;
         if (c.ok) {
             float* dst = a.ckz + ((c.row * TL + tile0 + tile) * kSt + 4 * c.q);
             *reinterpret_cast<float4*>(dst) = make_float4(h[0], h[1], h[2], h[3]);
             if (c.q == 0) a.wck[c.row * TL + tile0 + tile] = W;
         }
-        __syncthreads();
+        lds_barrier();
+        // unconditional (the last tile re-fetches itself): no branch around the loads
+        fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, k.t0 + (int64_t)min(tile + 1, k.tiles - 1) * kT, r);
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
             const float dt = sm.dt[c.r][j], dtu = sm.x2[c.r][j];
@@ -212,7 +256,7 @@ void m1_bwd_summary_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * c.Al2[i]), h[i], dtu * bb[i]);
         }
-        __syncthreads();
+        lds_barrier();
     }
     const int64_t cell = (c.row * a.G + k.g) * kSt + 4 * c.q;
     if (c.ok) {
@@ -222,26 +266,26 @@ void m1_bwd_summary_kernel(BwdArgs a) {
     if (a.G == 1) return;   // uniform over the grid
 
     float mu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, k.t0 + (int64_t)(k.tiles - 1) * kT, r);
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
         const int64_t tt0 = k.t0 + (int64_t)tile * kT;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int64_t t = tt0 + p.pj + jj;
-            float dt = 0.0f, dy = 0.0f;
-            if (p.ok && t < k.t_end) {
-                float dd;
-                dt = delta_of<SP>(ld1(reinterpret_cast<const Tin*>(a.delta), p.row * a.L + t) + p.bias, dd);
-                dy = ld1(reinterpret_cast<const Tout*>(a.dout), p.row * a.L + t);
-                if (a.z) {
-                    const float zz = ld1(reinterpret_cast<const Tin*>(a.z), p.row * a.L + t);
-                    dy *= zz * sigmoid(zz);
-                }
+            float dd;
+            const float dt = delta_of<SP>(f32_of(r.x[jj]) + p.bias, dd);
+            const bool ok = p.ok && tt0 + p.pj + jj < k.t_end;
+            const float g = f32_of(r.g[jj]);
+            float dy = g;
+            if (a.z) {
+                const float zz = f32_of(r.z[jj]);
+                dy = g * zz * sigmoid(zz);
             }
-            sm.dt[p.pr][p.pj + jj] = dt;
-            sm.x2[p.pr][p.pj + jj] = dy;
+            sm.dt[p.pr][p.pj + jj] = ok ? dt : 0.0f;
+            sm.x2[p.pr][p.pj + jj] = ok ? dy : 0.0f;
         }
-        load_bc_tile<Tin>(a, a.C, k.b, tt0, k.t_end, sm.bc);
-        __syncthreads();
+        if (bc_thread) sm.bc[bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.cv) : 0.0f;
+        lds_barrier();
+        fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, k.t0 + (int64_t)max(tile - 1, 0) * kT, r);
 #pragma unroll
         for (int j = kT - 1; j >= 0; --j) {
             const float dt = sm.dt[c.r][j], dy = sm.x2[c.r][j];
@@ -250,7 +294,7 @@ void m1_bwd_summary_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) mu[i] = fast_exp2(dt * c.Al2[i]) * __builtin_fmaf(dy, cc[i], mu[i]);
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (c.ok) *reinterpret_cast<float4*>(a.mubuf + cell) = make_float4(mu[0], mu[1], mu[2], mu[3]);
 }
@@ -328,22 +372,28 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
     const int64_t TL = (a.L + kT - 1) / kT;
     const int64_t tile0 = k.t0 / kT;
     const int64_t cell = (c.row * a.G + k.g) * kSt + 4 * c.q;
+    const bool bc_thread = tid < kT * kSt;
+    const int bj = (tid >> 4) & (kT - 1), bn = tid & 15;
 
     // state entering the chunk and adjoint entering it from the right
+    // (c.row is clamped in bounds: loads are unconditional, results masked)
     float h_in[4] = {0.0f, 0.0f, 0.0f, 0.0f}, lamn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (c.ok) {
-        if (a.G > 1) {
-            const float4 hv = *reinterpret_cast<const float4*>(a.hbuf + cell);
-            const float4 mv = *reinterpret_cast<const float4*>(a.mubuf + cell);
-            h_in[0] = hv.x; h_in[1] = hv.y; h_in[2] = hv.z; h_in[3] = hv.w;
-            lamn[0] = mv.x; lamn[1] = mv.y; lamn[2] = mv.z; lamn[3] = mv.w;
-        } else if (a.h0) {
+    if (a.G > 1) {
+        const float4 hv = *reinterpret_cast<const float4*>(a.hbuf + cell);
+        const float4 mv = *reinterpret_cast<const float4*>(a.mubuf + cell);
+        h_in[0] = hv.x; h_in[1] = hv.y; h_in[2] = hv.z; h_in[3] = hv.w;
+        lamn[0] = mv.x; lamn[1] = mv.y; lamn[2] = mv.z; lamn[3] = mv.w;
+    } else if (a.h0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = 4 * c.q + i;
-                h_in[i] = n < a.N ? a.h0[c.row * a.N + n] : 0.0f;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int n = 4 * c.q + i;
+            h_in[i] = a.h0[c.row * a.N + min(n, a.N - 1)] * (n < a.N ? 1.0f : 0.0f);
         }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h_in[i] = c.ok ? h_in[i] : 0.0f;
+        lamn[i] = c.ok ? lamn[i] : 0.0f;
     }
     float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float dD_acc = 0.0f, dbias_acc = 0.0f;
@@ -352,46 +402,60 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
     const int vidx = (kk >> 2) * kSt + 4 * c.q + (kk & 3);
     const bool writer = (c.l & 16) == 0;
 
+    // prefetched inputs of the next tile (processed from the last)
+    Raw<Tin, Tout> r;
+    float4 zck;
+    float wc;
+    auto fetch = [&](int tile) {   // c.row is clamped in bounds
+        fetch_raw<Tin, Tout, true, true, true, true>(a, k, p, k.t0 + (int64_t)tile * kT, r);
+        zck = *reinterpret_cast<const float4*>(a.ckz + ((c.row * TL + tile0 + tile) * kSt + 4 * c.q));
+        wc = a.wck[c.row * TL + tile0 + tile];
+    };
+    fetch(k.tiles - 1);
+
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
         const int64_t tt0 = k.t0 + (int64_t)tile * kT;
-        // the tile's first state: zero-start checkpoint + decayed entering state
-        float ck[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (c.ok) {
-            const float4 z = *reinterpret_cast<const float4*>(a.ckz + ((c.row * TL + tile0 + tile) * kSt + 4 * c.q));
-            const float Wc = a.wck[c.row * TL + tile0 + tile];
-            const float zz[4] = {z.x, z.y, z.z, z.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ck[i] = __builtin_fmaf(fast_exp2(Wc * c.Al2[i]), h_in[i], zz[i]);
-        }
         // per-channel tile values
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j = p.pj + jj;
-            const int64_t t = tt0 + j;
-            float dt = 0.0f, dd = 0.0f, uu = 0.0f, dy = 0.0f, zf = 0.0f;
-            if (p.ok && t < k.t_end) {
-                const int64_t o = p.row * a.L + t;
-                dt = delta_of<SP>(ld1(reinterpret_cast<const Tin*>(a.delta), o) + p.bias, dd);
-                uu = ld1(reinterpret_cast<const Tin*>(a.u), o);
-                const float g = ld1(reinterpret_cast<const Tout*>(a.dout), o);
-                dy = g;
-                if (a.z) {
-                    const float zz = ld1(reinterpret_cast<const Tin*>(a.z), o);
-                    const float sg = sigmoid(zz);
-                    dy = g * zz * sg;
-                    zf = g * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
-                }
+            const bool ok = p.ok && tt0 + j < k.t_end;
+            float dd;
+            const float dt = delta_of<SP>(f32_of(r.x[jj]) + p.bias, dd);
+            const float g = f32_of(r.g[jj]), uu = f32_of(r.u[jj]);
+            float dy = g, zf = 0.0f;
+            if (a.z) {
+                const float zz = f32_of(r.z[jj]), sg = sigmoid(zz);
+                dy = g * zz * sg;
+                zf = g * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
             }
-            sm.dt[p.pr][j] = dt;
-            sm.dtu[p.pr][j] = dt * uu;
-            sm.dy[p.pr][j] = dy;
+            sm.dt[p.pr][j] = ok ? dt : 0.0f;
+            sm.dtu[p.pr][j] = ok ? dt * uu : 0.0f;
+            sm.dy[p.pr][j] = ok ? dy : 0.0f;
             sm.u[p.pr][j] = uu;
             sm.dd[p.pr][j] = dd;
             sm.zf[p.pr][j] = zf;
         }
-        load_bc_tile<Tin>(a, a.B, k.b, tt0, k.t_end, sm.B);
-        load_bc_tile<Tin>(a, a.C, k.b, tt0, k.t_end, sm.C);
-        __syncthreads();
+        if (bc_thread) {
+            const bool ok = bc_valid(a, k, tt0);
+            sm.B[bj][bn] = ok ? f32_of(r.bv) : 0.0f;
+            sm.C[bj][bn] = ok ? f32_of(r.cv) : 0.0f;
+        }
+        lds_barrier();
+        // the tile's first state: zero-start checkpoint + decayed entering
+        // state (taken from the prefetch registers before they are reused)
+        float ck[4];
+        {
+            const float zz[4] = {zck.x, zck.y, zck.z, zck.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ck[i] = c.ok ? __builtin_fmaf(fast_exp2(wc * c.Al2[i]), h_in[i], zz[i]) : 0.0f;
+        }
+        // ck is computed here, before the next loads: the prefetch registers
+        // are then free for them and the loop carries no copies (whose waits
+        // would drain the prefetch every tile)
+        asm volatile("" ::"v"(ck[0]), "v"(ck[1]), "v"(ck[2]), "v"(ck[3]) : "memory");
+        fetch(tile > 0 ? tile - 1 : 0);   // unconditional: no branch around the loads
 
         // recompute the tile's states
         float hs[kT][4];
@@ -444,7 +508,7 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
             const float s = reduce_bc(v, c.rr);
             if (writer) sm.red[c.w][j][vidx] = s;
         }
-        __syncthreads();
+        lds_barrier();
 
         // per-channel outputs (producer mapping)
 #pragma unroll
@@ -500,60 +564,60 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
     }
 }
 
-// dB, dC: sum of the channel-block partials for 64 tokens of one batch,
-// transposed through LDS to the [batch, N, L] layout.
+// dB, dC: sums of the channel-block partials; thread = (token, value) of 8
+// tokens of one batch, partials read 128 bytes per token.
 __global__ __launch_bounds__(256) void m1_bwd_bc_reduce_kernel(BwdArgs a) {
-    __shared__ float tr[2 * kSt][64 + 1];
     const int64_t nbc = (a.dim + kCh - 1) / kCh;
-    const int64_t tblocks = (a.L + 63) / 64;
+    const int64_t tblocks = (a.L + kT - 1) / kT;
     const int64_t b = blockIdx.x / tblocks;
-    const int64_t t0 = (blockIdx.x - b * tblocks) * 64;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int e = s * 256 + tid;          // 64 tokens x 32 values
-        const int j = e >> 5, v = e & 31;
-        const int64_t t = t0 + j;
-        float acc = 0.0f;
-        if (t < a.L)
-            for (int64_t cb = 0; cb < nbc; ++cb) acc += a.part[((cb * a.batch + b) * a.L + t) * (2 * kSt) + v];
-        tr[v][j] = acc;
+    const int64_t t = (blockIdx.x - b * tblocks) * kT + (threadIdx.x >> 5);
+    const int v = threadIdx.x & 31, n = v & (kSt - 1);
+    if (t >= a.L) return;
+    const float* src = a.part + (b * a.L + t) * (2 * kSt) + v;
+    const int64_t stride = a.batch * a.L * (2 * kSt);
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    int64_t cb = 0;
+    for (; cb + 4 <= nbc; cb += 4) {
+        s0 += src[(cb + 0) * stride];
+        s1 += src[(cb + 1) * stride];
+        s2 += src[(cb + 2) * stride];
+        s3 += src[(cb + 3) * stride];
     }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int e = s * 256 + tid;
-        const int v = e >> 6, j = e & 63;
-        const int64_t t = t0 + j;
-        const int n = v & (kSt - 1);
-        if (t < a.L && n < a.N) {
-            float* dst = v < kSt ? a.dB : a.dC;
-            dst[(b * a.N + n) * a.L + t] = tr[v][j];
-        }
-    }
+    for (; cb < nbc; ++cb) s0 += src[cb * stride];
+    const float s = (s0 + s1) + (s2 + s3);
+    if (n < a.N) (v < kSt ? a.dB : a.dC)[(b * a.N + n) * a.L + t] = s;
 }
 
-// dA, dD, dbias: sums over batches and chunks.
+// dA, dD, dbias: one wave per channel sums the (batch, chunk) partials, each
+// lane a fixed strided share, then a fixed butterfly over the wave.
 __global__ __launch_bounds__(256) void m1_bwd_param_reduce_kernel(BwdArgs a) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid < a.dim * a.N) {
-        const int64_t d = gid / a.N, n = gid - d * a.N;
-        float s = 0.0f;
-        for (int64_t b = 0; b < a.batch; ++b)
-            for (int64_t g = 0; g < a.G; ++g) s += a.pA[((b * a.dim + d) * a.G + g) * kSt + n];
-        a.dA[gid] = s;
-        return;
+    const int64_t d = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    if (d >= a.dim) return;   // uniform per wave
+    float acc[kSt + 2];
+#pragma unroll
+    for (int i = 0; i < kSt + 2; ++i) acc[i] = 0.0f;
+    const int64_t recs = a.batch * a.G;
+    for (int64_t e = l; e < recs; e += 64) {
+        const int64_t b = e / a.G, g = e - b * a.G;
+        const int64_t rg = (b * a.dim + d) * a.G + g;
+        const float4* q = reinterpret_cast<const float4*>(a.pA + rg * kSt);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 x = q[m];
+            acc[4 * m] += x.x; acc[4 * m + 1] += x.y; acc[4 * m + 2] += x.z; acc[4 * m + 3] += x.w;
+        }
+        acc[kSt] += a.pD[rg];
+        acc[kSt + 1] += a.pbias[rg];
     }
-    const int64_t d = gid - a.dim * a.N;
-    if (d < a.dim) {
-        float sd = 0.0f, sbias = 0.0f;
-        for (int64_t b = 0; b < a.batch; ++b)
-            for (int64_t g = 0; g < a.G; ++g) {
-                sd += a.pD[(b * a.dim + d) * a.G + g];
-                sbias += a.pbias[(b * a.dim + d) * a.G + g];
-            }
-        if (a.dD) a.dD[d] = sd;
-        if (a.dbias) a.dbias[d] = sbias;
+#pragma unroll
+    for (int i = 0; i < kSt + 2; ++i)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc[i] += __shfl_xor(acc[i], o, 64);
+    if (l == 0) {
+        for (int n = 0; n < a.N; ++n) a.dA[d * a.N + n] = acc[n];
+        if (a.dD) a.dD[d] = acc[kSt];
+        if (a.dbias) a.dbias[d] = acc[kSt + 1];
     }
 }
 
@@ -576,12 +640,11 @@ hipError_t launch_sp(const BwdArgs& a, hipStream_t stream) {
     }
     {
         KTime kt("m1_bwd_bc_reduce", stream);
-        const unsigned rb = (unsigned)(a.batch * ((a.L + 63) / 64));
+        const unsigned rb = (unsigned)(a.batch * ((a.L + kT - 1) / kT));
         hipLaunchKernelGGL(m1_bwd_bc_reduce_kernel, dim3(rb), dim3(256), 0, stream, a);
     }
     KTime kt("m1_bwd_param_reduce", stream);
-    const int64_t total = a.dim * a.N + a.dim;
-    hipLaunchKernelGGL(m1_bwd_param_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(m1_bwd_param_reduce_kernel, dim3((unsigned)((a.dim + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
