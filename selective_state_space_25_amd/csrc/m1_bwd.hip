@@ -95,9 +95,25 @@ __device__ __forceinline__ float delta_of(float x, float& deriv) {
     return softplus_log2(x * kLog2e) * kLn2;
 }
 
+// Uniform per workgroup: its (batch, channel block, chunk) and the first row
+// of its channel block.  Tensors are addressed from per-workgroup base
+// pointers (scalar registers) with 32-bit per-thread byte offsets, which the
+// hardware adds to the base itself; the host keeps L <= 2^22, so every byte
+// offset within a workgroup's rows fits in 32 bits.
+// element idx of base through a 32-bit byte offset
+template <typename T>
+__device__ __forceinline__ T ldo(const T* base, uint32_t idx) {
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + idx * (uint32_t)sizeof(T));
+}
+template <typename T>
+__device__ __forceinline__ void sto(T* base, uint32_t idx, T v) {
+    *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + idx * (uint32_t)sizeof(T)) = v;
+}
+
 struct Blk {
-    int64_t b, cb, g, t0, t_end;
-    int tiles;
+    int64_t b, cb, g, row0;       // row0 = b dim + 64 cb
+    int t0, t_end, tiles, rows;   // rows: channels of this block below dim
+    int L, TL;                    // tokens; 8-token tiles per row
 };
 
 __device__ __forceinline__ Blk blk(const BwdArgs& a) {
@@ -107,18 +123,21 @@ __device__ __forceinline__ Blk blk(const BwdArgs& a) {
     const int64_t rb = blockIdx.x / a.G;
     k.b = rb / nbc;
     k.cb = rb - k.b * nbc;
-    k.t0 = k.g * a.chunk;
-    k.t_end = min<int64_t>(a.L, k.t0 + a.chunk);
-    k.tiles = (int)((k.t_end - k.t0 + kT - 1) / kT);
+    k.row0 = k.b * a.dim + k.cb * kCh;
+    k.L = (int)a.L;
+    k.TL = (k.L + kT - 1) / kT;
+    k.t0 = (int)(k.g * a.chunk);
+    k.t_end = min(k.L, k.t0 + (int)a.chunk);
+    k.tiles = (k.t_end - k.t0 + kT - 1) / kT;
+    k.rows = (int)min<int64_t>(kCh, a.dim - k.cb * kCh);
     return k;
 }
 
 // Consumer view: this lane's channel and its 4 states.
 struct Con {
-    int l, w, rr, q, r;
-    bool ok;          // channel < dim
-    int64_t row;      // b * dim + channel (clamped)
-    float Al2[4];     // A[n] log2(e), 0 for padded states
+    int l, w, rr, q, r, rc;   // rc: r clamped below the block's rows
+    bool ok;                  // channel < dim
+    float Al2[4];             // A[n] log2(e), 0 for padded states
     __device__ Con(const BwdArgs& a, const Blk& k) {
         const int tid = threadIdx.x;
         l = tid & 63;
@@ -126,34 +145,50 @@ struct Con {
         rr = l & 3;
         q = (l >> 2) & 3;
         r = w * 16 + (l >> 4) * 4 + rr;
-        const int64_t d = k.cb * kCh + r;
-        ok = d < a.dim;
-        const int64_t dc = ok ? d : a.dim - 1;
-        row = k.b * a.dim + dc;
+        ok = r < k.rows;
+        rc = ok ? r : k.rows - 1;
+        const float* Ab = a.A + k.cb * kCh * a.N;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int n = 4 * q + i;
-            Al2[i] = (n < a.N ? a.A[dc * a.N + n] : 0.0f) * kLog2e;
+            Al2[i] = (n < a.N ? Ab[rc * a.N + n] : 0.0f) * kLog2e;
         }
     }
 };
 
 // Producer view: channel pr, tokens pj, pj + 1 of each tile.
 struct Pro {
-    int pr, pj;
+    int pr, pj, rc;
     bool ok;
-    int64_t row;
+    uint32_t off;   // rc * L: the channel's row within the block's rows
     float bias, D;
     __device__ Pro(const BwdArgs& a, const Blk& k) {
         const int tid = threadIdx.x;
         pr = tid >> 2;
         pj = (tid & 3) * 2;
-        const int64_t d = k.cb * kCh + pr;
-        ok = d < a.dim;
-        const int64_t dc = ok ? d : a.dim - 1;
-        row = k.b * a.dim + dc;
-        bias = a.bias ? a.bias[dc] : 0.0f;
-        D = a.D ? a.D[dc] : 0.0f;
+        ok = pr < k.rows;
+        rc = ok ? pr : k.rows - 1;
+        off = (uint32_t)rc * (uint32_t)k.L;
+        const int64_t d = k.cb * kCh + rc;
+        bias = a.bias ? a.bias[d] : 0.0f;
+        D = a.D ? a.D[d] : 0.0f;
+    }
+};
+
+// The block's rows of the per-token inputs, and its batch's B and C.
+template <typename Tin, typename Tout>
+struct In {
+    const Tin *delta, *u, *z, *B, *C;
+    const Tout* dout;
+    __device__ In(const BwdArgs& a, const Blk& k) {
+        const int64_t o = k.row0 * a.L;
+        delta = reinterpret_cast<const Tin*>(a.delta) + o;
+        u = reinterpret_cast<const Tin*>(a.u) + o;
+        // without a gate: a valid address whose values are ignored
+        z = reinterpret_cast<const Tin*>(a.z ? a.z : a.delta) + o;
+        dout = reinterpret_cast<const Tout*>(a.dout) + o;
+        B = reinterpret_cast<const Tin*>(a.B) + k.b * a.N * a.L;
+        C = reinterpret_cast<const Tin*>(a.C) + k.b * a.N * a.L;
     }
 };
 
@@ -174,30 +209,28 @@ __device__ __forceinline__ float f32_of(uint16_t v) { return bf16_to_f32(v); }
 
 // U: u, Z: z and dout, BB: B, CC: C.
 template <typename Tin, typename Tout, bool U, bool Z, bool BB, bool CC>
-__device__ __forceinline__ void fetch_raw(const BwdArgs& a, const Blk& k, const Pro& p, int64_t tt0,
-                                          Raw<Tin, Tout>& r) {
+__device__ __forceinline__ void fetch_raw(const BwdArgs& a, const Blk& k, const Pro& p, const In<Tin, Tout>& in,
+                                          int tt0, Raw<Tin, Tout>& r) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-        const int64_t t = min<int64_t>(tt0 + p.pj + jj, a.L - 1);
-        const int64_t o = p.row * a.L + t;
-        r.x[jj] = reinterpret_cast<const Tin*>(a.delta)[o];
-        if (U) r.u[jj] = reinterpret_cast<const Tin*>(a.u)[o];
+        const uint32_t o = p.off + (uint32_t)min(tt0 + p.pj + jj, k.L - 1);
+        r.x[jj] = ldo(in.delta, o);
+        if (U) r.u[jj] = ldo(in.u, o);
         if (Z) {
-            r.g[jj] = reinterpret_cast<const Tout*>(a.dout)[o];
-            // without a gate: a valid address whose value is ignored
-            r.z[jj] = reinterpret_cast<const Tin*>(a.z ? a.z : a.delta)[o];
+            r.g[jj] = ldo(in.dout, o);
+            r.z[jj] = ldo(in.z, o);
         }
     }
     {   // threads 0..127 hold entry (j, n); the others load a duplicate
         const int j = (threadIdx.x >> 4) & (kT - 1), n = min<int>(threadIdx.x & 15, a.N - 1);
-        const int64_t o = (k.b * a.N + n) * a.L + min<int64_t>(tt0 + j, a.L - 1);
-        if (BB) r.bv = reinterpret_cast<const Tin*>(a.B)[o];
-        if (CC) r.cv = reinterpret_cast<const Tin*>(a.C)[o];
+        const uint32_t o = (uint32_t)n * (uint32_t)k.L + (uint32_t)min(tt0 + j, k.L - 1);
+        if (BB) r.bv = ldo(in.B, o);
+        if (CC) r.cv = ldo(in.C, o);
     }
 }
 
 // whether entry (j, n) of a B/C tile is a real value
-__device__ __forceinline__ bool bc_valid(const BwdArgs& a, const Blk& k, int64_t tt0) {
+__device__ __forceinline__ bool bc_valid(const BwdArgs& a, const Blk& k, int tt0) {
     const int j = threadIdx.x >> 4, n = threadIdx.x & 15;
     return n < a.N && tt0 + j < k.t_end;
 }
@@ -218,18 +251,21 @@ void m1_bwd_summary_kernel(BwdArgs a) {
     const Blk k = blk(a);
     const Con c(a, k);
     const Pro p(a, k);
+    const In<Tin, Tout> in(a, k);
     const int tid = threadIdx.x;
-    const int64_t TL = (a.L + kT - 1) / kT;
-    const int64_t tile0 = k.t0 / kT;
+    const int tile0 = k.t0 / kT;
     const bool bc_thread = tid < kT * kSt;
     const int bj = (tid >> 4) & (kT - 1), bn = tid & 15;
+    float* ckz = a.ckz + k.row0 * k.TL * kSt;
+    float* wck = a.wck + k.row0 * k.TL;
+    const uint32_t ckrow = (uint32_t)c.rc * (uint32_t)k.TL;
 
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float W = 0.0f;
     Raw<Tin, Tout> r;
-    fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, k.t0, r);
+    fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, in, k.t0, r);
     for (int tile = 0; tile < k.tiles; ++tile) {
-        const int64_t tt0 = k.t0 + (int64_t)tile * kT;
+        const int tt0 = k.t0 + tile * kT;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             float dd;
@@ -240,13 +276,13 @@ void m1_bwd_summary_kernel(BwdArgs a) {
         }
         if (bc_thread) sm.bc[bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.bv) : 0.0f;
         if (c.ok) {
-            float* dst = a.ckz + ((c.row * TL + tile0 + tile) * kSt + 4 * c.q);
-            *reinterpret_cast<float4*>(dst) = make_float4(h[0], h[1], h[2], h[3]);
-            if (c.q == 0) a.wck[c.row * TL + tile0 + tile] = W;
+            const uint32_t ct = ckrow + (uint32_t)(tile0 + tile);
+            sto(reinterpret_cast<float4*>(ckz), ct * 4 + c.q, make_float4(h[0], h[1], h[2], h[3]));
+            if (c.q == 0) sto(wck, ct, W);
         }
         lds_barrier();
         // unconditional (the last tile re-fetches itself): no branch around the loads
-        fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, k.t0 + (int64_t)min(tile + 1, k.tiles - 1) * kT, r);
+        fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, in, k.t0 + min(tile + 1, k.tiles - 1) * kT, r);
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
             const float dt = sm.dt[c.r][j], dtu = sm.x2[c.r][j];
@@ -258,17 +294,20 @@ void m1_bwd_summary_kernel(BwdArgs a) {
         }
         lds_barrier();
     }
-    const int64_t cell = (c.row * a.G + k.g) * kSt + 4 * c.q;
+    const int G = (int)a.G;
+    const uint32_t cg = (uint32_t)c.rc * (uint32_t)G + (uint32_t)k.g;
+    const uint32_t cell = cg * kSt + 4 * c.q;
+    float* hbuf = a.hbuf + k.row0 * G * kSt;
     if (c.ok) {
-        *reinterpret_cast<float4*>(a.hbuf + cell) = make_float4(h[0], h[1], h[2], h[3]);
-        if (c.q == 0) a.wbuf[c.row * a.G + k.g] = W;
+        *reinterpret_cast<float4*>(hbuf + cell) = make_float4(h[0], h[1], h[2], h[3]);
+        if (c.q == 0) (a.wbuf + k.row0 * G)[cg] = W;
     }
-    if (a.G == 1) return;   // uniform over the grid
+    if (G == 1) return;   // uniform over the grid
 
     float mu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, k.t0 + (int64_t)(k.tiles - 1) * kT, r);
+    fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, in, k.t0 + (k.tiles - 1) * kT, r);
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
-        const int64_t tt0 = k.t0 + (int64_t)tile * kT;
+        const int tt0 = k.t0 + tile * kT;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             float dd;
@@ -285,7 +324,7 @@ void m1_bwd_summary_kernel(BwdArgs a) {
         }
         if (bc_thread) sm.bc[bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.cv) : 0.0f;
         lds_barrier();
-        fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, k.t0 + (int64_t)max(tile - 1, 0) * kT, r);
+        fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, in, k.t0 + max(tile - 1, 0) * kT, r);
 #pragma unroll
         for (int j = kT - 1; j >= 0; --j) {
             const float dt = sm.dt[c.r][j], dy = sm.x2[c.r][j];
@@ -296,7 +335,7 @@ void m1_bwd_summary_kernel(BwdArgs a) {
         }
         lds_barrier();
     }
-    if (c.ok) *reinterpret_cast<float4*>(a.mubuf + cell) = make_float4(mu[0], mu[1], mu[2], mu[3]);
+    if (c.ok) *reinterpret_cast<float4*>(a.mubuf + k.row0 * G * kSt + cell) = make_float4(mu[0], mu[1], mu[2], mu[3]);
 }
 
 // Per (row, n): the true state entering each chunk and the true adjoint
@@ -368,26 +407,33 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
     const Blk k = blk(a);
     const Con c(a, k);
     const Pro p(a, k);
+    const In<Tin, Tout> in(a, k);
     const int tid = threadIdx.x;
-    const int64_t TL = (a.L + kT - 1) / kT;
-    const int64_t tile0 = k.t0 / kT;
-    const int64_t cell = (c.row * a.G + k.g) * kSt + 4 * c.q;
+    const int tile0 = k.t0 / kT;
+    const int G = (int)a.G;
+    const uint32_t cg = (uint32_t)c.rc * (uint32_t)G + (uint32_t)k.g;   // (channel, chunk) record
+    const uint32_t cell = cg * kSt + 4 * c.q;
+    const int64_t cell0 = k.row0 * G * kSt;
     const bool bc_thread = tid < kT * kSt;
     const int bj = (tid >> 4) & (kT - 1), bn = tid & 15;
+    const float* ckz = a.ckz + k.row0 * k.TL * kSt;
+    const float* wck = a.wck + k.row0 * k.TL;
+    const uint32_t ckrow = (uint32_t)c.rc * (uint32_t)k.TL;
 
     // state entering the chunk and adjoint entering it from the right
-    // (c.row is clamped in bounds: loads are unconditional, results masked)
+    // (c.rc is clamped in bounds: loads are unconditional, results masked)
     float h_in[4] = {0.0f, 0.0f, 0.0f, 0.0f}, lamn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (a.G > 1) {
-        const float4 hv = *reinterpret_cast<const float4*>(a.hbuf + cell);
-        const float4 mv = *reinterpret_cast<const float4*>(a.mubuf + cell);
+    if (G > 1) {
+        const float4 hv = *reinterpret_cast<const float4*>(a.hbuf + cell0 + cell);
+        const float4 mv = *reinterpret_cast<const float4*>(a.mubuf + cell0 + cell);
         h_in[0] = hv.x; h_in[1] = hv.y; h_in[2] = hv.z; h_in[3] = hv.w;
         lamn[0] = mv.x; lamn[1] = mv.y; lamn[2] = mv.z; lamn[3] = mv.w;
     } else if (a.h0) {
+        const float* h0 = a.h0 + k.row0 * a.N;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int n = 4 * c.q + i;
-            h_in[i] = a.h0[c.row * a.N + min(n, a.N - 1)] * (n < a.N ? 1.0f : 0.0f);
+            h_in[i] = h0[c.rc * a.N + min(n, a.N - 1)] * (n < a.N ? 1.0f : 0.0f);
         }
     }
 #pragma unroll
@@ -406,15 +452,20 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
     Raw<Tin, Tout> r;
     float4 zck;
     float wc;
-    auto fetch = [&](int tile) {   // c.row is clamped in bounds
-        fetch_raw<Tin, Tout, true, true, true, true>(a, k, p, k.t0 + (int64_t)tile * kT, r);
-        zck = *reinterpret_cast<const float4*>(a.ckz + ((c.row * TL + tile0 + tile) * kSt + 4 * c.q));
-        wc = a.wck[c.row * TL + tile0 + tile];
+    auto fetch = [&](int tile) {   // c.rc is clamped in bounds
+        fetch_raw<Tin, Tout, true, true, true, true>(a, k, p, in, k.t0 + tile * kT, r);
+        const uint32_t ct = ckrow + (uint32_t)(tile0 + tile);
+        zck = ldo(reinterpret_cast<const float4*>(ckz), ct * 4 + c.q);
+        wc = ldo(wck, ct);
     };
     fetch(k.tiles - 1);
 
+    float* du = a.du + k.row0 * a.L;
+    float* ddelta = a.ddelta + k.row0 * a.L;
+    float* dz = a.dz ? a.dz + k.row0 * a.L : nullptr;
+    float* part = a.part + (k.cb * a.batch + k.b) * a.L * (2 * kSt);
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
-        const int64_t tt0 = k.t0 + (int64_t)tile * kT;
+        const int tt0 = k.t0 + tile * kT;
         // per-channel tile values
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -514,27 +565,27 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j = p.pj + jj;
-            const int64_t t = tt0 + j;
+            const int t = tt0 + j;
             if (p.ok && t < k.t_end) {
                 const float sLB = sm.sLB[p.pr][j], sLAq = sm.sLAq[p.pr][j], sCh = sm.sCh[p.pr][j];
                 const float dt = sm.dt[p.pr][j], dy = sm.dy[p.pr][j], uu = sm.u[p.pr][j];
-                const int64_t o = p.row * a.L + t;
-                a.du[o] = __builtin_fmaf(dt, sLB, p.D * dy);
+                const uint32_t o = p.off + (uint32_t)t;
+                sto(du, o, __builtin_fmaf(dt, sLB, p.D * dy));
                 const float dx = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd[p.pr][j];
-                a.ddelta[o] = dx;
-                if (a.z) a.dz[o] = __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j];
+                sto(ddelta, o, dx);
+                if (dz) sto(dz, o, __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j]);
                 dD_acc = __builtin_fmaf(dy, uu, dD_acc);
                 dbias_acc += dx;
             }
         }
         {   // dB, dC partials of this channel block: thread = (token j, value v)
             const int j = tid >> 5, v = tid & 31;
-            const int64_t t = tt0 + j;
+            const int t = tt0 + j;
             if (t < k.t_end) {
                 float s = 0.0f;
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) s += sm.red[w][j][v];
-                a.part[((k.cb * a.batch + k.b) * a.L + t) * (2 * kSt) + v] = s;
+                sto(part, (uint32_t)t * (2 * kSt) + v, s);
             }
         }
         // No barrier needed before the next tile: a producer thread rewrites
@@ -544,12 +595,13 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
     }
 
     if (c.ok) {
-        *reinterpret_cast<float4*>(a.pA + cell) = make_float4(dA[0], dA[1], dA[2], dA[3]);
+        *reinterpret_cast<float4*>(a.pA + cell0 + cell) = make_float4(dA[0], dA[1], dA[2], dA[3]);
         if (k.g == 0 && a.dh0) {
+            float* dh0 = a.dh0 + k.row0 * a.N;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 4 * c.q + i;
-                if (n < a.N) a.dh0[c.row * a.N + n] = lamn[i];   // a_0 lam_0
+                if (n < a.N) dh0[c.rc * a.N + n] = lamn[i];   // a_0 lam_0
             }
         }
     }
@@ -559,8 +611,9 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
     dbias_acc += dpp<kQuadX1>(dbias_acc);
     dbias_acc += dpp<kQuadX2>(dbias_acc);
     if (p.ok && (tid & 3) == 0) {
-        a.pD[p.row * a.G + k.g] = dD_acc;
-        a.pbias[p.row * a.G + k.g] = dbias_acc;
+        const uint32_t pg = (uint32_t)p.rc * (uint32_t)G + (uint32_t)k.g;
+        (a.pD + k.row0 * G)[pg] = dD_acc;
+        (a.pbias + k.row0 * G)[pg] = dbias_acc;
     }
 }
 

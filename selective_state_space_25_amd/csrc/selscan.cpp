@@ -250,6 +250,8 @@ BwdPlan plan_m1_bwd(const selscan_shape_t* s) {
 selscan_status_t check_m1_bwd_shape(const selscan_shape_t* s) {
     selscan_status_t st = check_m1_shape(s);
     if (st != SELSCAN_OK) return st;
+    // per-thread byte offsets within a workgroup's rows are 32-bit
+    if (s->seqlen > (int64_t(1) << 22)) return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-1 backward supports seqlen <= 2^22");
     const int64_t nbc = (s->dim + selscan::m1_bwd_channels_per_block() - 1) / selscan::m1_bwd_channels_per_block();
     const int64_t tiles = (s->seqlen + selscan::m1_bwd_tile() - 1) / selscan::m1_bwd_tile();
     if (mul_checked({nbc, s->batch, 32, s->seqlen, 4}) < 0 || mul_checked({s->batch, s->dim, tiles, 17, 4}) < 0)
