@@ -262,6 +262,25 @@ def time_backward(name, steps, device, warmup=2, seed=0):
     return res
 
 
+def copy_calibration(device, gib):
+    """Kernels of known traffic for scaling the HBM byte counters: a plain copy
+    (torch.neg over fp32, reads and writes `gib` GiB) and a read of the first
+    64 bytes of every 128-byte line of a `gib` GiB bf16 buffer."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    del src, dst
+    xb = torch.ones(n * 4 // 128, 64, dtype=torch.bfloat16, device=device)
+    for _ in range(3):
+        half = xb[:, :32].contiguous()
+    del xb, half
+    torch.cuda.synchronize(device)
+    return n * 4
+
+
 def dominant_kernel(res):
     name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["total_ms"])
     return name, k
@@ -347,27 +366,16 @@ def main():
     ss.lib()  # fail loudly if the HIP library is missing
 
     if args.profile and args.backward:
-        print(json.dumps(time_backward(args.workload, args.steps, device, warmup=args.warmup, seed=args.seed)))
+        res = time_backward(args.workload, args.steps, device, warmup=args.warmup, seed=args.seed)
+        if args.copy_gib > 0:
+            res["copy_calibration_bytes_each_way"] = copy_calibration(device, args.copy_gib)
+        print(json.dumps(res))
         return
     w, head = time_workload(args.workload, args.steps, args.warmup, args.seed, device,
                             kernel_timing=not args.profile)
     if args.profile:
         if args.copy_gib > 0:
-            # calibration of the HBM byte counters: a plain copy (torch.neg
-            # over fp32, reads and writes copy_gib GiB) and a read of the first
-            # 64 bytes of every 128-byte line of a copy_gib GiB bf16 buffer
-            n = int(args.copy_gib * (1 << 30)) // 4
-            src = torch.ones(n, dtype=torch.float32, device=device)
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                torch.neg(src, out=dst)
-            del src, dst
-            xb = torch.ones(n * 4 // 128, 64, dtype=torch.bfloat16, device=device)
-            for _ in range(3):
-                half = xb[:, :32].contiguous()
-            del xb, half
-            torch.cuda.synchronize(device)
-            head["copy_calibration_bytes_each_way"] = n * 4
+            head["copy_calibration_bytes_each_way"] = copy_calibration(device, args.copy_gib)
         print(json.dumps(head))
         return
     extras = {}

@@ -162,6 +162,7 @@ size_t selscan_bwd_workspace_bytes(const selscan_shape_t* shape);
  *                                      ignored otherwise)
  *   ddelta_bias [D]        fp32        (written; NULL = skip)
  *   dh0         [B, D, N]  fp32        (written; NULL = skip)
+ * seqlen <= 4194304 (2^22; UNSUPPORTED above).
  * Gradients must not alias inputs or each other.  Sums over channels,
  * batches and time are taken in a fixed order: results are reproducible
  * bit for bit.  shape->workspace as for selscan_fwd, sized by
