@@ -29,7 +29,7 @@ struct M1Args {
     void* y;
     float* last;
     const float* h0;  // [batch, dim, N] initial state, or NULL for zero
-    float* ws_state;  // [rows, G, 16] chunk end states, then carries-in
+    float* ws_state;  // [rows, G, 16] chunk end states from a zero start
     float* ws_w;      // [rows, G] chunk sums of Delta / ln2
     float* bcq;       // [batch, L, 32] fp32 copy of B and C (B0..B15, C0..C15 per token)
     int64_t batch, dim, L;

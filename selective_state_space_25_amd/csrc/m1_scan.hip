@@ -26,9 +26,10 @@
 //
 // Long sequences are cut into G chunks so that enough waves exist to fill
 // the 256 CUs: a summary pass computes, per chunk, the end state from a zero
-// start and the chunk's sum of Delta; a carry pass folds the summaries in
-// order (h_in(g+1) = exp(A sum Delta_g) h_in(g) + b_g); the output pass then
-// rescans each chunk from its true carry-in.  G = 1 is a single pass.
+// start and the chunk's sum of Delta; the output pass folds the summaries of
+// the chunks before its own in order (h_in(g+1) = exp(A sum Delta_g) h_in(g)
+// + b_g, at most G - 1 steps per wave) and rescans its chunk from that true
+// carry-in.  G = 1 is a single pass.
 //
 // Two decay paths, chosen per wave at run time:
 //  - general A: exp(Delta A[n]) = 2^(w A[n]) per update, w = Delta / ln2;
@@ -325,9 +326,25 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     const float Dv = (MODE == 0 && a.D) ? a.D[d] : 0.0f;
     L.Dp = STRUCT ? Dv * kInvLn2 : Dv;
     if (MODE == 0 && g > 0) {
-        const float* cin = a.ws_state + (row * a.G + g) * kNS;
+        // carry-in: fold the zero-start end states of the chunks before this
+        // one (written by the summary pass) from h0, h <- exp(A w_j) h + e_j
 #pragma unroll
-        for (int n = 0; n < kNS; ++n) L.k[n] = cin[n];
+        for (int n = 0; n < kNS; ++n) L.k[n] = (a.h0 && n < a.N) ? a.h0[row * a.N + n] : 0.0f;
+        const float* st = a.ws_state + row * a.G * kNS;
+        const float* W = a.ws_w + row * a.G;
+#pragma nounroll
+        for (int j = 0; j < g; ++j) {
+            const float wj = W[j];
+            const float4* e = reinterpret_cast<const float4*>(st + (int64_t)j * kNS);
+#pragma unroll
+            for (int q = 0; q < kNS / 4; ++q) {
+                const float4 v = e[q];
+                const float ev[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    L.k[4 * q + i] = __builtin_fmaf(fast_exp2(L.Ar[4 * q + i] * wj), L.k[4 * q + i], ev[i]);
+            }
+        }
     } else if (MODE == 0 && a.h0) {
         // chunk 0 starts from the caller's state (k = h while s_prev = 1/ln2)
 #pragma unroll
@@ -555,41 +572,6 @@ __global__ __launch_bounds__(256) void m1_bc_kernel(M1Args a) {
     }
 }
 
-// Carry pass: one thread per (row, n).  Turns the per-chunk end states b_g
-// (slot g) into carries-in h_in(g) (slot g), in chunk order:
-//   h_in(0) = h0 (or 0),   h_in(g+1) = 2^(A[d,n] W_g) h_in(g) + b_g.
-// The summaries are read sixteen chunks at a time before the dependent chain
-// runs over them, so their loads overlap.
-__global__ __launch_bounds__(256) void m1_carry_kernel(M1Args a) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t rows = a.batch * a.dim;
-    if (idx >= rows * kNS) return;
-    const int64_t row = idx / kNS;
-    const int n = (int)(idx - row * kNS);
-    const int64_t d = row % a.dim;
-    const float An = (n < a.N) ? a.A[d * a.N + n] : 0.0f;
-    float h = (a.h0 && n < a.N) ? a.h0[row * a.N + n] : 0.0f;
-    float* st = a.ws_state + row * a.G * kNS + n;
-    const float* W = a.ws_w + row * a.G;
-    for (int g0 = 0; g0 < a.G; g0 += 16) {
-        float bg[16], wg[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int g = g0 + j;
-            bg[j] = (g < a.G - 1) ? st[(int64_t)g * kNS] : 0.0f;
-            wg[j] = (g < a.G - 1) ? W[g] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int g = g0 + j;
-            if (g < a.G) {
-                st[(int64_t)g * kNS] = h;
-                h = __builtin_fmaf(fast_exp2(An * wg[j]), h, bg[j]);
-            }
-        }
-    }
-}
-
 template <typename Tin, typename Tout, bool SP>
 hipError_t launch_sp(const M1Args& a, hipStream_t stream) {
     const int64_t bc_blocks = a.batch * ((a.L + 31) / 32);
@@ -609,9 +591,6 @@ hipError_t launch_sp(const M1Args& a, hipStream_t stream) {
                 hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 1, SP>), dim3(gx, (unsigned)(a.G - 1)), dim3(kRows), 0,
                                    stream, a);
         }
-        const int64_t threads = a.batch * a.dim * kNS;
-        KTime kt("m1_chunk_carry", stream);
-        hipLaunchKernelGGL(m1_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
     }
     KTime kt("m1_scan_output", stream);
     if (a.xcd_chunks)

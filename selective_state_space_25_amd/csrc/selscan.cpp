@@ -117,9 +117,10 @@ M1Plan plan_m1(const selscan_shape_t* s) {
             "SELSCAN_M1_WAVES",
             (int64_t)device_cus() * selscan::m1_resident_waves_per_cu(s->in_dtype == SELSCAN_BF16));
         G = std::max<int64_t>(1, target / waves_per_chunk);
-        G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 256));
-        // whole groups of 8 chunks let each XCD own the chunks it scans
-        if (G >= 8) G = G / 8 * 8;
+        G = std::min<int64_t>(G, std::max<int64_t>(1, s->seqlen / 128));
+        // whole groups of 8 chunks let each XCD own the chunks it scans,
+        // unless rounding down to them gives up more than a tenth of the waves
+        if (G >= 8 && (G / 8 * 8) * 10 >= G * 9) G = G / 8 * 8;
     }
     const int64_t align = selscan::m1_chunk_align();
     G = std::max<int64_t>(1, std::min<int64_t>(G, (s->seqlen + align - 1) / align));
