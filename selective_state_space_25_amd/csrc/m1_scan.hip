@@ -142,14 +142,21 @@ __device__ __forceinline__ bool s_in_range(float s) { return fabsf(s) >= kSigLo 
 template <int MODE>
 __device__ __forceinline__ float tok_fast(Lane& L, const float* bc, float w, float s, float uu) {
     const float r = fast_exp2(w * L.A0);
-    float q = L.s_prev * fast_rcp(s) * r;
+    // q r^n as four independent product chains (q, q r, q r^2, q r^3, then
+    // steps of r^4) rather than one chain of sixteen dependent multiplies
+    const float r2 = r * r, r4 = r2 * r2;
+    float qq[kNS];
+    qq[0] = L.s_prev * fast_rcp(s) * r;
+    qq[1] = qq[0] * r;
+    qq[2] = qq[0] * r2;
+    qq[3] = qq[1] * r2;
+#pragma unroll
+    for (int n = 4; n < kNS; ++n) qq[n] = qq[n - 4] * r4;
     float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
     for (int n = 0; n < kNS; n += 2) {
-        L.k[n] = __builtin_fmaf(q, L.k[n], bc[n]);
-        q *= r;
-        L.k[n + 1] = __builtin_fmaf(q, L.k[n + 1], bc[n + 1]);
-        q *= r;
+        L.k[n] = __builtin_fmaf(qq[n], L.k[n], bc[n]);
+        L.k[n + 1] = __builtin_fmaf(qq[n + 1], L.k[n + 1], bc[n + 1]);
         if (MODE == 0) {
             acc0 = __builtin_fmaf(bc[kNS + n], L.k[n], acc0);
             acc1 = __builtin_fmaf(bc[kNS + n + 1], L.k[n + 1], acc1);
@@ -318,6 +325,17 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     Tout* yrow = reinterpret_cast<Tout*>(a.y) + row * a.L;
     const Tin* rowp[3] = {urow, drow, zrow};
 
+    // this batch's B/C, 32 floats per token; the address is wave-uniform
+    const float* bcb = uniform_ptr(a.bcq + (b * a.L) * (2 * kNS));
+    const int64_t t_full_end = a.vec_ok ? t_begin + ((t_end - t_begin) / kTile) * kTile : t_begin;
+    const uint32_t bc_base0 = lds_base + (uint32_t)(NT * In<Tin>::kPieces * kRows * 16);
+    // request the first tile before the per-row set-up and the carry-in fold,
+    // so that its latency overlaps theirs
+    if (t_begin < t_full_end) {
+        issue_rows<Tin, NT>(rowp, t_begin, lds_base);
+        issue_bc<MODE>(bcb, t_begin, bc_base0);
+    }
+
     Lane L;
     L.bias_l = (a.bias ? a.bias[d] : 0.0f) * kLog2e;
 #pragma unroll
@@ -359,17 +377,10 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     const float gscale = STRUCT ? kInvLn2 : 1.0f;
     const float nogate = STRUCT ? kLn2 : 1.0f;
 
-    // this batch's B/C, 32 floats per token; the address is wave-uniform
-    const float* bcb = uniform_ptr(a.bcq + (b * a.L) * (2 * kNS));
-
-    const int64_t t_full_end = a.vec_ok ? t_begin + ((t_end - t_begin) / kTile) * kTile : t_begin;
     if (t_begin < t_full_end) {
         constexpr int RS = kRec<MODE> / 4;   // floats per B/C record in LDS
         constexpr int kBCBytes = kTile * kRec<MODE>;
-        const uint32_t bc_base0 = lds_base + (uint32_t)(NT * In<Tin>::kPieces * kRows * 16);
         const float* bcl0 = reinterpret_cast<const float*>(lds + NT * In<Tin>::kPieces * kRows);
-        issue_rows<Tin, NT>(rowp, t_begin, lds_base);
-        issue_bc<MODE>(bcb, t_begin, bc_base0);
         wait_vm();   // the first tile is in LDS
         int par = 0;   // B/C buffer of the current tile
 #pragma nounroll
