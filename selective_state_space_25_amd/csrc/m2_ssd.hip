@@ -85,6 +85,8 @@ struct SsdSmem {
     uint16_t Ml[kQ][kPadQ];
     uint16_t STh[kPd][kPadN];     // state entering the chunk, split, [p][n]
     uint16_t STl[kPd][kPadN];
+    uint16_t XWh[kPd][kPadQ];     // x weighted by 2^(cum_last - cum_s) Delta_s, split, [p][s]
+    uint16_t XWl[kPd][kPadQ];
     float dl[kQ];                 // Delta
     float cum[kQ];                // inclusive prefix of w A within the chunk
     float wts[kQ];                // 2^(cum_last - cum_s) Delta_s
@@ -223,6 +225,24 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
         lds_barrier();
 
         // ---- M = (C B^T) o decay: blocks (0,0), (1,0), (1,1) ------------
+        // (wave 3 meanwhile splits the weighted x for the state update)
+        if (wave == 3) {
+            const int p = lane;
+#pragma unroll
+            for (int s8 = 0; s8 < kQ / 8; ++s8) {
+                const bf16x8 xv = ld8(&sm.xT[p][8 * s8]);
+                bf16x8 xh, xl;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float v = (float)xv[j] * sm.wts[8 * s8 + j];
+                    const __bf16 vh = (__bf16)v;
+                    xh[j] = vh;
+                    xl[j] = (__bf16)(v - (float)vh);
+                }
+                *reinterpret_cast<bf16x8*>(&sm.XWh[p][8 * s8]) = xh;
+                *reinterpret_cast<bf16x8*>(&sm.XWl[p][8 * s8]) = xl;
+            }
+        }
         if (wave < 3) {
             const int ti = wave == 0 ? 0 : 1;
             const int si = wave == 2 ? 1 : 0;
@@ -294,17 +314,8 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
                 for (int kk = 0; kk < 4; ++kk) {
                     const bf16x8 bv = ld8(&sm.BT[32 * s_ni[k] + col][16 * kk + khalf]);
                     const int p = 32 * s_pj[k] + col;
-                    const bf16x8 xv = ld8(&sm.xT[p][16 * kk + khalf]);
-                    bf16x8 xh, xl;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float v = (float)xv[j] * sm.wts[16 * kk + khalf + j];
-                        const __bf16 vh = (__bf16)v;
-                        xh[j] = vh;
-                        xl[j] = (__bf16)(v - (float)vh);
-                    }
-                    S[k] = mfma(bv, xh, S[k]);
-                    S[k] = mfma(bv, xl, S[k]);
+                    S[k] = mfma(bv, ld8(&sm.XWh[p][16 * kk + khalf]), S[k]);
+                    S[k] = mfma(bv, ld8(&sm.XWl[p][16 * kk + khalf]), S[k]);
                 }
             }
         }
