@@ -14,7 +14,7 @@
 // y_t = C_t h_t, regrouped (the contractions over n and s are exact sums).
 // y then gets D x and the silu(z) gate as in the recurrent kernel.
 //
-// One workgroup (4 waves) owns one (batch, head) and walks its chunks in
+// One workgroup (8 waves) owns one (batch, head) and walks its chunks in
 // order, the state in MFMA accumulators.  The products run as
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  x, B and C are bf16 on
 // input and enter exactly; M, S and the weighted X are fp32 and enter as a
@@ -60,11 +60,15 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One thread's share of a chunk's inputs, fetched a chunk ahead.
+constexpr int kWaves = 8;                  // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+
+// One thread's share of a chunk's inputs, fetched a chunk ahead: token
+// tid / 8, eight channels of x and z and N / 8 states of B and C.
 template <int N>
 struct ChunkRegs {
-    static constexpr int PER = N / 4;
-    uint4 x[2], z[2];
+    static constexpr int PER = N / 8;
+    uint4 x, z;
     uint4 b[PER / 8], c[PER / 8];
     uint16_t dt;
 };
@@ -87,15 +91,26 @@ struct SsdSmem {
     uint16_t STl[kPd][kPadN];
     uint16_t XWh[kPd][kPadQ];     // x weighted by 2^(cum_last - cum_s) Delta_s, split, [p][s]
     uint16_t XWl[kPd][kPadQ];
+    float yoff[4][16][64];        // C S of each 32 x 32 output block, [block][register][lane]
     float dl[kQ];                 // Delta
     float cum[kQ];                // inclusive prefix of w A within the chunk
     float wts[kQ];                // 2^(cum_last - cum_s) Delta_s
 };
 
+// Eight waves per (batch, head).  Per chunk:
+//   stage   all      inputs into LDS (x also transposed, B also as [n][s]),
+//                    the entering state as split bf16; wave 0: Delta, the
+//                    decay prefix and the state-update weights
+//   M       0..2     the three causal 32 x 32 blocks of (C B^T) o decay
+//           4..7     the weighted x, split (16 tokens each)
+//   Y       0..3     M X of output block (t, p) = (w / 2, w % 2)
+//           4..7     C S of the same block, to LDS
+//   out     0..3     Y = M X + 2^cum C S + D x, gate, store
+//   S       w < 2N/32  state block (n, p) = (w / 2, w % 2):
+//                    S = 2^cum_last S + B^T (w X)
 template <typename Tout, int N, bool SP>
-__global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
+__global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
     constexpr int NB = N / 32;               // row blocks of the state
-    constexpr int SPW = NB * 2 / 4;          // state blocks per wave (2 or 1)
     __shared__ __attribute__((aligned(16))) SsdSmem<N> sm;
 
     const int tid = threadIdx.x;
@@ -119,40 +134,27 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
     const uint16_t* Z = reinterpret_cast<const uint16_t*>(a.z);
     Tout* Y = reinterpret_cast<Tout*>(a.y);
 
-    // state blocks of this wave: (ni, pj)
-    int s_ni[SPW], s_pj[SPW];
+    // this wave's state block (n, p), if any
+    const bool owns = wave < 2 * NB;
+    const int s_ni = wave >> 1, s_pj = wave & 1;
+    f32x16 S;
 #pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-        const int blk = wave * SPW + k;      // 0 .. 2 NB - 1
-        s_ni[k] = blk >> 1;
-        s_pj[k] = blk & 1;
-    }
-    f32x16 S[SPW];
-#pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int n = 32 * s_ni[k] + acc_row(i, lane);
-            const int p = 32 * s_pj[k] + col;
-            S[k][i] = a.h0 ? a.h0[(bh * kPd + p) * N + n] : 0.0f;
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int n = 32 * s_ni + acc_row(i, lane);
+        const int p = 32 * s_pj + col;
+        S[i] = (owns && a.h0) ? a.h0[(bh * kPd + p) * N + n] : 0.0f;
     }
 
     const int64_t nch = (L + kQ - 1) / kQ;
-    // this thread's slices of a chunk: token rt, channels rp0.. (x, z) and
-    // states rn0.. (B, C); lane t of wave 0 holds dt of token t
-    constexpr int PER = N / 4;
-    const int rt = tid >> 2, rp0 = (tid & 3) * 16, rn0 = (tid & 3) * PER;
+    constexpr int PER = N / 8;
+    const int rt = tid >> 3, rp0 = (tid & 7) * 8, rn0 = (tid & 7) * PER;
     auto fetch = [&](int64_t t0, ChunkRegs<N>& r) {
         const bool in = t0 + rt < L;
         const uint4 zero = make_uint4(0, 0, 0, 0);
         const int64_t xo = ((b * L + t0 + rt) * H + h) * kPd + rp0;
         const int64_t bo = ((b * L + t0 + rt) * G + grp) * N + rn0;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            r.x[q] = in ? reinterpret_cast<const uint4*>(X + xo)[q] : zero;
-            r.z[q] = (in && Z) ? reinterpret_cast<const uint4*>(Z + xo)[q] : zero;
-        }
+        r.x = in ? *reinterpret_cast<const uint4*>(X + xo) : zero;
+        r.z = (in && Z) ? *reinterpret_cast<const uint4*>(Z + xo) : zero;
 #pragma unroll
         for (int q = 0; q < PER / 8; ++q) {
             r.b[q] = in ? reinterpret_cast<const uint4*>(Bg + bo)[q] : zero;
@@ -164,30 +166,26 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
     fetch(0, cr);
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t t0 = c * kQ;
-        // ---- state entering the chunk, split, [p][n] -------------------
-#pragma unroll
-        for (int k = 0; k < SPW; ++k) {
+        // ---- stage: the entering state, split, [p][n]; this chunk's inputs
+        if (owns) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int n = 32 * s_ni[k] + acc_row(i, lane);
-                const int p = 32 * s_pj[k] + col;
+                const int n = 32 * s_ni + acc_row(i, lane);
+                const int p = 32 * s_pj + col;
                 uint16_t hi, lo;
-                split(S[k][i], hi, lo);
+                split(S[i], hi, lo);
                 sm.STh[p][n] = hi;
                 sm.STl[p][n] = lo;
             }
         }
-        // ---- this chunk's inputs into LDS, the next chunk's requested ----
         {
-            const uint32_t w[8] = {cr.x[0].x, cr.x[0].y, cr.x[0].z, cr.x[0].w,
-                                   cr.x[1].x, cr.x[1].y, cr.x[1].z, cr.x[1].w};
+            const uint32_t w[4] = {cr.x.x, cr.x.y, cr.x.z, cr.x.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 sm.xT[rp0 + 2 * j][rt] = (uint16_t)(w[j] & 0xffffu);
                 sm.xT[rp0 + 2 * j + 1][rt] = (uint16_t)(w[j] >> 16);
             }
-            *reinterpret_cast<uint4*>(&sm.zs[rt][rp0]) = cr.z[0];
-            *reinterpret_cast<uint4*>(&sm.zs[rt][rp0 + 8]) = cr.z[1];
+            *reinterpret_cast<uint4*>(&sm.zs[rt][rp0]) = cr.z;
 #pragma unroll
             for (int q = 0; q < PER / 8; ++q) {
                 *reinterpret_cast<uint4*>(&sm.Bs[rt][rn0 + 8 * q]) = cr.b[q];
@@ -224,25 +222,7 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
         if (c + 1 < nch) fetch(t0 + kQ, cr);
         lds_barrier();
 
-        // ---- M = (C B^T) o decay: blocks (0,0), (1,0), (1,1) ------------
-        // (wave 3 meanwhile splits the weighted x for the state update)
-        if (wave == 3) {
-            const int p = lane;
-#pragma unroll
-            for (int s8 = 0; s8 < kQ / 8; ++s8) {
-                const bf16x8 xv = ld8(&sm.xT[p][8 * s8]);
-                bf16x8 xh, xl;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float v = (float)xv[j] * sm.wts[8 * s8 + j];
-                    const __bf16 vh = (__bf16)v;
-                    xh[j] = vh;
-                    xl[j] = (__bf16)(v - (float)vh);
-                }
-                *reinterpret_cast<bf16x8*>(&sm.XWh[p][8 * s8]) = xh;
-                *reinterpret_cast<bf16x8*>(&sm.XWl[p][8 * s8]) = xl;
-            }
-        }
+        // ---- M = (C B^T) o decay: blocks (0,0), (1,0), (1,1); weighted x --
         if (wave < 3) {
             const int ti = wave == 0 ? 0 : 1;
             const int si = wave == 2 ? 1 : 0;
@@ -265,13 +245,31 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
                 sm.Mh[t][s] = hi;
                 sm.Ml[t][s] = lo;
             }
+        } else if (wave >= 4) {
+            const int p = lane;
+#pragma unroll
+            for (int s8 = 0; s8 < 2; ++s8) {
+                const int s0 = 16 * (wave - 4) + 8 * s8;
+                const bf16x8 xv = ld8(&sm.xT[p][s0]);
+                bf16x8 xh, xl;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float v = (float)xv[j] * sm.wts[s0 + j];
+                    const __bf16 vh = (__bf16)v;
+                    xh[j] = vh;
+                    xl[j] = (__bf16)(v - (float)vh);
+                }
+                *reinterpret_cast<bf16x8*>(&sm.XWh[p][s0]) = xh;
+                *reinterpret_cast<bf16x8*>(&sm.XWl[p][s0]) = xl;
+            }
         }
         lds_barrier();
 
-        // ---- Y = M X + diag(2^cum) C S, then D x and the gate ------------
-        {
-            const int ti = wave >> 1, pj = wave & 1;
-            f32x16 yi = {}, yc = {};
+        // ---- Y: M X on waves 0..3, C S (to LDS) on waves 4..7 ------------
+        const int yb = wave & 3;
+        const int ti = yb >> 1, pj = yb & 1;
+        f32x16 yi = {};
+        if (wave < 4) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 if (kk >= 2 * (ti + 1)) break;   // causal: s < 32 (ti + 1)
@@ -279,19 +277,28 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
                 yi = mfma(ld8(&sm.Mh[32 * ti + col][16 * kk + khalf]), xv, yi);
                 yi = mfma(ld8(&sm.Ml[32 * ti + col][16 * kk + khalf]), xv, yi);
             }
+        } else {
+            f32x16 yc = {};
 #pragma unroll
             for (int kk = 0; kk < N / 16; ++kk) {
                 const bf16x8 cv = ld8(&sm.Cs[32 * ti + col][16 * kk + khalf]);
                 yc = mfma(cv, ld8(&sm.STh[32 * pj + col][16 * kk + khalf]), yc);
                 yc = mfma(cv, ld8(&sm.STl[32 * pj + col][16 * kk + khalf]), yc);
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sm.yoff[yb][i][lane] = yc[i];
+        }
+        lds_barrier();
+
+        // ---- out: Y = M X + 2^cum C S + D x, the gate, the store -----------
+        if (wave < 4) {
             const int p = 32 * pj + col;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int t = 32 * ti + acc_row(i, lane);
                 if (t0 + t >= L) continue;
                 const float xv = bf16_to_f32(sm.xT[p][t]);
-                float yv = __builtin_fmaf(fast_exp2(sm.cum[t]), yc[i], yi[i]);
+                float yv = __builtin_fmaf(fast_exp2(sm.cum[t]), sm.yoff[yb][i][lane], yi[i]);
                 yv = __builtin_fmaf(Dh, xv, yv);
                 const int64_t idx = ((b * L + t0 + t) * H + h) * kPd + p;
                 if (Z) yv *= silu_scaled(bf16_to_f32(sm.zs[t][p]), 1.0f);
@@ -301,36 +308,29 @@ __global__ __launch_bounds__(256) void m2_ssd_kernel(M2Args a) {
                     Y[idx] = f32_to_bf16(yv);
             }
         }
-        lds_barrier();
 
         // ---- S = 2^cum_last S + B^T diag(wts) X ---------------------------
-        {
+        if (owns) {
             const float dec = fast_exp2(sm.cum[kQ - 1]);
 #pragma unroll
-            for (int k = 0; k < SPW; ++k) {
+            for (int i = 0; i < 16; ++i) S[i] *= dec;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) S[k][i] *= dec;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x8 bv = ld8(&sm.BT[32 * s_ni[k] + col][16 * kk + khalf]);
-                    const int p = 32 * s_pj[k] + col;
-                    S[k] = mfma(bv, ld8(&sm.XWh[p][16 * kk + khalf]), S[k]);
-                    S[k] = mfma(bv, ld8(&sm.XWl[p][16 * kk + khalf]), S[k]);
-                }
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 bv = ld8(&sm.BT[32 * s_ni + col][16 * kk + khalf]);
+                const int p = 32 * s_pj + col;
+                S = mfma(bv, ld8(&sm.XWh[p][16 * kk + khalf]), S);
+                S = mfma(bv, ld8(&sm.XWl[p][16 * kk + khalf]), S);
             }
         }
         lds_barrier();
     }
 
-    if (a.last) {
+    if (a.last && owns) {
 #pragma unroll
-        for (int k = 0; k < SPW; ++k) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int n = 32 * s_ni[k] + acc_row(i, lane);
-                const int p = 32 * s_pj[k] + col;
-                a.last[(bh * kPd + p) * N + n] = S[k][i];
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int n = 32 * s_ni + acc_row(i, lane);
+            const int p = 32 * s_pj + col;
+            a.last[(bh * kPd + p) * N + n] = S[i];
         }
     }
 }
@@ -340,9 +340,9 @@ hipError_t launch_n(const M2Args& a, hipStream_t stream) {
     const unsigned blocks = (unsigned)(a.batch * a.H);
     KTime kt("m2_ssd", stream);
     if (a.softplus)
-        hipLaunchKernelGGL((m2_ssd_kernel<Tout, N, true>), dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((m2_ssd_kernel<Tout, N, true>), dim3(blocks), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((m2_ssd_kernel<Tout, N, false>), dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((m2_ssd_kernel<Tout, N, false>), dim3(blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
