@@ -451,8 +451,11 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                 }
                 // the next tile has landed (its request left one block ago);
                 // waiting before the y stores keeps their write latency off
-                // this wait
-                if (more) wait_vm();
+                // this wait.  The wait is unconditional so that no path into
+                // the next iteration leaves a tile copy in flight: the
+                // compiler would otherwise drain the y stores as well before
+                // the tile's first LDS read
+                wait_vm();
                 if (MODE == 0 && row_ok) Out<Tout>::burst(yrow + t0, yb);
             } else {
                 // general A: token by token out of the LDS tile
@@ -470,7 +473,7 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                     if (MODE == 0 && row_ok)
                         Out<Tout>::st(yrow, t0 + j, pre * (has_z ? silu_scaled(zz, 1.0f) : 1.0f));
                 }
-                if (more) wait_vm();
+                wait_vm();
             }
         }
     }
