@@ -15,12 +15,21 @@
 // y then gets D x and the silu(z) gate as in the recurrent kernel.
 //
 // One workgroup (8 waves) owns one (batch, head) and walks its chunks in
-// order, the state in MFMA accumulators.  The products run as
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  x, B and C are bf16 on
-// input and enter exactly; M, S and the weighted X are fp32 and enter as a
-// bf16 pair hi + lo (hi = bf16(v), lo = bf16(v - hi)), two MFMAs each, which
-// keeps their relative error near 2^-16.  bf16 inputs, P = 64 and N in
-// {64, 128} only; other shapes use the recurrent kernel.
+// order.  The products run as v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation.  x, B and C are bf16 on input and enter exactly; M, S and the
+// weighted x are fp32 and enter as a bf16 pair hi + lo (hi = bf16(v),
+// lo = bf16(v - hi)), two MFMAs each, which keeps their relative error near
+// 2^-16.  bf16 inputs, P = 64 and N in {64, 128} only; other shapes use the
+// recurrent kernel.
+//
+// Waves 0..3 own the state: wave w holds S[:, 16w .. 16w + 16) in N / 16
+// accumulator tiles and computes C S, M X and the state update for those
+// columns, the state entering C S straight from its registers.  Waves 4..7
+// build M, the weighted x and the decay prefix, and write y.  Every chunk
+// input stays in LDS in its memory layout ([token][channel] rows): operands
+// that need the other orientation are read with the transposing LDS load
+// (ds_read_b64_tr_b16), which hands each lane four consecutive rows of one
+// column.
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -29,26 +38,22 @@ namespace selscan {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
 
-constexpr int kQ = 64;    // tokens per chunk
-constexpr int kPd = 64;   // headdim handled by this kernel
-constexpr int kPadQ = kQ + 8;
+constexpr int kQ = 64;                     // tokens per chunk
+constexpr int kPd = 64;                    // headdim handled by this kernel
+constexpr int kWaves = 8;                  // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kOwners = 4;                 // waves holding the state, 16 columns each
+constexpr int kRowX = kPd + 8;             // padded row (elements) of x, z, weighted x
+constexpr int kRowM = kQ + 8;              // padded row of M
+constexpr int kRowY = kPd + 4;             // padded row (floats) of Y
 
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-
-__device__ __forceinline__ uint16_t bf16_bits(float v) { return f32_to_bf16(v); }
-
-// v = hi + lo with both halves bf16
-__device__ __forceinline__ void split(float v, uint16_t& hi, uint16_t& lo) {
-    hi = f32_to_bf16(v);
-    lo = f32_to_bf16(v - bf16_to_f32(hi));
-}
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Workgroup barrier for LDS traffic only: global loads and stores in flight
@@ -60,64 +65,103 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-constexpr int kWaves = 8;                  // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Eight consecutive k of an MFMA operand from two 4-element pieces.
+__device__ __forceinline__ bf16x8 cat(s16x4 a, s16x4 b) {
+    const s16x8 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ s16x4 ld4(const uint16_t* p) { return *reinterpret_cast<const s16x4*>(p); }
+
+// Transposing LDS load.  Within each group of 16 lanes, lane a passes the
+// address of 4 consecutive elements; lane i receives element i % 4 of the
+// pieces of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.  With lane a
+// pointing at row r0 + a / 4, columns c0 + 4 (a % 4) .. + 3 of a row-major
+// matrix, lane i gets rows r0 .. r0 + 3 of column c0 + i.
+__device__ __forceinline__ s16x4 ld_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p));
+}
+
+// MFMA operand with k running down a row-major matrix m (row stride `rs`):
+// lane l = 16 g + i gets rows r0 + 8 g .. r0 + 8 g + 7 of column c0 + i.
+__device__ __forceinline__ bf16x8 ld_col8(const uint16_t* m, int rs, int r0, int c0, int lane) {
+    const int g = lane >> 4, a = lane & 15;
+    const uint16_t* p = m + (r0 + 8 * g + (a >> 2)) * rs + c0 + 4 * (a & 3);
+    return cat(ld_tr(p), ld_tr(p + 4 * rs));
+}
+
+// bf16 hi/lo halves of four fp32 values, packed for a 64-bit store.
+__device__ __forceinline__ void split4(const float v[4], uint2& hi, uint2& lo) {
+    float h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h[q] = bf16_to_f32(f32_to_bf16(v[q]));
+    hi = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+    lo = make_uint2(pack_bf16x2(v[0] - h[0], v[1] - h[1]), pack_bf16x2(v[2] - h[2], v[3] - h[3]));
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // One thread's share of a chunk's inputs, fetched a chunk ahead: token
-// tid / 8, eight channels of x and z and N / 8 states of B and C.
+// tid / 8, eight channels of x and z and N / 8 states of B and C.  The words
+// are the loads' raw bits (past L: the last token's); they are zeroed when
+// staged, so no use of them sits right behind the loads.
 template <int N>
 struct ChunkRegs {
-    static constexpr int PER = N / 8;
-    uint4 x, z;
-    uint4 b[PER / 8], c[PER / 8];
+    static constexpr int kPer = N / 8;
+    u32x4 x, z;
+    u32x4 b[kPer / 8], c[kPer / 8];
     uint16_t dt;
 };
 
-// Row index of accumulator register i (= 4 r + q) of this lane inside a
-// 32 x 32 block; the column is lane % 32.
-__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
-
 template <int N>
 struct SsdSmem {
-    static constexpr int kPadN = N + 8;
-    uint16_t xT[kPd][kPadQ];      // x of the chunk, [p][s]
-    uint16_t zs[kQ][kPd + 8];     // z of the chunk, [t][p]
-    uint16_t Cs[kQ][kPadN];       // C, [t][n]
-    uint16_t Bs[kQ][kPadN];       // B, [s][n]
-    uint16_t BT[N][kPadQ];        // B, [n][s]
-    uint16_t Mh[kQ][kPadQ];       // M split, [t][s]
-    uint16_t Ml[kQ][kPadQ];
-    uint16_t STh[kPd][kPadN];     // state entering the chunk, split, [p][n]
-    uint16_t STl[kPd][kPadN];
-    uint16_t XWh[kPd][kPadQ];     // x weighted by 2^(cum_last - cum_s) Delta_s, split, [p][s]
-    uint16_t XWl[kPd][kPadQ];
-    float yoff[4][16][64];        // C S of each 32 x 32 output block, [block][register][lane]
-    float dl[kQ];                 // Delta
-    float cum[kQ];                // inclusive prefix of w A within the chunk
-    float wts[kQ];                // 2^(cum_last - cum_s) Delta_s
+    static constexpr int kRowN = N + 8;
+    uint16_t xs[kQ][kRowX];       // x of the chunk, [s][p]
+    uint16_t zs[kQ][kRowX];       // z, [t][p]
+    uint16_t Bs[kQ][kRowN];       // B, [s][n]
+    uint16_t Cs[kQ][kRowN];       // C, [t][n]
+    uint16_t Mh[kQ][kRowM];       // M split, [t][s]
+    uint16_t Ml[kQ][kRowM];
+    uint16_t Wh[kQ][kRowX];       // x weighted by 2^(cum_last - cum_s) Delta_s, split, [s][p]
+    uint16_t Wl[kQ][kRowX];
+    float Y[kQ][kRowY];           // M X + 2^cum C S, [t][p]
+    float dl[2][kQ];              // Delta, by chunk parity
+    float cum[2][kQ];             // inclusive prefix of w A within the chunk
+    float wts[2][kQ];             // 2^(cum_last - cum_s) Delta_s
 };
 
-// Eight waves per (batch, head).  Per chunk:
-//   stage   all      inputs into LDS (x also transposed, B also as [n][s]),
-//                    the entering state as split bf16; wave 0: Delta, the
-//                    decay prefix and the state-update weights
-//   M       0..2     the three causal 32 x 32 blocks of (C B^T) o decay
-//           4..7     the weighted x, split (16 tokens each)
-//   Y       0..3     M X of output block (t, p) = (w / 2, w % 2)
-//           4..7     C S of the same block, to LDS
-//   out     0..3     Y = M X + 2^cum C S + D x, gate, store
-//   S       w < 2N/32  state block (n, p) = (w / 2, w % 2):
-//                    S = 2^cum_last S + B^T (w X)
+// The causal 16 x 16 tiles (t-tile, s-tile) of M; helper k of the four
+// builds tiles k, k + 4, k + 8.  Tiles (0, 1) and (2, 3) lie above the
+// diagonal but inside the 32-wide k-steps of M X: they stay zero.
+__device__ __forceinline__ void m_tile(int k, int& tb, int& sb) {
+    tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
+    sb = k - tb * (tb + 1) / 2;
+}
+
+// Per chunk (barriers between phases):
+//   A  all      inputs into LDS in their memory layout; next chunk requested
+//   B  0..3     Y = 2^cum C S for the wave's 16 columns (S from registers)
+//      4..7     M (causal tiles, split) and the weighted x (split)
+//   C  0..3     Y += M X, to LDS
+//      4        Delta, decay prefix and weights of the next chunk
+//   D  4..7     y = (Y + D x) silu(z), stored
+//      0..3     S = 2^cum_last S + B^T (w X); its split for the next C S
 template <typename Tout, int N, bool SP>
 __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
-    constexpr int NB = N / 32;               // row blocks of the state
+    constexpr int NT = N / 16;               // 16-row state tiles per owner
+    constexpr int KS = N / 32;               // k-steps over n
+    constexpr int kRowN = SsdSmem<N>::kRowN;
     __shared__ __attribute__((aligned(16))) SsdSmem<N> sm;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int col = lane & 31;
-    const int khalf = (lane >> 5) * 8;       // k offset of this lane inside a 16-wide step
+    const int li = lane & 15;                // MFMA column / row within a 16-tile
+    const int lg = lane >> 4;                // lane group: k offset 8 lg, output rows 4 lg + q
+    const bool owner = wave < kOwners;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / a.H;
     const int64_t h = bh - b * a.H;
@@ -132,206 +176,256 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
     const uint16_t* Bg = reinterpret_cast<const uint16_t*>(a.B);
     const uint16_t* Cg = reinterpret_cast<const uint16_t*>(a.C);
     const uint16_t* Z = reinterpret_cast<const uint16_t*>(a.z);
-    Tout* Y = reinterpret_cast<Tout*>(a.y);
+    Tout* Yg = reinterpret_cast<Tout*>(a.y);
 
-    // this wave's state block (n, p), if any
-    const bool owns = wave < 2 * NB;
-    const int s_ni = wave >> 1, s_pj = wave & 1;
-    f32x16 S;
+    // owners: state column p = 16 wave + li; tile j holds rows n = 16 j + 4 lg + q
+    const int pcol = 16 * wave + li;
+    f32x4 S[NT];
+    bf16x8 Sh[KS], Sl[KS];   // the state split as C S operands (k-step ks: tiles 2 ks, 2 ks + 1)
+    auto split_state = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int n = 32 * s_ni + acc_row(i, lane);
-        const int p = 32 * s_pj + col;
-        S[i] = (owns && a.h0) ? a.h0[(bh * kPd + p) * N + n] : 0.0f;
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = S[2 * ks + (j >> 2)][j & 3];
+                const __bf16 hv = (__bf16)v;
+                Sh[ks][j] = hv;
+                Sl[ks][j] = (__bf16)(v - (float)hv);
+            }
+        }
+    };
+    if (owner) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                S[j][q] = a.h0 ? a.h0[(bh * kPd + pcol) * N + 16 * j + 4 * lg + q] : 0.0f;
+        split_state();
     }
 
     const int64_t nch = (L + kQ - 1) / kQ;
     constexpr int PER = N / 8;
     const int rt = tid >> 3, rp0 = (tid & 7) * 8, rn0 = (tid & 7) * PER;
+    // Loads are unconditional, from the last token's addresses past L (and
+    // from x when there is no z).
     auto fetch = [&](int64_t t0, ChunkRegs<N>& r) {
-        const bool in = t0 + rt < L;
-        const uint4 zero = make_uint4(0, 0, 0, 0);
-        const int64_t xo = ((b * L + t0 + rt) * H + h) * kPd + rp0;
-        const int64_t bo = ((b * L + t0 + rt) * G + grp) * N + rn0;
-        r.x = in ? *reinterpret_cast<const uint4*>(X + xo) : zero;
-        r.z = (in && Z) ? *reinterpret_cast<const uint4*>(Z + xo) : zero;
+        const int64_t tt = t0 + rt < L ? t0 + rt : L - 1;
+        const int64_t xo = ((b * L + tt) * H + h) * kPd + rp0;
+        const int64_t bo = ((b * L + tt) * G + grp) * N + rn0;
+        // Delta first: the prefix wave waits for it before its other loads
+        if (wave == kOwners) r.dt = DT[(b * L + (t0 + lane < L ? t0 + lane : L - 1)) * H + h];
+        r.x = *reinterpret_cast<const u32x4*>(X + xo);
+        r.z = *reinterpret_cast<const u32x4*>((Z ? Z : X) + xo);
 #pragma unroll
         for (int q = 0; q < PER / 8; ++q) {
-            r.b[q] = in ? reinterpret_cast<const uint4*>(Bg + bo)[q] : zero;
-            r.c[q] = in ? reinterpret_cast<const uint4*>(Cg + bo)[q] : zero;
+            r.b[q] = reinterpret_cast<const u32x4*>(Bg + bo)[q];
+            r.c[q] = reinterpret_cast<const u32x4*>(Cg + bo)[q];
         }
-        r.dt = (wave == 0 && t0 + lane < L) ? DT[(b * L + t0 + lane) * H + h] : (uint16_t)0;
     };
+    // Delta, the in-chunk prefix of the log2 decay and the state-update
+    // weights of the chunk at t0 (tokens past L: Delta 0, decay 1, no input)
+    auto prefix = [&](int64_t t0, uint16_t dt, int buf) {
+        float wv = 0.0f;
+        if (t0 + lane < L) {
+            const float vl = __builtin_fmaf(bf16_to_f32(dt), kLog2e, bias_l);
+            wv = SP ? softplus_log2(vl) : vl;
+        }
+        float cs = wv * Ah;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float up = __shfl_up(cs, o, 64);
+            if (lane >= o) cs += up;
+        }
+        const float last = __shfl(cs, 63, 64);
+        const float dlv = wv * kLn2;
+        sm.dl[buf][lane] = dlv;
+        sm.cum[buf][lane] = cs;
+        sm.wts[buf][lane] = fast_exp2(last - cs) * dlv;
+    };
+
     ChunkRegs<N> cr;
     fetch(0, cr);
+    if (wave == kOwners) prefix(0, cr.dt, 0);
+    if (!owner) {
+        // the zero tiles of M, written once: 256 threads, one 16-byte piece
+        // each of tile (0, 1) or (2, 3), hi or lo
+        const int ht = tid - kOwners * 64;
+        const int tile = ht >> 7, hl = (ht >> 6) & 1, r = (ht >> 2) & 15, c8 = (ht >> 1) & 1;
+        if ((ht & 1) == 0) {
+            const int t = 32 * tile + r, s = 32 * tile + 16 + 8 * c8;
+            uint16_t* dst = hl ? &sm.Ml[t][s] : &sm.Mh[t][s];
+            *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+        }
+    }
+
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t t0 = c * kQ;
-        // ---- stage: the entering state, split, [p][n]; this chunk's inputs
-        if (owns) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int n = 32 * s_ni + acc_row(i, lane);
-                const int p = 32 * s_pj + col;
-                uint16_t hi, lo;
-                split(S[i], hi, lo);
-                sm.STh[p][n] = hi;
-                sm.STl[p][n] = lo;
-            }
-        }
+        const int cb = (int)(c & 1);
+        // ---- A: stage this chunk in its memory layout; request the next ----
         {
-            const uint32_t w[4] = {cr.x.x, cr.x.y, cr.x.z, cr.x.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sm.xT[rp0 + 2 * j][rt] = (uint16_t)(w[j] & 0xffffu);
-                sm.xT[rp0 + 2 * j + 1][rt] = (uint16_t)(w[j] >> 16);
-            }
-            *reinterpret_cast<uint4*>(&sm.zs[rt][rp0]) = cr.z;
+            const unsigned keep = t0 + rt < L ? ~0u : 0u;   // tokens past L: zero
+            const unsigned keepz = Z ? keep : 0u;
+            *reinterpret_cast<u32x4*>(&sm.xs[rt][rp0]) = cr.x & keep;
+            *reinterpret_cast<u32x4*>(&sm.zs[rt][rp0]) = cr.z & keepz;
 #pragma unroll
             for (int q = 0; q < PER / 8; ++q) {
-                *reinterpret_cast<uint4*>(&sm.Bs[rt][rn0 + 8 * q]) = cr.b[q];
-                *reinterpret_cast<uint4*>(&sm.Cs[rt][rn0 + 8 * q]) = cr.c[q];
-                const uint32_t wb[4] = {cr.b[q].x, cr.b[q].y, cr.b[q].z, cr.b[q].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sm.BT[rn0 + 8 * q + 2 * j][rt] = (uint16_t)(wb[j] & 0xffffu);
-                    sm.BT[rn0 + 8 * q + 2 * j + 1][rt] = (uint16_t)(wb[j] >> 16);
-                }
+                *reinterpret_cast<u32x4*>(&sm.Bs[rt][rn0 + 8 * q]) = cr.b[q] & keep;
+                *reinterpret_cast<u32x4*>(&sm.Cs[rt][rn0 + 8 * q]) = cr.c[q] & keep;
             }
-        }
-        if (wave == 0) {
-            // Delta and the in-chunk prefix of the log2 decay (tokens past L:
-            // Delta 0, decay 1, no input)
-            const int t = lane;
-            float wv = 0.0f;
-            if (t0 + t < L) {
-                const float vl = __builtin_fmaf(bf16_to_f32(cr.dt), kLog2e, bias_l);
-                wv = SP ? softplus_log2(vl) : vl;
-            }
-            float cs = wv * Ah;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float up = __shfl_up(cs, o, 64);
-                if (lane >= o) cs += up;
-            }
-            const float last = __shfl(cs, 63, 64);
-            const float dlv = wv * kLn2;
-            sm.dl[t] = dlv;
-            sm.cum[t] = cs;
-            sm.wts[t] = fast_exp2(last - cs) * dlv;
         }
         if (c + 1 < nch) fetch(t0 + kQ, cr);
         lds_barrier();
 
-        // ---- M = (C B^T) o decay: blocks (0,0), (1,0), (1,1); weighted x --
-        if (wave < 3) {
-            const int ti = wave == 0 ? 0 : 1;
-            const int si = wave == 2 ? 1 : 0;
-            f32x16 g = {};
+        f32x4 Yacc[4];
+        if (owner) {
+            // ---- B (owners): Y = 2^cum C S, the state from registers ----------
+            // k-step ks pairs state tiles 2 ks and 2 ks + 1, whose rows
+            // 4 lg .. 4 lg + 3 this lane holds: the C operand takes columns
+            // 32 ks + 4 lg .. + 3 and 32 ks + 16 + 4 lg .. + 3 in that order
 #pragma unroll
-            for (int kk = 0; kk < N / 16; ++kk) {
-                const bf16x8 av = ld8(&sm.Cs[32 * ti + col][16 * kk + khalf]);
-                const bf16x8 bv = ld8(&sm.Bs[32 * si + col][16 * kk + khalf]);
-                g = mfma(av, bv, g);
+            for (int tb = 0; tb < 4; ++tb) {
+                Yacc[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                const uint16_t* crow = &sm.Cs[16 * tb + li][4 * lg];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 cv = cat(ld4(crow + 32 * ks), ld4(crow + 32 * ks + 16));
+                    Yacc[tb] = mfma(cv, Sh[ks], Yacc[tb]);
+                    Yacc[tb] = mfma(cv, Sl[ks], Yacc[tb]);
+                }
+                const f32x4 cm = *reinterpret_cast<const f32x4*>(&sm.cum[cb][16 * tb + 4 * lg]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Yacc[tb][q] *= fast_exp2(cm[q]);
             }
-            const int s = 32 * si + col;
-            const float cs = sm.cum[s];
-            const float ds = sm.dl[s];
+        } else {
+            // ---- B (helpers): M tiles and the weighted x ---------------------
+            for (int k = wave - kOwners; k < 10; k += 4) {
+                int tb, sb;
+                m_tile(k, tb, sb);
+                // M^T tile = B C^T: rows s = 16 sb + 4 lg + q, column t = 16 tb + li
+                f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = 32 * ti + acc_row(i, lane);
-                const float m = t >= s ? g[i] * fast_exp2(sm.cum[t] - cs) * ds : 0.0f;
-                uint16_t hi, lo;
-                split(m, hi, lo);
-                sm.Mh[t][s] = hi;
-                sm.Ml[t][s] = lo;
+                for (int ks = 0; ks < KS; ++ks)
+                    g = mfma(ld8(&sm.Bs[16 * sb + li][32 * ks + 8 * lg]), ld8(&sm.Cs[16 * tb + li][32 * ks + 8 * lg]),
+                             g);
+                const int t = 16 * tb + li, s0 = 16 * sb + 4 * lg;
+                const float ct = sm.cum[cb][t];
+                const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[cb][s0]);
+                const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dl[cb][s0]);
+                float m[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) m[q] = (s0 + q <= t) ? g[q] * fast_exp2(ct - cs[q]) * ds[q] : 0.0f;
+                uint2 mh, ml;
+                split4(m, mh, ml);
+                *reinterpret_cast<uint2*>(&sm.Mh[t][s0]) = mh;
+                *reinterpret_cast<uint2*>(&sm.Ml[t][s0]) = ml;
             }
-        } else if (wave >= 4) {
-            const int p = lane;
+            const int ht = tid - kOwners * 64;   // 0..255: token s, 16 columns
+            const int s = ht >> 2, p0 = (ht & 3) * 16;
+            const float wv = sm.wts[cb][s];
 #pragma unroll
-            for (int s8 = 0; s8 < 2; ++s8) {
-                const int s0 = 16 * (wave - 4) + 8 * s8;
-                const bf16x8 xv = ld8(&sm.xT[p][s0]);
+            for (int half = 0; half < 2; ++half) {
+                const bf16x8 xv = ld8(&sm.xs[s][p0 + 8 * half]);
                 bf16x8 xh, xl;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float v = (float)xv[j] * sm.wts[s0 + j];
+                    const float v = (float)xv[j] * wv;
                     const __bf16 vh = (__bf16)v;
                     xh[j] = vh;
                     xl[j] = (__bf16)(v - (float)vh);
                 }
-                *reinterpret_cast<bf16x8*>(&sm.XWh[p][s0]) = xh;
-                *reinterpret_cast<bf16x8*>(&sm.XWl[p][s0]) = xl;
+                *reinterpret_cast<bf16x8*>(&sm.Wh[s][p0 + 8 * half]) = xh;
+                *reinterpret_cast<bf16x8*>(&sm.Wl[s][p0 + 8 * half]) = xl;
             }
         }
         lds_barrier();
 
-        // ---- Y: M X on waves 0..3, C S (to LDS) on waves 4..7 ------------
-        const int yb = wave & 3;
-        const int ti = yb >> 1, pj = yb & 1;
-        f32x16 yi = {};
-        if (wave < 4) {
+        if (owner) {
+            // ---- C (owners): Y += M X over the causal k-steps; Y to LDS -------
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk >= 2 * (ti + 1)) break;   // causal: s < 32 (ti + 1)
-                const bf16x8 xv = ld8(&sm.xT[32 * pj + col][16 * kk + khalf]);
-                yi = mfma(ld8(&sm.Mh[32 * ti + col][16 * kk + khalf]), xv, yi);
-                yi = mfma(ld8(&sm.Ml[32 * ti + col][16 * kk + khalf]), xv, yi);
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int ks = 0; ks <= (tb >> 1); ++ks) {
+                    const bf16x8 xv = ld_col8(&sm.xs[0][0], kRowX, 32 * ks, 16 * wave, lane);
+                    Yacc[tb] = mfma(ld8(&sm.Mh[16 * tb + li][32 * ks + 8 * lg]), xv, Yacc[tb]);
+                    Yacc[tb] = mfma(ld8(&sm.Ml[16 * tb + li][32 * ks + 8 * lg]), xv, Yacc[tb]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sm.Y[16 * tb + 4 * lg + q][pcol] = Yacc[tb][q];
+            }
+        } else if (wave == kOwners && c + 1 < nch) {
+            // ---- C (first helper): the next chunk's prefix ---------------------
+            prefix(t0 + kQ, cr.dt, cb ^ 1);
+        }
+        lds_barrier();
+
+        if (!owner) {
+            // ---- D (helpers): y = (Y + D x) silu(z), stored --------------------
+            const int ht = tid - kOwners * 64;
+            const int t = ht >> 2, p0 = (ht & 3) * 16;
+            if (t0 + t < L) {
+                float yv[16];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const bf16x8 xv = ld8(&sm.xs[t][p0 + 8 * half]);
+                    const bf16x8 zv = ld8(&sm.zs[t][p0 + 8 * half]);
+#pragma unroll
+                    for (int j4 = 0; j4 < 2; ++j4) {
+                        const f32x4 yy = *reinterpret_cast<const f32x4*>(&sm.Y[t][p0 + 8 * half + 4 * j4]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int j = 4 * j4 + q;
+                            float v = __builtin_fmaf(Dh, (float)xv[j], yy[q]);
+                            if (Z) v *= silu_scaled((float)zv[j], 1.0f);
+                            yv[8 * half + j] = v;
+                        }
+                    }
+                }
+                Tout* dst = Yg + ((b * L + t0 + t) * H + h) * kPd + p0;
+                if constexpr (sizeof(Tout) == 4) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        reinterpret_cast<float4*>(dst)[q] =
+                            make_float4(yv[4 * q], yv[4 * q + 1], yv[4 * q + 2], yv[4 * q + 3]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        reinterpret_cast<uint4*>(dst)[q] =
+                            make_uint4(pack_bf16x2(yv[8 * q], yv[8 * q + 1]), pack_bf16x2(yv[8 * q + 2], yv[8 * q + 3]),
+                                       pack_bf16x2(yv[8 * q + 4], yv[8 * q + 5]),
+                                       pack_bf16x2(yv[8 * q + 6], yv[8 * q + 7]));
+                }
             }
         } else {
-            f32x16 yc = {};
+            // ---- D (owners): S = 2^cum_last S + B^T (w X) ---------------------
+            const float dec = fast_exp2(sm.cum[cb][kQ - 1]);
+            bf16x8 wh[2], wl[2];
 #pragma unroll
-            for (int kk = 0; kk < N / 16; ++kk) {
-                const bf16x8 cv = ld8(&sm.Cs[32 * ti + col][16 * kk + khalf]);
-                yc = mfma(cv, ld8(&sm.STh[32 * pj + col][16 * kk + khalf]), yc);
-                yc = mfma(cv, ld8(&sm.STl[32 * pj + col][16 * kk + khalf]), yc);
+            for (int ks = 0; ks < 2; ++ks) {
+                wh[ks] = ld_col8(&sm.Wh[0][0], kRowX, 32 * ks, 16 * wave, lane);
+                wl[ks] = ld_col8(&sm.Wl[0][0], kRowX, 32 * ks, 16 * wave, lane);
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sm.yoff[yb][i][lane] = yc[i];
-        }
-        lds_barrier();
-
-        // ---- out: Y = M X + 2^cum C S + D x, the gate, the store -----------
-        if (wave < 4) {
-            const int p = 32 * pj + col;
+            for (int j = 0; j < NT; ++j) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = 32 * ti + acc_row(i, lane);
-                if (t0 + t >= L) continue;
-                const float xv = bf16_to_f32(sm.xT[p][t]);
-                float yv = __builtin_fmaf(fast_exp2(sm.cum[t]), sm.yoff[yb][i][lane], yi[i]);
-                yv = __builtin_fmaf(Dh, xv, yv);
-                const int64_t idx = ((b * L + t0 + t) * H + h) * kPd + p;
-                if (Z) yv *= silu_scaled(bf16_to_f32(sm.zs[t][p]), 1.0f);
-                if constexpr (sizeof(Tout) == 4)
-                    Y[idx] = yv;
-                else
-                    Y[idx] = f32_to_bf16(yv);
+                for (int q = 0; q < 4; ++q) S[j][q] *= dec;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    // B^T operand: row n = 16 j + li, k = s
+                    const bf16x8 bt = ld_col8(&sm.Bs[0][0], kRowN, 32 * ks, 16 * j, lane);
+                    S[j] = mfma(bt, wh[ks], S[j]);
+                    S[j] = mfma(bt, wl[ks], S[j]);
+                }
             }
-        }
-
-        // ---- S = 2^cum_last S + B^T diag(wts) X ---------------------------
-        if (owns) {
-            const float dec = fast_exp2(sm.cum[kQ - 1]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) S[i] *= dec;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 bv = ld8(&sm.BT[32 * s_ni + col][16 * kk + khalf]);
-                const int p = 32 * s_pj + col;
-                S = mfma(bv, ld8(&sm.XWh[p][16 * kk + khalf]), S);
-                S = mfma(bv, ld8(&sm.XWl[p][16 * kk + khalf]), S);
-            }
+            split_state();
         }
         lds_barrier();
     }
 
-    if (a.last && owns) {
+    if (a.last && owner) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int n = 32 * s_ni + acc_row(i, lane);
-            const int p = 32 * s_pj + col;
-            a.last[(bh * kPd + p) * N + n] = S[i];
-        }
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a.last[(bh * kPd + pcol) * N + 16 * j + 4 * lg + q] = S[j][q];
     }
 }
 
