@@ -104,16 +104,17 @@ __device__ __forceinline__ void split4(const float v[4], uint2& hi, uint2& lo) {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// One thread's share of a chunk's inputs, fetched a chunk ahead: token
-// tid / 8, eight channels of x and z and N / 8 states of B and C.  The words
-// are the loads' raw bits (past L: the last token's); they are zeroed when
-// staged, so no use of them sits right behind the loads.
+// One state owner's share of a chunk's inputs, fetched a chunk ahead: token
+// tid / 4 and a quarter of its x, z, B and C rows.  The words are the loads'
+// raw bits (past L: the last token's); they are zeroed when staged, so no use
+// of them sits right behind the loads.  Only the owners load and only the
+// helpers store, so neither waits on the other kind of memory operation.
 template <int N>
 struct ChunkRegs {
-    static constexpr int kPer = N / 8;
-    u32x4 x, z;
-    u32x4 b[kPer / 8], c[kPer / 8];
-    uint16_t dt;
+    static constexpr int kBC = N / 32;   // 16-byte pieces of a quarter row of B (and of C)
+    u32x4 x[2], z[2];
+    u32x4 b[kBC], c[kBC];
+    uint16_t dt;                          // wave 0: Delta of token lane
 };
 
 template <int N>
@@ -131,23 +132,24 @@ struct SsdSmem {
     float dl[2][kQ];              // Delta, by chunk parity
     float cum[2][kQ];             // inclusive prefix of w A within the chunk
     float wts[2][kQ];             // 2^(cum_last - cum_s) Delta_s
+    float ecum[2][kQ];            // 2^cum_t
+    uint16_t dtraw[2][kQ];        // Delta input of the next chunk, as loaded
 };
 
-// The causal 16 x 16 tiles (t-tile, s-tile) of M; helper k of the four
-// builds tiles k, k + 4, k + 8.  Tiles (0, 1) and (2, 3) lie above the
-// diagonal but inside the 32-wide k-steps of M X: they stay zero.
-__device__ __forceinline__ void m_tile(int k, int& tb, int& sb) {
-    tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
-    sb = k - tb * (tb + 1) / 2;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Per chunk (barriers between phases):
-//   A  all      inputs into LDS in their memory layout; next chunk requested
+//   A  0..3     inputs into LDS in their memory layout; next chunk requested
 //   B  0..3     Y = 2^cum C S for the wave's 16 columns (S from registers)
-//      4..7     M (causal tiles, split) and the weighted x (split)
+//      4..6     M: its causal 32 x 32 blocks (0,0), (1,0), (1,1), split
 //   C  0..3     Y += M X, to LDS
-//      4        Delta, decay prefix and weights of the next chunk
-//   D  4..7     y = (Y + D x) silu(z), stored
+//      4..7     the weighted x (split); silu(z) and D x silu(z) of the
+//               thread's 16 outputs; wave 4: the next chunk's decay prefix
+//   D  4..7     y = Y silu(z) + D x silu(z), stored
 //      0..3     S = 2^cum_last S + B^T (w X); its split for the next C S
 template <typename Tout, int N, bool SP>
 __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
@@ -204,30 +206,33 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
     }
 
     const int64_t nch = (L + kQ - 1) / kQ;
-    constexpr int PER = N / 8;
-    const int rt = tid >> 3, rp0 = (tid & 7) * 8, rn0 = (tid & 7) * PER;
+    constexpr int NBC = ChunkRegs<N>::kBC;
+    const int rt = tid >> 2, rq = tid & 3;   // owners: token, quarter row
     // Loads are unconditional, from the last token's addresses past L (and
     // from x when there is no z).
     auto fetch = [&](int64_t t0, ChunkRegs<N>& r) {
+        // Delta first: wave 0 hands it on through LDS before the rest lands
+        if (wave == 0) r.dt = DT[(b * L + (t0 + lane < L ? t0 + lane : L - 1)) * H + h];
         const int64_t tt = t0 + rt < L ? t0 + rt : L - 1;
-        const int64_t xo = ((b * L + tt) * H + h) * kPd + rp0;
-        const int64_t bo = ((b * L + tt) * G + grp) * N + rn0;
-        // Delta first: the prefix wave waits for it before its other loads
-        if (wave == kOwners) r.dt = DT[(b * L + (t0 + lane < L ? t0 + lane : L - 1)) * H + h];
-        r.x = *reinterpret_cast<const u32x4*>(X + xo);
-        r.z = *reinterpret_cast<const u32x4*>((Z ? Z : X) + xo);
+        const u32x4* xp = reinterpret_cast<const u32x4*>(X + ((b * L + tt) * H + h) * kPd + 16 * rq);
+        const u32x4* zp = reinterpret_cast<const u32x4*>((Z ? Z : X) + ((b * L + tt) * H + h) * kPd + 16 * rq);
+        const int64_t bo = ((b * L + tt) * G + grp) * N + (N / 4) * rq;
+        r.x[0] = xp[0];
+        r.x[1] = xp[1];
+        r.z[0] = zp[0];
+        r.z[1] = zp[1];
 #pragma unroll
-        for (int q = 0; q < PER / 8; ++q) {
+        for (int q = 0; q < NBC; ++q) {
             r.b[q] = reinterpret_cast<const u32x4*>(Bg + bo)[q];
             r.c[q] = reinterpret_cast<const u32x4*>(Cg + bo)[q];
         }
     };
-    // Delta, the in-chunk prefix of the log2 decay and the state-update
-    // weights of the chunk at t0 (tokens past L: Delta 0, decay 1, no input)
-    auto prefix = [&](int64_t t0, uint16_t dt, int buf) {
+    // Delta, the in-chunk prefix of the log2 decay and the per-token factors
+    // of the chunk at t0 (tokens past L: Delta 0, decay 1, no input)
+    auto prefix = [&](int64_t t0, int buf) {
         float wv = 0.0f;
         if (t0 + lane < L) {
-            const float vl = __builtin_fmaf(bf16_to_f32(dt), kLog2e, bias_l);
+            const float vl = __builtin_fmaf(bf16_to_f32(sm.dtraw[buf][lane]), kLog2e, bias_l);
             wv = SP ? softplus_log2(vl) : vl;
         }
         float cs = wv * Ah;
@@ -240,40 +245,47 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
         const float dlv = wv * kLn2;
         sm.dl[buf][lane] = dlv;
         sm.cum[buf][lane] = cs;
+        sm.ecum[buf][lane] = fast_exp2(cs);
         sm.wts[buf][lane] = fast_exp2(last - cs) * dlv;
     };
 
     ChunkRegs<N> cr;
-    fetch(0, cr);
-    if (wave == kOwners) prefix(0, cr.dt, 0);
-    if (!owner) {
-        // the zero tiles of M, written once: 256 threads, one 16-byte piece
-        // each of tile (0, 1) or (2, 3), hi or lo
-        const int ht = tid - kOwners * 64;
-        const int tile = ht >> 7, hl = (ht >> 6) & 1, r = (ht >> 2) & 15, c8 = (ht >> 1) & 1;
-        if ((ht & 1) == 0) {
-            const int t = 32 * tile + r, s = 32 * tile + 16 + 8 * c8;
-            uint16_t* dst = hl ? &sm.Ml[t][s] : &sm.Mh[t][s];
-            *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
-        }
+    if (owner) {
+        fetch(0, cr);
+        if (wave == 0) sm.dtraw[0][lane] = cr.dt;
     }
+    lds_barrier();
+    if (wave == kOwners) prefix(0, 0);
+
+    // helpers: the thread's token and 16 outputs of the epilogue (and of the
+    // weighted x): t = ht / 4, p = 16 (ht % 4) ..
+    const int ht = tid - kOwners * 64;
+    const int et = ht >> 2, ep0 = (ht & 3) * 16;
+    float eg[16], edg[16];   // silu(z) and D x silu(z), from phase C to D
 
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t t0 = c * kQ;
         const int cb = (int)(c & 1);
-        // ---- A: stage this chunk in its memory layout; request the next ----
-        {
-            const unsigned keep = t0 + rt < L ? ~0u : 0u;   // tokens past L: zero
+        if (owner) {
+            // ---- A: stage this chunk in its memory layout; request the next ----
+            const bool part = t0 + kQ > L;   // a partial last chunk: zero past L
+            const unsigned keep = (!part || t0 + rt < L) ? ~0u : 0u;
             const unsigned keepz = Z ? keep : 0u;
-            *reinterpret_cast<u32x4*>(&sm.xs[rt][rp0]) = cr.x & keep;
-            *reinterpret_cast<u32x4*>(&sm.zs[rt][rp0]) = cr.z & keepz;
+            u32x4* xd = reinterpret_cast<u32x4*>(&sm.xs[rt][16 * rq]);
+            u32x4* zd = reinterpret_cast<u32x4*>(&sm.zs[rt][16 * rq]);
+            xd[0] = cr.x[0] & keep;
+            xd[1] = cr.x[1] & keep;
+            zd[0] = cr.z[0] & keepz;
+            zd[1] = cr.z[1] & keepz;
+            u32x4* bd = reinterpret_cast<u32x4*>(&sm.Bs[rt][(N / 4) * rq]);
+            u32x4* cd = reinterpret_cast<u32x4*>(&sm.Cs[rt][(N / 4) * rq]);
 #pragma unroll
-            for (int q = 0; q < PER / 8; ++q) {
-                *reinterpret_cast<u32x4*>(&sm.Bs[rt][rn0 + 8 * q]) = cr.b[q] & keep;
-                *reinterpret_cast<u32x4*>(&sm.Cs[rt][rn0 + 8 * q]) = cr.c[q] & keep;
+            for (int q = 0; q < NBC; ++q) {
+                bd[q] = cr.b[q] & keep;
+                cd[q] = cr.c[q] & keep;
             }
+            if (c + 1 < nch) fetch(t0 + kQ, cr);
         }
-        if (c + 1 < nch) fetch(t0 + kQ, cr);
         lds_barrier();
 
         f32x4 Yacc[4];
@@ -292,49 +304,36 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
                     Yacc[tb] = mfma(cv, Sh[ks], Yacc[tb]);
                     Yacc[tb] = mfma(cv, Sl[ks], Yacc[tb]);
                 }
-                const f32x4 cm = *reinterpret_cast<const f32x4*>(&sm.cum[cb][16 * tb + 4 * lg]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) Yacc[tb][q] *= fast_exp2(cm[q]);
+                Yacc[tb] *= *reinterpret_cast<const f32x4*>(&sm.ecum[cb][16 * tb + 4 * lg]);
             }
-        } else {
-            // ---- B (helpers): M tiles and the weighted x ---------------------
-            for (int k = wave - kOwners; k < 10; k += 4) {
-                int tb, sb;
-                m_tile(k, tb, sb);
-                // M^T tile = B C^T: rows s = 16 sb + 4 lg + q, column t = 16 tb + li
-                f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+            // the next chunk's Delta inputs for the prefix wave
+            if (wave == 0 && c + 1 < nch) sm.dtraw[cb ^ 1][lane] = cr.dt;
+        } else if (wave < kOwners + 3) {
+            // ---- B (helpers): a causal 32 x 32 block of M ---------------------
+            // block (t, s) = (0, 0), (1, 0), (1, 1) as M^T = B C^T: lane
+            // column t = 32 tb + lane % 32, rows s = 32 sb + 8 r + 4 h + q
+            const int hw = wave - kOwners;
+            const int tb = hw == 0 ? 0 : 1, sb = hw == 2 ? 1 : 0;
+            const int l32 = lane & 31, h = lane >> 5;
+            f32x16 g = {};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    g = mfma(ld8(&sm.Bs[16 * sb + li][32 * ks + 8 * lg]), ld8(&sm.Cs[16 * tb + li][32 * ks + 8 * lg]),
-                             g);
-                const int t = 16 * tb + li, s0 = 16 * sb + 4 * lg;
-                const float ct = sm.cum[cb][t];
+            for (int kk = 0; kk < N / 16; ++kk)
+                g = mfma32(ld8(&sm.Bs[32 * sb + l32][16 * kk + 8 * h]), ld8(&sm.Cs[32 * tb + l32][16 * kk + 8 * h]), g);
+            const int t = 32 * tb + l32;
+            const float ct = sm.cum[cb][t];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s0 = 32 * sb + 8 * r + 4 * h;
                 const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[cb][s0]);
                 const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dl[cb][s0]);
                 float m[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) m[q] = (s0 + q <= t) ? g[q] * fast_exp2(ct - cs[q]) * ds[q] : 0.0f;
+                for (int q = 0; q < 4; ++q)
+                    m[q] = (s0 + q <= t) ? g[4 * r + q] * fast_exp2(ct - cs[q]) * ds[q] : 0.0f;
                 uint2 mh, ml;
                 split4(m, mh, ml);
                 *reinterpret_cast<uint2*>(&sm.Mh[t][s0]) = mh;
                 *reinterpret_cast<uint2*>(&sm.Ml[t][s0]) = ml;
-            }
-            const int ht = tid - kOwners * 64;   // 0..255: token s, 16 columns
-            const int s = ht >> 2, p0 = (ht & 3) * 16;
-            const float wv = sm.wts[cb][s];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const bf16x8 xv = ld8(&sm.xs[s][p0 + 8 * half]);
-                bf16x8 xh, xl;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float v = (float)xv[j] * wv;
-                    const __bf16 vh = (__bf16)v;
-                    xh[j] = vh;
-                    xl[j] = (__bf16)(v - (float)vh);
-                }
-                *reinterpret_cast<bf16x8*>(&sm.Wh[s][p0 + 8 * half]) = xh;
-                *reinterpret_cast<bf16x8*>(&sm.Wl[s][p0 + 8 * half]) = xl;
             }
         }
         lds_barrier();
@@ -352,35 +351,43 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) sm.Y[16 * tb + 4 * lg + q][pcol] = Yacc[tb][q];
             }
-        } else if (wave == kOwners && c + 1 < nch) {
-            // ---- C (first helper): the next chunk's prefix ---------------------
-            prefix(t0 + kQ, cr.dt, cb ^ 1);
+        } else {
+            // ---- C (helpers): weighted x; the gate of the thread's outputs ----
+            const float wv = sm.wts[cb][et];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const bf16x8 xv = ld8(&sm.xs[et][ep0 + 8 * half]);
+                const bf16x8 zv = ld8(&sm.zs[et][ep0 + 8 * half]);
+                bf16x8 xh, xl;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float x = (float)xv[j];
+                    const float v = x * wv;
+                    const __bf16 vh = (__bf16)v;
+                    xh[j] = vh;
+                    xl[j] = (__bf16)(v - (float)vh);
+                    const float gz = Z ? silu_scaled((float)zv[j], 1.0f) : 1.0f;
+                    eg[8 * half + j] = gz;
+                    edg[8 * half + j] = Dh * x * gz;
+                }
+                *reinterpret_cast<bf16x8*>(&sm.Wh[et][ep0 + 8 * half]) = xh;
+                *reinterpret_cast<bf16x8*>(&sm.Wl[et][ep0 + 8 * half]) = xl;
+            }
+            if (wave == kOwners && c + 1 < nch) prefix(t0 + kQ, cb ^ 1);
         }
         lds_barrier();
 
         if (!owner) {
-            // ---- D (helpers): y = (Y + D x) silu(z), stored --------------------
-            const int ht = tid - kOwners * 64;
-            const int t = ht >> 2, p0 = (ht & 3) * 16;
-            if (t0 + t < L) {
+            // ---- D (helpers): y = Y silu(z) + D x silu(z), stored --------------
+            if (t0 + et < L) {
                 float yv[16];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const bf16x8 xv = ld8(&sm.xs[t][p0 + 8 * half]);
-                    const bf16x8 zv = ld8(&sm.zs[t][p0 + 8 * half]);
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const f32x4 yy = *reinterpret_cast<const f32x4*>(&sm.Y[et][ep0 + 4 * j4]);
 #pragma unroll
-                    for (int j4 = 0; j4 < 2; ++j4) {
-                        const f32x4 yy = *reinterpret_cast<const f32x4*>(&sm.Y[t][p0 + 8 * half + 4 * j4]);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int j = 4 * j4 + q;
-                            float v = __builtin_fmaf(Dh, (float)xv[j], yy[q]);
-                            if (Z) v *= silu_scaled((float)zv[j], 1.0f);
-                            yv[8 * half + j] = v;
-                        }
-                    }
+                    for (int q = 0; q < 4; ++q) yv[4 * j4 + q] = __builtin_fmaf(yy[q], eg[4 * j4 + q], edg[4 * j4 + q]);
                 }
-                Tout* dst = Yg + ((b * L + t0 + t) * H + h) * kPd + p0;
+                Tout* dst = Yg + ((b * L + t0 + et) * H + h) * kPd + ep0;
                 if constexpr (sizeof(Tout) == 4) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
@@ -397,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
             }
         } else {
             // ---- D (owners): S = 2^cum_last S + B^T (w X) ---------------------
-            const float dec = fast_exp2(sm.cum[cb][kQ - 1]);
+            const float dec = sm.ecum[cb][kQ - 1];
             bf16x8 wh[2], wl[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -406,8 +413,7 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
             }
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) S[j][q] *= dec;
+                S[j] *= dec;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     // B^T operand: row n = 16 j + li, k = s
