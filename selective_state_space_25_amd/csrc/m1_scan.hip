@@ -11,18 +11,18 @@
 // Work layout.  A workgroup is one wave; lane l owns channel ("row") d0 + l of
 // one batch and keeps its 16 fp32 states in registers, walking its tokens in
 // order.  All lanes of the wave read the same B_t and C_t, so they come from
-// an fp32 copy laid out [batch][token][B0..B15, C0..C15] through scalar loads
-// (the next token's are requested while the current one is computed) and
-// enter the FMAs as SGPR operands.
+// an fp32 copy laid out [batch][token][B0..B15, C0..C15] (one 128-byte
+// record per token), copied into LDS with each tile and read back as
+// same-address (broadcast) LDS reads.
 //
-// Memory traffic moves whole 128-byte lines.  u, delta and z arrive in tiles
-// of one line per row and tensor (64 bf16 or 32 fp32 tokens), copied by the
-// memory system straight into LDS (global_load_lds_dwordx4: every lane fetches
-// eight 16-byte pieces of its own row, all eight pieces of a line in one
-// burst).  The next tile is requested as soon as the last 8-token block of the
-// current one has been read out of LDS, so its latency overlaps that block's
-// arithmetic.  y collects 32 tokens per lane in registers (128 bytes of fp32
-// per row) and leaves as one burst of 16-byte stores covering whole lines.
+// u, delta and z arrive in tiles of 32 tokens per row and tensor (64 bytes
+// of bf16 or 128 of fp32 per row), copied by the memory system straight
+// into LDS (global_load_lds_dwordx4: each lane fetches the 16-byte pieces of
+// its own row), and the tile's B/C records follow into one of two buffers.
+// The next tile is requested as soon as the current one's last two 8-token
+// blocks are in registers, so its latency overlaps their arithmetic.  y
+// collects the tile's 32 tokens per lane in registers and leaves as one
+// burst of 16-byte stores per row.
 //
 // Long sequences are cut into G chunks so that enough waves exist to fill
 // the 256 CUs: a summary pass computes, per chunk, the end state from a zero
