@@ -22,14 +22,21 @@
 // 2^-16.  bf16 inputs, P = 64 and N in {64, 128} only; other shapes use the
 // recurrent kernel.
 //
-// Waves 0..3 own the state: wave w holds S[:, 16w .. 16w + 16) in N / 16
-// accumulator tiles and computes C S, M X and the state update for those
-// columns, the state entering C S straight from its registers.  Waves 4..7
-// build M, the weighted x and the decay prefix, and write y.  Every chunk
-// input stays in LDS in its memory layout ([token][channel] rows): operands
-// that need the other orientation are read with the transposing LDS load
+// The eight waves share every step.  Wave w holds the state rows of one
+// half of n (w / 4) for 16 columns (w % 4) in accumulator tiles, and
+// computes its part of C S (straight from those registers), of M X and of
+// the state update; two LDS buffers collect the two halves' parts of Y.
+// Every thread also stages an eighth of a token's inputs, builds M tiles,
+// splits the weighted x, prepares the gate and writes y.  Chunk inputs stay
+// in LDS in their memory layout ([token][channel] rows); operands that need
+// the other orientation are read with the transposing LDS load
 // (ds_read_b64_tr_b16), which hands each lane four consecutive rows of one
-// column.
+// column.  Global memory is read and written through buffer descriptors
+// bounded at the last token, so tokens past L load as zero and their stores
+// are dropped by the hardware: every chunk issues the same memory
+// operations.
+#include <type_traits>
+
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -41,16 +48,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
 
 constexpr int kQ = 64;                     // tokens per chunk
 constexpr int kPd = 64;                    // headdim handled by this kernel
 constexpr int kWaves = 8;                  // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kOwners = 4;                 // waves holding the state, 16 columns each
 constexpr int kRowX = kPd + 8;             // padded row (elements) of x, z, weighted x
 constexpr int kRowM = kQ + 8;              // padded row of M
 constexpr int kRowY = kPd + 4;             // padded row (floats) of Y
+constexpr int kBufWord3 = 0x00020000;      // buffer descriptor word 3: 32-bit data format, raw access
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -63,6 +71,15 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// A buffer descriptor over `rows` rows of `row_bytes` bytes spaced `stride`
+// bytes apart from p: accesses at or past the last row's end read zero and
+// drop their stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, int64_t rows, int64_t stride,
+                                                           int row_bytes) {
+    const int n = rows > 0 ? (int)((rows - 1) * stride + row_bytes) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, kBufWord3);
 }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
@@ -102,19 +119,15 @@ __device__ __forceinline__ void split4(const float v[4], uint2& hi, uint2& lo) {
     lo = make_uint2(pack_bf16x2(v[0] - h[0], v[1] - h[1]), pack_bf16x2(v[2] - h[2], v[3] - h[3]));
 }
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// One state owner's share of a chunk's inputs, fetched a chunk ahead: token
-// tid / 4 and a quarter of its x, z, B and C rows.  The words are the loads'
-// raw bits (past L: the last token's); they are zeroed when staged, so no use
-// of them sits right behind the loads.  Only the owners load and only the
-// helpers store, so neither waits on the other kind of memory operation.
+// One thread's share of a chunk's inputs, fetched a chunk ahead: token
+// tid / 8 and an eighth of its x, z, B and C rows; wave 4 (which runs the
+// decay prefix) also Delta of token lane.
 template <int N>
 struct ChunkRegs {
-    static constexpr int kBC = N / 32;   // 16-byte pieces of a quarter row of B (and of C)
-    u32x4 x[2], z[2];
+    static constexpr int kBC = N / 64;   // 16-byte pieces of an eighth of a B (or C) row
+    u32x4 x, z;
     u32x4 b[kBC], c[kBC];
-    uint16_t dt;                          // wave 0: Delta of token lane
+    unsigned short dt;
 };
 
 template <int N>
@@ -128,33 +141,34 @@ struct SsdSmem {
     uint16_t Ml[kQ][kRowM];
     uint16_t Wh[kQ][kRowX];       // x weighted by 2^(cum_last - cum_s) Delta_s, split, [s][p]
     uint16_t Wl[kQ][kRowX];
-    float Y[kQ][kRowY];           // M X + 2^cum C S, [t][p]
+    float Y[2][kQ][kRowY];        // each n-half's 2^cum C S (+ its share of M X), [t][p]
     float dl[2][kQ];              // Delta, by chunk parity
     float cum[2][kQ];             // inclusive prefix of w A within the chunk
     float wts[2][kQ];             // 2^(cum_last - cum_s) Delta_s
     float ecum[2][kQ];            // 2^cum_t
-    uint16_t dtraw[2][kQ];        // Delta input of the next chunk, as loaded
 };
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// The causal 16 x 16 tiles (t-tile, s-tile) of M; wave w builds tiles w and
+// w + 8.  Tiles (0, 1) and (2, 3) lie above the diagonal but inside the
+// 32-wide k-steps of M X: they stay zero.
+__device__ __forceinline__ void m_tile(int k, int& tb, int& sb) {
+    tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
+    sb = k - tb * (tb + 1) / 2;
 }
 
-// Per chunk (barriers between phases):
-//   A  0..3     inputs into LDS in their memory layout; next chunk requested
-//   B  0..3     Y = 2^cum C S for the wave's 16 columns (S from registers)
-//      4..6     M: its causal 32 x 32 blocks (0,0), (1,0), (1,1), split
-//   C  0..3     Y += M X, to LDS
-//      4..7     the weighted x (split); silu(z) and D x silu(z) of the
-//               thread's 16 outputs; wave 4: the next chunk's decay prefix
-//   D  4..7     y = Y silu(z) + D x silu(z), stored
-//      0..3     S = 2^cum_last S + B^T (w X); its split for the next C S
+// Per chunk (barriers between phases), every wave:
+//   B  Y_half = 2^cum C S over its n-half and 16 columns; M tiles
+//   C  its t-tiles of M X added, Y_half to LDS; its piece of the weighted x;
+//      silu(z) and D x silu(z) of its 8 outputs (wave 4: the next prefix)
+//   D  y of its 8 outputs = (Y_0 + Y_1) silu(z) + D x silu(z), stored;
+//      S = 2^cum_last S + B^T (w X) for its tiles, and their split
+//   A  its piece of the next chunk into LDS; the one after requested
 template <typename Tout, int N, bool SP>
 __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
-    constexpr int NT = N / 16;               // 16-row state tiles per owner
-    constexpr int KS = N / 32;               // k-steps over n
+    constexpr int NH = N / 2;                // state rows per wave
+    constexpr int NT = NH / 16;              // 16-row state tiles per wave
+    constexpr int KS = NH / 32;              // k-steps of C S per wave
+    constexpr int NBC = ChunkRegs<N>::kBC;
     constexpr int kRowN = SsdSmem<N>::kRowN;
     __shared__ __attribute__((aligned(16))) SsdSmem<N> sm;
 
@@ -163,7 +177,10 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
     const int lane = tid & 63;
     const int li = lane & 15;                // MFMA column / row within a 16-tile
     const int lg = lane >> 4;                // lane group: k offset 8 lg, output rows 4 lg + q
-    const bool owner = wave < kOwners;
+    const int nh = wave >> 2;                // n-half of the wave's state rows
+    const int nb0 = NH * nh;
+    const int pq = wave & 3;                 // the wave's 16 state columns
+    const int pcol = 16 * pq + li;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / a.H;
     const int64_t h = bh - b * a.H;
@@ -179,9 +196,10 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
     const uint16_t* Cg = reinterpret_cast<const uint16_t*>(a.C);
     const uint16_t* Z = reinterpret_cast<const uint16_t*>(a.z);
     Tout* Yg = reinterpret_cast<Tout*>(a.y);
+    // byte strides of one token
+    const int64_t sx = H * kPd * 2, sbc = G * N * 2, sd = H * 2, sy = H * kPd * (int64_t)sizeof(Tout);
 
-    // owners: state column p = 16 wave + li; tile j holds rows n = 16 j + 4 lg + q
-    const int pcol = 16 * wave + li;
+    // state tile j: rows n = nb0 + 16 j + 4 lg + q, column pcol
     f32x4 S[NT];
     bf16x8 Sh[KS], Sl[KS];   // the state split as C S operands (k-step ks: tiles 2 ks, 2 ks + 1)
     auto split_state = [&]() {
@@ -196,43 +214,45 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
             }
         }
     };
-    if (owner) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                S[j][q] = a.h0 ? a.h0[(bh * kPd + pcol) * N + 16 * j + 4 * lg + q] : 0.0f;
-        split_state();
-    }
+        for (int q = 0; q < 4; ++q)
+            S[j][q] = a.h0 ? a.h0[(bh * kPd + pcol) * N + nb0 + 16 * j + 4 * lg + q] : 0.0f;
+    split_state();
 
     const int64_t nch = (L + kQ - 1) / kQ;
-    constexpr int NBC = ChunkRegs<N>::kBC;
-    const int rt = tid >> 2, rq = tid & 3;   // owners: token, quarter row
-    // Loads are unconditional, from the last token's addresses past L (and
-    // from x when there is no z).
+    const int rt = tid >> 3, rq = tid & 7;   // staging and output: token, eighth of a row
+    // The chunk at t0 through descriptors bounded at token L - 1 (past it:
+    // zeros).  Issued for every chunk, also the one past the end.
     auto fetch = [&](int64_t t0, ChunkRegs<N>& r) {
-        // Delta first: wave 0 hands it on through LDS before the rest lands
-        if (wave == 0) r.dt = DT[(b * L + (t0 + lane < L ? t0 + lane : L - 1)) * H + h];
-        const int64_t tt = t0 + rt < L ? t0 + rt : L - 1;
-        const u32x4* xp = reinterpret_cast<const u32x4*>(X + ((b * L + tt) * H + h) * kPd + 16 * rq);
-        const u32x4* zp = reinterpret_cast<const u32x4*>((Z ? Z : X) + ((b * L + tt) * H + h) * kPd + 16 * rq);
-        const int64_t bo = ((b * L + tt) * G + grp) * N + (N / 4) * rq;
-        r.x[0] = xp[0];
-        r.x[1] = xp[1];
-        r.z[0] = zp[0];
-        r.z[1] = zp[1];
+        const int64_t rows = L - t0 < kQ ? L - t0 : kQ;
+        if (wave == 4) {
+            const auto rd = rows_rsrc(DT + (b * L + t0) * H + h, rows, sd, 2);
+            r.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)(lane * sd), 0, 0);
+        }
+        const int64_t xo = ((b * L + t0) * H + h) * kPd;
+        const auto rx = rows_rsrc(X + xo, rows, sx, kPd * 2);
+        r.x = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(rt * sx) + 16 * rq, 0, 0);
+        if (Z) {
+            const auto rz = rows_rsrc(Z + xo, rows, sx, kPd * 2);
+            r.z = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)(rt * sx) + 16 * rq, 0, 0);
+        }
+        const int64_t bo = ((b * L + t0) * G + grp) * N;
+        const auto rb = rows_rsrc(Bg + bo, rows, sbc, N * 2);
+        const auto rc = rows_rsrc(Cg + bo, rows, sbc, N * 2);
 #pragma unroll
         for (int q = 0; q < NBC; ++q) {
-            r.b[q] = reinterpret_cast<const u32x4*>(Bg + bo)[q];
-            r.c[q] = reinterpret_cast<const u32x4*>(Cg + bo)[q];
+            r.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(rt * sbc) + 16 * (NBC * rq + q), 0, 0);
+            r.c[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(rt * sbc) + 16 * (NBC * rq + q), 0, 0);
         }
     };
     // Delta, the in-chunk prefix of the log2 decay and the per-token factors
     // of the chunk at t0 (tokens past L: Delta 0, decay 1, no input)
-    auto prefix = [&](int64_t t0, int buf) {
+    auto prefix = [&](int64_t t0, unsigned short dt, int buf) {
         float wv = 0.0f;
         if (t0 + lane < L) {
-            const float vl = __builtin_fmaf(bf16_to_f32(sm.dtraw[buf][lane]), kLog2e, bias_l);
+            const float vl = __builtin_fmaf(bf16_to_f32(dt), kLog2e, bias_l);
             wv = SP ? softplus_log2(vl) : vl;
         }
         float cs = wv * Ah;
@@ -249,189 +269,188 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
         sm.wts[buf][lane] = fast_exp2(last - cs) * dlv;
     };
 
+    // this thread's piece of a chunk into LDS
+    auto stage = [&](const ChunkRegs<N>& r) {
+        *reinterpret_cast<u32x4*>(&sm.xs[rt][8 * rq]) = r.x;
+        *reinterpret_cast<u32x4*>(&sm.zs[rt][8 * rq]) = r.z;
+#pragma unroll
+        for (int q = 0; q < NBC; ++q) {
+            *reinterpret_cast<u32x4*>(&sm.Bs[rt][8 * (NBC * rq + q)]) = r.b[q];
+            *reinterpret_cast<u32x4*>(&sm.Cs[rt][8 * (NBC * rq + q)]) = r.c[q];
+        }
+    };
+
+    // Chunk 0 is staged here and every iteration ends by staging the next
+    // one, so the chunk's loads are always followed by exactly the y stores
+    // of one chunk: the wait at the staging then never includes those stores.
     ChunkRegs<N> cr;
-    if (owner) {
-        fetch(0, cr);
-        if (wave == 0) sm.dtraw[0][lane] = cr.dt;
+    cr.z = u32x4{0u, 0u, 0u, 0u};
+    fetch(0, cr);
+    if (wave == 4) prefix(0, cr.dt, 0);
+    stage(cr);
+    fetch(kQ, cr);
+    if (tid < 256) {
+        // the zero tiles of M, written once: one 16-byte piece per even
+        // thread of tile (0, 1) or (2, 3), hi or lo
+        const int tile = tid >> 7, hl = (tid >> 6) & 1, r = (tid >> 2) & 15, c8 = (tid >> 1) & 1;
+        if ((tid & 1) == 0) {
+            const int t = 32 * tile + r, s = 32 * tile + 16 + 8 * c8;
+            uint16_t* dst = hl ? &sm.Ml[t][s] : &sm.Mh[t][s];
+            *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+        }
     }
     lds_barrier();
-    if (wave == kOwners) prefix(0, 0);
 
-    // helpers: the thread's token and 16 outputs of the epilogue (and of the
-    // weighted x): t = ht / 4, p = 16 (ht % 4) ..
-    const int ht = tid - kOwners * 64;
-    const int et = ht >> 2, ep0 = (ht & 3) * 16;
-    float eg[16], edg[16];   // silu(z) and D x silu(z), from phase C to D
+    float eg[8], edg[8];   // silu(z) and D x silu(z) of the thread's outputs, from phase C to D
 
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t t0 = c * kQ;
         const int cb = (int)(c & 1);
-        if (owner) {
-            // ---- A: stage this chunk in its memory layout; request the next ----
-            const bool part = t0 + kQ > L;   // a partial last chunk: zero past L
-            const unsigned keep = (!part || t0 + rt < L) ? ~0u : 0u;
-            const unsigned keepz = Z ? keep : 0u;
-            u32x4* xd = reinterpret_cast<u32x4*>(&sm.xs[rt][16 * rq]);
-            u32x4* zd = reinterpret_cast<u32x4*>(&sm.zs[rt][16 * rq]);
-            xd[0] = cr.x[0] & keep;
-            xd[1] = cr.x[1] & keep;
-            zd[0] = cr.z[0] & keepz;
-            zd[1] = cr.z[1] & keepz;
-            u32x4* bd = reinterpret_cast<u32x4*>(&sm.Bs[rt][(N / 4) * rq]);
-            u32x4* cd = reinterpret_cast<u32x4*>(&sm.Cs[rt][(N / 4) * rq]);
+        // ---- B: 2^cum C S over the wave's n-half; M tiles ------------------
+        // k-step ks pairs state tiles 2 ks and 2 ks + 1, whose rows
+        // 4 lg .. 4 lg + 3 this lane holds: the C operand takes columns
+        // nb0 + 32 ks + 4 lg .. + 3 and nb0 + 32 ks + 16 + 4 lg .. + 3
+        f32x4 Yacc[4];
 #pragma unroll
-            for (int q = 0; q < NBC; ++q) {
-                bd[q] = cr.b[q] & keep;
-                cd[q] = cr.c[q] & keep;
+        for (int tb = 0; tb < 4; ++tb) {
+            Yacc[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const uint16_t* crow = &sm.Cs[16 * tb + li][nb0 + 4 * lg];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 cv = cat(ld4(crow + 32 * ks), ld4(crow + 32 * ks + 16));
+                Yacc[tb] = mfma(cv, Sh[ks], Yacc[tb]);
+                Yacc[tb] = mfma(cv, Sl[ks], Yacc[tb]);
             }
-            if (c + 1 < nch) fetch(t0 + kQ, cr);
+            Yacc[tb] *= *reinterpret_cast<const f32x4*>(&sm.ecum[cb][16 * tb + 4 * lg]);
+        }
+        for (int k = wave; k < 10; k += kWaves) {
+            int tb, sb;
+            m_tile(k, tb, sb);
+            // M^T tile = B C^T: rows s = 16 sb + 4 lg + q, column t = 16 tb + li
+            f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks)
+                g = mfma(ld8(&sm.Bs[16 * sb + li][32 * ks + 8 * lg]), ld8(&sm.Cs[16 * tb + li][32 * ks + 8 * lg]), g);
+            const int t = 16 * tb + li, s0 = 16 * sb + 4 * lg;
+            const float ct = sm.cum[cb][t];
+            const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[cb][s0]);
+            const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dl[cb][s0]);
+            float m[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m[q] = (s0 + q <= t) ? g[q] * fast_exp2(ct - cs[q]) * ds[q] : 0.0f;
+            uint2 mh, ml;
+            split4(m, mh, ml);
+            *reinterpret_cast<uint2*>(&sm.Mh[t][s0]) = mh;
+            *reinterpret_cast<uint2*>(&sm.Ml[t][s0]) = ml;
         }
         lds_barrier();
 
-        f32x4 Yacc[4];
-        if (owner) {
-            // ---- B (owners): Y = 2^cum C S, the state from registers ----------
-            // k-step ks pairs state tiles 2 ks and 2 ks + 1, whose rows
-            // 4 lg .. 4 lg + 3 this lane holds: the C operand takes columns
-            // 32 ks + 4 lg .. + 3 and 32 ks + 16 + 4 lg .. + 3 in that order
+        // ---- C: M X for the wave's t-tiles, Y_half to LDS; weighted x; gate -
+        // n-half 0 takes t-tiles 0 and 3, n-half 1 t-tiles 1 and 2 (six
+        // MFMAs each: t-tiles 2 and 3 span both 32-token k-steps)
+        // (the t-tiles are compile-time constants in each branch, so Yacc
+        // stays in fixed registers)
+        auto mx = [&](auto tbc) {
+            constexpr int tb = decltype(tbc)::value;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                Yacc[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                const uint16_t* crow = &sm.Cs[16 * tb + li][4 * lg];
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 cv = cat(ld4(crow + 32 * ks), ld4(crow + 32 * ks + 16));
-                    Yacc[tb] = mfma(cv, Sh[ks], Yacc[tb]);
-                    Yacc[tb] = mfma(cv, Sl[ks], Yacc[tb]);
-                }
-                Yacc[tb] *= *reinterpret_cast<const f32x4*>(&sm.ecum[cb][16 * tb + 4 * lg]);
+            for (int ks = 0; ks <= (tb >> 1); ++ks) {
+                const bf16x8 xv = ld_col8(&sm.xs[0][0], kRowX, 32 * ks, 16 * pq, lane);
+                Yacc[tb] = mfma(ld8(&sm.Mh[16 * tb + li][32 * ks + 8 * lg]), xv, Yacc[tb]);
+                Yacc[tb] = mfma(ld8(&sm.Ml[16 * tb + li][32 * ks + 8 * lg]), xv, Yacc[tb]);
             }
-            // the next chunk's Delta inputs for the prefix wave
-            if (wave == 0 && c + 1 < nch) sm.dtraw[cb ^ 1][lane] = cr.dt;
-        } else if (wave < kOwners + 3) {
-            // ---- B (helpers): a causal 32 x 32 block of M ---------------------
-            // block (t, s) = (0, 0), (1, 0), (1, 1) as M^T = B C^T: lane
-            // column t = 32 tb + lane % 32, rows s = 32 sb + 8 r + 4 h + q
-            const int hw = wave - kOwners;
-            const int tb = hw == 0 ? 0 : 1, sb = hw == 2 ? 1 : 0;
-            const int l32 = lane & 31, h = lane >> 5;
-            f32x16 g = {};
+        };
+        if (nh == 0) {
+            mx(std::integral_constant<int, 0>{});
+            mx(std::integral_constant<int, 3>{});
+        } else {
+            mx(std::integral_constant<int, 1>{});
+            mx(std::integral_constant<int, 2>{});
+        }
 #pragma unroll
-            for (int kk = 0; kk < N / 16; ++kk)
-                g = mfma32(ld8(&sm.Bs[32 * sb + l32][16 * kk + 8 * h]), ld8(&sm.Cs[32 * tb + l32][16 * kk + 8 * h]), g);
-            const int t = 32 * tb + l32;
-            const float ct = sm.cum[cb][t];
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s0 = 32 * sb + 8 * r + 4 * h;
-                const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[cb][s0]);
-                const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dl[cb][s0]);
-                float m[4];
+            for (int q = 0; q < 4; ++q) sm.Y[nh][16 * tb + 4 * lg + q][pcol] = Yacc[tb][q];
+        {
+            const float wv = sm.wts[cb][rt];
+            const bf16x8 xv = ld8(&sm.xs[rt][8 * rq]);
+            const bf16x8 zv = ld8(&sm.zs[rt][8 * rq]);
+            bf16x8 xh, xl;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = (float)xv[j];
+                const float v = x * wv;
+                const __bf16 vh = (__bf16)v;
+                xh[j] = vh;
+                xl[j] = (__bf16)(v - (float)vh);
+                const float gz = Z ? silu_scaled((float)zv[j], 1.0f) : 1.0f;
+                eg[j] = gz;
+                edg[j] = Dh * x * gz;
+            }
+            *reinterpret_cast<bf16x8*>(&sm.Wh[rt][8 * rq]) = xh;
+            *reinterpret_cast<bf16x8*>(&sm.Wl[rt][8 * rq]) = xl;
+        }
+        // the next chunk's prefix (cr holds chunk c + 1)
+        if (wave == 4 && c + 1 < nch) prefix(t0 + kQ, cr.dt, cb ^ 1);
+        lds_barrier();
+
+        // ---- D: y of the thread's 8 outputs; the state update --------------
+        {
+            float yv[8];
+#pragma unroll
+            for (int j4 = 0; j4 < 2; ++j4) {
+                const f32x4 y0 = *reinterpret_cast<const f32x4*>(&sm.Y[0][rt][8 * rq + 4 * j4]);
+                const f32x4 y1 = *reinterpret_cast<const f32x4*>(&sm.Y[1][rt][8 * rq + 4 * j4]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    m[q] = (s0 + q <= t) ? g[4 * r + q] * fast_exp2(ct - cs[q]) * ds[q] : 0.0f;
-                uint2 mh, ml;
-                split4(m, mh, ml);
-                *reinterpret_cast<uint2*>(&sm.Mh[t][s0]) = mh;
-                *reinterpret_cast<uint2*>(&sm.Ml[t][s0]) = ml;
+                    yv[4 * j4 + q] = __builtin_fmaf(y0[q] + y1[q], eg[4 * j4 + q], edg[4 * j4 + q]);
+            }
+            const int64_t rows = L - t0 < kQ ? L - t0 : kQ;
+            const auto ry = rows_rsrc(Yg + ((b * L + t0) * H + h) * kPd, rows, sy, kPd * (int)sizeof(Tout));
+            const int yo = (int)(rt * sy) + 8 * rq * (int)sizeof(Tout);
+            if constexpr (sizeof(Tout) == 4) {
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(yv[0]), __float_as_uint(yv[1]),
+                                                             __float_as_uint(yv[2]), __float_as_uint(yv[3])},
+                                                       ry, yo, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(yv[4]), __float_as_uint(yv[5]),
+                                                             __float_as_uint(yv[6]), __float_as_uint(yv[7])},
+                                                       ry, yo + 16, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]),
+                                                             pack_bf16x2(yv[4], yv[5]), pack_bf16x2(yv[6], yv[7])},
+                                                       ry, yo, 0, 0);
             }
         }
-        lds_barrier();
-
-        if (owner) {
-            // ---- C (owners): Y += M X over the causal k-steps; Y to LDS -------
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-                for (int ks = 0; ks <= (tb >> 1); ++ks) {
-                    const bf16x8 xv = ld_col8(&sm.xs[0][0], kRowX, 32 * ks, 16 * wave, lane);
-                    Yacc[tb] = mfma(ld8(&sm.Mh[16 * tb + li][32 * ks + 8 * lg]), xv, Yacc[tb]);
-                    Yacc[tb] = mfma(ld8(&sm.Ml[16 * tb + li][32 * ks + 8 * lg]), xv, Yacc[tb]);
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) sm.Y[16 * tb + 4 * lg + q][pcol] = Yacc[tb][q];
-            }
-        } else {
-            // ---- C (helpers): weighted x; the gate of the thread's outputs ----
-            const float wv = sm.wts[cb][et];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const bf16x8 xv = ld8(&sm.xs[et][ep0 + 8 * half]);
-                const bf16x8 zv = ld8(&sm.zs[et][ep0 + 8 * half]);
-                bf16x8 xh, xl;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float x = (float)xv[j];
-                    const float v = x * wv;
-                    const __bf16 vh = (__bf16)v;
-                    xh[j] = vh;
-                    xl[j] = (__bf16)(v - (float)vh);
-                    const float gz = Z ? silu_scaled((float)zv[j], 1.0f) : 1.0f;
-                    eg[8 * half + j] = gz;
-                    edg[8 * half + j] = Dh * x * gz;
-                }
-                *reinterpret_cast<bf16x8*>(&sm.Wh[et][ep0 + 8 * half]) = xh;
-                *reinterpret_cast<bf16x8*>(&sm.Wl[et][ep0 + 8 * half]) = xl;
-            }
-            if (wave == kOwners && c + 1 < nch) prefix(t0 + kQ, cb ^ 1);
-        }
-        lds_barrier();
-
-        if (!owner) {
-            // ---- D (helpers): y = Y silu(z) + D x silu(z), stored --------------
-            if (t0 + et < L) {
-                float yv[16];
-#pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const f32x4 yy = *reinterpret_cast<const f32x4*>(&sm.Y[et][ep0 + 4 * j4]);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) yv[4 * j4 + q] = __builtin_fmaf(yy[q], eg[4 * j4 + q], edg[4 * j4 + q]);
-                }
-                Tout* dst = Yg + ((b * L + t0 + et) * H + h) * kPd + ep0;
-                if constexpr (sizeof(Tout) == 4) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        reinterpret_cast<float4*>(dst)[q] =
-                            make_float4(yv[4 * q], yv[4 * q + 1], yv[4 * q + 2], yv[4 * q + 3]);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        reinterpret_cast<uint4*>(dst)[q] =
-                            make_uint4(pack_bf16x2(yv[8 * q], yv[8 * q + 1]), pack_bf16x2(yv[8 * q + 2], yv[8 * q + 3]),
-                                       pack_bf16x2(yv[8 * q + 4], yv[8 * q + 5]),
-                                       pack_bf16x2(yv[8 * q + 6], yv[8 * q + 7]));
-                }
-            }
-        } else {
-            // ---- D (owners): S = 2^cum_last S + B^T (w X) ---------------------
+        {
             const float dec = sm.ecum[cb][kQ - 1];
-            bf16x8 wh[2], wl[2];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) S[j] *= dec;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                wh[ks] = ld_col8(&sm.Wh[0][0], kRowX, 32 * ks, 16 * wave, lane);
-                wl[ks] = ld_col8(&sm.Wl[0][0], kRowX, 32 * ks, 16 * wave, lane);
-            }
+                const bf16x8 wh = ld_col8(&sm.Wh[0][0], kRowX, 32 * ks, 16 * pq, lane);
+                const bf16x8 wl = ld_col8(&sm.Wl[0][0], kRowX, 32 * ks, 16 * pq, lane);
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                S[j] *= dec;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    // B^T operand: row n = 16 j + li, k = s
-                    const bf16x8 bt = ld_col8(&sm.Bs[0][0], kRowN, 32 * ks, 16 * j, lane);
-                    S[j] = mfma(bt, wh[ks], S[j]);
-                    S[j] = mfma(bt, wl[ks], S[j]);
+                for (int j = 0; j < NT; ++j) {
+                    // B^T operand: row n = nb0 + 16 j + li, k = s
+                    const bf16x8 bt = ld_col8(&sm.Bs[0][0], kRowN, 32 * ks, nb0 + 16 * j, lane);
+                    S[j] = mfma(bt, wh, S[j]);
+                    S[j] = mfma(bt, wl, S[j]);
                 }
             }
             split_state();
         }
         lds_barrier();
+
+        // ---- A: stage the next chunk; request the one after ----------------
+        stage(cr);
+        fetch(t0 + 2 * kQ, cr);
+        lds_barrier();
     }
 
-    if (a.last && owner) {
+    if (a.last) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) a.last[(bh * kPd + pcol) * N + 16 * j + 4 * lg + q] = S[j][q];
+            for (int q = 0; q < 4; ++q) a.last[(bh * kPd + pcol) * N + nb0 + 16 * j + 4 * lg + q] = S[j][q];
     }
 }
 
@@ -448,8 +467,12 @@ hipError_t launch_n(const M2Args& a, hipStream_t stream) {
 
 }  // namespace
 
+// The buffer descriptors hold 32-bit byte counts and offsets: one chunk of
+// 64 tokens of x or y (or of B) must span less than 2 GB.
 bool m2_ssd_supported(const M2Args& a, int in_bf16) {
-    return in_bf16 && a.P == kPd && (a.N == 64 || a.N == 128) && a.batch * a.H < 0x7fffffff;
+    const int64_t chunk_x = kQ * a.H * a.P * 4, chunk_b = kQ * a.G * a.N * 2;
+    return in_bf16 && a.P == kPd && (a.N == 64 || a.N == 128) && a.batch * a.H < 0x7fffffff &&
+           chunk_x < (int64_t(1) << 31) && chunk_b < (int64_t(1) << 31);
 }
 
 hipError_t launch_m2_ssd(const M2Args& a, int out_bf16, hipStream_t stream) {
