@@ -131,3 +131,33 @@ def test_full_size_workload_sampled(gpu):
     for i, (b, h) in enumerate(units):
         check_close(host(y[b, :, h]).double().numpy(), yr[i], TOL_BF16, f"y unit {(b, h)}")
         check_close(host(last[b, h]).double().numpy(), lr[i], TOL_BF16, f"last unit {(b, h)}")
+
+
+@pytest.mark.parametrize("case", ["h0_n128_g2", "h0_n128_g2_bf16_out", "h0_single_token", "no_softplus",
+                                  "group_per_head", "ragged_many_heads"])
+def test_chunked_mfma_form_edge_cases(gpu, case):
+    """The chunked matrix form (bf16 inputs, headdim 64, N 64 or 128) on an
+    initial state, a single token, softplus off, one group per head and a
+    ragged length over several batches and heads, against the oracle."""
+    N = 64 if case in ("group_per_head", "h0_single_token") else 128
+    L = {"h0_single_token": 1, "ragged_many_heads": 197}.get(case, 333)
+    batch, H, G = (3, 6, 3) if case == "ragged_many_heads" else (2, 4, 4 if case == "group_per_head" else 2)
+    inp = _inputs(batch, L, H, 64, G, N, torch.bfloat16, seed=len(case))
+    softplus = case != "no_softplus"
+    if not softplus:
+        # Delta = dt + dt_bias must stay positive without softplus
+        inp["dt"] = (inp["dt"].float().abs() * 0.05).to(torch.bfloat16)
+        inp["dt_bias"] = inp["dt_bias"].abs() * 0.01
+    h0 = None
+    if case.startswith("h0"):
+        g = torch.Generator(device=DEV).manual_seed(len(case))
+        h0 = torch.randn((batch, H, 64, N), generator=g, device=DEV)
+    out_dtype = torch.bfloat16 if case.endswith("bf16_out") else None
+    y, last = ss.mamba2_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                            inp["dt_bias"], softplus=softplus, out_dtype=out_dtype, h0=h0)
+    torch.cuda.synchronize()
+    yr, lr = oracle.m2(host(inp["x"]), host(inp["dt"]), host(inp["A"]), host(inp["B"]), host(inp["C"]),
+                       host(inp["D"]), host(inp["z"]), host(inp["dt_bias"]), softplus=softplus,
+                       h0=None if h0 is None else host(h0))
+    check_close(host(y).double().numpy(), yr, tol_out_bf16(TOL_BF16) if out_dtype else TOL_BF16, "y")
+    check_close(host(last).double().numpy(), lr, TOL_BF16, "last_state")
