@@ -130,6 +130,7 @@ struct StepArgs {
     int64_t H, P, G;          // Mamba-2
     int N;
     int softplus;
+    int vec;                  // A (16 bytes), B and C (4 elements) aligned for vector loads
 };
 hipError_t launch_step(const StepArgs& a, int in_bf16, int out_bf16, int mamba2, hipStream_t stream);
 

@@ -426,6 +426,8 @@ selscan_status_t selscan_step(const selscan_shape_t* s, float* state, const void
         a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
         a.y = y; a.state = state;
         a.batch = s->batch; a.dim = s->dim; a.N = (int)s->dstate; a.softplus = softplus;
+        const uintptr_t v4 = s->in_dtype == SELSCAN_BF16 ? 8 : 16;   // bytes of 4 input elements
+        a.vec = aligned16(A) && (reinterpret_cast<uintptr_t>(B) % v4) == 0 && (reinterpret_cast<uintptr_t>(C) % v4) == 0;
         hipError_t e = selscan::launch_step(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, 0,
                                             reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -503,6 +505,8 @@ selscan_status_t selscan_mamba2_step(const selscan_m2_shape_t* s, float* state, 
         a.y = y; a.state = state;
         a.batch = s->batch; a.H = s->nheads; a.P = s->headdim; a.G = s->ngroups; a.N = (int)s->dstate;
         a.softplus = softplus;
+        const uintptr_t v4 = s->in_dtype == SELSCAN_BF16 ? 8 : 16;   // bytes of 4 input elements
+        a.vec = (reinterpret_cast<uintptr_t>(B) % v4) == 0 && (reinterpret_cast<uintptr_t>(C) % v4) == 0;
         hipError_t e = selscan::launch_step(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, 1,
                                             reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));

@@ -11,8 +11,9 @@
 //
 // This pass reads and writes the whole state once per token, so it is bound
 // by HBM bandwidth on the state; each thread owns four consecutive states
-// (one 16-byte access), the lanes of a row reduce y with cross-lane shuffles
-// (state sizes that are not a multiple of 4: one thread per row).
+// (one 16-byte access) and reads their A, B and C as one vector each when
+// aligned, and the lanes of a row reduce y with cross-lane shuffles (state
+// sizes that are not a multiple of 4: one thread per row).
 #include "device_math.hpp"
 #include "kernels.hpp"
 
@@ -28,6 +29,17 @@ template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p, in
 template <typename T> __device__ __forceinline__ void st1(T* p, int64_t i, float v);
 template <> __device__ __forceinline__ void st1<float>(float* p, int64_t i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void st1<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+// Four consecutive elements (16-byte aligned for fp32, 8-byte for bf16).
+template <typename T> __device__ __forceinline__ void ld4(const T* p, float v[4]);
+template <> __device__ __forceinline__ void ld4<float>(const float* p, float v[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+template <> __device__ __forceinline__ void ld4<uint16_t>(const uint16_t* p, float v[4]) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
+}
 
 template <bool SP>
 __device__ __forceinline__ float delta_log2(float dl, float bias) {
@@ -69,12 +81,23 @@ __global__ __launch_bounds__(256) void m1_step_kernel(StepArgs a) {
     float4* st = reinterpret_cast<float4*>(a.state + row * N) + qi;
     float4 h = *st;
     float* hv = reinterpret_cast<float*>(&h);
+    float Av[4], Bv[4], Cv[4];
+    if (a.vec) {
+        ld4(a.A + d * N + 4 * qi, Av);
+        ld4(Bm + b * N + 4 * qi, Bv);
+        ld4(Cm + b * N + 4 * qi, Cv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Av[i] = a.A[d * N + 4 * qi + i];
+            Bv[i] = ld1(Bm, b * N + 4 * qi + i);
+            Cv[i] = ld1(Cm, b * N + 4 * qi + i);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int n = 4 * qi + i;
-        const float dA = fast_exp2(w * a.A[d * N + n]);
-        hv[i] = __builtin_fmaf(dA, hv[i], x * ld1(Bm, b * N + n));
-        acc = __builtin_fmaf(ld1(Cm, b * N + n), hv[i], acc);
+        hv[i] = __builtin_fmaf(fast_exp2(w * Av[i]), hv[i], x * Bv[i]);
+        acc = __builtin_fmaf(Cv[i], hv[i], acc);
     }
     acc = group_sum<Q>(acc);
     if (!ok) return;
@@ -139,11 +162,21 @@ __global__ __launch_bounds__(256) void m2_step_kernel(StepArgs a) {
     float4* st = reinterpret_cast<float4*>(a.state + row * N) + qi;
     float4 s = *st;
     float* sv = reinterpret_cast<float*>(&s);
+    float Bv[4], Cv[4];
+    if (a.vec) {
+        ld4(Bm + 4 * qi, Bv);
+        ld4(Cm + 4 * qi, Cv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Bv[i] = ld1(Bm, 4 * qi + i);
+            Cv[i] = ld1(Cm, 4 * qi + i);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int n = 4 * qi + i;
-        sv[i] = __builtin_fmaf(dA, sv[i], x * ld1(Bm, n));
-        acc = __builtin_fmaf(ld1(Cm, n), sv[i], acc);
+        sv[i] = __builtin_fmaf(dA, sv[i], x * Bv[i]);
+        acc = __builtin_fmaf(Cv[i], sv[i], acc);
     }
     acc = group_sum<Q>(acc);
     if (!ok) return;

@@ -159,3 +159,37 @@ def test_step_does_not_touch_other_rows(gpu):
     assert state.is_contiguous()
     _m1_steps(inp, state, T)
     assert torch.equal(host(big[:, 5]), torch.full((1, 16), 7.0))
+
+
+@pytest.mark.parametrize("mamba2", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_step_with_unaligned_b_c(gpu, mamba2, dtype):
+    """B and C starting one element past an aligned address take the
+    element-wise loads of the step kernels and give the same result."""
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    if mamba2:
+        inp = synth.m2_inputs(2, 1, 4, 16, 2, 64, dtype, seed=95, device=DEV)
+        sl = lambda k: inp[k][:, 0].contiguous()
+        args = lambda B, C: (sl("x"), sl("dt"), inp["A"], B, C, inp["D"], sl("z"), inp["dt_bias"])
+        run = lambda st, B, C: ss.mamba2_step(st, *args(B, C))
+        h0 = _h0((2, 4, 16, 64), 11)
+    else:
+        inp = synth.m1_inputs(2, 48, 16, 1, dtype, "s4d_jitter", seed=96, device=DEV)
+        sl = lambda k: inp[k][..., 0].contiguous()
+        args = lambda B, C: (sl("u"), sl("delta"), inp["A"], B, C, inp["D"], sl("z"), inp["delta_bias"])
+        run = lambda st, B, C: ss.step(st, *args(B, C))
+        h0 = _h0((2, 48, 16), 12)
+    B, C = sl("B"), sl("C")
+    Bs, Cs = shifted(B), shifted(C)
+    assert Bs.data_ptr() % 8 != 0 and Cs.data_ptr() % 8 != 0
+    s_al, s_un = h0.clone(), h0.clone()
+    y_al = run(s_al, B, C)
+    y_un = run(s_un, Bs, Cs)
+    torch.cuda.synchronize()
+    assert torch.equal(y_al, y_un)
+    assert torch.equal(s_al, s_un)
