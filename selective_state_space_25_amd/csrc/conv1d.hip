@@ -56,14 +56,18 @@ template <> struct Vec<float> {
 
 __device__ __forceinline__ float act(float v, bool silu) { return silu ? silu_scaled(v, 1.0f) : v; }
 
-// K <= 8: the halo fits in the previous eight tokens.
+constexpr int kConvThreads = 256;
+
+// K <= 8: the halo fits in the previous eight tokens.  Each row gets whole
+// workgroups (`bpr` of them), so the row and channel of a workgroup come
+// from one scalar division instead of per-thread 64-bit ones.
 template <typename Tin, typename Tout, int K, bool SILU>
-__global__ __launch_bounds__(256) void conv_vec_kernel(ConvArgs a) {
+__global__ __launch_bounds__(kConvThreads) void conv_vec_kernel(ConvArgs a, uint32_t bpr) {
     const int64_t groups = a.L / kV;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= a.batch * a.dim * groups) return;
-    const int64_t row = gid / groups;
-    const int64_t g = gid - row * groups;
+    const uint32_t blk = blockIdx.x;
+    const int64_t row = blk / bpr;
+    const int64_t g = (int64_t)(blk - (uint32_t)row * bpr) * kConvThreads + threadIdx.x;
+    if (g >= groups) return;
     const int64_t d = row % a.dim;
     const Tin* x = reinterpret_cast<const Tin*>(a.x) + row * a.L + g * kV;
     float cur[kV], prev[kV];
@@ -112,13 +116,14 @@ __global__ __launch_bounds__(256) void conv_tok_kernel(ConvArgs a) {
 template <typename Tin, typename Tout, bool SILU>
 hipError_t launch_silu(const ConvArgs& a, hipStream_t stream) {
     KTime kt("conv1d", stream);
-    if (a.vec_ok && a.K >= 1 && a.K <= kV) {
-        const int64_t threads = a.batch * a.dim * (a.L / kV);
-        const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const int64_t bpr = (a.L / kV + kConvThreads - 1) / kConvThreads;   // workgroups per row
+    if (a.vec_ok && a.K >= 1 && a.K <= kV && a.batch * a.dim * bpr < 0x7fffffff) {
+        const unsigned blocks = (unsigned)(a.batch * a.dim * bpr);
         switch (a.K) {
-#define SELSCAN_CONV_K(KK)                                                                                      \
-    case KK:                                                                                                    \
-        hipLaunchKernelGGL((conv_vec_kernel<Tin, Tout, KK, SILU>), dim3(blocks), dim3(256), 0, stream, a); \
+#define SELSCAN_CONV_K(KK)                                                                                          \
+    case KK:                                                                                                        \
+        hipLaunchKernelGGL((conv_vec_kernel<Tin, Tout, KK, SILU>), dim3(blocks), dim3(kConvThreads), 0, stream, a, \
+                           (uint32_t)bpr);                                                                          \
         break;
             SELSCAN_CONV_K(1) SELSCAN_CONV_K(2) SELSCAN_CONV_K(3) SELSCAN_CONV_K(4)
             SELSCAN_CONV_K(5) SELSCAN_CONV_K(6) SELSCAN_CONV_K(7) SELSCAN_CONV_K(8)

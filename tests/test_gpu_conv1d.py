@@ -38,7 +38,7 @@ def test_widths_and_dtypes(gpu, K, dtype):
     _check(x, w, b, silu=True)
 
 
-@pytest.mark.parametrize("L", [1, 3, 7, 8, 9, 64, 1001])
+@pytest.mark.parametrize("L", [1, 3, 7, 8, 9, 40, 64, 1001, 4104])
 def test_lengths_and_ragged_rows(gpu, L):
     x, w, b = _inputs(2, 33, L, 4, torch.bfloat16, seed=L)
     _check(x, w, b, silu=True)
