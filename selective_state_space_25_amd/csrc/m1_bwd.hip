@@ -138,6 +138,8 @@ struct Con {
     int l, w, rr, q, r, rc;   // rc: r clamped below the block's rows
     bool ok;                  // channel < dim
     float Al2[4];             // A[n] log2(e), 0 for padded states
+    float A0l2;               // A[0] log2(e) of the channel
+    bool st;                  // the lane's A[n] == fl32((n + 1) A[0]) and all 16 states real
     __device__ Con(const BwdArgs& a, const Blk& k) {
         const int tid = threadIdx.x;
         l = tid & 63;
@@ -148,13 +150,44 @@ struct Con {
         ok = r < k.rows;
         rc = ok ? r : k.rows - 1;
         const float* Ab = a.A + k.cb * kCh * a.N;
+        const float A0 = Ab[rc * a.N];
+        A0l2 = A0 * kLog2e;
+        st = a.N == kSt;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int n = 4 * q + i;
-            Al2[i] = (n < a.N ? Ab[rc * a.N + n] : 0.0f) * kLog2e;
+            const float An = n < a.N ? Ab[rc * a.N + n] : 0.0f;
+            Al2[i] = An * kLog2e;
+            st = st && An == (float)(n + 1) * A0;
         }
     }
 };
+
+// exp(Delta A[n]) of the lane's 4 states, dt = Delta.  With a structured A
+// (A[n] = (n + 1) A[0] in every lane of the workgroup) they are consecutive
+// powers r^(4q+1) .. r^(4q+4) of r = exp(Delta A[0]): two exponentials and
+// three multiplies instead of four exponentials.
+template <bool ST>
+__device__ __forceinline__ void decay4(const Con& c, float dt, float at[4]) {
+    if constexpr (ST) {
+        const float r = fast_exp2(dt * c.A0l2);
+        at[0] = fast_exp2(dt * c.Al2[0]);
+        at[1] = at[0] * r;
+        at[2] = at[1] * r;
+        at[3] = at[2] * r;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) at[i] = fast_exp2(dt * c.Al2[i]);
+    }
+}
+
+// True in every thread when every channel of the workgroup has a structured A
+// (a workgroup-wide vote: all threads must call it).
+__device__ __forceinline__ bool structured_block(const BwdArgs& a) {
+    const Blk k = blk(a);
+    const Con c(a, k);
+    return __syncthreads_and(c.st ? 1 : 0) != 0;
+}
 
 // Producer view: channel pr, tokens pj, pj + 1 of each tile.
 struct Pro {
@@ -244,10 +277,8 @@ struct SumSmem {
 // Per chunk, from zero: state every 8 tokens and at the end, running sum of
 // Delta; and (when the sequence has several chunks) the adjoint leaving the
 // chunk's first token, a_{t0} lam_{t0}, from a zero right boundary.
-template <typename Tin, typename Tout, bool SP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void m1_bwd_summary_kernel(BwdArgs a) {
-    __shared__ SumSmem sm;
+template <typename Tin, typename Tout, bool SP, bool ST>
+__device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
     const Blk k = blk(a);
     const Con c(a, k);
     const Pro p(a, k);
@@ -289,8 +320,10 @@ void m1_bwd_summary_kernel(BwdArgs a) {
             const float4 Bv = *reinterpret_cast<const float4*>(&sm.bc[j][4 * c.q]);
             const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
             W += dt;
+            float at[4];
+            decay4<ST>(c, dt, at);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) h[i] = __builtin_fmaf(fast_exp2(dt * c.Al2[i]), h[i], dtu * bb[i]);
+            for (int i = 0; i < 4; ++i) h[i] = __builtin_fmaf(at[i], h[i], dtu * bb[i]);
         }
         lds_barrier();
     }
@@ -330,12 +363,24 @@ void m1_bwd_summary_kernel(BwdArgs a) {
             const float dt = sm.dt[c.r][j], dy = sm.x2[c.r][j];
             const float4 Cv = *reinterpret_cast<const float4*>(&sm.bc[j][4 * c.q]);
             const float cc[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
+            float at[4];
+            decay4<ST>(c, dt, at);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mu[i] = fast_exp2(dt * c.Al2[i]) * __builtin_fmaf(dy, cc[i], mu[i]);
+            for (int i = 0; i < 4; ++i) mu[i] = at[i] * __builtin_fmaf(dy, cc[i], mu[i]);
         }
         lds_barrier();
     }
     if (c.ok) *reinterpret_cast<float4*>(a.mubuf + k.row0 * G * kSt + cell) = make_float4(mu[0], mu[1], mu[2], mu[3]);
+}
+
+template <typename Tin, typename Tout, bool SP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void m1_bwd_summary_kernel(BwdArgs a) {
+    __shared__ SumSmem sm;
+    if (structured_block(a))
+        summary_body<Tin, Tout, SP, true>(a, sm);
+    else
+        summary_body<Tin, Tout, SP, false>(a, sm);
 }
 
 // Per (row, n): the true state entering each chunk and the true adjoint
@@ -400,10 +445,8 @@ __device__ __forceinline__ float reduce_bc(const float* v, int rr) {
     return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
 }
 
-template <typename Tin, typename Tout, bool SP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
-void m1_bwd_chunk_kernel(BwdArgs a) {
-    __shared__ ChunkSmem sm;
+template <typename Tin, typename Tout, bool SP, bool ST>
+__device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
     const Blk k = blk(a);
     const Con c(a, k);
     const Pro p(a, k);
@@ -517,9 +560,11 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
                 const float dt = sm.dt[c.r][j], dtu = sm.dtu[c.r][j];
                 const float4 Bv = *reinterpret_cast<const float4*>(&sm.B[j][4 * c.q]);
                 const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+                float at[4];
+                decay4<ST>(c, dt, at);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    h[i] = __builtin_fmaf(fast_exp2(dt * c.Al2[i]), h[i], dtu * bb[i]);
+                    h[i] = __builtin_fmaf(at[i], h[i], dtu * bb[i]);
                     hs[j][i] = h[i];
                 }
             }
@@ -534,10 +579,12 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
             const float cc[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
             float sLB = 0.0f, sLAq = 0.0f, sCh = 0.0f;
             float v[8];
+            float ats[4];
+            decay4<ST>(c, dt, ats);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float hp = j > 0 ? hs[j - 1][i] : ck[i];
-                const float at = fast_exp2(dt * c.Al2[i]);
+                const float at = ats[i];
                 const float lam = __builtin_fmaf(dy, cc[i], lamn[i]);
                 const float tq = lam * at * hp;
                 sLB = __builtin_fmaf(lam, bb[i], sLB);
@@ -615,6 +662,16 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
         (a.pD + k.row0 * G)[pg] = dD_acc;
         (a.pbias + k.row0 * G)[pg] = dbias_acc;
     }
+}
+
+template <typename Tin, typename Tout, bool SP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void m1_bwd_chunk_kernel(BwdArgs a) {
+    __shared__ ChunkSmem sm;
+    if (structured_block(a))
+        chunk_body<Tin, Tout, SP, true>(a, sm);
+    else
+        chunk_body<Tin, Tout, SP, false>(a, sm);
 }
 
 // dB, dC: sums of the channel-block partials; thread = (token, value) of 8
