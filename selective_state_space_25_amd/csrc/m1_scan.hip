@@ -219,14 +219,18 @@ __device__ __forceinline__ void load_bc(float* dst, cfptr p) {
 // tile's can land while the last block of this one still reads its own.  `lds_base` is the LDS byte address of the
 // image.  The instruction offset moves both the global and the LDS address,
 // so M0 is set 16 p bytes short of piece p's slot.
+// (The instruction's immediate offset is 13-bit signed: larger offsets would
+// wrap silently, so they are kept below 4096.)
 template <int P>
 __device__ __forceinline__ void dma_piece(const void* g, uint32_t slot) {
+    static_assert(16 * P < 4096, "immediate offset out of range");
     __builtin_amdgcn_global_load_lds(g, (ldsptr)(uintptr_t)(slot - 16 * P), 16, 16 * P, 0);
 }
 
 // 16 bytes per lane from g + OFF into LDS at slot + 16 * lane.
 template <int OFF>
 __device__ __forceinline__ void dma_at(const void* g, uint32_t slot) {
+    static_assert(OFF >= 0 && OFF < 4096, "immediate offset out of range");
     __builtin_amdgcn_global_load_lds(g, (ldsptr)(uintptr_t)(slot - OFF), 16, OFF, 0);
 }
 
