@@ -428,11 +428,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 state and out" if w.dtype == torch.bfloat16 else "f32",
+        # the arithmetic of the path: every update, exponential and sum in fp32
+        "dtype": "f32",
         "data": "synthetic (seeded; distributions of the workload definitions)",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dstate": w.dstate,
                    **({"dim": w.dim} if w.kind == "m1" else {"nheads": w.nheads, "headdim": w.headdim,
                                                              "ngroups": w.ngroups}),
+                   "inputs": str(w.dtype).replace("torch.", ""), "state": "float32",
+                   "output": str(w.out_dtype).replace("torch.", ""),
                    "parallelism": "single GPU"},
         "hbm_gbs": head["hbm_gbs"],
         "hbm_frac_of_peak": head["hbm_frac_of_peak"],
