@@ -268,10 +268,12 @@ __device__ __forceinline__ bool bc_valid(const BwdArgs& a, const Blk& k, int tt0
     return n < a.N && tt0 + j < k.t_end;
 }
 
+// Tile values by tile parity: the producers fill one copy while the
+// consumers may still read the other, so each tile needs one barrier.
 struct SumSmem {
-    float dt[kCh][kPad];
-    float x2[kCh][kPad];     // Delta u (forward) or dy (reverse)
-    float bc[kT][kSt];       // B (forward) or C (reverse)
+    float dt[2][kCh][kPad];
+    float x2[2][kCh][kPad];  // Delta u (forward) or dy (reverse)
+    float bc[2][kT][kSt];    // B (forward) or C (reverse)
 };
 
 // Per chunk, from zero: state every 8 tokens and at the end, running sum of
@@ -297,15 +299,16 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
     fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, in, k.t0, r);
     for (int tile = 0; tile < k.tiles; ++tile) {
         const int tt0 = k.t0 + tile * kT;
+        const int pb = tile & 1;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             float dd;
             const float dt = delta_of<SP>(f32_of(r.x[jj]) + p.bias, dd);
             const bool ok = p.ok && tt0 + p.pj + jj < k.t_end;
-            sm.dt[p.pr][p.pj + jj] = ok ? dt : 0.0f;
-            sm.x2[p.pr][p.pj + jj] = ok ? dt * f32_of(r.u[jj]) : 0.0f;
+            sm.dt[pb][p.pr][p.pj + jj] = ok ? dt : 0.0f;
+            sm.x2[pb][p.pr][p.pj + jj] = ok ? dt * f32_of(r.u[jj]) : 0.0f;
         }
-        if (bc_thread) sm.bc[bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.bv) : 0.0f;
+        if (bc_thread) sm.bc[pb][bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.bv) : 0.0f;
         if (c.ok) {
             const uint32_t ct = ckrow + (uint32_t)(tile0 + tile);
             sto(reinterpret_cast<float4*>(ckz), ct * 4 + c.q, make_float4(h[0], h[1], h[2], h[3]));
@@ -316,8 +319,8 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
         fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, in, k.t0 + min(tile + 1, k.tiles - 1) * kT, r);
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
-            const float dt = sm.dt[c.r][j], dtu = sm.x2[c.r][j];
-            const float4 Bv = *reinterpret_cast<const float4*>(&sm.bc[j][4 * c.q]);
+            const float dt = sm.dt[pb][c.r][j], dtu = sm.x2[pb][c.r][j];
+            const float4 Bv = *reinterpret_cast<const float4*>(&sm.bc[pb][j][4 * c.q]);
             const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
             W += dt;
             float at[4];
@@ -325,7 +328,9 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) h[i] = __builtin_fmaf(at[i], h[i], dtu * bb[i]);
         }
-        lds_barrier();
+        // no barrier: the next tile's values go to the other copy, and the
+        // one after it is written only past the next tile's barrier, which
+        // every thread reaches after reading this copy
     }
     const int G = (int)a.G;
     const uint32_t cg = (uint32_t)c.rc * (uint32_t)G + (uint32_t)k.g;
@@ -339,8 +344,11 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
 
     float mu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, in, k.t0 + (k.tiles - 1) * kT, r);
+    // every thread is past its reads of the forward sweep's last tile
+    lds_barrier();
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
         const int tt0 = k.t0 + tile * kT;
+        const int pb = tile & 1;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             float dd;
@@ -352,23 +360,22 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
                 const float zz = f32_of(r.z[jj]);
                 dy = g * zz * sigmoid(zz);
             }
-            sm.dt[p.pr][p.pj + jj] = ok ? dt : 0.0f;
-            sm.x2[p.pr][p.pj + jj] = ok ? dy : 0.0f;
+            sm.dt[pb][p.pr][p.pj + jj] = ok ? dt : 0.0f;
+            sm.x2[pb][p.pr][p.pj + jj] = ok ? dy : 0.0f;
         }
-        if (bc_thread) sm.bc[bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.cv) : 0.0f;
+        if (bc_thread) sm.bc[pb][bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.cv) : 0.0f;
         lds_barrier();
         fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, in, k.t0 + max(tile - 1, 0) * kT, r);
 #pragma unroll
         for (int j = kT - 1; j >= 0; --j) {
-            const float dt = sm.dt[c.r][j], dy = sm.x2[c.r][j];
-            const float4 Cv = *reinterpret_cast<const float4*>(&sm.bc[j][4 * c.q]);
+            const float dt = sm.dt[pb][c.r][j], dy = sm.x2[pb][c.r][j];
+            const float4 Cv = *reinterpret_cast<const float4*>(&sm.bc[pb][j][4 * c.q]);
             const float cc[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
             float at[4];
             decay4<ST>(c, dt, at);
 #pragma unroll
             for (int i = 0; i < 4; ++i) mu[i] = at[i] * __builtin_fmaf(dy, cc[i], mu[i]);
         }
-        lds_barrier();
     }
     if (c.ok) *reinterpret_cast<float4*>(a.mubuf + k.row0 * G * kSt + cell) = make_float4(mu[0], mu[1], mu[2], mu[3]);
 }

@@ -138,6 +138,20 @@ __device__ __forceinline__ float delta_log2(const Lane& L, float dl) {
 
 __device__ __forceinline__ bool s_in_range(float s) { return fabsf(s) >= kSigLo && fabsf(s) <= kSigHi; }
 
+// Every |s_j| of an 8-token block within [2^-60, 2^60], from the block's
+// smallest and largest |s| (min3/max3 trees rather than 16 compares).  A NaN
+// s_j can pass, since min and max drop a NaN operand; the fast update then
+// turns the state into NaN from that token on, as the plain recurrence does.
+__device__ __forceinline__ bool block_in_range(const float* s) {
+    float lo = fabsf(s[0]), hi = lo;
+#pragma unroll
+    for (int j = 1; j < kBlk; ++j) {
+        lo = fminf(lo, fabsf(s[j]));
+        hi = fmaxf(hi, fabsf(s[j]));
+    }
+    return lo >= kSigLo && hi <= kSigHi;
+}
+
 // Structured path, every lane's s in range.  Returns the read-out / ln2.
 template <int MODE>
 __device__ __forceinline__ float tok_fast(Lane& L, const float* bc, float w, float s, float uu) {
@@ -409,14 +423,12 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                         issue_bc<MODE>(bcb, t0 + kTile, bc_next);
                     }
                     float w[kBlk], sg[kBlk];
-                    bool ok = true;
 #pragma unroll
                     for (int j = 0; j < kBlk; ++j) {
                         w[j] = delta_log2<SP>(L, In<Tin>::get(cur.d, j));
                         sg[j] = w[j] * In<Tin>::get(cur.u, j);
-                        ok = ok && s_in_range(sg[j]);
                     }
-                    if (wave_all(ok)) {
+                    if (wave_all(block_in_range(sg))) {
 #pragma unroll
                         for (int j = 0; j < kBlk; ++j) {
                             const float* bc = bcl + (blk * kBlk + j) * RS;   // same address in every lane
