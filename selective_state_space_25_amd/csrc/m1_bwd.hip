@@ -273,7 +273,7 @@ __device__ __forceinline__ bool bc_valid(const BwdArgs& a, const Blk& k, int tt0
 struct SumSmem {
     float dt[2][kCh][kPad];
     float x2[2][kCh][kPad];  // Delta u (forward) or dy (reverse)
-    float bc[2][kT][kSt];    // B (forward) or C (reverse)
+    alignas(16) float bc[2][kT][kSt];   // B (forward) or C (reverse); read as float4
 };
 
 // Per chunk, from zero: state every 8 tokens and at the end, running sum of
@@ -419,7 +419,8 @@ __global__ __launch_bounds__(256) void m1_bwd_carry_kernel(BwdArgs a) {
 struct ChunkSmem {
     float dt[kCh][kPad], dtu[kCh][kPad], dy[kCh][kPad];   // read by the adjoint lanes
     float u[kCh][kPad], dd[kCh][kPad], zf[kCh][kPad];     // kept for the output pass
-    float B[kT][kSt], C[kT][kSt];
+    alignas(16) float B[kT][kSt];   // read as float4
+    alignas(16) float C[kT][kSt];
     float sLB[kCh][kPad], sLAq[kCh][kPad], sCh[kCh][kPad];
     float red[kWaves][kT][2 * kSt];                       // per wave: dB[16], dC[16] per token
 };

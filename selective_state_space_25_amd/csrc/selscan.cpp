@@ -235,8 +235,9 @@ BwdPlan plan_m1_bwd(const selscan_shape_t* s) {
     const int64_t nbc = (s->dim + selscan::m1_bwd_channels_per_block() - 1) / selscan::m1_bwd_channels_per_block();
     int64_t chunk = env_int("SELSCAN_BWD_CHUNK", 0);
     if (chunk <= 0) {
-        // the longest chunk that still gives every compute unit several
-        // workgroups (one 1024-thread workgroup is resident per unit)
+        // the longest chunk that still gives every compute unit eight
+        // workgroups of 64 channels (two to eight are resident per unit,
+        // depending on the pass)
         chunk = selscan::m1_bwd_max_chunk();
         const int64_t want = 8 * (int64_t)device_cus();
         while (chunk > 2 * tile && s->batch * nbc * ((s->seqlen + chunk - 1) / chunk) < want) chunk /= 2;
