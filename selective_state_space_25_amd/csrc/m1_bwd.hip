@@ -110,6 +110,28 @@ __device__ __forceinline__ void sto(T* base, uint32_t idx, T v) {
     *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + idx * (uint32_t)sizeof(T)) = v;
 }
 
+// Stores inside the tile loops go through a buffer descriptor spanning the
+// block's part of the output; a lane that must not store passes the span's
+// end as its offset, and the hardware drops out-of-range stores.  Every lane
+// thus issues the same stores with no branch around them: after a branch the
+// compiler cannot count the stores in flight and waits for all of them
+// before the next tile's prefetched loads are used.
+constexpr int kBufWord3 = 0x00020000;   // descriptor word 3: 32-bit data format, raw access
+struct Span {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t end;   // bytes; an offset here stores nothing
+    __device__ Span(const void* p, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufWord3)), end(bytes) {}
+    __device__ void st(bool ok, uint32_t byte_off, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)(ok ? byte_off : end), 0, 0);
+    }
+    __device__ void st4(bool ok, uint32_t byte_off, const float* v) const {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)(ok ? byte_off : end), 0, 0);
+    }
+};
+
 struct Blk {
     int64_t b, cb, g, row0;       // row0 = b dim + 64 cb
     int t0, t_end, tiles, rows;   // rows: channels of this block below dim
@@ -289,8 +311,9 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
     const int tile0 = k.t0 / kT;
     const bool bc_thread = tid < kT * kSt;
     const int bj = (tid >> 4) & (kT - 1), bn = tid & 15;
-    float* ckz = a.ckz + k.row0 * k.TL * kSt;
-    float* wck = a.wck + k.row0 * k.TL;
+    // the block's rows of the checkpoints (at most 64 rows x 2^19 tiles x 64 bytes)
+    const Span ckz(a.ckz + k.row0 * k.TL * kSt, (uint32_t)k.rows * (uint32_t)k.TL * (kSt * 4));
+    const Span wck(a.wck + k.row0 * k.TL, (uint32_t)k.rows * (uint32_t)k.TL * 4);
     const uint32_t ckrow = (uint32_t)c.rc * (uint32_t)k.TL;
 
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -309,14 +332,17 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
             sm.x2[pb][p.pr][p.pj + jj] = ok ? dt * f32_of(r.u[jj]) : 0.0f;
         }
         if (bc_thread) sm.bc[pb][bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.bv) : 0.0f;
-        if (c.ok) {
+        {
             const uint32_t ct = ckrow + (uint32_t)(tile0 + tile);
-            sto(reinterpret_cast<float4*>(ckz), ct * 4 + c.q, make_float4(h[0], h[1], h[2], h[3]));
-            if (c.q == 0) sto(wck, ct, W);
+            ckz.st4(c.ok, (ct * 4 + c.q) * 16, h);
+            wck.st(c.ok && c.q == 0, ct * 4, W);
         }
         lds_barrier();
         // unconditional (the last tile re-fetches itself): no branch around the loads
         fetch_raw<Tin, Tout, true, false, true, false>(a, k, p, in, k.t0 + min(tile + 1, k.tiles - 1) * kT, r);
+        // keeps the loads here, a tile ahead of their use (the compiler
+        // would otherwise sink them to the next tile, next to their use)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
             const float dt = sm.dt[pb][c.r][j], dtu = sm.x2[pb][c.r][j];
@@ -366,6 +392,7 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
         if (bc_thread) sm.bc[pb][bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.cv) : 0.0f;
         lds_barrier();
         fetch_raw<Tin, Tout, false, true, false, true>(a, k, p, in, k.t0 + max(tile - 1, 0) * kT, r);
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int j = kT - 1; j >= 0; --j) {
             const float dt = sm.dt[pb][c.r][j], dy = sm.x2[pb][c.r][j];
@@ -511,10 +538,24 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
     };
     fetch(k.tiles - 1);
 
-    float* du = a.du + k.row0 * a.L;
-    float* ddelta = a.ddelta + k.row0 * a.L;
-    float* dz = a.dz ? a.dz + k.row0 * a.L : nullptr;
-    float* part = a.part + (k.cb * a.batch + k.b) * a.L * (2 * kSt);
+    // the block's rows of du, ddelta, dz (at most 64 rows x 2^22 tokens x 4
+    // bytes) and its dB/dC partials; no dz: an empty span, nothing stored
+    const uint32_t row_bytes = (uint32_t)k.rows * (uint32_t)k.L * 4;
+    const Span du(a.du + k.row0 * a.L, row_bytes);
+    const Span ddelta(a.ddelta + k.row0 * a.L, row_bytes);
+    const Span dz(a.dz ? a.dz + k.row0 * a.L : a.du, a.dz ? row_bytes : 0);
+    const Span part(a.part + (k.cb * a.batch + k.b) * a.L * (2 * kSt), (uint32_t)k.L * (2 * kSt * 4));
+    // Stores that store nothing, in the number each tile issues after its
+    // prefetch: the first tile then finds the same memory operations in
+    // flight as every later one (prefetch, then stores), and the compiler's
+    // wait for the prefetch need not cover the previous tile's stores.
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        du.st(false, 0, 0.0f);
+        ddelta.st(false, 0, 0.0f);
+        dz.st(false, 0, 0.0f);
+    }
+    part.st(false, 0, 0.0f);
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
         const int tt0 = k.t0 + tile * kT;
         // per-channel tile values
@@ -621,27 +662,24 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
         for (int jj = 0; jj < 2; ++jj) {
             const int j = p.pj + jj;
             const int t = tt0 + j;
-            if (p.ok && t < k.t_end) {
-                const float sLB = sm.sLB[p.pr][j], sLAq = sm.sLAq[p.pr][j], sCh = sm.sCh[p.pr][j];
-                const float dt = sm.dt[p.pr][j], dy = sm.dy[p.pr][j], uu = sm.u[p.pr][j];
-                const uint32_t o = p.off + (uint32_t)t;
-                sto(du, o, __builtin_fmaf(dt, sLB, p.D * dy));
-                const float dx = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd[p.pr][j];
-                sto(ddelta, o, dx);
-                if (dz) sto(dz, o, __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j]);
-                dD_acc = __builtin_fmaf(dy, uu, dD_acc);
-                dbias_acc += dx;
-            }
+            const bool ok = p.ok && t < k.t_end;
+            const float sLB = sm.sLB[p.pr][j], sLAq = sm.sLAq[p.pr][j], sCh = sm.sCh[p.pr][j];
+            const float dt = sm.dt[p.pr][j], dy = sm.dy[p.pr][j], uu = sm.u[p.pr][j];
+            const uint32_t o = (p.off + (uint32_t)t) * 4;
+            du.st(ok, o, __builtin_fmaf(dt, sLB, p.D * dy));
+            const float dx = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd[p.pr][j];
+            ddelta.st(ok, o, dx);
+            dz.st(ok, o, __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j]);
+            dD_acc += ok ? dy * uu : 0.0f;
+            dbias_acc += ok ? dx : 0.0f;
         }
         {   // dB, dC partials of this channel block: thread = (token j, value v)
             const int j = tid >> 5, v = tid & 31;
             const int t = tt0 + j;
-            if (t < k.t_end) {
-                float s = 0.0f;
+            float s = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) s += sm.red[w][j][v];
-                sto(part, (uint32_t)t * (2 * kSt) + v, s);
-            }
+            for (int w = 0; w < kWaves; ++w) s += sm.red[w][j][v];
+            part.st(t < k.t_end, ((uint32_t)t * (2 * kSt) + v) * 4, s);
         }
         // No barrier needed before the next tile: a producer thread rewrites
         // only the entries it has just read itself, sm.B/C were last read
