@@ -60,7 +60,7 @@ typedef enum {
 /*
  * Mamba-1 problem description.
  *   batch  B >= 1, dim D >= 1 (channels, d_inner), dstate N in {1..16},
- *   seqlen L >= 1.
+ *   1 <= seqlen L <= 16777216 (2^24; UNSUPPORTED above).
  *   in_dtype : dtype of u, delta, z, B, C.
  *   out_dtype: dtype of y.
  *   workspace: optional device scratch of at least selscan_workspace_bytes()

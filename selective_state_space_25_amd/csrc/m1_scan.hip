@@ -17,8 +17,9 @@
 //
 // u, delta and z arrive in tiles of 32 tokens per row and tensor (64 bytes
 // of bf16 or 128 of fp32 per row), copied by the memory system straight
-// into LDS (global_load_lds_dwordx4: each lane fetches the 16-byte pieces of
-// its own row), and the tile's B/C records follow into one of two buffers.
+// into LDS (global_load_lds_dwordx4; one instruction takes 64 bytes of each
+// of 16 rows, so a row's part of the tile is a single request), and the
+// tile's B/C records follow into one of two buffers.
 // The next tile is requested as soon as the current one's last two 8-token
 // blocks are in registers, so its latency overlaps their arithmetic.  y
 // collects the tile's 32 tokens per lane in registers and leaves as one
@@ -227,19 +228,15 @@ __device__ __forceinline__ void load_bc(float* dst, cfptr p) {
     for (int e = 0; e < n; ++e) dst[e] = p[e];
 }
 
-// LDS image of one 32-token tile: [tensor][piece][lane] 16-byte pieces (4 per
-// row for bf16, 8 for fp32).  Tensor 0 u, 1 delta, 2 z (output pass only).
-// The B/C records of the tile follow, double-buffered so that the next
-// tile's can land while the last block of this one still reads its own.  `lds_base` is the LDS byte address of the
-// image.  The instruction offset moves both the global and the LDS address,
-// so M0 is set 16 p bytes short of piece p's slot.
-// (The instruction's immediate offset is 13-bit signed: larger offsets would
-// wrap silently, so they are kept below 4096.)
-template <int P>
-__device__ __forceinline__ void dma_piece(const void* g, uint32_t slot) {
-    static_assert(16 * P < 4096, "immediate offset out of range");
-    __builtin_amdgcn_global_load_lds(g, (ldsptr)(uintptr_t)(slot - 16 * P), 16, 16 * P, 0);
-}
+// LDS image of one 32-token tile: per tensor (0 u, 1 delta, 2 z, the last in
+// the output pass only) the rows' 16-byte pieces (4 per row for bf16, 8 for
+// fp32) in the order the row copies below write them.  The B/C records of
+// the tile follow, double-buffered so that the next tile's can land while
+// the last block of this one still reads its own.  `lds_base` is the LDS
+// byte address of the image.  The instruction's immediate offset moves both
+// the global and the LDS address, so M0 is set that many bytes short of the
+// slot; the immediate is 13-bit signed and larger offsets would wrap
+// silently, so it is kept below 4096.
 
 // 16 bytes per lane from g + OFF into LDS at slot + 16 * lane.
 template <int OFF>
@@ -252,23 +249,31 @@ __device__ __forceinline__ void dma_at(const void* g, uint32_t slot) {
 // half (16 floats, summary pass) at bc_base + j * kRec<MODE> bytes.
 template <int MODE> constexpr int kRec = MODE == 0 ? 128 : 64;
 
+// Row copies.  One instruction fills 1 KB of LDS with 16 rows x 64 bytes
+// (four consecutive 16-byte pieces of each row), so each row's pieces leave
+// as one request; lane i takes row 16k + i%16, piece 4h + i/16 of the
+// instruction (h, k).  Per tensor the LDS image is [h][k][p4][r] in 16-byte
+// slots, and lane l finds piece p of its own row at slot
+// (p/4) 256 + (p%4) 16 + (l/16) 64 + l%16.
+struct RowDma {
+    const char* base[3];   // per tensor: the block's first row (wave-uniform)
+    uint32_t kb[4];        // per row group k: byte offset of its first row (clamped)
+    uint32_t voff[4];      // per row group: this lane's row and piece, from kb[k]
+};
+// (Both offsets are below 64 rows x L x 4 bytes, under 2^32 for L <= 2^24.)
+
 template <typename Tin, int NT>
-__device__ __forceinline__ void issue_rows(const Tin* const* rowp, int64_t t0, uint32_t lds_base) {
+__device__ __forceinline__ void issue_rows(const RowDma& R, int64_t t0, uint32_t lds_base) {
     constexpr int NP = In<Tin>::kPieces;
-    constexpr uint32_t kPiece = kRows * 16;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const void* g = rowp[t] + t0;
-        const uint32_t s0 = lds_base + (uint32_t)(t * NP) * kPiece;
-        dma_piece<0>(g, s0);
-        dma_piece<1>(g, s0 + 1 * kPiece);
-        dma_piece<2>(g, s0 + 2 * kPiece);
-        dma_piece<3>(g, s0 + 3 * kPiece);
-        if constexpr (NP == 8) {
-            dma_piece<4>(g, s0 + 4 * kPiece);
-            dma_piece<5>(g, s0 + 5 * kPiece);
-            dma_piece<6>(g, s0 + 6 * kPiece);
-            dma_piece<7>(g, s0 + 7 * kPiece);
+        const char* bt = R.base[t] + t0 * (int64_t)sizeof(Tin);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const char* g = bt + R.kb[k] + R.voff[k];
+            const uint32_t s0 = lds_base + (uint32_t)(t * NP + k) * 1024u;
+            dma_at<0>(g, s0);
+            if constexpr (NP == 8) dma_at<64>(g, s0 + 4 * 1024u);
         }
     }
 }
@@ -296,17 +301,24 @@ struct Blk {
     uint32_t u[In<Tin>::kWords], d[In<Tin>::kWords], z[In<Tin>::kWords];
 };
 
+// 16-byte slot of piece p of tensor t for the lane whose slot offset is ls
+template <typename Tin>
+__device__ __forceinline__ int piece_slot(int t, int p, int ls) {
+    return t * In<Tin>::kPieces * kRows + (p >> 2) * 256 + (p & 3) * 16 + ls;
+}
+
 template <typename Tin, int MODE>
-__device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int blk, int lane) {
+__device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int blk, int ls) {
     constexpr int per = In<Tin>::kWords / 4;   // 16-byte pieces per block
 #pragma unroll
     for (int q = 0; q < per; ++q) {
-        const uint4 x = lds[(0 * In<Tin>::kPieces + blk * per + q) * kRows + lane];
+        const int p = blk * per + q;
+        const uint4 x = lds[piece_slot<Tin>(0, p, ls)];
         b.u[4 * q] = x.x; b.u[4 * q + 1] = x.y; b.u[4 * q + 2] = x.z; b.u[4 * q + 3] = x.w;
-        const uint4 y = lds[(1 * In<Tin>::kPieces + blk * per + q) * kRows + lane];
+        const uint4 y = lds[piece_slot<Tin>(1, p, ls)];
         b.d[4 * q] = y.x; b.d[4 * q + 1] = y.y; b.d[4 * q + 2] = y.z; b.d[4 * q + 3] = y.w;
         if (MODE == 0) {
-            const uint4 v = lds[(2 * In<Tin>::kPieces + blk * per + q) * kRows + lane];
+            const uint4 v = lds[piece_slot<Tin>(2, p, ls)];
             b.z[4 * q] = v.x; b.z[4 * q + 1] = v.y; b.z[4 * q + 2] = v.z; b.z[4 * q + 3] = v.w;
         }
     }
@@ -314,10 +326,9 @@ __device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int blk,
 
 // One input element of token j of the tile in LDS (tensor t).
 template <typename Tin>
-__device__ __forceinline__ float lds_elem(const uint4* lds, int t, int j, int lane) {
+__device__ __forceinline__ float lds_elem(const uint4* lds, int t, int j, int ls) {
     constexpr int per = 16 / sizeof(Tin);
-    const char* p = reinterpret_cast<const char*>(lds + (t * In<Tin>::kPieces + j / per) * kRows + lane) +
-                    (j % per) * sizeof(Tin);
+    const char* p = reinterpret_cast<const char*>(lds + piece_slot<Tin>(t, j / per, ls)) + (j % per) * sizeof(Tin);
     return In<Tin>::ld(reinterpret_cast<const Tin*>(p), 0);
 }
 
@@ -341,7 +352,28 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     const Tin* drow = reinterpret_cast<const Tin*>(a.delta) + row * a.L;
     const Tin* zrow = has_z ? reinterpret_cast<const Tin*>(a.z) + row * a.L : urow;
     Tout* yrow = reinterpret_cast<Tout*>(a.y) + row * a.L;
-    const Tin* rowp[3] = {urow, drow, zrow};
+    // row copies: the block's first row per tensor, row groups clamped to the
+    // block's rows below dim (rows past it read the last one, never stored)
+    RowDma R;
+    {
+        const int64_t row0 = b * a.dim + d0;
+        const uint32_t rb = (uint32_t)(a.L * (int64_t)sizeof(Tin));
+        const int last = (int)min<int64_t>(kRows, a.dim - d0) - 1;
+        R.base[0] = reinterpret_cast<const char*>(uniform_ptr(reinterpret_cast<const float*>(
+            reinterpret_cast<const Tin*>(a.u) + row0 * a.L)));
+        R.base[1] = reinterpret_cast<const char*>(uniform_ptr(reinterpret_cast<const float*>(
+            reinterpret_cast<const Tin*>(a.delta) + row0 * a.L)));
+        R.base[2] = has_z ? reinterpret_cast<const char*>(uniform_ptr(reinterpret_cast<const float*>(
+                                reinterpret_cast<const Tin*>(a.z) + row0 * a.L)))
+                          : R.base[0];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int k0 = min(16 * k, last);
+            R.kb[k] = (uint32_t)k0 * rb;
+            R.voff[k] = (uint32_t)min(lane & 15, last - k0) * rb + 16u * (uint32_t)(lane >> 4);
+        }
+    }
+    const int ls = (lane >> 4) * 64 + (lane & 15);   // this lane's LDS slot offset
 
     // this batch's B/C, 32 floats per token; the address is wave-uniform
     const float* bcb = uniform_ptr(a.bcq + (b * a.L) * (2 * kNS));
@@ -350,7 +382,7 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     // request the first tile before the per-row set-up and the carry-in fold,
     // so that its latency overlaps theirs
     if (t_begin < t_full_end) {
-        issue_rows<Tin, NT>(rowp, t_begin, lds_base);
+        issue_rows<Tin, NT>(R, t_begin, lds_base);
         issue_bc<MODE>(bcb, t_begin, bc_base0);
     }
 
@@ -408,18 +440,18 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
             const uint32_t bc_next = bc_base0 + (uint32_t)((par ^ 1) * kBCBytes);
             if constexpr (STRUCT) {
                 Blk<Tin> cur;
-                read_blk<Tin, MODE>(cur, lds, 0, lane);
+                read_blk<Tin, MODE>(cur, lds, 0, ls);
                 float yb[kTile];
 #pragma unroll
                 for (int blk = 0; blk < kBlocks; ++blk) {
                     Blk<Tin> nxt;
-                    if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, lane);
+                    if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, ls);
                     if (blk == kBlocks - 2 && more) {
                         // u, delta, z of this tile's last two blocks are in
                         // registers now and the other B/C buffer is free:
                         // fetch the next tile
                         wait_lgkm();
-                        issue_rows<Tin, NT>(rowp, t0 + kTile, lds_base);
+                        issue_rows<Tin, NT>(R, t0 + kTile, lds_base);
                         issue_bc<MODE>(bcb, t0 + kTile, bc_next);
                     }
                     float w[kBlk], sg[kBlk];
@@ -477,12 +509,12 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                 // general A: token by token out of the LDS tile
 #pragma nounroll
                 for (int j = 0; j < kTile; ++j) {
-                    const float uu = lds_elem<Tin>(lds, 0, j, lane);
-                    const float dl = lds_elem<Tin>(lds, 1, j, lane);
-                    const float zz = has_z ? lds_elem<Tin>(lds, 2, j, lane) : 0.0f;
+                    const float uu = lds_elem<Tin>(lds, 0, j, ls);
+                    const float dl = lds_elem<Tin>(lds, 1, j, ls);
+                    const float zz = has_z ? lds_elem<Tin>(lds, 2, j, ls) : 0.0f;
                     if (j == kTile - 1 && more) {
                         wait_lgkm();
-                        issue_rows<Tin, NT>(rowp, t0 + kTile, lds_base);
+                        issue_rows<Tin, NT>(R, t0 + kTile, lds_base);
                         issue_bc<MODE>(bcb, t0 + kTile, bc_next);
                     }
                     const float pre = tok_general<MODE>(L, bcl + j * RS, delta_log2<SP>(L, dl), uu);

@@ -100,6 +100,8 @@ selscan_status_t check_m1_shape(const selscan_shape_t* s) {
         return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
     if (s->batch * ((s->dim + 63) / 64) > 0x7fffffff || s->batch * ((s->seqlen + 31) / 32) > 0x7fffffff)
         return fail(SELSCAN_ERR_UNSUPPORTED, "too many channel blocks or token tiles for one launch");
+    // the scan's row copies address a block's 64 rows with 32-bit offsets
+    if (s->seqlen > (int64_t(1) << 24)) return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-1 scan supports seqlen <= 2^24");
     return SELSCAN_OK;
 }
 

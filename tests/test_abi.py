@@ -53,7 +53,7 @@ FAKE = 4096  # a non-null pointer value; never dereferenced because validation f
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, ss.ERR_INVALID_ARG), ("dim", -1, ss.ERR_INVALID_ARG), ("seqlen", 0, ss.ERR_INVALID_ARG),
     ("dstate", 0, ss.ERR_INVALID_ARG), ("dstate", 17, ss.ERR_UNSUPPORTED), ("in_dtype", 7, ss.ERR_UNSUPPORTED),
-    ("seqlen", 1 << 62, ss.ERR_INVALID_ARG)])
+    ("seqlen", 1 << 62, ss.ERR_INVALID_ARG), ("seqlen", (1 << 24) + 1, ss.ERR_UNSUPPORTED)])
 def test_m1_bad_shape_rejected(field, value, status):
     s = _m1(**{field: value})
     r = ss.lib().selscan_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE, None, None)
