@@ -22,8 +22,9 @@
 // tile's B/C records follow into one of two buffers.
 // The next tile is requested as soon as the current one's last two 8-token
 // blocks are in registers, so its latency overlaps their arithmetic.  y
-// collects the tile's 32 tokens per lane in registers and leaves as one
-// burst of 16-byte stores per row.
+// collects the tile's 32 tokens per lane in registers; at the tile's end it
+// is transposed through the tile's B/C buffer, now free, so that each store
+// instruction writes 64 contiguous bytes of each of 16 rows.
 //
 // Long sequences are cut into G chunks so that enough waves exist to fill
 // the 256 CUs: a summary pass computes, per chunk, the end state from a zero
@@ -101,25 +102,30 @@ template <> struct In<uint16_t> {
     static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 };
 
-// y stores: a whole 32-token burst, or one token.
+// y stores of one token (ragged tails and the general-A path).
 template <typename T> struct Out;
 template <> struct Out<float> {
-    static __device__ __forceinline__ void burst(float* p, const float* v) {
-        float4* q = reinterpret_cast<float4*>(p);
-#pragma unroll
-        for (int i = 0; i < kTile / 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-    }
     static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
 };
 template <> struct Out<uint16_t> {
-    static __device__ __forceinline__ void burst(uint16_t* p, const float* v) {
-        uint4* q = reinterpret_cast<uint4*>(p);
-#pragma unroll
-        for (int i = 0; i < kTile / 8; ++i)
-            q[i] = make_uint4(pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
-                              pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
-    }
     static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// A tile's y of one row as 32-bit words (fp32: 32 words, bf16: 16).
+template <typename T> struct YWords;
+template <> struct YWords<float> {
+    static constexpr int kN = kTile;
+    static __device__ __forceinline__ void pack(uint32_t* w, const float* v) {
+#pragma unroll
+        for (int i = 0; i < kN; ++i) w[i] = __float_as_uint(v[i]);
+    }
+};
+template <> struct YWords<uint16_t> {
+    static constexpr int kN = kTile / 2;
+    static __device__ __forceinline__ void pack(uint32_t* w, const float* v) {
+#pragma unroll
+        for (int i = 0; i < kN; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    }
 };
 
 // The per-row constants and state of one lane.
@@ -352,6 +358,12 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     const Tin* drow = reinterpret_cast<const Tin*>(a.delta) + row * a.L;
     const Tin* zrow = has_z ? reinterpret_cast<const Tin*>(a.z) + row * a.L : urow;
     Tout* yrow = reinterpret_cast<Tout*>(a.y) + row * a.L;
+    // y bursts leave through a buffer descriptor over the block's rows below
+    // dim: stores of rows past them fall outside it and are dropped
+    const uint32_t yrb = (uint32_t)(a.L * (int64_t)sizeof(Tout));
+    const __amdgpu_buffer_rsrc_t ydesc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<Tout*>(a.y) + (b * a.dim + d0) * a.L, 0,
+        (int)((uint32_t)min<int64_t>(kRows, a.dim - d0) * yrb), 0x00020000);
     // row copies: the block's first row per tensor, row groups clamped to the
     // block's rows below dim (rows past it read the last one, never stored)
     RowDma R;
@@ -504,7 +516,37 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                 // compiler would otherwise drain the y stores as well before
                 // the tile's first LDS read
                 wait_vm();
-                if (MODE == 0 && row_ok) Out<Tout>::burst(yrow + t0, yb);
+                if constexpr (MODE == 0) {
+                    // Transposed through this tile's B/C buffer (free now; 4 KB)
+                    // in halves of 64 bytes per row, so that one store covers
+                    // 64 contiguous bytes of each of 16 rows: a row's half is
+                    // one request rather than four.  Chunk c of row r sits at
+                    // r*64 + ((c + r/4) % 4)*16, which keeps both the lanes'
+                    // row-wise writes and the column-wise reads free of bank
+                    // conflicts.
+                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                    uint32_t yw[YWords<Tout>::kN];
+                    YWords<Tout>::pack(yw, yb);
+                    u32x4* sbuf = reinterpret_cast<u32x4*>(const_cast<float*>(bcl));
+                    const int rr = lane >> 2, cc = lane & 3;
+#pragma unroll
+                    for (int hh = 0; hh < YWords<Tout>::kN / 16; ++hh) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            sbuf[lane * 4 + ((c + (lane >> 2)) & 3)] =
+                                u32x4{yw[16 * hh + 4 * c], yw[16 * hh + 4 * c + 1], yw[16 * hh + 4 * c + 2],
+                                      yw[16 * hh + 4 * c + 3]};
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int r = 16 * k + rr;
+                            const u32x4 v = sbuf[r * 4 + ((cc + (r >> 2)) & 3)];
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v, ydesc,
+                                (int)((uint32_t)r * yrb + (uint32_t)(t0 * (int64_t)sizeof(Tout)) + 64u * hh + 16u * cc),
+                                0, 0);
+                        }
+                    }
+                }
             } else {
                 // general A: token by token out of the LDS tile
 #pragma nounroll

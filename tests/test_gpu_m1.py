@@ -109,6 +109,24 @@ def test_options(gpu, opt):
     assert y.dtype == (out_dtype or torch.float32)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_partial_channel_block_output(gpu, out_dtype):
+    """dim 100: the second 64-channel block has 36 real rows; the tile-wise y
+    stores of its other 28 rows must land nowhere (fp32 and bf16 y)."""
+    inp = _inputs(2, 100, 16, 300, torch.bfloat16, seed=17)
+    y, _ = _full_compare(inp, out_dtype=out_dtype)
+    assert y.shape == (2, 100, 300)
+    # y followed by a guard of 28 rows: stores of rows 100..127 of the last
+    # batch would land there
+    n = 2 * 100 * 300
+    buf = torch.full((n + 28 * 300,), 7.0, dtype=out_dtype, device=DEV)
+    yv = buf[:n].view(2, 100, 300)
+    ss.fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"], out=yv)
+    torch.cuda.synchronize()
+    assert torch.equal(host(buf[n:]), torch.full((28 * 300,), 7.0, dtype=out_dtype))
+    assert torch.equal(host(yv), host(y))
+
+
 def test_golden_fixture(gpu):
     fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "m1_small.json")))
     ins = {k: torch.tensor(v, dtype=torch.float32, device=DEV) for k, v in fx["inputs"].items()}
