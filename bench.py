@@ -51,20 +51,28 @@ def parse():
 def _call(ss, w, inp, out):
     if w.kind == "m1":
         return ss.fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"],
-                      softplus=True, out=out[0], last_state=out[1])
+                      softplus=True, out=out[0], last_state=out[1], workspace=out[2])
     return ss.mamba2_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["dt_bias"],
-                         softplus=True, out=out[0], last_state=out[1])
+                         softplus=True, out=out[0], last_state=out[1], workspace=out[2])
 
 
 def _outputs(w, device):
+    """y, last state and the library's workspace, allocated once (as a caller
+    that runs the layer repeatedly would) rather than inside every call."""
     import torch
+    import selective_state_space_25_amd as ss
+    code = ss.BF16 if w.dtype == torch.bfloat16 else ss.F32
+    ocode = ss.BF16 if w.out_dtype == torch.bfloat16 else ss.F32
     if w.kind == "m1":
         y = torch.empty((w.batch, w.dim, w.seqlen), dtype=w.out_dtype, device=device)
         last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=device)
+        nws = ss.workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, code, ocode)
     else:
         y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=w.out_dtype, device=device)
         last = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=device)
-    return y, last
+        nws = ss.mamba2_workspace_bytes(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, code, ocode)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=device) if nws > 0 else None
+    return y, last, ws
 
 
 def _timed(ss, w, inps, outs, steps, stream):
