@@ -14,16 +14,16 @@
 //
 // Time is cut into chunks so that the grid fills the chip:
 //   summary: per chunk, a forward sweep from a zero state that stores the
-//            state (and the running sum of Delta) every 8 tokens and the
+//            state (and the running sum of Delta) every 16 tokens and the
 //            state at the chunk's end; and a reverse sweep of the adjoint from
 //            a zero right boundary;
 //   carry:   the true state entering each chunk (forward over chunks, from
 //            h0) and the true adjoint entering it from the right (backward
 //            over chunks); both are linear, so a chunk's decay
 //            exp(A sum Delta) is all that links neighbours;
-//   chunk:   per chunk, 8-token tiles from the last: the tile's first state
+//   chunk:   per chunk, 16-token tiles from the last: the tile's first state
 //            is the stored zero-start state plus the decayed entering state;
-//            the tile's 8 states are recomputed into registers and the
+//            the tile's 16 states are recomputed into registers and the
 //            adjoint runs back through them;
 //   reduce:  sums of the per-block partials over channel blocks, batches and
 //            chunks (no atomics: results do not depend on scheduling).
@@ -31,7 +31,7 @@
 // A workgroup is 256 threads for 64 channels of one batch.  A lane holds 4 of
 // a channel's 16 states (n = 4q .. 4q+3); lane = 16 dr + 4 q + rr, channel =
 // 16 wave + 4 dr + rr.  Per-channel, per-token values (Delta, Delta u, dy, ...)
-// are computed once per tile by a "producer" mapping (thread = channel x 2
+// are computed once per tile by a "producer" mapping (thread = channel x 4
 // tokens) into LDS.  Sums over n go over a lane's 4 states and then across
 // the 4 lanes of the channel (DPP row rotations by 4 and 8); dB and dC, sums
 // over channels, are reduce-scattered across the 4 channels of a DPP row
@@ -46,10 +46,12 @@ namespace {
 
 constexpr int kCh = 64;          // channels per workgroup
 constexpr int kSt = 16;          // states per channel (padded)
-constexpr int kT = 8;            // tokens per tile
+constexpr int kT = 16;           // tokens per tile (16 rather than 8: half the requests per token)
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPad = kT + 1;     // LDS row pitch of per-channel tile values
+constexpr int kPT = kT / 4;      // tokens per producer thread (4 threads per channel)
+constexpr int kRT = 256 / (2 * kSt);   // tokens per 256-thread dB/dC partial pass
 
 template <typename T> __device__ __forceinline__ float ld1(const T* p, int64_t i);
 template <> __device__ __forceinline__ float ld1<float>(const float* p, int64_t i) { return p[i]; }
@@ -135,7 +137,7 @@ struct Span {
 struct Blk {
     int64_t b, cb, g, row0;       // row0 = b dim + 64 cb
     int t0, t_end, tiles, rows;   // rows: channels of this block below dim
-    int L, TL;                    // tokens; 8-token tiles per row
+    int L, TL;                    // tokens; tiles per row
 };
 
 __device__ __forceinline__ Blk blk(const BwdArgs& a) {
@@ -211,7 +213,7 @@ __device__ __forceinline__ bool structured_block(const BwdArgs& a) {
     return __syncthreads_and(c.st ? 1 : 0) != 0;
 }
 
-// Producer view: channel pr, tokens pj, pj + 1 of each tile.
+// Producer view: channel pr, tokens pj .. pj + kPT - 1 of each tile.
 struct Pro {
     int pr, pj, rc;
     bool ok;
@@ -220,7 +222,7 @@ struct Pro {
     __device__ Pro(const BwdArgs& a, const Blk& k) {
         const int tid = threadIdx.x;
         pr = tid >> 2;
-        pj = (tid & 3) * 2;
+        pj = (tid & 3) * kPT;
         ok = pr < k.rows;
         rc = ok ? pr : k.rows - 1;
         off = (uint32_t)rc * (uint32_t)k.L;
@@ -247,15 +249,15 @@ struct In {
     }
 };
 
-// A producer thread's raw inputs for its 2 tokens of one tile, and one entry
-// of the tile's B and C (threads 0..127), loaded a tile ahead of their use.
+// A producer thread's raw inputs for its kPT tokens of one tile, and one
+// entry of the tile's B and C, loaded a tile ahead of their use.
 // The loads are unconditional, from clamped in-bounds addresses, and the raw
 // bits are kept: the loads stay in flight until the values are used, where
 // tokens past the sequence and channels past dim are masked to zero.
 template <typename Tin, typename Tout>
 struct Raw {
-    Tin x[2], u[2], z[2];
-    Tout g[2];
+    Tin x[kPT], u[kPT], z[kPT];
+    Tout g[kPT];
     Tin bv, cv;
 };
 
@@ -267,7 +269,7 @@ template <typename Tin, typename Tout, bool U, bool Z, bool BB, bool CC>
 __device__ __forceinline__ void fetch_raw(const BwdArgs& a, const Blk& k, const Pro& p, const In<Tin, Tout>& in,
                                           int tt0, Raw<Tin, Tout>& r) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
+    for (int jj = 0; jj < kPT; ++jj) {
         const uint32_t o = p.off + (uint32_t)min(tt0 + p.pj + jj, k.L - 1);
         r.x[jj] = ldo(in.delta, o);
         if (U) r.u[jj] = ldo(in.u, o);
@@ -276,7 +278,7 @@ __device__ __forceinline__ void fetch_raw(const BwdArgs& a, const Blk& k, const 
             r.z[jj] = ldo(in.z, o);
         }
     }
-    {   // threads 0..127 hold entry (j, n); the others load a duplicate
+    {   // thread (j, n) holds entry (j, n) (threads past kT x 16 load a duplicate)
         const int j = (threadIdx.x >> 4) & (kT - 1), n = min<int>(threadIdx.x & 15, a.N - 1);
         const uint32_t o = (uint32_t)n * (uint32_t)k.L + (uint32_t)min(tt0 + j, k.L - 1);
         if (BB) r.bv = ldo(in.B, o);
@@ -298,7 +300,7 @@ struct SumSmem {
     alignas(16) float bc[2][kT][kSt];   // B (forward) or C (reverse); read as float4
 };
 
-// Per chunk, from zero: state every 8 tokens and at the end, running sum of
+// Per chunk, from zero: state every tile and at the end, running sum of
 // Delta; and (when the sequence has several chunks) the adjoint leaving the
 // chunk's first token, a_{t0} lam_{t0}, from a zero right boundary.
 template <typename Tin, typename Tout, bool SP, bool ST>
@@ -324,7 +326,7 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
         const int tt0 = k.t0 + tile * kT;
         const int pb = tile & 1;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < kPT; ++jj) {
             float dd;
             const float dt = delta_of<SP>(f32_of(r.x[jj]) + p.bias, dd);
             const bool ok = p.ok && tt0 + p.pj + jj < k.t_end;
@@ -376,7 +378,7 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
         const int tt0 = k.t0 + tile * kT;
         const int pb = tile & 1;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < kPT; ++jj) {
             float dd;
             const float dt = delta_of<SP>(f32_of(r.x[jj]) + p.bias, dd);
             const bool ok = p.ok && tt0 + p.pj + jj < k.t_end;
@@ -550,17 +552,18 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
     // flight as every later one (prefetch, then stores), and the compiler's
     // wait for the prefetch need not cover the previous tile's stores.
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
+    for (int jj = 0; jj < kPT; ++jj) {
         du.st(false, 0, 0.0f);
         ddelta.st(false, 0, 0.0f);
         dz.st(false, 0, 0.0f);
     }
-    part.st(false, 0, 0.0f);
+#pragma unroll
+    for (int jh = 0; jh < kT / kRT; ++jh) part.st(false, 0, 0.0f);
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
         const int tt0 = k.t0 + tile * kT;
         // per-channel tile values
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < kPT; ++jj) {
             const int j = p.pj + jj;
             const bool ok = p.ok && tt0 + j < k.t_end;
             float dd;
@@ -659,7 +662,7 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
 
         // per-channel outputs (producer mapping)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < kPT; ++jj) {
             const int j = p.pj + jj;
             const int t = tt0 + j;
             const bool ok = p.ok && t < k.t_end;
@@ -673,8 +676,9 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
             dD_acc += ok ? dy * uu : 0.0f;
             dbias_acc += ok ? dx : 0.0f;
         }
-        {   // dB, dC partials of this channel block: thread = (token j, value v)
-            const int j = tid >> 5, v = tid & 31;
+#pragma unroll
+        for (int jh = 0; jh < kT / kRT; ++jh) {   // dB, dC partials of this channel block: thread = (token j, value v)
+            const int j = jh * kRT + (tid >> 5), v = tid & 31;
             const int t = tt0 + j;
             float s = 0.0f;
 #pragma unroll
@@ -710,8 +714,10 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
     }
 }
 
+// 2 waves per SIMD: the tile's 16 recomputed states per lane need the
+// registers (3 would spill).
 template <typename Tin, typename Tout, bool SP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void m1_bwd_chunk_kernel(BwdArgs a) {
     __shared__ ChunkSmem sm;
     if (structured_block(a))
@@ -724,9 +730,9 @@ void m1_bwd_chunk_kernel(BwdArgs a) {
 // tokens of one batch, partials read 128 bytes per token.
 __global__ __launch_bounds__(256) void m1_bwd_bc_reduce_kernel(BwdArgs a) {
     const int64_t nbc = (a.dim + kCh - 1) / kCh;
-    const int64_t tblocks = (a.L + kT - 1) / kT;
+    const int64_t tblocks = (a.L + kRT - 1) / kRT;
     const int64_t b = blockIdx.x / tblocks;
-    const int64_t t = (blockIdx.x - b * tblocks) * kT + (threadIdx.x >> 5);
+    const int64_t t = (blockIdx.x - b * tblocks) * kRT + (threadIdx.x >> 5);
     const int v = threadIdx.x & 31, n = v & (kSt - 1);
     if (t >= a.L) return;
     const float* src = a.part + (b * a.L + t) * (2 * kSt) + v;
@@ -796,7 +802,7 @@ hipError_t launch_sp(const BwdArgs& a, hipStream_t stream) {
     }
     {
         KTime kt("m1_bwd_bc_reduce", stream);
-        const unsigned rb = (unsigned)(a.batch * ((a.L + kT - 1) / kT));
+        const unsigned rb = (unsigned)(a.batch * ((a.L + kRT - 1) / kRT));
         hipLaunchKernelGGL(m1_bwd_bc_reduce_kernel, dim3(rb), dim3(256), 0, stream, a);
     }
     KTime kt("m1_bwd_param_reduce", stream);

@@ -66,9 +66,10 @@ def test_lengths(gpu, L, dtype):
     _check_grads(_gpu(inp, dout), _oracle(inp, dout))
 
 
-@pytest.mark.parametrize("chunk", [32, 64, 96, 512])
+@pytest.mark.parametrize("chunk", [32, 48, 64, 96, 512])
 def test_chunked_time_matches_oracle(gpu, monkeypatch, chunk):
-    """Chunks of the sequence linked by the state and adjoint carries."""
+    """Chunks of the sequence linked by the state and adjoint carries (48: an
+    odd number of 16-token tiles per chunk)."""
     monkeypatch.setenv("SELSCAN_BWD_CHUNK", str(chunk))
     inp, dout = _case(2, 130, 16, 1000, torch.bfloat16, seed=chunk)
     _check_grads(_gpu(inp, dout), _oracle(inp, dout))
