@@ -49,6 +49,9 @@ int m1_rows_per_block();
 int m1_waves_per_block();
 size_t m1_bc_bytes(int64_t batch, int64_t L);
 hipError_t launch_m1(const M1Args& a, int in_bf16, int out_bf16, hipStream_t stream);
+// B, C [batch, N, L] -> bcq [batch, L, 32] fp32 records (zeros past N).
+hipError_t launch_m1_bc(const void* B, const void* C, int64_t batch, int N, int64_t L, float* bcq, int in_bf16,
+                        hipStream_t stream);
 
 // Mamba-1 backward.  Inputs as for M1Args plus dout [batch, dim, L]
 // (out dtype); gradients fp32 in the layouts of their inputs.  hbuf .. part
@@ -72,8 +75,10 @@ struct BwdArgs {
     float* pD;      // [rows, G]
     float* pbias;   // [rows, G]
     float* part;    // [dim / 64, batch, L, 32] per-channel-block dB (16) and dC (16)
-    float* ckz;     // [rows, L / 8, 16] state before every 8th token from the chunk's zero start
-    float* wck;     // [rows, L / 8] sum of Delta from the chunk's start to the same tokens
+    float* ckz;     // [rows, tiles, 16] state entering every tile (m1_bwd_tile() tokens) from the chunk's zero start
+    float* wck;     // [rows, tiles] sum of Delta from the chunk's start to the same tokens
+    float* bcq;     // [batch, L, 32] fp32 records of B and C (the lane-per-channel summary pass)
+    int lane_sum;   // the summary pass runs one channel per lane (rows 16-byte aligned)
     int64_t batch, dim, L;
     int64_t chunk;  // tokens per chunk: a multiple of m1_bwd_tile(), at most m1_bwd_max_chunk()
     int64_t G;      // chunks

@@ -39,6 +39,7 @@
 // then across the 4 waves in LDS.
 #include "device_math.hpp"
 #include "kernels.hpp"
+#include "lds_rows.hpp"
 
 namespace selscan {
 
@@ -419,6 +420,315 @@ void m1_bwd_summary_kernel(BwdArgs a) {
         summary_body<Tin, Tout, SP, false>(a, sm);
 }
 
+// ---------------------------------------------------------------------------
+// The summary pass with one channel per lane, for rows of u, delta, z and
+// dout that start on 16-byte boundaries: the same quantities as
+// m1_bwd_summary_kernel (checkpoints every tile, the chunk's end state and
+// sum of Delta, the adjoint leaving its first token), computed the way the
+// forward scan runs: a wave covers 64 channels, a lane keeps its channel's 16
+// states in registers, 32-token tiles of the rows arrive by row copies into
+// LDS (lds_rows.hpp) and each token's B (forward sweep) or C (reverse sweep)
+// record is read as a broadcast from the tile's copy of the fp32 records.
+// No barriers and no cross-lane sums: the 4-lanes-per-channel layout is kept
+// for the chunk pass, whose dB and dC are sums over channels.
+namespace lane_summary {
+
+constexpr int kTile = 32;   // tokens per row copy
+constexpr int kBlk = 8;     // tokens per block read from LDS into registers
+static_assert(kTile % kT == 0 && kT % kBlk == 0, "checkpoints fall on block starts");
+
+// An 8-token block of one row: 4 words of bf16 or 8 of fp32.
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+    static constexpr int kW = 8;
+    static __device__ __forceinline__ float get(const uint32_t* w, int j) { return __uint_as_float(w[j]); }
+};
+template <> struct Elt<uint16_t> {
+    static constexpr int kW = 4;
+    static __device__ __forceinline__ float get(const uint32_t* w, int j) {
+        return (j & 1) ? bf16hi(w[j >> 1]) : bf16lo(w[j >> 1]);
+    }
+};
+
+// Block blk of tensor t of an image (lds_rows.hpp layout) starting at uint4 `img`.
+template <typename T>
+__device__ __forceinline__ void read_block(uint32_t* w, const uint4* img, int t, int blk, int ls) {
+    constexpr int per = Elt<T>::kW / 4;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+        const uint4 x = img[rows::piece_slot<T>(t, blk * per + q, ls)];
+        w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+    }
+}
+
+// B (off 0) or C (off 16) halves of the records of tokens t .. t+31:
+// 64 bytes per token, 16 tokens per instruction.
+__device__ __forceinline__ void issue_half(const float* bcb, int t, uint32_t base, int off) {
+    const int lane = threadIdx.x;
+    const float* g = bcb + (int64_t)(t + (lane >> 2)) * (2 * kSt) + off + (lane & 3) * 4;
+    rows::dma_at<0>(g, base);
+    rows::dma_at<2048>(g, base + 1024);
+}
+
+// exp(Delta A[n]) for the 16 states, dt = Delta: powers of one exponential
+// when A is structured (A[n] = (n+1) A[0]), else one exponential each.
+template <bool ST>
+__device__ __forceinline__ void decay16(const float* Al2, float dt, float* a) {
+    if constexpr (ST) {
+        const float r = fast_exp2(dt * Al2[0]);
+        a[0] = r;
+        a[1] = r * r;
+        a[2] = a[1] * r;
+        a[3] = a[1] * a[1];
+#pragma unroll
+        for (int n = 4; n < kSt; ++n) a[n] = a[n - 4] * a[3];
+    } else {
+#pragma unroll
+        for (int n = 0; n < kSt; ++n) a[n] = fast_exp2(dt * Al2[n]);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p, int i) { return f32_of(p[i]); }
+
+// Ends a token: its 16 states are final here, and neither the next token's
+// record reads nor its updates move above this point.  (Without it the
+// compiler reads all of a block's records first and keeps them in registers,
+// which spills.)
+__device__ __forceinline__ void token_fence(float* v) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                 "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]),
+                 "+v"(v[14]), "+v"(v[15])
+                 :
+                 : "memory");
+}
+
+// LDS of one wave: the rows' images (forward: u, delta; reverse: delta, z,
+// then dout), then two buffers of 32 half-records.
+template <typename Tin, typename Tout>
+constexpr int kRowKB = 2 * rows::kPieces<Tin> + rows::kPieces<Tout>;
+
+template <typename Tin, typename Tout, bool SP, bool ST>
+__device__ __forceinline__ void body(const BwdArgs& a, uint4* lds) {
+    const int lane = threadIdx.x;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(rows::ldsptr)lds;
+    const int64_t nbc = (a.dim + kCh - 1) / kCh;
+    const int G = (int)a.G;
+    const int g = (int)(blockIdx.x % a.G);      // chunk fastest, as in the other passes
+    const int64_t rb = blockIdx.x / a.G;
+    const int64_t b = rb / nbc;
+    const int64_t d0 = (rb - b * nbc) * kCh;
+    const int last = (int)min<int64_t>(kCh, a.dim - d0) - 1;
+    const bool row_ok = lane <= last;
+    const int rc = min(lane, last);
+    const int64_t row0 = b * a.dim + d0;
+    const int L = (int)a.L;
+    const int t0 = (int)(g * a.chunk);
+    const int t_end = min(L, t0 + (int)a.chunk);
+    const int t_full = t0 + ((t_end - t0) / kTile) * kTile;
+    const int TL = (L + kT - 1) / kT;
+    const int ls = rows::lane_slot(lane);
+
+    float Al2[kSt];
+#pragma unroll
+    for (int n = 0; n < kSt; ++n) Al2[n] = n < a.N ? a.A[(d0 + rc) * a.N + n] * kLog2e : 0.0f;
+    const float bias = a.bias ? a.bias[d0 + rc] : 0.0f;
+    const float* bcb = rows::uniform(a.bcq + (int64_t)b * L * (2 * kSt));
+    const uint32_t bc_base0 = lds_base + (uint32_t)kRowKB<Tin, Tout> * 1024u;
+    const float* bcl0 = reinterpret_cast<const float*>(lds + kRowKB<Tin, Tout> * 64);
+    const Tin* urow0 = reinterpret_cast<const Tin*>(a.u) + row0 * a.L;
+    const Tin* drow0 = reinterpret_cast<const Tin*>(a.delta) + row0 * a.L;
+    const Tin* zrow0 = a.z ? reinterpret_cast<const Tin*>(a.z) + row0 * a.L : drow0;
+    const Tout* grow0 = reinterpret_cast<const Tout*>(a.dout) + row0 * a.L;
+    const int64_t ro = (int64_t)rc * a.L;   // this lane's row within the block's rows
+
+    // checkpoints: the state entering tile t / kT and the sum of Delta before it
+    const Span ckz(a.ckz + row0 * TL * kSt, (uint32_t)(last + 1) * (uint32_t)TL * (kSt * 4));
+    const Span wck(a.wck + row0 * TL, (uint32_t)(last + 1) * (uint32_t)TL * 4);
+    float h[kSt];
+#pragma unroll
+    for (int n = 0; n < kSt; ++n) h[n] = 0.0f;
+    float W = 0.0f;
+    auto ckpt = [&](int t) {
+        const uint32_t ct = (uint32_t)rc * (uint32_t)TL + (uint32_t)(t / kT);
+#pragma unroll
+        for (int q = 0; q < kSt / 4; ++q) ckz.st4(row_ok, (ct * kSt + 4 * q) * 4, &h[4 * q]);
+        wck.st(row_ok, ct * 4, W);
+    };
+    auto fwd_token = [&](float dl, float uu, const float* Bp) {
+        float dd;
+        const float dt = delta_of<SP>(dl + bias, dd);
+        const float x = dt * uu;
+        float at[kSt];
+        decay16<ST>(Al2, dt, at);
+#pragma unroll
+        for (int n = 0; n < kSt; ++n) h[n] = __builtin_fmaf(at[n], h[n], x * Bp[n]);
+        W += dt;
+        token_fence(h);
+    };
+
+    // forward sweep from a zero state
+    rows::RowDma<Tin> Rf;
+    Rf.init(urow0, drow0, drow0, a.L, last, lane);
+    if (t0 < t_full) {
+        rows::issue_rows<Tin, 2>(Rf, t0, lds_base);
+        issue_half(bcb, t0, bc_base0, 0);
+        rows::wait_vm();
+        int par = 0;
+#pragma nounroll
+        for (int t = t0; t < t_full; t += kTile, par ^= 1) {
+            const bool more = t + kTile < t_full;
+            const float* bcl = bcl0 + par * (kTile * kSt);
+            uint32_t cu[Elt<Tin>::kW], cd[Elt<Tin>::kW], nu[Elt<Tin>::kW], nd[Elt<Tin>::kW];
+            read_block<Tin>(cu, lds, 0, 0, ls);
+            read_block<Tin>(cd, lds, 1, 0, ls);
+            // not unrolled: one block per basic block keeps the compiler from
+            // reading all the tile's records ahead and spilling them
+#pragma nounroll
+            for (int blk = 0; blk < kTile / kBlk; ++blk) {
+                if (blk + 1 < kTile / kBlk) {
+                    read_block<Tin>(nu, lds, 0, blk + 1, ls);
+                    read_block<Tin>(nd, lds, 1, blk + 1, ls);
+                }
+                if (blk == kTile / kBlk - 2 && more) {
+                    // the last two blocks are in registers and the other
+                    // record buffer is free: request the next tile
+                    rows::wait_lgkm();
+                    rows::issue_rows<Tin, 2>(Rf, t + kTile, lds_base);
+                    issue_half(bcb, t + kTile, bc_base0 + (uint32_t)((par ^ 1) * kTile * 64), 0);
+                }
+                if ((blk * kBlk) % kT == 0) ckpt(t + blk * kBlk);
+#pragma unroll
+                for (int j = 0; j < kBlk; ++j)
+                    fwd_token(Elt<Tin>::get(cd, j), Elt<Tin>::get(cu, j), bcl + (blk * kBlk + j) * kSt);
+                if (blk + 1 < kTile / kBlk) {
+#pragma unroll
+                    for (int i = 0; i < Elt<Tin>::kW; ++i) { cu[i] = nu[i]; cd[i] = nd[i]; }
+                }
+                // one block at a time: otherwise the four blocks' record
+                // reads would all be hoisted to the tile's start and spill
+                asm volatile("" ::: "memory");
+            }
+            rows::wait_vm();
+        }
+    }
+    // the rest of the chunk token by token
+    for (int t = t_full; t < t_end; ++t) {
+        if ((t - t0) % kT == 0) ckpt(t);
+        fwd_token(ld1(drow0 + ro, t), ld1(urow0 + ro, t), bcb + (int64_t)t * (2 * kSt));
+    }
+    const uint32_t cell = ((uint32_t)rc * (uint32_t)G + (uint32_t)g) * kSt;
+    float* hbuf = a.hbuf + row0 * G * kSt;
+    if (row_ok) {
+#pragma unroll
+        for (int q = 0; q < kSt / 4; ++q)
+            *reinterpret_cast<float4*>(hbuf + cell + 4 * q) = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+        (a.wbuf + row0 * G)[(uint32_t)rc * (uint32_t)G + (uint32_t)g] = W;
+    }
+    if (G == 1) return;   // uniform over the grid
+
+    // reverse sweep of the adjoint from a zero right boundary
+    float mu[kSt];
+#pragma unroll
+    for (int n = 0; n < kSt; ++n) mu[n] = 0.0f;
+    auto rev_token = [&](float dl, float gg, float zz, const float* Cp) {
+        float dd;
+        const float dt = delta_of<SP>(dl + bias, dd);
+        const float dy = a.z ? gg * zz * sigmoid(zz) : gg;
+        float at[kSt];
+        decay16<ST>(Al2, dt, at);
+#pragma unroll
+        for (int n = 0; n < kSt; ++n) mu[n] = at[n] * __builtin_fmaf(dy, Cp[n], mu[n]);
+        token_fence(mu);
+    };
+    for (int t = t_end - 1; t >= t_full; --t)
+        rev_token(ld1(drow0 + ro, t), ld1(grow0 + ro, t), ld1(zrow0 + ro, t), bcb + (int64_t)t * (2 * kSt) + kSt);
+    if (t0 < t_full) {
+        rows::RowDma<Tin> Rr;
+        Rr.init(drow0, zrow0, drow0, a.L, last, lane);
+        rows::RowDma<Tout> Rg;
+        Rg.init(grow0, grow0, grow0, a.L, last, lane);
+        const uint32_t g_base = lds_base + (uint32_t)(2 * rows::kPieces<Tin>) * 1024u;
+        const uint4* gimg = lds + 2 * rows::kPieces<Tin> * 64;
+        auto issue = [&](int t, uint32_t bc) {
+            rows::issue_rows<Tin, 2>(Rr, t, lds_base);
+            rows::issue_rows<Tout, 1>(Rg, t, g_base);
+            issue_half(bcb, t, bc, kSt);
+        };
+        issue(t_full - kTile, bc_base0);
+        rows::wait_vm();
+        int par = 0;
+#pragma nounroll
+        for (int t = t_full - kTile; t >= t0; t -= kTile, par ^= 1) {
+            const bool more = t > t0;
+            const float* bcl = bcl0 + par * (kTile * kSt);
+            uint32_t cd[Elt<Tin>::kW], cz[Elt<Tin>::kW], cg[Elt<Tout>::kW];
+            uint32_t nd[Elt<Tin>::kW], nz[Elt<Tin>::kW], ng[Elt<Tout>::kW];
+            constexpr int NB = kTile / kBlk;
+            read_block<Tin>(cd, lds, 0, NB - 1, ls);
+            read_block<Tin>(cz, lds, 1, NB - 1, ls);
+            read_block<Tout>(cg, gimg, 0, NB - 1, ls);
+#pragma nounroll
+            for (int bi = 0; bi < NB; ++bi) {
+                const int blk = NB - 1 - bi;
+                if (blk > 0) {
+                    read_block<Tin>(nd, lds, 0, blk - 1, ls);
+                    read_block<Tin>(nz, lds, 1, blk - 1, ls);
+                    read_block<Tout>(ng, gimg, 0, blk - 1, ls);
+                }
+                if (bi == NB - 2 && more) {
+                    rows::wait_lgkm();
+                    issue(t - kTile, bc_base0 + (uint32_t)((par ^ 1) * kTile * 64));
+                }
+#pragma unroll
+                for (int j = kBlk - 1; j >= 0; --j)
+                    rev_token(Elt<Tin>::get(cd, j), Elt<Tout>::get(cg, j), Elt<Tin>::get(cz, j),
+                              bcl + (blk * kBlk + j) * kSt);
+                if (blk > 0) {
+#pragma unroll
+                    for (int i = 0; i < Elt<Tin>::kW; ++i) { cd[i] = nd[i]; cz[i] = nz[i]; }
+#pragma unroll
+                    for (int i = 0; i < Elt<Tout>::kW; ++i) cg[i] = ng[i];
+                }
+                asm volatile("" ::: "memory");
+            }
+            rows::wait_vm();
+        }
+    }
+    if (row_ok) {
+        float* mubuf = a.mubuf + row0 * G * kSt;
+#pragma unroll
+        for (int q = 0; q < kSt / 4; ++q)
+            *reinterpret_cast<float4*>(mubuf + cell + 4 * q) =
+                make_float4(mu[4 * q], mu[4 * q + 1], mu[4 * q + 2], mu[4 * q + 3]);
+    }
+}
+
+// True when every state of channel d satisfies A[d,n] == fl32((n+1) A[d,0])
+// and all 16 states are real.
+__device__ __forceinline__ bool row_structured(const BwdArgs& a, int64_t d) {
+    if (a.N != kSt) return false;
+    const float A0 = a.A[d * a.N];
+    bool s = true;
+    for (int n = 1; n < a.N; ++n) s = s && (a.A[d * a.N + n] == (float)(n + 1) * A0);
+    return s;
+}
+
+}  // namespace lane_summary
+
+template <typename Tin, typename Tout, bool SP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void m1_bwd_lane_summary_kernel(BwdArgs a) {
+    __shared__ uint4 lds[lane_summary::kRowKB<Tin, Tout> * 64 + 2 * lane_summary::kTile * kSt / 4];
+    const int64_t nbc = (a.dim + kCh - 1) / kCh;
+    const int64_t d0 = ((int64_t)(blockIdx.x / a.G) % nbc) * kCh;
+    const int64_t d = min<int64_t>(d0 + threadIdx.x, a.dim - 1);
+    const bool st = __builtin_amdgcn_ballot_w64(!lane_summary::row_structured(a, d)) == 0;
+    if (st)
+        lane_summary::body<Tin, Tout, SP, true>(a, lds);
+    else
+        lane_summary::body<Tin, Tout, SP, false>(a, lds);
+}
+
 // Per (row, n): the true state entering each chunk and the true adjoint
 // entering it from the right, in place of the summaries.
 __global__ __launch_bounds__(256) void m1_bwd_carry_kernel(BwdArgs a) {
@@ -787,7 +1097,15 @@ template <typename Tin, typename Tout, bool SP>
 hipError_t launch_sp(const BwdArgs& a, hipStream_t stream) {
     const int64_t nbc = (a.dim + kCh - 1) / kCh;
     const unsigned blocks = (unsigned)(a.batch * nbc * a.G);
-    {
+    if (a.lane_sum) {
+        {
+            KTime kt("m1_bwd_bc_convert", stream);
+            const hipError_t e = launch_m1_bc(a.B, a.C, a.batch, a.N, a.L, a.bcq, sizeof(Tin) == 2, stream);
+            if (e != hipSuccess) return e;
+        }
+        KTime kt("m1_bwd_summary", stream);
+        hipLaunchKernelGGL((m1_bwd_lane_summary_kernel<Tin, Tout, SP>), dim3(blocks), dim3(64), 0, stream, a);
+    } else {
         KTime kt("m1_bwd_summary", stream);
         hipLaunchKernelGGL((m1_bwd_summary_kernel<Tin, Tout, SP>), dim3(blocks), dim3(kThreads), 0, stream, a);
     }
@@ -829,7 +1147,7 @@ size_t m1_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t L, int64_t G) 
     const size_t cells = rows * G;
     const size_t TL = (size_t)((L + kT - 1) / kT);
     return 3 * a256(cells * kSt * 4) + 3 * a256(cells * 4) + a256((size_t)nbc * batch * 2 * kSt * L * 4) +
-           a256(rows * TL * kSt * 4) + a256(rows * TL * 4);
+           a256(rows * TL * kSt * 4) + a256(rows * TL * 4) + a256((size_t)batch * L * 2 * kSt * 4);
 }
 
 void m1_bwd_carve(BwdArgs& a, void* ws) {
@@ -852,6 +1170,7 @@ void m1_bwd_carve(BwdArgs& a, void* ws) {
     a.part = take((size_t)nbc * a.batch * 2 * kSt * a.L * 4);
     a.ckz = take(rows * TL * kSt * 4);
     a.wck = take(rows * TL * 4);
+    a.bcq = take((size_t)a.batch * a.L * 2 * kSt * 4);
 }
 
 hipError_t launch_m1_bwd(const BwdArgs& a, int in_bf16, int out_bf16, hipStream_t stream) {

@@ -51,6 +51,7 @@
 
 #include "device_math.hpp"
 #include "kernels.hpp"
+#include "lds_rows.hpp"
 
 namespace selscan {
 
@@ -65,25 +66,16 @@ constexpr float kSigLo = 8.673617379884035e-19f;   // 2^-60
 constexpr float kSigHi = 1.152921504606847e18f;    // 2^60
 
 typedef __attribute__((address_space(4))) const float* cfptr;
-typedef __attribute__((address_space(3))) void* ldsptr;
-
-// lgkmcnt(0), vmcnt and expcnt left at their maxima
-__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-// vmcnt(0), the others left at their maxima
-__device__ __forceinline__ void wait_vm() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    asm volatile("" ::: "memory");
-}
+using rows::ldsptr;
+using rows::wait_lgkm;
+using rows::wait_vm;
+using rows::dma_at;
+using rows::issue_rows;
+using rows::piece_slot;
+using rows::RowDma;
 
 __device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
 
-// A pointer whose value is the same in every lane, held in SGPRs.
-__device__ __forceinline__ const float* uniform_ptr(const float* p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
-}
 
 // Input element types: tokens per tile (one line per row), words per block.
 template <typename T> struct In;
@@ -236,53 +228,14 @@ __device__ __forceinline__ void load_bc(float* dst, cfptr p) {
 
 // LDS image of one 32-token tile: per tensor (0 u, 1 delta, 2 z, the last in
 // the output pass only) the rows' 16-byte pieces (4 per row for bf16, 8 for
-// fp32) in the order the row copies below write them.  The B/C records of
-// the tile follow, double-buffered so that the next tile's can land while
-// the last block of this one still reads its own.  `lds_base` is the LDS
-// byte address of the image.  The instruction's immediate offset moves both
-// the global and the LDS address, so M0 is set that many bytes short of the
-// slot; the immediate is 13-bit signed and larger offsets would wrap
-// silently, so it is kept below 4096.
-
-// 16 bytes per lane from g + OFF into LDS at slot + 16 * lane.
-template <int OFF>
-__device__ __forceinline__ void dma_at(const void* g, uint32_t slot) {
-    static_assert(OFF >= 0 && OFF < 4096, "immediate offset out of range");
-    __builtin_amdgcn_global_load_lds(g, (ldsptr)(uintptr_t)(slot - OFF), 16, OFF, 0);
-}
+// fp32) as lds_rows.hpp lays them out.  The B/C records of the tile follow,
+// double-buffered so that the next tile's can land while the last block of
+// this one still reads its own.  `lds_base` is the LDS byte address of the
+// image.
 
 // B/C records of a tile in LDS: record j (32 floats, output pass) or its B
 // half (16 floats, summary pass) at bc_base + j * kRec<MODE> bytes.
 template <int MODE> constexpr int kRec = MODE == 0 ? 128 : 64;
-
-// Row copies.  One instruction fills 1 KB of LDS with 16 rows x 64 bytes
-// (four consecutive 16-byte pieces of each row), so each row's pieces leave
-// as one request; lane i takes row 16k + i%16, piece 4h + i/16 of the
-// instruction (h, k).  Per tensor the LDS image is [h][k][p4][r] in 16-byte
-// slots, and lane l finds piece p of its own row at slot
-// (p/4) 256 + (p%4) 16 + (l/16) 64 + l%16.
-struct RowDma {
-    const char* base[3];   // per tensor: the block's first row (wave-uniform)
-    uint32_t kb[4];        // per row group k: byte offset of its first row (clamped)
-    uint32_t voff[4];      // per row group: this lane's row and piece, from kb[k]
-};
-// (Both offsets are below 64 rows x L x 4 bytes, under 2^32 for L <= 2^24.)
-
-template <typename Tin, int NT>
-__device__ __forceinline__ void issue_rows(const RowDma& R, int64_t t0, uint32_t lds_base) {
-    constexpr int NP = In<Tin>::kPieces;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const char* bt = R.base[t] + t0 * (int64_t)sizeof(Tin);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const char* g = bt + R.kb[k] + R.voff[k];
-            const uint32_t s0 = lds_base + (uint32_t)(t * NP + k) * 1024u;
-            dma_at<0>(g, s0);
-            if constexpr (NP == 8) dma_at<64>(g, s0 + 4 * 1024u);
-        }
-    }
-}
 
 // The tile's B/C records: 1 KB per instruction, contiguous in memory.
 template <int MODE>
@@ -306,12 +259,6 @@ template <typename Tin>
 struct Blk {
     uint32_t u[In<Tin>::kWords], d[In<Tin>::kWords], z[In<Tin>::kWords];
 };
-
-// 16-byte slot of piece p of tensor t for the lane whose slot offset is ls
-template <typename Tin>
-__device__ __forceinline__ int piece_slot(int t, int p, int ls) {
-    return t * In<Tin>::kPieces * kRows + (p >> 2) * 256 + (p & 3) * 16 + ls;
-}
 
 template <typename Tin, int MODE>
 __device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int blk, int ls) {
@@ -366,29 +313,18 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
         (int)((uint32_t)min<int64_t>(kRows, a.dim - d0) * yrb), 0x00020000);
     // row copies: the block's first row per tensor, row groups clamped to the
     // block's rows below dim (rows past it read the last one, never stored)
-    RowDma R;
+    RowDma<Tin> R;
     {
         const int64_t row0 = b * a.dim + d0;
-        const uint32_t rb = (uint32_t)(a.L * (int64_t)sizeof(Tin));
-        const int last = (int)min<int64_t>(kRows, a.dim - d0) - 1;
-        R.base[0] = reinterpret_cast<const char*>(uniform_ptr(reinterpret_cast<const float*>(
-            reinterpret_cast<const Tin*>(a.u) + row0 * a.L)));
-        R.base[1] = reinterpret_cast<const char*>(uniform_ptr(reinterpret_cast<const float*>(
-            reinterpret_cast<const Tin*>(a.delta) + row0 * a.L)));
-        R.base[2] = has_z ? reinterpret_cast<const char*>(uniform_ptr(reinterpret_cast<const float*>(
-                                reinterpret_cast<const Tin*>(a.z) + row0 * a.L)))
-                          : R.base[0];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int k0 = min(16 * k, last);
-            R.kb[k] = (uint32_t)k0 * rb;
-            R.voff[k] = (uint32_t)min(lane & 15, last - k0) * rb + 16u * (uint32_t)(lane >> 4);
-        }
+        const Tin* pu = reinterpret_cast<const Tin*>(a.u) + row0 * a.L;
+        const Tin* pd = reinterpret_cast<const Tin*>(a.delta) + row0 * a.L;
+        const Tin* pz = has_z ? reinterpret_cast<const Tin*>(a.z) + row0 * a.L : pu;
+        R.init(pu, pd, pz, a.L, (int)min<int64_t>(kRows, a.dim - d0) - 1, lane);
     }
-    const int ls = (lane >> 4) * 64 + (lane & 15);   // this lane's LDS slot offset
+    const int ls = rows::lane_slot(lane);   // this lane's LDS slot offset
 
     // this batch's B/C, 32 floats per token; the address is wave-uniform
-    const float* bcb = uniform_ptr(a.bcq + (b * a.L) * (2 * kNS));
+    const float* bcb = rows::uniform(a.bcq + (b * a.L) * (2 * kNS));
     const int64_t t_full_end = a.vec_ok ? t_begin + ((t_end - t_begin) / kTile) * kTile : t_begin;
     const uint32_t bc_base0 = lds_base + (uint32_t)(NT * In<Tin>::kPieces * kRows * 16);
     // request the first tile before the per-row set-up and the carry-in fold,
@@ -740,6 +676,23 @@ int m1_chunk_align() { return kChunkAlign; }
 int m1_rows_per_block() { return kRows; }
 int m1_waves_per_block() { return 1; }
 size_t m1_bc_bytes(int64_t batch, int64_t L) { return (size_t)batch * L * 2 * kNS * sizeof(float); }
+
+hipError_t launch_m1_bc(const void* B, const void* C, int64_t batch, int N, int64_t L, float* bcq, int in_bf16,
+                        hipStream_t stream) {
+    M1Args a{};
+    a.B = B;
+    a.C = C;
+    a.batch = batch;
+    a.N = N;
+    a.L = L;
+    a.bcq = bcq;
+    const dim3 grid((unsigned)(batch * ((L + 31) / 32)));
+    if (in_bf16)
+        hipLaunchKernelGGL(m1_bc_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(m1_bc_kernel<float>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_m1(const M1Args& a, int in_bf16, int out_bf16, hipStream_t stream) {
     if (in_bf16 && out_bf16) return launch_dt<uint16_t, uint16_t>(a, stream);

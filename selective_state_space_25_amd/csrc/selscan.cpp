@@ -468,11 +468,17 @@ selscan_status_t selscan_bwd(const selscan_shape_t* s, const void* u, const void
         a.dbias = ddelta_bias; a.dh0 = dh0;
         a.batch = s->batch; a.dim = s->dim; a.L = s->seqlen; a.N = (int)s->dstate; a.softplus = softplus;
         a.chunk = plan.chunk; a.G = plan.G;
+        {   // rows on 16-byte boundaries: the summary pass runs one channel per lane
+            const int64_t si = s->in_dtype == SELSCAN_BF16 ? 2 : 4, so = s->out_dtype == SELSCAN_BF16 ? 2 : 4;
+            a.lane_sum = aligned16(u) && aligned16(delta) && (!z || aligned16(z)) && aligned16(dout) &&
+                         (s->seqlen * si) % 16 == 0 && (s->seqlen * so) % 16 == 0 &&
+                         env_int("SELSCAN_BWD_LANE_SUMMARY", 1) != 0;
+        }
         selscan::m1_bwd_carve(a, ws.ptr);
         if (log_plans())
-            std::fprintf(stderr, "[selscan] m1 bwd B=%lld D=%lld N=%lld L=%lld chunks=%lld chunk=%lld ws=%zu\n",
+            std::fprintf(stderr, "[selscan] m1 bwd B=%lld D=%lld N=%lld L=%lld chunks=%lld chunk=%lld ws=%zu lane_sum=%d\n",
                          (long long)s->batch, (long long)s->dim, (long long)s->dstate, (long long)s->seqlen,
-                         (long long)plan.G, (long long)plan.chunk, plan.ws_bytes);
+                         (long long)plan.G, (long long)plan.chunk, plan.ws_bytes, a.lane_sum);
         hipError_t e = selscan::launch_m1_bwd(a, s->in_dtype == SELSCAN_BF16, s->out_dtype == SELSCAN_BF16, hs);
         ws.release();
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));

@@ -75,6 +75,21 @@ def test_chunked_time_matches_oracle(gpu, monkeypatch, chunk):
     _check_grads(_gpu(inp, dout), _oracle(inp, dout))
 
 
+@pytest.mark.parametrize("lane", ["0", "1"])
+@pytest.mark.parametrize("dtype,dout_dtype,a_kind,gate", [
+    (torch.bfloat16, torch.float32, "s4d_jitter", True), (torch.bfloat16, torch.bfloat16, "random", True),
+    (torch.float32, torch.float32, "s4d", False), (torch.float32, torch.bfloat16, "random", True)])
+def test_summary_pass_forms(gpu, monkeypatch, lane, dtype, dout_dtype, a_kind, gate):
+    """Rows on 16-byte boundaries take the one-channel-per-lane summary pass
+    unless it is switched off; both forms match the oracle with several
+    chunks, a last chunk of one 32-token tile plus 8 tokens, a partial
+    64-channel block, structured and general A, every dtype pair."""
+    monkeypatch.setenv("SELSCAN_BWD_LANE_SUMMARY", lane)
+    monkeypatch.setenv("SELSCAN_BWD_CHUNK", "64")
+    inp, dout = _case(2, 100, 16, 1000, dtype, a_kind=a_kind, seed=5, dout_dtype=dout_dtype, gate=gate)
+    _check_grads(_gpu(inp, dout), _oracle(inp, dout))
+
+
 @pytest.mark.parametrize("N", [1, 3, 8, 16])
 @pytest.mark.parametrize("a_kind", ["s4d", "random"])
 def test_state_sizes(gpu, monkeypatch, N, a_kind):
