@@ -79,6 +79,7 @@ struct BwdArgs {
     float* wck;     // [rows, tiles] sum of Delta from the chunk's start to the same tokens
     float* bcq;     // [batch, L, 32] fp32 records of B and C (the lane-per-channel summary pass)
     int lane_sum;   // the summary pass runs one channel per lane (rows 16-byte aligned)
+    int chunk_img;  // the chunk pass reads 32-token row images (lane_sum, bf16 inputs, L and chunk multiples of 32)
     int64_t batch, dim, L;
     int64_t chunk;  // tokens per chunk: a multiple of m1_bwd_tile(), at most m1_bwd_max_chunk()
     int64_t G;      // chunks

@@ -792,8 +792,35 @@ __device__ __forceinline__ float reduce_bc(const float* v, int rr) {
     return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
 }
 
-template <typename Tin, typename Tout, bool SP, bool ST>
-__device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
+// Row images for the chunk pass (bf16 inputs, rows on 16-byte boundaries,
+// chunks and L multiples of 32): 32 tokens of the block's rows of delta, u,
+// z and dout copied into LDS 64 bytes per row per instruction
+// (lds_rows.hpp), and the 32 tokens' fp32 B/C records.  Wave w copies row
+// group w of every tensor and records 8w .. 8w+7.  An image serves two
+// 16-token tiles; the producer mapping reads its 4 tokens per tensor from
+// it instead of from global memory.
+template <typename Tin, typename Tout>
+struct ImgSmem {
+    static constexpr int kIn = rows::kPieces<Tin>, kOut = rows::kPieces<Tout>;
+    uint4 img[(3 * kIn + kOut) * 64];   // delta, u, z, then dout
+    alignas(16) float rec[32][2 * kSt];
+};
+
+// This wave's row group of a 32-token image of one tensor (first row of the
+// block at `row0`, `last` its last real row) into LDS at `slot0` (the
+// tensor's image).
+template <typename T>
+__device__ __forceinline__ void img_rows(const T* row0, int64_t L, int last, int t, uint32_t slot0) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int k0 = min(16 * w, last);
+    const char* g = reinterpret_cast<const char*>(row0 + (int64_t)(k0 + min(lane & 15, last - k0)) * L + t) +
+                    16 * (lane >> 4);
+    rows::dma_at<0>(g, slot0 + (uint32_t)w * 1024u);
+    if constexpr (rows::kPieces<T> == 8) rows::dma_at<64>(g, slot0 + (uint32_t)(4 + w) * 1024u);
+}
+
+template <typename Tin, typename Tout, bool SP, bool ST, bool RI>
+__device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgSmem<Tin, Tout>* im) {
     const Blk k = blk(a);
     const Con c(a, k);
     const Pro p(a, k);
@@ -843,11 +870,30 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
     float4 zck;
     float wc;
     auto fetch = [&](int tile) {   // c.rc is clamped in bounds
-        fetch_raw<Tin, Tout, true, true, true, true>(a, k, p, in, k.t0 + tile * kT, r);
+        if constexpr (!RI) fetch_raw<Tin, Tout, true, true, true, true>(a, k, p, in, k.t0 + tile * kT, r);
         const uint32_t ct = ckrow + (uint32_t)(tile0 + tile);
         zck = ldo(reinterpret_cast<const float4*>(ckz), ct * 4 + c.q);
         wc = ldo(wck, ct);
     };
+    // image q covers tokens t0 + 32q .. t0 + 32q + 31 (tiles 2q, 2q + 1)
+    const int img_last = (int)min<int64_t>(kCh, a.dim - k.cb * kCh) - 1;
+    auto issue_img = [&](int q) {
+        if constexpr (RI) {
+            const int t = k.t0 + 32 * q;
+            const uint32_t base = (uint32_t)(uintptr_t)(rows::ldsptr)im->img;
+            constexpr int kIn = ImgSmem<Tin, Tout>::kIn;
+            const int64_t o = k.row0 * a.L;
+            img_rows<Tin>(reinterpret_cast<const Tin*>(a.delta) + o, a.L, img_last, t, base);
+            img_rows<Tin>(reinterpret_cast<const Tin*>(a.u) + o, a.L, img_last, t, base + kIn * 1024u);
+            img_rows<Tin>(reinterpret_cast<const Tin*>(a.z ? a.z : a.delta) + o, a.L, img_last, t,
+                          base + 2 * kIn * 1024u);
+            img_rows<Tout>(reinterpret_cast<const Tout*>(a.dout) + o, a.L, img_last, t, base + 3 * kIn * 1024u);
+            const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+            const float* g = a.bcq + ((int64_t)k.b * a.L + t + 8 * w + (lane >> 3)) * (2 * kSt) + (lane & 7) * 4;
+            rows::dma_at<0>(g, (uint32_t)(uintptr_t)(rows::ldsptr)&im->rec[0][0] + (uint32_t)w * 1024u);
+        }
+    };
+    if constexpr (RI) issue_img(k.tiles / 2 - 1);
     fetch(k.tiles - 1);
 
     // the block's rows of du, ddelta, dz (at most 64 rows x 2^22 tokens x 4
@@ -871,17 +917,55 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
     for (int jh = 0; jh < kT / kRT; ++jh) part.st(false, 0, 0.0f);
     for (int tile = k.tiles - 1; tile >= 0; --tile) {
         const int tt0 = k.t0 + tile * kT;
+        float vx[kPT], vu[kPT], vz[kPT], vg[kPT], vb = 0.0f, vc = 0.0f;
+        if constexpr (RI) {
+            if (tile & 1) {   // first tile of an image: this wave's copies are in, then everyone's
+                rows::wait_vm();
+                lds_barrier();
+            }
+            // this thread's 4 tokens of row pr from the image's half tile & 1
+            constexpr int kIn = ImgSmem<Tin, Tout>::kIn;
+            const int pos = (tile & 1) * kT + p.pj;
+            const int ls = rows::lane_slot(p.pr);
+            auto four = [&](const uint4* base, int t, auto tag, float* v) {
+                using T = decltype(tag);
+                const char* q = reinterpret_cast<const char*>(base + rows::piece_slot<T>(t, pos * (int)sizeof(T) / 16, ls)) +
+                                (pos * (int)sizeof(T)) % 16;
+                if constexpr (sizeof(T) == 2) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(q);
+                    v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+                } else {
+                    const uint4 w = *reinterpret_cast<const uint4*>(q);
+                    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+                    v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+                }
+            };
+            four(im->img, 0, Tin{}, vx);
+            four(im->img, 1, Tin{}, vu);
+            four(im->img, 2, Tin{}, vz);
+            four(im->img + 3 * kIn * 64, 0, Tout{}, vg);
+            vb = im->rec[(tile & 1) * kT + bj][bn];
+            vc = im->rec[(tile & 1) * kT + bj][kSt + bn];
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < kPT; ++jj) {
+                vx[jj] = f32_of(r.x[jj]); vu[jj] = f32_of(r.u[jj]);
+                vz[jj] = f32_of(r.z[jj]); vg[jj] = f32_of(r.g[jj]);
+            }
+            vb = f32_of(r.bv);
+            vc = f32_of(r.cv);
+        }
         // per-channel tile values
 #pragma unroll
         for (int jj = 0; jj < kPT; ++jj) {
             const int j = p.pj + jj;
             const bool ok = p.ok && tt0 + j < k.t_end;
             float dd;
-            const float dt = delta_of<SP>(f32_of(r.x[jj]) + p.bias, dd);
-            const float g = f32_of(r.g[jj]), uu = f32_of(r.u[jj]);
+            const float dt = delta_of<SP>(vx[jj] + p.bias, dd);
+            const float g = vg[jj], uu = vu[jj];
             float dy = g, zf = 0.0f;
             if (a.z) {
-                const float zz = f32_of(r.z[jj]), sg = sigmoid(zz);
+                const float zz = vz[jj], sg = sigmoid(zz);
                 dy = g * zz * sg;
                 zf = g * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
             }
@@ -894,10 +978,15 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm) {
         }
         if (bc_thread) {
             const bool ok = bc_valid(a, k, tt0);
-            sm.B[bj][bn] = ok ? f32_of(r.bv) : 0.0f;
-            sm.C[bj][bn] = ok ? f32_of(r.cv) : 0.0f;
+            sm.B[bj][bn] = ok ? vb : 0.0f;
+            sm.C[bj][bn] = ok ? vc : 0.0f;
         }
         lds_barrier();
+        // every thread has read the image: the second tile of an image
+        // requests the next (earlier) one
+        if constexpr (RI) {
+            if (!(tile & 1) && tile > 0) issue_img(tile / 2 - 1);
+        }
         // the tile's first state: zero-start checkpoint + decayed entering
         // state (taken from the prefetch registers before they are reused)
         float ck[4];
@@ -1031,9 +1120,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void m1_bwd_chunk_kernel(BwdArgs a) {
     __shared__ ChunkSmem sm;
     if (structured_block(a))
-        chunk_body<Tin, Tout, SP, true>(a, sm);
+        chunk_body<Tin, Tout, SP, true, false>(a, sm, nullptr);
     else
-        chunk_body<Tin, Tout, SP, false>(a, sm);
+        chunk_body<Tin, Tout, SP, false, false>(a, sm, nullptr);
+}
+
+// The chunk pass with row images (see ImgSmem).
+template <typename Tin, typename Tout, bool SP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void m1_bwd_chunk_img_kernel(BwdArgs a) {
+    __shared__ ChunkSmem sm;
+    __shared__ ImgSmem<Tin, Tout> im;
+    if (structured_block(a))
+        chunk_body<Tin, Tout, SP, true, true>(a, sm, &im);
+    else
+        chunk_body<Tin, Tout, SP, false, true>(a, sm, &im);
 }
 
 // dB, dC: sums of the channel-block partials; thread = (token, value) of 8
@@ -1093,6 +1194,8 @@ __global__ __launch_bounds__(256) void m1_bwd_param_reduce_kernel(BwdArgs a) {
     }
 }
 
+hipError_t launch_reduces(const BwdArgs& a, hipStream_t stream);
+
 template <typename Tin, typename Tout, bool SP>
 hipError_t launch_sp(const BwdArgs& a, hipStream_t stream) {
     const int64_t nbc = (a.dim + kCh - 1) / kCh;
@@ -1116,8 +1219,20 @@ hipError_t launch_sp(const BwdArgs& a, hipStream_t stream) {
     }
     {
         KTime kt("m1_bwd_chunk", stream);
-        hipLaunchKernelGGL((m1_bwd_chunk_kernel<Tin, Tout, SP>), dim3(blocks), dim3(kThreads), 0, stream, a);
+        bool img = false;
+        if constexpr (sizeof(Tin) == 2) {
+            if (a.chunk_img) {
+                hipLaunchKernelGGL((m1_bwd_chunk_img_kernel<Tin, Tout, SP>), dim3(blocks), dim3(kThreads), 0, stream, a);
+                img = true;
+            }
+        }
+        if (!img)
+            hipLaunchKernelGGL((m1_bwd_chunk_kernel<Tin, Tout, SP>), dim3(blocks), dim3(kThreads), 0, stream, a);
     }
+    return launch_reduces(a, stream);
+}
+
+hipError_t launch_reduces(const BwdArgs& a, hipStream_t stream) {
     {
         KTime kt("m1_bwd_bc_reduce", stream);
         const unsigned rb = (unsigned)(a.batch * ((a.L + kRT - 1) / kRT));

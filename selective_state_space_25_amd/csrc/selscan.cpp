@@ -473,6 +473,8 @@ selscan_status_t selscan_bwd(const selscan_shape_t* s, const void* u, const void
             a.lane_sum = aligned16(u) && aligned16(delta) && (!z || aligned16(z)) && aligned16(dout) &&
                          (s->seqlen * si) % 16 == 0 && (s->seqlen * so) % 16 == 0 &&
                          env_int("SELSCAN_BWD_LANE_SUMMARY", 1) != 0;
+            a.chunk_img = a.lane_sum && s->in_dtype == SELSCAN_BF16 && s->seqlen % 32 == 0 && plan.chunk % 32 == 0 &&
+                          env_int("SELSCAN_BWD_CHUNK_IMAGES", 1) != 0;
         }
         selscan::m1_bwd_carve(a, ws.ptr);
         if (log_plans())

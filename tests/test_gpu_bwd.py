@@ -90,6 +90,22 @@ def test_summary_pass_forms(gpu, monkeypatch, lane, dtype, dout_dtype, a_kind, g
     _check_grads(_gpu(inp, dout), _oracle(inp, dout))
 
 
+@pytest.mark.parametrize("images", ["0", "1"])
+@pytest.mark.parametrize("dout_dtype,a_kind,gate,chunk", [
+    (torch.float32, "s4d_jitter", True, "64"), (torch.bfloat16, "random", True, "96"),
+    (torch.float32, "random", False, "32"), (torch.float32, "s4d", True, "0")])
+def test_chunk_pass_row_images(gpu, monkeypatch, images, dout_dtype, a_kind, gate, chunk):
+    """bf16 inputs with L and the chunk multiples of 32 take the chunk pass
+    that reads 32-token row images from LDS unless it is switched off; both
+    match the oracle (a partial 64-channel block, several chunks, a shorter
+    last chunk for chunk 96)."""
+    monkeypatch.setenv("SELSCAN_BWD_CHUNK_IMAGES", images)
+    if chunk != "0":
+        monkeypatch.setenv("SELSCAN_BWD_CHUNK", chunk)
+    inp, dout = _case(2, 100, 16, 1024, torch.bfloat16, a_kind=a_kind, seed=9, dout_dtype=dout_dtype, gate=gate)
+    _check_grads(_gpu(inp, dout), _oracle(inp, dout))
+
+
 @pytest.mark.parametrize("N", [1, 3, 8, 16])
 @pytest.mark.parametrize("a_kind", ["s4d", "random"])
 def test_state_sizes(gpu, monkeypatch, N, a_kind):
