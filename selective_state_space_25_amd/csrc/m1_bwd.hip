@@ -582,9 +582,7 @@ __device__ __forceinline__ void body(const BwdArgs& a, uint4* lds) {
             uint32_t cu[Elt<Tin>::kW], cd[Elt<Tin>::kW], nu[Elt<Tin>::kW], nd[Elt<Tin>::kW];
             read_block<Tin>(cu, lds, 0, 0, ls);
             read_block<Tin>(cd, lds, 1, 0, ls);
-            // not unrolled: one block per basic block keeps the compiler from
-            // reading all the tile's records ahead and spilling them
-#pragma nounroll
+#pragma unroll
             for (int blk = 0; blk < kTile / kBlk; ++blk) {
                 if (blk + 1 < kTile / kBlk) {
                     read_block<Tin>(nu, lds, 0, blk + 1, ls);
@@ -605,9 +603,6 @@ __device__ __forceinline__ void body(const BwdArgs& a, uint4* lds) {
 #pragma unroll
                     for (int i = 0; i < Elt<Tin>::kW; ++i) { cu[i] = nu[i]; cd[i] = nd[i]; }
                 }
-                // one block at a time: otherwise the four blocks' record
-                // reads would all be hoisted to the tile's start and spill
-                asm volatile("" ::: "memory");
             }
             rows::wait_vm();
         }
@@ -668,7 +663,7 @@ __device__ __forceinline__ void body(const BwdArgs& a, uint4* lds) {
             read_block<Tin>(cd, lds, 0, NB - 1, ls);
             read_block<Tin>(cz, lds, 1, NB - 1, ls);
             read_block<Tout>(cg, gimg, 0, NB - 1, ls);
-#pragma nounroll
+#pragma unroll
             for (int bi = 0; bi < NB; ++bi) {
                 const int blk = NB - 1 - bi;
                 if (blk > 0) {
@@ -690,7 +685,6 @@ __device__ __forceinline__ void body(const BwdArgs& a, uint4* lds) {
 #pragma unroll
                     for (int i = 0; i < Elt<Tout>::kW; ++i) cg[i] = ng[i];
                 }
-                asm volatile("" ::: "memory");
             }
             rows::wait_vm();
         }
