@@ -135,10 +135,11 @@ def test_bf16_dout(gpu):
 
 
 @pytest.mark.parametrize("chunk", [0, 64])
-def test_initial_state_and_its_gradient(gpu, monkeypatch, chunk):
+@pytest.mark.parametrize("L", [400, 384])   # 384: the chunk pass's row images too
+def test_initial_state_and_its_gradient(gpu, monkeypatch, chunk, L):
     if chunk:
         monkeypatch.setenv("SELSCAN_BWD_CHUNK", str(chunk))
-    inp, dout = _case(2, 70, 16, 400, torch.bfloat16, seed=11)
+    inp, dout = _case(2, 70, 16, L, torch.bfloat16, seed=11)
     h0 = synth.m1_state(2, 70, 16, seed=11, device=DEV)
     got = _gpu(inp, dout, h0=h0)
     _check_grads(got, _oracle(inp, dout, h0=h0))
