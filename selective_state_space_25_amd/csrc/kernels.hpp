@@ -33,7 +33,7 @@ struct M1Args {
     float* ws_w;      // [rows, G] chunk sums of Delta / ln2
     float* bcq;       // [batch, L, 32] fp32 copy of B and C (B0..B15, C0..C15 per token)
     int64_t batch, dim, L;
-    int64_t chunk;    // tokens per chunk (a multiple of m1_chunk_align()); the last may be short
+    int64_t chunk;    // longest chunk in tokens; the kernels split a row's tiles evenly over G chunks
     int N;            // d_state
     int G;            // chunks per row
     int softplus;

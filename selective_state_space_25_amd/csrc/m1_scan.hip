@@ -297,8 +297,13 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     const bool row_ok = d0 + lane < a.dim;
     const int64_t d = row_ok ? d0 + lane : a.dim - 1;
     const int64_t row = b * a.dim + d;
-    const int64_t t_begin = (int64_t)g * a.chunk;
-    const int64_t t_end = min<int64_t>(a.L, t_begin + a.chunk);
+    // G chunks of whole tiles, as even as they can be: the first T mod G
+    // chunks take one tile more (T tiles in a row, the last possibly
+    // partial), and they are dispatched first, so that the wave slots they
+    // take are paired with the shorter chunks' waves
+    const int64_t T = (a.L + kTile - 1) / kTile, q = T / a.G, r = T % a.G;
+    const int64_t t_begin = kTile * ((int64_t)g * q + min<int64_t>(g, r));
+    const int64_t t_end = min<int64_t>(a.L, kTile * ((int64_t)(g + 1) * q + min<int64_t>(g + 1, r)));
     const bool has_z = MODE == 0 && a.z != nullptr;
 
     const Tin* urow = reinterpret_cast<const Tin*>(a.u) + row * a.L;

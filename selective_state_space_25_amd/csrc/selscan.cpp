@@ -127,9 +127,10 @@ M1Plan plan_m1(const selscan_shape_t* s) {
     const int64_t align = selscan::m1_chunk_align();
     G = std::max<int64_t>(1, std::min<int64_t>(G, (s->seqlen + align - 1) / align));
     G = std::min<int64_t>(G, 65535);
-    int64_t chunk = (s->seqlen + G - 1) / G;
-    chunk = (chunk + align - 1) / align * align;
-    G = (s->seqlen + chunk - 1) / chunk;
+    // the kernels split the row's tiles as evenly as they can: the first
+    // (tiles mod G) chunks take one tile more; chunk is the longest
+    const int64_t tiles = (s->seqlen + align - 1) / align;
+    const int64_t chunk = (tiles + G - 1) / G * align;
     p.G = (int)G;
     p.chunk = chunk;
     p.xcd = G % 8 == 0 && wgs * G < (int64_t(1) << 24) && env_int("SELSCAN_M1_XCD", 1) != 0;
