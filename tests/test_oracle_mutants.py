@@ -30,6 +30,9 @@ MUTANTS = {
     "m2_group": ("const int64_t g = hh / heads_per_group;", "const int64_t g = hh % ng;"),
     "m2_dt_head": ("double xv = dt[bt * nh + hh] + (dtb ? dtb[hh] : 0.0);", "double xv = dt[bt * nh + (hh % 1)] + (dtb ? dtb[hh] : 0.0);"),
     "m2_state_order": ("s[n] = dA * s[n] + delt * Bt[n] * xt;", "s[n] = dA * s[n] + delt * Bt[nn - 1 - n] * xt;"),
+    "m2_h0_ignored": ("s[n] = h0 ? h0[unit * nn + n] : 0.0;", "s[n] = 0.0;"),
+    "m2_h0_transposed": ("s[n] = h0 ? h0[unit * nn + n] : 0.0;",
+                         "s[n] = h0 ? h0[((b * nh + hh) * nn + n) * np + p] : 0.0;"),
     "bwd_adjoint_undecayed": ("lam[n] = a * l;", "lam[n] = l;"),
     "bwd_no_state_path": ("ddl += l * (bb * ur[t] + A[d * nn + n] * a * hp);", "ddl += l * (bb * ur[t]);"),
     "bwd_softplus_derivative": ("ddl / (1.0 + exp(-x))", "ddl / (1.0 + exp(x))"),

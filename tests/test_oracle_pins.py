@@ -14,7 +14,8 @@ wrong index or a transposed operand anywhere in the oracle fails at least one:
   [B, N, L] layout of B and C         brute force with asymmetric B, C
   [D, N] layout of A                  brute force with asymmetric A
   [B, D, N] layout of last_state      one-hot C
-  initial state h0                    split = whole
+  initial state h0                    split = whole (Mamba-1 and Mamba-2)
+  [B, H, P, N] layout of Mamba-2 h0   x = 0 decay closed form, one-hot C
   Mamba-2 group/head mapping          Mamba-2 = broadcast Mamba-1, brute force
 
 Sources of the definitions: the "Understanding Mamba and Selective State Space
@@ -385,6 +386,52 @@ def test_m2_one_hot_c_reads_out_last_state():
         np.testing.assert_array_equal(y[:, -1], last[..., k])
 
 
+# Mamba-2 from a carried state (blog section 2.2: the scan resumes from the
+# state it was left in; README "Mamba-2": the state is [batch, heads, headdim,
+# d_state]).  Two pins: splitting the sequence and resuming from the first
+# part's last_state reproduces the whole; and with x = 0 the state only decays,
+# h_t = exp(A_h sum_{s<=t} Delta_s) h0, so a one-hot C reads out h0 scaled by a
+# closed-form factor -- which fixes h0's [B, H, P, N] layout on its own.
+def test_m2_split_equals_whole_with_h0():
+    rng = np.random.default_rng(17)
+    m = _rand_m2(rng, nl=23)
+    t1 = 9
+    seq = ("x", "dt", "B", "C", "z")
+    yw, lw = oracle.m2(**m)
+    ya, la = oracle.m2(**{k: (v[:, :t1] if k in seq else v) for k, v in m.items()})
+    yb, lb = oracle.m2(**{k: (v[:, t1:] if k in seq else v) for k, v in m.items()}, h0=la)
+    _close(np.concatenate([ya, yb], axis=1), yw, 1e-14)
+    _close(lb, lw, 1e-14)
+    # a nonzero h0 must change the result (an ignored h0 would pass the above
+    # only if la were zero, which it is not)
+    assert np.max(np.abs(la)) > 1e-3
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_m2_h0_decays_in_closed_form(softplus):
+    rng = np.random.default_rng(18)
+    m = _rand_m2(rng, nb=2, nl=7, nh=4, npd=3, ng=2, nn=5)
+    nb, nl, nh, npd = m["x"].shape
+    nn = m["B"].shape[-1]
+    m["x"] = np.zeros_like(m["x"])
+    m["D"] = None
+    m["z"] = None
+    if not softplus:
+        m["dt"] = np.abs(m["dt"]) * 0.3
+        m["dt_bias"] = None
+    h0 = rng.standard_normal((nb, nh, npd, nn))
+    raw = m["dt"] + (m["dt_bias"][None, None, :] if m["dt_bias"] is not None else 0.0)
+    dts = np.logaddexp(0.0, raw) if softplus else raw           # [nb, nl, nh]
+    decay = np.exp(m["A"][None, None, :] * np.cumsum(dts, axis=1))   # [nb, nl, nh]
+    for k in range(nn):
+        C = np.zeros_like(m["C"])
+        C[..., k] = 1.0
+        y, last = oracle.m2(**{**m, "C": C}, softplus=softplus, h0=h0)
+        ref = decay[:, :, :, None] * h0[:, None, :, :, k]       # [nb, nl, nh, npd]
+        _close(y, ref, 1e-13)
+    _close(last, decay[:, -1, :, None, None] * h0, 1e-13)
+
+
 def test_bad_arguments_are_rejected():
     with pytest.raises(RuntimeError):
         m = _rand_m2(np.random.default_rng(0), nh=3, ng=2)
@@ -414,10 +461,6 @@ def test_oracle_matches_stored_fixture(name):
 #   causal offset / zero padding   shift kernel, numpy.convolve, causality
 #   [dim, K] layout of w, bias     numpy.convolve with distinct rows
 #   silu after the bias            numpy.convolve + scipy expit
-
-def _silu(v):
-    return v * expit(v)
-
 
 @pytest.mark.parametrize("K", [1, 2, 4, 7])
 @pytest.mark.parametrize("silu", [False, True])
