@@ -24,14 +24,15 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9   # 256 CUs x 64 fp32 lanes/clk x 2.4 GHz (non-packed)
-HEADLINE = "mamba130m_l2k"
-EXTRA = ["mamba2p8b_l8k", "long_1m", "mamba2_mh"]
+# the largest single-GPU workload: the million-token Mamba-1 layer scan
+HEADLINE = "long_1m"
+EXTRA = ["mamba130m_l2k", "mamba2p8b_l8k", "mamba2p8b_l8k_alog", "mamba2_mh"]
 
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--extra", default=",".join(EXTRA),
@@ -313,32 +314,63 @@ def copy_calibration(device, gib):
     return n * 4
 
 
+def decay_path(w):
+    """Which Mamba-1 decay path the workload's A takes: "structured" when every
+    row has A[d, n] == fl32((n + 1) A[d, 0]) (one exponential per token),
+    else "general" (one per state update)."""
+    if w.kind != "m1":
+        return "scalar per head"
+    import torch
+    import synth
+    A = synth.a_matrix(w.dim, w.dstate, w.a_kind, 0)
+    n1 = torch.arange(1, w.dstate + 1, dtype=torch.float32)
+    s = (A == n1[None, :] * A[:, :1]).all(dim=1)
+    return "structured" if bool(s.all()) else ("general" if not bool(s.any()) else "mixed")
+
+
 def dominant_kernel(res):
     name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["total_ms"])
     return name, k
 
 
-def read_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 counter summary, or None when there is none or the kernel's
-    source has changed since the counters were taken."""
+def read_profile(workload, kernel):
+    """Fields of the committed rocprofv3 counter summary of `kernel` on
+    `workload` (profiles/traffic_<kernel>_<workload>.txt), or {} when there
+    is none or the kernel's source has changed since the counters were taken."""
     import hashlib
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     src = kv.get("source")
-    if not src or "source_sha256" not in kv or "hbm_bytes_per_launch" not in kv:
-        return None
+    if not src or "source_sha256" not in kv:
+        return {}
     spath = os.path.join(os.path.dirname(os.path.abspath(__file__)), src)
     if not os.path.exists(spath) or hashlib.sha256(open(spath, "rb").read()).hexdigest() != kv["source_sha256"]:
-        return None
-    return float(kv["hbm_bytes_per_launch"])
+        return {}
+    return kv
+
+
+def read_traffic(workload, kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled) or None."""
+    kv = read_profile(workload, kernel)
+    return float(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None
+
+
+def read_valu(workload, kernel):
+    """VALU lane-instructions per state update and VALU busy at the measured
+    clock, from the same committed summary, or None."""
+    kv = read_profile(workload, kernel)
+    out = {}
+    for k in ("valu_lane_ops_per_update", "valu_busy_at_measured_clock", "measured_clock_ghz"):
+        if k in kv:
+            out[k] = float(kv[k])
+    return out or None
 
 
 def cpu_baseline(name, seed, min_s=10.0, max_s=30.0):
@@ -358,8 +390,19 @@ def cpu_baseline(name, seed, min_s=10.0, max_s=30.0):
     w = synth.WORKLOADS[name]
     if w.kind != "m1":
         raise ValueError("cpu baseline implemented for Mamba-1 workloads")
-    inp = synth.m1_inputs(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.a_kind, seed=seed, device="cpu")
+    elems = w.batch * w.dim * w.seqlen
+    if elems <= (1 << 28):
+        inp = synth.m1_inputs(w.batch, w.dim, w.dstate, w.seqlen, w.dtype, w.a_kind, seed=seed, device="cpu")
+        what = f"{name}"
+    else:
+        # too large to hold in fp64 on the host: the first channels of batch
+        # element 0 at the full length (the oracle's time is linear in rows)
+        rows = max(1, (1 << 27) // w.seqlen)
+        inp = synth.m1_row_sample(w, rows, seed=seed)
+        what = f"the first {rows} of {w.dim} channels of batch element 0 of {name}"
     f64 = {k: (None if v is None else np.ascontiguousarray(v.double().numpy())) for k, v in inp.items()}
+    nb, nd, nl = f64["u"].shape
+    nn = f64["A"].shape[1]
 
     def one(rows_b):
         t = time.perf_counter()
@@ -369,16 +412,16 @@ def cpu_baseline(name, seed, min_s=10.0, max_s=30.0):
 
     # probe with one batch element, then size the sample
     t1 = one(1)
-    per_pass = t1 * w.batch
-    rows_b = w.batch if per_pass <= max_s else max(1, int(max_s / t1))
+    per_pass = t1 * nb
+    rows_b = nb if per_pass <= max_s else max(1, int(max_s / t1))
     passes, elapsed = 0, 0.0
     while elapsed < min_s or passes == 0:
         elapsed += one(rows_b)
         passes += 1
-    upd = passes * rows_b * w.dim * w.seqlen * w.dstate
+    upd = passes * rows_b * nd * nl * nn
     return {"value": upd / elapsed, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
-            "sample": f"{passes} pass(es) over {rows_b} of {w.batch} batch elements of {name} "
-                      f"({rows_b * w.dim} (batch, channel) rows, full L={w.seqlen}, N={w.dstate}), "
+            "sample": f"{passes} pass(es) over {rows_b} of {nb} batch elements of {what} "
+                      f"({rows_b * nd} (batch, channel) rows, full L={nl}, N={nn}), "
                       f"fp64 with {cores} OpenMP threads, {elapsed:.1f} s of oracle time",
             "seconds": elapsed}
 
@@ -410,13 +453,18 @@ def main():
             head["copy_calibration_bytes_each_way"] = copy_calibration(device, args.copy_gib)
         print(json.dumps(head))
         return
+    import synth
     extras = {}
     for name in [e for e in args.extra.split(",") if e and e != args.workload]:
-        _, r = time_workload(name, max(3, min(args.steps, 20)), 2, args.seed, device)
+        ew = synth.WORKLOADS[name]
+        steps = max(10, min(args.steps, 50))
+        _, r = time_workload(name, steps, 3, args.seed, device)
         kn, kk = dominant_kernel(r)
+        r["decay_path"] = decay_path(ew)
         r["dominant_kernel"] = {"name": kn, "avg_ms": kk["avg_ms"],
                                 "gbs": r["algorithmic_bytes"] / (kk["avg_ms"] * 1e-3) / 1e9,
-                                "traffic": read_traffic(name, kn)}
+                                "frac": r["algorithmic_bytes"] / (kk["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "traffic": read_traffic(name, kn), "valu": read_valu(name, kn)}
         extras[name] = r
 
     kname, k = dominant_kernel(head)
@@ -444,13 +492,18 @@ def main():
                                                              "ngroups": w.ngroups}),
                    "inputs": str(w.dtype).replace("torch.", ""), "state": "float32",
                    "output": str(w.out_dtype).replace("torch.", ""),
-                   "parallelism": "single GPU"},
+                   "decay_path": decay_path(w), "parallelism": "single GPU"},
         "hbm_gbs": head["hbm_gbs"],
         "hbm_frac_of_peak": head["hbm_frac_of_peak"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kname, "avg_launch_ms": avg_ms, "launches": k["launches"],
-                     "bytes_per_launch": head["algorithmic_bytes"]},
+                     "bytes_per_launch": head["algorithmic_bytes"],
+                     # the whole call (every kernel and the gaps between them)
+                     "whole_call": {"achieved": head["hbm_gbs"], "frac": head["hbm_frac_of_peak"],
+                                    "ms": head["ms_per_step"]},
+                     "kernels": {n: v["avg_ms"] for n, v in head["kernels"].items()},
+                     "valu": read_valu(args.workload, kname)},
         "workloads": {args.workload: head, **extras},
         "library": ss.version(),
     }

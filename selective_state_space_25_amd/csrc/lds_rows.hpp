@@ -53,7 +53,7 @@ __device__ __forceinline__ void dma_at(const void* g, uint32_t slot) {
 // Addresses of the row copies of up to three tensors of element type T with
 // the same row length L.  Rows past the block's last real row read that row
 // (their values are never stored).  Both offsets stay below 64 rows x L x 4
-// bytes, under 2^32 for L <= 2^24.
+// bytes, under 2^32 for L < 2^24.
 template <typename T>
 struct RowDma {
     const char* base[3];   // per tensor: the block's first row (wave-uniform)

@@ -66,13 +66,30 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// The current device must be a gfx950.  The architecture check runs once per
+// device (cached like device_cus()); later calls only read the current device.
 selscan_status_t device_check() {
+    static std::mutex mu;
+    static signed char verdict[64] = {0};   // 0 unknown, 1 gfx950, -1 other
+    static std::string other[64];
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(SELSCAN_ERR_NO_DEVICE, "no HIP device available");
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(SELSCAN_ERR_NO_DEVICE, "no HIP device available");
+    if (dev < 64) {
+        std::lock_guard<std::mutex> lk(mu);
+        if (verdict[dev] == 1) return SELSCAN_OK;
+        if (verdict[dev] == -1)
+            return fail(SELSCAN_ERR_NO_DEVICE, "libselscan is built for gfx950, device is " + other[dev]);
+    }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
         return fail(SELSCAN_ERR_NO_DEVICE, "cannot query the HIP device");
-    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) {
+        std::lock_guard<std::mutex> lk(mu);
+        verdict[dev] = ok ? 1 : -1;
+        if (!ok) other[dev] = prop.gcnArchName;
+    }
+    if (!ok)
         return fail(SELSCAN_ERR_NO_DEVICE, std::string("libselscan is built for gfx950, device is ") +
                                                prop.gcnArchName);
     return SELSCAN_OK;
@@ -100,8 +117,10 @@ selscan_status_t check_m1_shape(const selscan_shape_t* s) {
         return fail(SELSCAN_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte counts");
     if (s->batch * ((s->dim + 63) / 64) > 0x7fffffff || s->batch * ((s->seqlen + 31) / 32) > 0x7fffffff)
         return fail(SELSCAN_ERR_UNSUPPORTED, "too many channel blocks or token tiles for one launch");
-    // the scan's row copies address a block's 64 rows with 32-bit offsets
-    if (s->seqlen > (int64_t(1) << 24)) return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-1 scan supports seqlen <= 2^24");
+    // the scan addresses a block's 64 rows with 32-bit byte offsets, and the
+    // buffer descriptor of its y stores spans 64 rows of fp32 y: 64 L 4 bytes
+    // stay below 2^32 only for L < 2^24
+    if (s->seqlen >= (int64_t(1) << 24)) return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-1 scan supports seqlen < 2^24");
     return SELSCAN_OK;
 }
 
@@ -305,6 +324,8 @@ selscan_status_t selscan_fwd_h0(const selscan_shape_t* s, const void* u, const v
         if (!u || !delta || !A || !B || !C || !y)
             return fail(SELSCAN_ERR_INVALID_ARG, "u, delta, A, B, C and y must be non-NULL");
         if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        if (h0 && last_state && static_cast<const void*>(h0) == static_cast<const void*>(last_state))
+            return fail(SELSCAN_ERR_INVALID_ARG, "h0 and last_state must not alias");
         st = device_check();
         if (st != SELSCAN_OK) return st;
         const M1Plan plan = plan_m1(s);
@@ -361,6 +382,8 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* s, const void* 
         if (!x || !dt || !A || !B || !C || !y)
             return fail(SELSCAN_ERR_INVALID_ARG, "x, dt, A, B, C and y must be non-NULL");
         if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        if (h0 && last_state && static_cast<const void*>(h0) == static_cast<const void*>(last_state))
+            return fail(SELSCAN_ERR_INVALID_ARG, "h0 and last_state must not alias");
         st = device_check();
         if (st != SELSCAN_OK) return st;
         const M2Plan plan = plan_m2(s);

@@ -17,6 +17,9 @@ Distributions (the workloads' definitions):
   D[d] ~ N(0, 1) per channel;
   A[d, n] = -(n + 1)                              ("s4d", S4D-real);
   A[d, n] = -(n + 1) * exp(eps_d), eps_d ~ N(0, 0.1) per row ("s4d_jitter");
+  A[d, n] = -exp(A_log[d, n]), A_log = log(n + 1) + eps_d in fp32 ("alog": the
+      same values up to the roundings of log and exp, which leave most rows
+      without the exact (n + 1) A[d, 0] structure, as a trained A_log would);
   Mamba-2: A[h] = -U[1, 16], D[h] ~ N(0, 1), dt_bias as above, all per head.
 """
 from __future__ import annotations
@@ -65,6 +68,10 @@ WORKLOADS = {
     "long_1m": Workload("long_1m", "m1", batch=1, seqlen=1 << 20, dstate=16, dtype=torch.bfloat16,
                         dim=2048, a_kind="s4d_jitter",
                         note="million-token scan: d_inner 2048, d_state 16, batch 1, L 2^20"),
+    "mamba2p8b_l8k_alog": Workload("mamba2p8b_l8k_alog", "m1", batch=4, seqlen=8192, dstate=16,
+                                   dtype=torch.bfloat16, dim=5120, a_kind="alog",
+                                   note="Mamba-2.8b-shaped layer with A = -exp(A_log) (no exact S4D-real "
+                                        "structure: the general decay path)"),
     "mamba2_mh": Workload("mamba2_mh", "m2", batch=8, seqlen=4096, dstate=128, dtype=torch.bfloat16,
                           nheads=32, headdim=64, ngroups=1,
                           note="Mamba-2 multi-head: 32 heads x headdim 64, d_state 128, ngroups 1, "
@@ -111,6 +118,11 @@ def a_matrix(dim: int, dstate: int, kind: str, seed: int) -> torch.Tensor:
         g = _gen(seed, "A", "cpu")
         scale = torch.exp(torch.randn(dim, generator=g, dtype=torch.float32) * 0.1)
         return (-(n1[None, :] * scale[:, None])).contiguous()
+    if kind == "alog":   # A = -exp(A_log), A_log = log(n + 1) + eps_d, both steps in fp32
+        g = _gen(seed, "A", "cpu")
+        eps = torch.randn(dim, generator=g, dtype=torch.float32) * 0.1
+        a_log = torch.log(n1)[None, :] + eps[:, None]
+        return (-torch.exp(a_log)).contiguous()
     if kind == "random":  # unstructured negative A, for the general decay path
         g = _gen(seed, "A", "cpu")
         return (-torch.rand(dim, dstate, generator=g, dtype=torch.float32) * 15.9 - 0.1).contiguous()
@@ -136,6 +148,24 @@ def m1_inputs(batch, dim, dstate, seqlen, dtype=torch.bfloat16, a_kind="s4d", se
         "delta_bias": delta_bias(dim, seed).to(dev) if bias else None,
     }
     return out
+
+
+def m1_row_sample(w: "Workload", rows: int, seed: int = 0):
+    """The first `rows` channels of batch element 0 of a Mamba-1 workload, on
+    the CPU, with the workload's distributions (a bounded sample for timing
+    the CPU oracle on shapes too large for it)."""
+    rows = max(1, min(rows, w.dim))
+    cpu = torch.device("cpu")
+    return {
+        "u": _normal((1, rows, w.seqlen), seed, "u", w.dtype, cpu),
+        "delta": _normal((1, rows, w.seqlen), seed, "delta", w.dtype, cpu),
+        "B": _normal((1, w.dstate, w.seqlen), seed, "B", w.dtype, cpu),
+        "C": _normal((1, w.dstate, w.seqlen), seed, "C", w.dtype, cpu),
+        "A": a_matrix(w.dim, w.dstate, w.a_kind, seed)[:rows].contiguous(),
+        "z": _normal((1, rows, w.seqlen), seed, "z", w.dtype, cpu),
+        "D": torch.randn(w.dim, generator=_gen(seed, "D", "cpu"))[:rows].contiguous(),
+        "delta_bias": delta_bias(w.dim, seed)[:rows].contiguous(),
+    }
 
 
 def m2_inputs(batch, seqlen, nheads, headdim, ngroups, dstate, dtype=torch.bfloat16, seed=0,
@@ -206,5 +236,5 @@ def algorithmic_bytes(w: Workload) -> int:
             + w.batch * w.nheads * w.headdim * w.dstate * 4)
 
 
-__all__ = ["WORKLOADS", "Workload", "m1_inputs", "m2_inputs", "workload_inputs",
+__all__ = ["WORKLOADS", "Workload", "m1_inputs", "m1_row_sample", "m2_inputs", "workload_inputs",
            "algorithmic_bytes", "bwd_algorithmic_bytes", "a_matrix", "delta_bias", "m1_dout", "m1_state"]

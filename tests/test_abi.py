@@ -53,7 +53,8 @@ FAKE = 4096  # a non-null pointer value; never dereferenced because validation f
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, ss.ERR_INVALID_ARG), ("dim", -1, ss.ERR_INVALID_ARG), ("seqlen", 0, ss.ERR_INVALID_ARG),
     ("dstate", 0, ss.ERR_INVALID_ARG), ("dstate", 17, ss.ERR_UNSUPPORTED), ("in_dtype", 7, ss.ERR_UNSUPPORTED),
-    ("seqlen", 1 << 62, ss.ERR_INVALID_ARG), ("seqlen", (1 << 24) + 1, ss.ERR_UNSUPPORTED)])
+    ("seqlen", 1 << 62, ss.ERR_INVALID_ARG), ("seqlen", 1 << 24, ss.ERR_UNSUPPORTED),
+    ("seqlen", (1 << 24) + 1, ss.ERR_UNSUPPORTED)])
 def test_m1_bad_shape_rejected(field, value, status):
     s = _m1(**{field: value})
     r = ss.lib().selscan_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE, None, None)
@@ -131,6 +132,17 @@ def test_h0_entry_points_validate_like_fwd():
     r = ss.lib().selscan_mamba2_fwd_h0(ctypes.byref(m2), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None,
                                        FAKE, None, None)
     assert r == ss.ERR_INVALID_ARG
+
+
+def test_h0_aliasing_last_state_rejected():
+    s = _m1()
+    r = ss.lib().selscan_fwd_h0(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE, FAKE,
+                                FAKE, None)
+    assert r == ss.ERR_INVALID_ARG and "alias" in ss.last_error()
+    m2 = _m2()
+    r = ss.lib().selscan_mamba2_fwd_h0(ctypes.byref(m2), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, FAKE,
+                                       FAKE, FAKE, None)
+    assert r == ss.ERR_INVALID_ARG and "alias" in ss.last_error()
 
 
 def test_workspace_sizes_are_consistent():
