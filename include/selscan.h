@@ -120,6 +120,29 @@ selscan_status_t selscan_fwd_h0(const selscan_shape_t* shape,
                                 const float* h0, void* y, float* last_state, void* stream);
 
 /*
+ * selscan_fwd_h0 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It allocates nothing (no hipMalloc, hipFree or allocating library call):
+ * its scratch is a file-scope device array of SELSCAN_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that each GPU the library runs on holds until the process ends.
+ *   shape      as for selscan_fwd; its workspace fields are ignored.
+ *   other arguments as for selscan_fwd_h0 (h0 NULL = zero state).
+ * Errors as for selscan_fwd_h0, plus SELSCAN_ERR_WORKSPACE when the shape
+ * needs more scratch than the maximum (selscan_workspace_bytes(shape) >
+ * SELSCAN_NOALLOC_SCRATCH_BYTES; e.g. batch 1, dim 2048, L 2^20 needs
+ * ~137 MB), before any device work.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (concurrent streams without ordering
+ * between them) race and must not be issued.  Device ids >= 64 are
+ * UNSUPPORTED.
+ */
+#define SELSCAN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+selscan_status_t selscan_fwd_noalloc(const selscan_shape_t* shape,
+                                     const void* u, const void* delta, const float* A,
+                                     const void* B, const void* C, const float* D,
+                                     const void* z, const float* delta_bias, int softplus,
+                                     const float* h0, void* y, float* last_state, void* stream);
+
+/*
  * One-token state update (decoding; the recurrent view of section 2.2 of the
  * "Understanding Mamba ..." blog, one token at a time as the tutorial and
  * skill pages use it for generation).  shape: batch, dim, dstate N (1..16),

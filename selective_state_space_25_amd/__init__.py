@@ -48,7 +48,7 @@ _lib = None
 
 EXPORTED = ("selscan_fwd", "selscan_mamba2_fwd", "selscan_workspace_bytes", "selscan_mamba2_workspace_bytes",
             "selscan_fwd_h0", "selscan_mamba2_fwd_h0", "selscan_step", "selscan_mamba2_step", "selscan_conv1d",
-            "selscan_bwd", "selscan_bwd_workspace_bytes",
+            "selscan_bwd", "selscan_bwd_workspace_bytes", "selscan_fwd_noalloc",
             "selscan_last_error", "selscan_version", "selscan_timing_enable", "selscan_timing_collect")
 
 
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.selscan_mamba2_fwd_h0.argtypes = [ctypes.POINTER(M2Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp,
                                             vp]
         L.selscan_mamba2_fwd_h0.restype = i32
+        L.selscan_fwd_noalloc.argtypes = [ctypes.POINTER(Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp,
+                                          vp]
+        L.selscan_fwd_noalloc.restype = i32
         L.selscan_step.argtypes = [ctypes.POINTER(Shape), fp, vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, vp]
         L.selscan_step.restype = i32
         L.selscan_mamba2_step.argtypes = [ctypes.POINTER(M2Shape), fp, vp, vp, fp, vp, vp, fp, vp, fp, i32, vp, vp]

@@ -5,7 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "selscan.h"
+
 namespace selscan {
+
+// Records `msg` as the calling thread's selscan_last_error() and returns s.
+selscan_status_t set_error(selscan_status_t s, const std::string& msg);
 
 // Per-kernel timing bracket (no-op unless selscan_timing_enable(1)).
 void ktime_mark(const char* kernel, hipStream_t stream, bool begin);

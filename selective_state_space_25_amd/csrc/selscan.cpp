@@ -287,6 +287,8 @@ selscan_status_t check_m1_bwd_shape(const selscan_shape_t* s) {
 
 }  // namespace
 
+selscan_status_t selscan::set_error(selscan_status_t s, const std::string& msg) { return fail(s, msg); }
+
 extern "C" {
 
 const char* selscan_last_error(void) { return g_error.c_str(); }

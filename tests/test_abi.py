@@ -145,6 +145,13 @@ def test_h0_aliasing_last_state_rejected():
     assert r == ss.ERR_INVALID_ARG and "alias" in ss.last_error()
 
 
+def test_noalloc_refuses_shapes_beyond_its_scratch_without_device_work():
+    s = _m1(batch=1, dim=2048, seqlen=1 << 20)
+    r = ss.lib().selscan_fwd_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None,
+                                     FAKE, None, None)
+    assert r == ss.ERR_WORKSPACE and "maximum" in ss.last_error()
+
+
 def test_workspace_sizes_are_consistent():
     # the fp32 copy of B and C is always needed; a long sequence is split
     # into chunks and needs room for the chunk states too
