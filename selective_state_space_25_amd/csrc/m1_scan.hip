@@ -219,6 +219,16 @@ __device__ __forceinline__ float tok_general(Lane& L, const float* bc, float w, 
     return MODE == 0 ? __builtin_fmaf(L.Dp, uu, acc0 + acc1) : 0.0f;
 }
 
+// Ends a token of the general path: its states are final here and no later
+// token's record reads or decays move above this point.
+__device__ __forceinline__ void state_fence(float* v) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                 "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]),
+                 "+v"(v[14]), "+v"(v[15])
+                 :
+                 : "memory");
+}
+
 template <int MODE>
 __device__ __forceinline__ void load_bc(float* dst, cfptr p) {
     constexpr int n = MODE == 0 ? 2 * kNS : kNS;
@@ -275,14 +285,6 @@ __device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int blk,
             b.z[4 * q] = v.x; b.z[4 * q + 1] = v.y; b.z[4 * q + 2] = v.z; b.z[4 * q + 3] = v.w;
         }
     }
-}
-
-// One input element of token j of the tile in LDS (tensor t).
-template <typename Tin>
-__device__ __forceinline__ float lds_elem(const uint4* lds, int t, int j, int ls) {
-    constexpr int per = 16 / sizeof(Tin);
-    const char* p = reinterpret_cast<const char*>(lds + piece_slot<Tin>(t, j / per, ls)) + (j % per) * sizeof(Tin);
-    return In<Tin>::ld(reinterpret_cast<const Tin*>(p), 0);
 }
 
 // The chunk [t_begin, t_end) of one wave's 64 rows.  MODE 0: output pass,
@@ -391,28 +393,28 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
             const bool more = t0 + kTile < t_full_end;
             const float* bcl = bcl0 + par * (kBCBytes / 4);
             const uint32_t bc_next = bc_base0 + (uint32_t)((par ^ 1) * kBCBytes);
-            if constexpr (STRUCT) {
-                Blk<Tin> cur;
-                read_blk<Tin, MODE>(cur, lds, 0, ls);
-                float yb[kTile];
+            Blk<Tin> cur;
+            read_blk<Tin, MODE>(cur, lds, 0, ls);
+            float yb[kTile];
 #pragma unroll
-                for (int blk = 0; blk < kBlocks; ++blk) {
-                    Blk<Tin> nxt;
-                    if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, ls);
-                    if (blk == kBlocks - 2 && more) {
-                        // u, delta, z of this tile's last two blocks are in
-                        // registers now and the other B/C buffer is free:
-                        // fetch the next tile
-                        wait_lgkm();
-                        issue_rows<Tin, NT>(R, t0 + kTile, lds_base);
-                        issue_bc<MODE>(bcb, t0 + kTile, bc_next);
-                    }
-                    float w[kBlk], sg[kBlk];
+            for (int blk = 0; blk < kBlocks; ++blk) {
+                Blk<Tin> nxt;
+                if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, ls);
+                if (blk == kBlocks - 2 && more) {
+                    // u, delta, z of this tile's last two blocks are in
+                    // registers now and the other B/C buffer is free: fetch
+                    // the next tile
+                    wait_lgkm();
+                    issue_rows<Tin, NT>(R, t0 + kTile, lds_base);
+                    issue_bc<MODE>(bcb, t0 + kTile, bc_next);
+                }
+                float w[kBlk];
 #pragma unroll
-                    for (int j = 0; j < kBlk; ++j) {
-                        w[j] = delta_log2<SP>(L, In<Tin>::get(cur.d, j));
-                        sg[j] = w[j] * In<Tin>::get(cur.u, j);
-                    }
+                for (int j = 0; j < kBlk; ++j) w[j] = delta_log2<SP>(L, In<Tin>::get(cur.d, j));
+                if constexpr (STRUCT) {
+                    float sg[kBlk];
+#pragma unroll
+                    for (int j = 0; j < kBlk; ++j) sg[j] = w[j] * In<Tin>::get(cur.u, j);
                     if (wave_all(block_in_range(sg))) {
 #pragma unroll
                         for (int j = 0; j < kBlk; ++j) {
@@ -448,63 +450,66 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                             for (int j = 0; j < kBlk; ++j) yb[blk * kBlk + j] = ys[j];
                         }
                     }
-                    if (blk + 1 < kBlocks) cur = nxt;
-                }
-                // the next tile has landed (its request left one block ago);
-                // waiting before the y stores keeps their write latency off
-                // this wait.  The wait is unconditional so that no path into
-                // the next iteration leaves a tile copy in flight: the
-                // compiler would otherwise drain the y stores as well before
-                // the tile's first LDS read
-                wait_vm();
-                if constexpr (MODE == 0) {
-                    // Transposed through this tile's B/C buffer (free now; 4 KB)
-                    // in halves of 64 bytes per row, so that one store covers
-                    // 64 contiguous bytes of each of 16 rows: a row's half is
-                    // one request rather than four.  Chunk c of row r sits at
-                    // r*64 + ((c + r/4) % 4)*16, which keeps both the lanes'
-                    // row-wise writes and the column-wise reads free of bank
-                    // conflicts.
-                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                    uint32_t yw[YWords<Tout>::kN];
-                    YWords<Tout>::pack(yw, yb);
-                    u32x4* sbuf = reinterpret_cast<u32x4*>(const_cast<float*>(bcl));
-                    const int rr = lane >> 2, cc = lane & 3;
+                } else {
+                    // general A: one exponential per update, the state is h.
+                    // The fences keep the compiler from computing every
+                    // token's sixteen decays (and reading every record)
+                    // ahead, which spills.
 #pragma unroll
-                    for (int hh = 0; hh < YWords<Tout>::kN / 16; ++hh) {
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            sbuf[lane * 4 + ((c + (lane >> 2)) & 3)] =
-                                u32x4{yw[16 * hh + 4 * c], yw[16 * hh + 4 * c + 1], yw[16 * hh + 4 * c + 2],
-                                      yw[16 * hh + 4 * c + 3]};
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const int r = 16 * k + rr;
-                            const u32x4 v = sbuf[r * 4 + ((cc + (r >> 2)) & 3)];
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                v, ydesc,
-                                (int)((uint32_t)r * yrb + (uint32_t)(t0 * (int64_t)sizeof(Tout)) + 64u * hh + 16u * cc),
-                                0, 0);
+                    for (int j = 0; j < kBlk; ++j) {
+                        const float* bc = bcl + (blk * kBlk + j) * RS;   // same address in every lane
+                        float wj = w[j];
+                        asm volatile("" : "+v"(wj));
+                        const float pre = tok_general<MODE>(L, bc, wj, In<Tin>::get(cur.u, j));
+                        if (MODE == 0) {
+                            // y is formed here (not deferred to the tile's
+                            // stores, which keeps the gate inputs live: spills)
+                            float yv = pre * (has_z ? silu_scaled(In<Tin>::get(cur.z, j), 1.0f) : 1.0f);
+                            asm volatile("" : "+v"(yv));
+                            yb[blk * kBlk + j] = yv;
                         }
+                        state_fence(L.k);
                     }
                 }
-            } else {
-                // general A: token by token out of the LDS tile
-#pragma nounroll
-                for (int j = 0; j < kTile; ++j) {
-                    const float uu = lds_elem<Tin>(lds, 0, j, ls);
-                    const float dl = lds_elem<Tin>(lds, 1, j, ls);
-                    const float zz = has_z ? lds_elem<Tin>(lds, 2, j, ls) : 0.0f;
-                    if (j == kTile - 1 && more) {
-                        wait_lgkm();
-                        issue_rows<Tin, NT>(R, t0 + kTile, lds_base);
-                        issue_bc<MODE>(bcb, t0 + kTile, bc_next);
+                if (blk + 1 < kBlocks) cur = nxt;
+            }
+            // the next tile has landed (its request left one block ago);
+            // waiting before the y stores keeps their write latency off
+            // this wait.  The wait is unconditional so that no path into
+            // the next iteration leaves a tile copy in flight: the
+            // compiler would otherwise drain the y stores as well before
+            // the tile's first LDS read
+            wait_vm();
+            if constexpr (MODE == 0) {
+                // Transposed through this tile's B/C buffer (free now; 4 KB)
+                // in halves of 64 bytes per row, so that one store covers
+                // 64 contiguous bytes of each of 16 rows: a row's half is
+                // one request rather than four.  Chunk c of row r sits at
+                // r*64 + ((c + r/4) % 4)*16, which keeps both the lanes'
+                // row-wise writes and the column-wise reads free of bank
+                // conflicts.
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                uint32_t yw[YWords<Tout>::kN];
+                YWords<Tout>::pack(yw, yb);
+                u32x4* sbuf = reinterpret_cast<u32x4*>(const_cast<float*>(bcl));
+                const int rr = lane >> 2, cc = lane & 3;
+#pragma unroll
+                for (int hh = 0; hh < YWords<Tout>::kN / 16; ++hh) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        sbuf[lane * 4 + ((c + (lane >> 2)) & 3)] =
+                            u32x4{yw[16 * hh + 4 * c], yw[16 * hh + 4 * c + 1], yw[16 * hh + 4 * c + 2],
+                                  yw[16 * hh + 4 * c + 3]};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int r = 16 * k + rr;
+                        const u32x4 v = sbuf[r * 4 + ((cc + (r >> 2)) & 3)];
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v, ydesc,
+                            (int)((uint32_t)r * yrb + (uint32_t)(t0 * (int64_t)sizeof(Tout)) + 64u * hh + 16u * cc),
+                            0, 0);
                     }
-                    const float pre = tok_general<MODE>(L, bcl + j * RS, delta_log2<SP>(L, dl), uu);
-                    if (MODE == 0 && row_ok)
-                        Out<Tout>::st(yrow, t0 + j, pre * (has_z ? silu_scaled(zz, 1.0f) : 1.0f));
                 }
-                wait_vm();
             }
         }
     }
