@@ -50,7 +50,7 @@ struct M1Args {
 };
 
 int m1_padded_states(int N);
-int m1_chunk_align();
+int m1_chunk_align(int in_bf16);
 int m1_resident_waves_per_cu(int in_bf16);
 int m1_rows_per_block();
 int m1_waves_per_block();

@@ -61,7 +61,12 @@ constexpr int kRows = 64;       // channels per workgroup = lanes of the wave
 constexpr int kNS = 16;         // states per channel (padded)
 constexpr int kBlk = 8;         // tokens per block (one 16-byte piece of bf16)
 constexpr int kTile = 32;       // tokens per tile = tokens per y burst (128 bytes of fp32 y per row)
-constexpr int kChunkAlign = 32; // chunk starts are multiples of a tile
+#ifndef SELSCAN_M1_WIDE
+#define SELSCAN_M1_WIDE 1
+#endif
+#ifndef SELSCAN_M1_PRE_BLOCKS
+#define SELSCAN_M1_PRE_BLOCKS (sizeof(Tin) == 2 ? 4 : 2)
+#endif
 constexpr float kSigLo = 8.673617379884035e-19f;   // 2^-60
 constexpr float kSigHi = 1.152921504606847e18f;    // 2^60
 
@@ -70,8 +75,6 @@ using rows::ldsptr;
 using rows::wait_lgkm;
 using rows::wait_vm;
 using rows::dma_at;
-using rows::issue_rows;
-using rows::piece_slot;
 using rows::RowDma;
 
 __device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
@@ -93,6 +96,20 @@ template <> struct In<uint16_t> {
     }
     static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 };
+
+// Rows reach LDS in copies of kImg 16-byte pieces per row.  The summary pass
+// copies whole 128-byte lines (8 pieces: 64 tokens of 16-bit inputs, two
+// 32-token sub-tiles), so that no line is read half now and half a tile later,
+// by when the L2 has often evicted it and the other half is fetched again
+// (measured: the 1M-token summary pass 4.99 -> 3.73 ms).  The output pass,
+// which also stages z and holds two B/C buffers, keeps 32-token copies: whole
+// lines there need 32 KB of LDS per wave, and the 5 waves per CU that leave
+// ran it twice as slowly.  kCopyTok: tokens per whole copy; chunk starts are
+// multiples of the summary pass's.
+template <typename Tin, int MODE>
+constexpr int kImg = (SELSCAN_M1_WIDE && MODE == 1) ? 8 : In<Tin>::kPieces;
+template <typename Tin, int MODE>
+constexpr int kCopyTok = kImg<Tin, MODE> * 16 / (int)sizeof(Tin);
 
 // y stores of one token (ragged tails and the general-A path).
 template <typename T> struct Out;
@@ -270,18 +287,45 @@ struct Blk {
     uint32_t u[In<Tin>::kWords], d[In<Tin>::kWords], z[In<Tin>::kWords];
 };
 
+// 16-byte slot of piece p of tensor t in an image of NP pieces per row (as
+// lds_rows.hpp lays a row group's pieces out) for the lane at slot offset ls.
+template <int NP>
+__device__ __forceinline__ int img_slot(int t, int p, int ls) {
+    return t * NP * 64 + (p >> 2) * 256 + (p & 3) * 16 + ls;
+}
+
+// Pieces [0, 4 halves) of tokens t0.. of tensors 0 .. NT-1 into the image:
+// one instruction takes 64 bytes of each of 16 rows; with both halves the two
+// instructions of a row group read the two halves of the same lines.
+template <typename T, int NT, int NP>
+__device__ __forceinline__ void issue_img(const RowDma<T>& R, int64_t t0, uint32_t lds_base, bool both) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const char* bt = R.base[t] + t0 * (int64_t)sizeof(T);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const char* g = bt + R.kb[k] + R.voff[k];
+            const uint32_t s0 = lds_base + (uint32_t)(t * NP + k) * 1024u;
+            dma_at<0>(g, s0);
+            if (NP == 8 && both) dma_at<64>(g, s0 + 4 * 1024u);
+        }
+    }
+}
+
+// Block of 8 tokens starting at piece p0 of the image.
 template <typename Tin, int MODE>
-__device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int blk, int ls) {
+__device__ __forceinline__ void read_blk(Blk<Tin>& b, const uint4* lds, int p0, int ls) {
     constexpr int per = In<Tin>::kWords / 4;   // 16-byte pieces per block
+    constexpr int NP = kImg<Tin, MODE>;
 #pragma unroll
     for (int q = 0; q < per; ++q) {
-        const int p = blk * per + q;
-        const uint4 x = lds[piece_slot<Tin>(0, p, ls)];
+        const int p = p0 + q;
+        const uint4 x = lds[img_slot<NP>(0, p, ls)];
         b.u[4 * q] = x.x; b.u[4 * q + 1] = x.y; b.u[4 * q + 2] = x.z; b.u[4 * q + 3] = x.w;
-        const uint4 y = lds[piece_slot<Tin>(1, p, ls)];
+        const uint4 y = lds[img_slot<NP>(1, p, ls)];
         b.d[4 * q] = y.x; b.d[4 * q + 1] = y.y; b.d[4 * q + 2] = y.z; b.d[4 * q + 3] = y.w;
         if (MODE == 0) {
-            const uint4 v = lds[piece_slot<Tin>(2, p, ls)];
+            const uint4 v = lds[img_slot<NP>(2, p, ls)];
             b.z[4 * q] = v.x; b.z[4 * q + 1] = v.y; b.z[4 * q + 2] = v.z; b.z[4 * q + 3] = v.w;
         }
     }
@@ -294,6 +338,9 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                                           uint32_t lds_base) {
     constexpr int NT = MODE == 0 ? 3 : 2;
     constexpr int kBlocks = kTile / kBlk;         // blocks per tile
+    // blocks held in registers when the next tile is requested: a whole tile
+    // for 16-bit inputs (48 VGPRs in the output pass), two for fp32
+    constexpr int kPre = SELSCAN_M1_PRE_BLOCKS;
     constexpr int kBC = MODE == 0 ? 2 * kNS : kNS;
     const int lane = threadIdx.x;
     const bool row_ok = d0 + lane < a.dim;
@@ -303,9 +350,10 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     // chunks take one tile more (T tiles in a row, the last possibly
     // partial), and they are dispatched first, so that the wave slots they
     // take are paired with the shorter chunks' waves
-    const int64_t T = (a.L + kTile - 1) / kTile, q = T / a.G, r = T % a.G;
-    const int64_t t_begin = kTile * ((int64_t)g * q + min<int64_t>(g, r));
-    const int64_t t_end = min<int64_t>(a.L, kTile * ((int64_t)(g + 1) * q + min<int64_t>(g + 1, r)));
+    constexpr int kUnit = kCopyTok<Tin, 1>;        // chunk starts are multiples of a whole summary copy
+    const int64_t T = (a.L + kUnit - 1) / kUnit, q = T / a.G, r = T % a.G;
+    const int64_t t_begin = kUnit * ((int64_t)g * q + min<int64_t>(g, r));
+    const int64_t t_end = min<int64_t>(a.L, kUnit * ((int64_t)(g + 1) * q + min<int64_t>(g + 1, r)));
     const bool has_z = MODE == 0 && a.z != nullptr;
 
     const Tin* urow = reinterpret_cast<const Tin*>(a.u) + row * a.L;
@@ -333,11 +381,11 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     // this batch's B/C, 32 floats per token; the address is wave-uniform
     const float* bcb = rows::uniform(a.bcq + (b * a.L) * (2 * kNS));
     const int64_t t_full_end = a.vec_ok ? t_begin + ((t_end - t_begin) / kTile) * kTile : t_begin;
-    const uint32_t bc_base0 = lds_base + (uint32_t)(NT * In<Tin>::kPieces * kRows * 16);
+    const uint32_t bc_base0 = lds_base + (uint32_t)(NT * kImg<Tin, MODE> * kRows * 16);
     // request the first tile before the per-row set-up and the carry-in fold,
     // so that its latency overlaps theirs
     if (t_begin < t_full_end) {
-        issue_rows<Tin, NT>(R, t_begin, lds_base);
+        issue_img<Tin, NT, kImg<Tin, MODE>>(R, t_begin, lds_base, t_begin + kCopyTok<Tin, MODE> <= t_full_end);
         issue_bc<MODE>(bcb, t_begin, bc_base0);
     }
 
@@ -385,29 +433,43 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
     if (t_begin < t_full_end) {
         constexpr int RS = kRec<MODE> / 4;   // floats per B/C record in LDS
         constexpr int kBCBytes = kTile * kRec<MODE>;
-        const float* bcl0 = reinterpret_cast<const float*>(lds + NT * In<Tin>::kPieces * kRows);
+        const float* bcl0 = reinterpret_cast<const float*>(lds + NT * kImg<Tin, MODE> * kRows);
+        constexpr int kSubPieces = kTile * (int)sizeof(Tin) / 16;   // image pieces per 32-token sub-tile
+        constexpr int kPer = In<Tin>::kWords / 4;                   // pieces per 8-token block
         wait_vm();   // the first tile is in LDS
-        int par = 0;   // B/C buffer of the current tile
+        int par = 0;   // B/C buffer of the current sub-tile
+        int64_t c0 = t_begin;   // first token of the copy in the image
+        int nsub = (kCopyTok<Tin, MODE> > kTile && c0 + kCopyTok<Tin, MODE> <= t_full_end) ? kCopyTok<Tin, MODE> / kTile : 1;
+        int sub = 0;            // sub-tile of that copy
 #pragma nounroll
         for (int64_t t0 = t_begin; t0 < t_full_end; t0 += kTile, par ^= 1) {
-            const bool more = t0 + kTile < t_full_end;
+            const bool last_sub = sub == nsub - 1;
+            const int64_t c_next = c0 + (int64_t)nsub * kTile;
+            const bool more_rows = last_sub && c_next < t_full_end;
+            const bool more_bc = t0 + kTile < t_full_end;
+            const int p_sub = sub * kSubPieces;
             const float* bcl = bcl0 + par * (kBCBytes / 4);
             const uint32_t bc_next = bc_base0 + (uint32_t)((par ^ 1) * kBCBytes);
-            Blk<Tin> cur;
-            read_blk<Tin, MODE>(cur, lds, 0, ls);
+            // blocks are read from LDS kPre - 1 blocks ahead of their use;
+            // once the copy's last block is in registers its LDS rows are free
+            // and the next copy is requested (kPre blocks = 8 kPre tokens of
+            // arithmetic before it is needed); the next sub-tile's B/C go to
+            // the other buffer at the same point
+            Blk<Tin> blks[kBlocks];
+#pragma unroll
+            for (int i = 0; i < kPre - 1; ++i) read_blk<Tin, MODE>(blks[i], lds, p_sub + i * kPer, ls);
             float yb[kTile];
 #pragma unroll
             for (int blk = 0; blk < kBlocks; ++blk) {
-                Blk<Tin> nxt;
-                if (blk + 1 < kBlocks) read_blk<Tin, MODE>(nxt, lds, blk + 1, ls);
-                if (blk == kBlocks - 2 && more) {
-                    // u, delta, z of this tile's last two blocks are in
-                    // registers now and the other B/C buffer is free: fetch
-                    // the next tile
+                if (blk + kPre - 1 < kBlocks)
+                    read_blk<Tin, MODE>(blks[blk + kPre - 1], lds, p_sub + (blk + kPre - 1) * kPer, ls);
+                if (blk == kBlocks - kPre && (more_rows || more_bc)) {
                     wait_lgkm();
-                    issue_rows<Tin, NT>(R, t0 + kTile, lds_base);
-                    issue_bc<MODE>(bcb, t0 + kTile, bc_next);
+                    if (more_rows)
+                        issue_img<Tin, NT, kImg<Tin, MODE>>(R, c_next, lds_base, c_next + kCopyTok<Tin, MODE> <= t_full_end);
+                    if (more_bc) issue_bc<MODE>(bcb, t0 + kTile, bc_next);
                 }
+                const Blk<Tin>& cur = blks[blk];
                 float w[kBlk];
 #pragma unroll
                 for (int j = 0; j < kBlk; ++j) w[j] = delta_log2<SP>(L, In<Tin>::get(cur.d, j));
@@ -471,7 +533,6 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                         state_fence(L.k);
                     }
                 }
-                if (blk + 1 < kBlocks) cur = nxt;
             }
             // the next tile has landed (its request left one block ago);
             // waiting before the y stores keeps their write latency off
@@ -510,6 +571,13 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
                             0, 0);
                     }
                 }
+            }
+            if (last_sub) {
+                c0 = c_next;
+                nsub = (kCopyTok<Tin, MODE> > kTile && c0 + kCopyTok<Tin, MODE> <= t_full_end) ? kCopyTok<Tin, MODE> / kTile : 1;
+                sub = 0;
+            } else {
+                ++sub;
             }
         }
     }
@@ -556,9 +624,9 @@ __device__ __forceinline__ bool row_is_structured(const M1Args& a, int64_t d) {
 }
 
 template <typename Tin, typename Tout, int MODE, bool SP>
-__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(MODE == 0 || sizeof(Tin) == 4 ? 2 : 4)))
+__global__ __launch_bounds__(kRows) __attribute__((amdgpu_waves_per_eu(MODE == 0 || sizeof(Tin) == 4 || SELSCAN_M1_WIDE ? 2 : 4)))
 void m1_scan_kernel(M1Args a) {
-    __shared__ uint4 lds[(MODE == 0 ? 3 : 2) * In<Tin>::kPieces * kRows + 2 * kTile * kRec<MODE> / 16];
+    __shared__ uint4 lds[(MODE == 0 ? 3 : 2) * kImg<Tin, MODE> * kRows + 2 * kTile * kRec<MODE> / 16];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(ldsptr)lds;
     const int64_t blocks_per_batch = (a.dim + kRows - 1) / kRows;
     int64_t rb;   // (batch, 64-channel block) index
@@ -678,11 +746,11 @@ int m1_padded_states(int) { return kNS; }
 // Output-pass waves one CU holds at once: LDS-limited (160 KB per CU), at
 // most two waves per SIMD by registers.
 int m1_resident_waves_per_cu(int in_bf16) {
-    const int bytes = in_bf16 ? 3 * In<uint16_t>::kPieces * kRows * 16 + 2 * kTile * kRec<0>
-                              : 3 * In<float>::kPieces * kRows * 16 + 2 * kTile * kRec<0>;
+    const int bytes = in_bf16 ? 3 * kImg<uint16_t, 0> * kRows * 16 + 2 * kTile * kRec<0>
+                              : 3 * kImg<float, 0> * kRows * 16 + 2 * kTile * kRec<0>;
     return std::min(8, 160 * 1024 / bytes);
 }
-int m1_chunk_align() { return kChunkAlign; }
+int m1_chunk_align(int in_bf16) { return in_bf16 ? kCopyTok<uint16_t, 1> : kCopyTok<float, 1>; }
 int m1_rows_per_block() { return kRows; }
 int m1_waves_per_block() { return 1; }
 size_t m1_bc_bytes(int64_t batch, int64_t L) { return (size_t)batch * L * 2 * kNS * sizeof(float); }

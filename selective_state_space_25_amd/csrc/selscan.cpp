@@ -143,7 +143,7 @@ M1Plan plan_m1(const selscan_shape_t* s) {
         // unless rounding down to them gives up more than a tenth of the waves
         if (G >= 8 && (G / 8 * 8) * 10 >= G * 9) G = G / 8 * 8;
     }
-    const int64_t align = selscan::m1_chunk_align();
+    const int64_t align = selscan::m1_chunk_align(s->in_dtype == SELSCAN_BF16);
     G = std::max<int64_t>(1, std::min<int64_t>(G, (s->seqlen + align - 1) / align));
     G = std::min<int64_t>(G, 65535);
     // the kernels split the row's tiles as evenly as they can: the first
