@@ -153,6 +153,7 @@ def time_decode(name, steps, device):
         args = [inp[k][..., 0].contiguous() if inp[k] is not None and inp[k].dim() == 3 else inp[k]
                 for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
         f = lambda: ss.step(state, *args)
+        bound, _ = ss.bind_step(state, *args)
         es = torch.tensor([], dtype=w.dtype).element_size()
         rows = w.batch * w.dim
         nbytes = rows * w.dstate * 4 * 2 + rows * (3 * es + 4) + 2 * w.batch * w.dstate * es + w.dim * (w.dstate + 2) * 4
@@ -162,6 +163,7 @@ def time_decode(name, steps, device):
         args = [inp[k][:, 0].contiguous() if inp[k] is not None and inp[k].dim() >= 3 else inp[k]
                 for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")]
         f = lambda: ss.mamba2_step(state, *args)
+        bound, _ = ss.bind_mamba2_step(state, *args)
         es = torch.tensor([], dtype=w.dtype).element_size()
         rows = w.batch * w.nheads * w.headdim
         nbytes = (rows * w.dstate * 4 * 2 + rows * (2 * es + 4) + w.batch * w.nheads * es
@@ -177,6 +179,23 @@ def time_decode(name, steps, device):
     e1.record(stream)
     torch.cuda.synchronize()
     us_call = e0.elapsed_time(e1) * 1e3 / steps
+    # the same steps through a call bound once (arguments marshalled at
+    # binding), and the host time of the C-ABI call alone (wall clock per
+    # call, kernels left to run behind it)
+    for _ in range(5):
+        bound()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        bound()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_bound = e0.elapsed_time(e1) * 1e3 / steps
+    t = time.perf_counter()
+    for _ in range(steps):
+        bound()
+    us_host = (time.perf_counter() - t) * 1e6 / steps
+    torch.cuda.synchronize()
     # The kernels alone: the call above is bound by the host issuing it, and
     # events around one small launch add their own microseconds, so the
     # steps are captured once as a graph of back-to-back launches (kernel
@@ -214,7 +233,8 @@ def time_decode(name, steps, device):
             ss.timing_enable(False)
         us = list(ss.timing_collect().values())[0]["avg_ms"] * 1e3
     return {"shape_of": name, "us_per_token_kernel": us, "kernel_timing": how,
-            "us_per_token_call": us_call, "bytes_per_token": nbytes, "kernel_gbs": nbytes / (us * 1e-6) / 1e9,
+            "us_per_token_call": us_call, "us_per_token_bound_call": us_bound,
+            "host_us_per_bound_call": us_host, "bytes_per_token": nbytes, "kernel_gbs": nbytes / (us * 1e-6) / 1e9,
             "kernel_state_updates_per_s": rows * w.dstate / (us * 1e-6)}
 
 
@@ -509,7 +529,8 @@ def main():
     }
     line["decode"] = {n: time_decode(n, 200, device) for n in ("mamba2p8b_l8k", "mamba2_mh")}
     line["conv1d"] = time_conv1d("mamba2p8b_l8k", 10, device)
-    line["backward"] = {n: time_backward(n, 5, device) for n in ("mamba130m_l2k", "mamba2p8b_l8k")}
+    line["backward"] = {n: time_backward(n, 5 if n != "long_1m" else 3, device)
+                        for n in ("mamba130m_l2k", "mamba2p8b_l8k", "long_1m")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
     print(json.dumps(line))

@@ -229,6 +229,69 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     return out
 
 
+class _BoundCall:
+    """A C-ABI call with its arguments marshalled once: calling it enqueues
+    the kernel again on the same buffers (whose contents the caller may
+    change in place between calls, as a decoding loop does)."""
+
+    def __init__(self, fn, shape, args):
+        self._fn, self._shape, self._args = fn, shape, args
+
+    def __call__(self):
+        st = self._fn(ctypes.byref(self._shape), *self._args)
+        if st != OK:
+            raise SelscanError(st, last_error())
+
+
+def bind_step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, out=None, out_dtype=None):
+    """selscan_step with its arguments checked and marshalled once: returns
+    (call, y).  Each call() updates `state` in place with the token currently
+    held in u, delta, B, C, z and writes y, on the stream that was current at
+    binding time."""
+    torch = _torch()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.bind_step needs tensors on a GPU device")
+    batch, dim = u.shape
+    N = A.shape[1]
+    dt = u.dtype
+    odt = (out.dtype if out is not None else torch.float32) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((batch, dim), dtype=odt, device=dev)
+    s = Shape(batch, dim, N, 1, _dtype_code(u), _dtype_code(out), None, 0)
+    args = (_ptr(state, "state", (batch, dim, N), torch.float32, dev),
+            _ptr(u, "u", (batch, dim), dt, dev), _ptr(delta, "delta", (batch, dim), dt, dev),
+            _ptr(A, "A", (dim, N), torch.float32, dev), _ptr(B, "B", (batch, N), dt, dev),
+            _ptr(C, "C", (batch, N), dt, dev), _ptr(D, "D", (dim,), torch.float32, dev),
+            _ptr(z, "z", (batch, dim), dt, dev), _ptr(delta_bias, "delta_bias", (dim,), torch.float32, dev),
+            int(bool(softplus)), _ptr(out, "out", (batch, dim), odt, dev), _stream_handle(dev))
+    return _BoundCall(lib().selscan_step, s, args), out
+
+
+def bind_mamba2_step(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=True, out=None,
+                     out_dtype=None):
+    """selscan_mamba2_step with its arguments checked and marshalled once:
+    returns (call, y); see bind_step."""
+    torch = _torch()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.bind_mamba2_step needs tensors on a GPU device")
+    batch, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dtp = x.dtype
+    odt = (out.dtype if out is not None else torch.float32) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((batch, H, P), dtype=odt, device=dev)
+    s = M2Shape(batch, 1, H, P, G, N, _dtype_code(x), _dtype_code(out), None, 0)
+    args = (_ptr(state, "state", (batch, H, P, N), torch.float32, dev),
+            _ptr(x, "x", (batch, H, P), dtp, dev), _ptr(dt, "dt", (batch, H), dtp, dev),
+            _ptr(A, "A", (H,), torch.float32, dev), _ptr(B, "B", (batch, G, N), dtp, dev),
+            _ptr(C, "C", (batch, G, N), dtp, dev), _ptr(D, "D", (H,), torch.float32, dev),
+            _ptr(z, "z", (batch, H, P), dtp, dev), _ptr(dt_bias, "dt_bias", (H,), torch.float32, dev),
+            int(bool(softplus)), _ptr(out, "out", (batch, H, P), odt, dev), _stream_handle(dev))
+    return _BoundCall(lib().selscan_mamba2_step, s, args), out
+
+
 def bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, softplus=True, h0=None,
         want_dh0=False, workspace=None):
     """Gradients of the Mamba-1 scan on the GPU.
@@ -397,5 +460,5 @@ def timing_collect() -> dict:
     return res
 
 
-__all__ = ["bwd", "bwd_workspace_bytes", "conv1d", "ConvShape", "step", "mamba2_step", "timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
+__all__ = ["bind_step", "bind_mamba2_step", "bwd", "bwd_workspace_bytes", "conv1d", "ConvShape", "step", "mamba2_step", "timing_enable", "timing_collect", "KernelTime", "fwd", "mamba2_fwd", "workspace_bytes", "mamba2_workspace_bytes", "version", "last_error", "lib",
            "SelscanError", "Shape", "M2Shape", "m1_shape", "EXPORTED", "LIB_PATH"]

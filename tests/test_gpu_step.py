@@ -193,3 +193,37 @@ def test_step_with_unaligned_b_c(gpu, mamba2, dtype):
     torch.cuda.synchronize()
     assert torch.equal(y_al, y_un)
     assert torch.equal(s_al, s_un)
+
+
+@pytest.mark.parametrize("mamba2", [False, True])
+def test_bound_step_in_a_decoding_loop(gpu, mamba2):
+    """bind_step / bind_mamba2_step marshal the arguments once; the loop
+    refills the same token buffers in place and calls again.  The tokens
+    decoded this way equal the oracle from the same initial state."""
+    T = 7
+    if mamba2:
+        inp = synth.m2_inputs(2, T, 4, 24, 2, 64, torch.bfloat16, seed=97, device=DEV)
+        h0 = _h0((2, 4, 24, 64), 11)
+        cur = {k: inp[k][:, 0].clone() for k in ("x", "dt", "B", "C", "z")}
+        state = h0.clone()
+        call, y = ss.bind_mamba2_step(state, cur["x"], cur["dt"], inp["A"], cur["B"], cur["C"], inp["D"],
+                                      cur["z"], inp["dt_bias"])
+        ref_y, ref_last = _m2_oracle(inp, h0)
+    else:
+        inp = synth.m1_inputs(2, 90, 16, T, torch.bfloat16, "s4d_jitter", seed=98, device=DEV)
+        h0 = _h0((2, 90, 16), 12)
+        cur = {k: inp[k][..., 0].clone() for k in ("u", "delta", "B", "C", "z")}
+        state = h0.clone()
+        call, y = ss.bind_step(state, cur["u"], cur["delta"], inp["A"], cur["B"], cur["C"], inp["D"], cur["z"],
+                               inp["delta_bias"])
+        ref_y, ref_last = _m1_oracle(inp, h0)
+    ys = []
+    for t in range(T):
+        for k, v in cur.items():
+            v.copy_(inp[k][:, t] if mamba2 else inp[k][..., t])
+        call()
+        ys.append(y.clone())
+    torch.cuda.synchronize()
+    got = torch.stack(ys, dim=1 if mamba2 else -1)
+    check_close(host(got).double().numpy(), ref_y, TOL_BF16, "y over the bound steps")
+    check_close(host(state).double().numpy(), ref_last, TOL_BF16, "state after the bound steps")
