@@ -47,6 +47,8 @@ struct M1Args {
     int vec_ok;       // rows of u, delta, z, y start on 16-byte boundaries (tile path)
     int force_general;
     int xcd_chunks;   // G is a multiple of 8 and chunk g runs on XCD g % 8 (1-D grid)
+    int carry_scan;   // the carries come from a scan over the chunk summaries (its own
+                      // kernel) rather than from a fold at the start of each chunk
 };
 
 int m1_padded_states(int N);

@@ -394,9 +394,23 @@ __device__ __forceinline__ void run_chunk(const M1Args& a, int64_t b, int64_t d0
 #pragma unroll
     for (int n = 0; n < kNS; ++n) L.Ar[n] = (n < a.N) ? a.A[d * a.N + n] : 0.0f;
     L.A0 = L.Ar[0];
+    // A's row is opaque to the optimiser from here: without this the
+    // general path's output pass derives values from it ahead of the token
+    // loop and spills there (the spill slots alone make the kernel a
+    // scratch user, which slows every launch of it)
+    state_fence(L.Ar);
     const float Dv = (MODE == 0 && a.D) ? a.D[d] : 0.0f;
     L.Dp = STRUCT ? Dv * kInvLn2 : Dv;
-    if (MODE == 0 && g > 0) {
+    if (MODE == 0 && g > 0 && a.carry_scan) {
+        // carry-in: the true state at the end of chunk g - 1, which the
+        // carry kernel wrote over that chunk's zero-start summary
+        const float4* e = reinterpret_cast<const float4*>(a.ws_state + (row * a.G + g - 1) * kNS);
+#pragma unroll
+        for (int q = 0; q < kNS / 4; ++q) {
+            const float4 v = e[q];
+            L.k[4 * q] = v.x; L.k[4 * q + 1] = v.y; L.k[4 * q + 2] = v.z; L.k[4 * q + 3] = v.w;
+        }
+    } else if (MODE == 0 && g > 0) {
         // carry-in: fold the zero-start end states of the chunks before this
         // one (written by the summary pass) from h0, h <- exp(A w_j) h + e_j
 #pragma unroll
@@ -657,6 +671,82 @@ void m1_scan_kernel(M1Args a) {
         run_chunk<Tin, Tout, MODE, false, SP>(a, b, d0, g, lds, lds_base);
 }
 
+// Carries of all chunks of one row from their summaries (the associative
+// combine of (decay, state) pairs across a wave).  Chunk j's summary is the
+// pair (W_j, e_j): the sum of w = Delta / ln2 over the chunk and its end state
+// from a zero start, so that h_out = 2^(A W_j) h_in + e_j per state.  Two such
+// maps compose as (W1, e1) then (W2, e2) = (W1 + W2, 2^(A W2) e1 + e2).  Lane
+// l folds a strip of consecutive summaries (one chunk per lane up to 64
+// chunks), an inclusive scan over the lanes combines the strips in log2(64)
+// shuffle steps, and each lane walks its strip again from the carry into it
+// (h0 folded in first), writing the true state at the end of every chunk over
+// that chunk's summary.  One wave per (batch, channel) row.
+__global__ __launch_bounds__(64) void m1_carry_kernel(M1Args a) {
+    const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int64_t d = row % a.dim;
+    const int nsum = a.G - 1;                 // summaries that feed some carry
+    const int per = (nsum + 63) / 64;         // chunks per lane
+    const int j0 = min(lane * per, nsum), j1 = min(j0 + per, nsum);
+    float* st = a.ws_state + row * a.G * kNS;
+    const float* W = a.ws_w + row * a.G;
+    float Ar[kNS];
+#pragma unroll
+    for (int n = 0; n < kNS; ++n) Ar[n] = (n < a.N) ? a.A[d * a.N + n] : 0.0f;
+    // this lane's strip as one map
+    float ws = 0.0f, e[kNS];
+#pragma unroll
+    for (int n = 0; n < kNS; ++n) e[n] = 0.0f;
+    for (int j = j0; j < j1; ++j) {
+        const float wj = W[j];
+        const float4* sj = reinterpret_cast<const float4*>(st + (int64_t)j * kNS);
+#pragma unroll
+        for (int q = 0; q < kNS / 4; ++q) {
+            const float4 v = sj[q];
+            const float ev[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[4 * q + i] = __builtin_fmaf(fast_exp2(Ar[4 * q + i] * wj), e[4 * q + i], ev[i]);
+        }
+        ws += wj;
+    }
+    // inclusive scan of the strips' maps over the lanes (empty strips are the
+    // identity map (0, 0))
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float wp = __shfl_up(ws, off, 64);
+        float ep[kNS];
+#pragma unroll
+        for (int n = 0; n < kNS; ++n) ep[n] = __shfl_up(e[n], off, 64);
+        if (lane >= off) {
+#pragma unroll
+            for (int n = 0; n < kNS; ++n) e[n] = __builtin_fmaf(fast_exp2(Ar[n] * ws), ep[n], e[n]);
+            ws += wp;
+        }
+    }
+    // the carry into this lane's strip: the lanes before it applied to h0
+    const float wx = __shfl_up(ws, 1, 64);
+    float h[kNS];
+#pragma unroll
+    for (int n = 0; n < kNS; ++n) {
+        const float ex = __shfl_up(e[n], 1, 64);
+        const float h0 = (a.h0 && n < a.N) ? a.h0[row * a.N + n] : 0.0f;
+        h[n] = lane == 0 ? h0 : __builtin_fmaf(fast_exp2(Ar[n] * wx), h0, ex);
+    }
+    // walk the strip again: the true state at the end of each chunk
+    for (int j = j0; j < j1; ++j) {
+        const float wj = W[j];
+        float4* sj = reinterpret_cast<float4*>(st + (int64_t)j * kNS);
+#pragma unroll
+        for (int q = 0; q < kNS / 4; ++q) {
+            const float4 v = sj[q];
+            const float ev[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[4 * q + i] = __builtin_fmaf(fast_exp2(Ar[4 * q + i] * wj), h[4 * q + i], ev[i]);
+            sj[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+        }
+    }
+}
+
 // B, C [batch, N, L] -> fp32 [batch, L, (B0..B15, C0..C15)] (zeros past N).
 // A workgroup converts 32 tokens of one batch: coalesced reads along L of
 // the 32 source rows, a transpose through LDS, coalesced 128-byte records.
@@ -708,6 +798,10 @@ hipError_t launch_sp(const M1Args& a, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((m1_scan_kernel<Tin, Tout, 1, SP>), dim3(gx, (unsigned)(a.G - 1)), dim3(kRows), 0,
                                    stream, a);
+        }
+        if (a.carry_scan) {
+            KTime kt("m1_scan_carry", stream);
+            hipLaunchKernelGGL(m1_carry_kernel, dim3((unsigned)(a.batch * a.dim)), dim3(64), 0, stream, a);
         }
     }
     KTime kt("m1_scan_output", stream);

@@ -99,6 +99,7 @@ selscan_status_t device_check() {
 struct M1Plan {
     int G;
     int xcd;   // chunk g on XCD g % 8 (G a multiple of 8)
+    int carry_scan;   // carries from the scan kernel rather than a fold per chunk
     int64_t chunk;
     int NS;
     size_t bc_bytes, state_bytes, w_bytes, ws_bytes;
@@ -153,6 +154,11 @@ M1Plan plan_m1(const selscan_shape_t* s) {
     p.G = (int)G;
     p.chunk = chunk;
     p.xcd = G % 8 == 0 && wgs * G < (int64_t(1) << 24) && env_int("SELSCAN_M1_XCD", 1) != 0;
+    // chunk g folds the g summaries before it at its start: hidden behind the
+    // scan up to about 16 chunks (measured), beyond that the fold's latency
+    // grows into the output pass and one scan over all summaries (a launch of
+    // its own, 20-35 us on Mamba-130m/2.8b-sized layers) is cheaper
+    p.carry_scan = G > 1 && env_int("SELSCAN_M1_CARRY_SCAN", G > 16 ? 1 : 0) != 0;
     const int64_t rows = s->batch * s->dim;
     p.bc_bytes = align256(selscan::m1_bc_bytes(s->batch, s->seqlen));
     p.state_bytes = G > 1 ? align256((size_t)rows * G * p.NS * 4) : 0;
@@ -346,6 +352,7 @@ selscan_status_t selscan_fwd_h0(const selscan_shape_t* s, const void* u, const v
         a.G = plan.G; a.chunk = plan.chunk; a.softplus = softplus;
         a.force_general = env_int("SELSCAN_FORCE_GENERAL", 0) != 0;
         a.xcd_chunks = plan.xcd;
+        a.carry_scan = plan.carry_scan;
         // 32-token runs of every row start on 16-byte boundaries
         a.vec_ok = (s->seqlen * in_es) % 16 == 0 && (s->seqlen * out_es) % 16 == 0 && aligned16(u) &&
                    aligned16(delta) && aligned16(y) && (!z || aligned16(z));
@@ -356,9 +363,9 @@ selscan_status_t selscan_fwd_h0(const selscan_shape_t* s, const void* u, const v
             a.ws_w = reinterpret_cast<float*>(base + plan.bc_bytes + plan.state_bytes);
         }
         if (log_plans())
-            std::fprintf(stderr, "[selscan] m1 B=%lld D=%lld N=%lld L=%lld chunks=%d chunk=%lld ws=%zu vec=%d xcd=%d\n",
+            std::fprintf(stderr, "[selscan] m1 B=%lld D=%lld N=%lld L=%lld chunks=%d chunk=%lld ws=%zu vec=%d xcd=%d scan=%d\n",
                          (long long)s->batch, (long long)s->dim, (long long)s->dstate, (long long)s->seqlen, plan.G,
-                         (long long)plan.chunk, plan.ws_bytes, a.vec_ok, a.xcd_chunks);
+                         (long long)plan.chunk, plan.ws_bytes, a.vec_ok, a.xcd_chunks, a.carry_scan);
         hipError_t e = selscan::launch_m1(a, in_bf16, out_bf16, hs);
         ws.release();
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));

@@ -57,16 +57,46 @@ def test_state_sizes(gpu, N, a_kind):
     _full_compare(inp)
 
 
+@pytest.mark.parametrize("scan", ["0", "1"])
 @pytest.mark.parametrize("chunks", [1, 2, 3, 7, 8, 40])
 @pytest.mark.parametrize("general", [False, True])
-def test_chunk_carry_plans(gpu, monkeypatch, chunks, general):
+def test_chunk_carry_plans(gpu, monkeypatch, chunks, general, scan):
     """Forced chunk counts (including chunks that end mid-sequence with a
-    ragged tail) and both decay paths agree with the oracle."""
+    ragged tail), both decay paths and both ways of forming the carries (a
+    fold at the start of each chunk, or the scan kernel) agree with the
+    oracle."""
     monkeypatch.setenv("SELSCAN_M1_CHUNKS", str(chunks))
+    monkeypatch.setenv("SELSCAN_M1_CARRY_SCAN", scan)
     if general:
         monkeypatch.setenv("SELSCAN_FORCE_GENERAL", "1")
     inp = _inputs(3, 300, 16, 1250, torch.bfloat16, seed=chunks)
     _full_compare(inp)
+
+
+@pytest.mark.parametrize("chunks", [64, 65, 130, 200])
+@pytest.mark.parametrize("general,h0,scan", [(False, False, "1"), (True, True, "1"), (False, True, "0")])
+def test_chunk_carry_scan_over_many_chunks(gpu, monkeypatch, chunks, general, h0, scan):
+    """More chunks than lanes: each lane of the carry scan folds a strip of
+    two to four chunk summaries (with empty strips at the end), and the carry
+    from the caller's initial state reaches every chunk; the per-chunk fold
+    gives the same at these counts."""
+    monkeypatch.setenv("SELSCAN_M1_CHUNKS", str(chunks))
+    monkeypatch.setenv("SELSCAN_M1_CARRY_SCAN", scan)
+    if general:
+        monkeypatch.setenv("SELSCAN_FORCE_GENERAL", "1")
+    L = 64 * 200 + 37
+    inp = _inputs(2, 70, 16, L, torch.bfloat16, seed=chunks)
+    if not h0:
+        _full_compare(inp)
+        return
+    h = synth.m1_state(2, 70, 16, seed=chunks, device=DEV)
+    y, last = ss.fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"],
+                     h0=h)
+    torch.cuda.synchronize()
+    yr, lr = oracle.m1(host(inp["u"]), host(inp["delta"]), host(inp["A"]), host(inp["B"]), host(inp["C"]),
+                       host(inp["D"]), host(inp["z"]), host(inp["delta_bias"]), softplus=True, h0=host(h))
+    check_close(host(y).double().numpy(), yr, TOL_BF16, "y")
+    check_close(host(last).double().numpy(), lr, TOL_BF16, "last_state")
 
 
 def test_xcd_chunk_mapping_is_bitwise_neutral(gpu, monkeypatch):
