@@ -5,11 +5,17 @@
 Each source compiles to its own object (in parallel), then one shared
 library is linked next to this file.  All device code is compiled with
 packed-FP32 instructions disabled.
+
+The build fails when a kernel needs scratch memory (register spills): a
+kernel with spill slots, even in a branch that never runs, is launched as a
+scratch user, which has cost ~30% of a whole launch here.  Set
+SELSCAN_ALLOW_SCRATCH=1 to build anyway.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -37,16 +43,39 @@ def flags() -> list[str]:
             "-I", INCLUDE, "-I", CSRC]
 
 
+def scratch_users(remarks: str) -> list[tuple[str, int]]:
+    """(kernel, bytes per lane) for every kernel whose resource-usage remarks
+    report scratch memory."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    device = src.endswith(".hip")
+    cmd = [hipcc()] + flags() + (["-Rpass-analysis=kernel-resource-usage"] if device else []) + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    lines = [l for l in r.stderr.splitlines() if noise not in l]
+    # the remarks and the source lines they quote stay out of the log
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l and not re.match(r"\s*\d*\s*\|", l))
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{err}")
     if err.strip():
         sys.stderr.write(err + "\n")
+    spills = scratch_users("\n".join(lines)) if device else []
+    if spills and os.environ.get("SELSCAN_ALLOW_SCRATCH", "0") != "1":
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills): "
+                           + ", ".join(f"{k} {b} B/lane" for k, b in spills))
     return obj
 
 
