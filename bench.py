@@ -23,6 +23,9 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+# fp32 VALU lane-instructions per second: 256 CUs x 4 SIMDs x 64 lanes per 4 cycles x 2.4 GHz (an FMA is one;
+# the 157.3 TFLOP/s vector figure counts an FMA as two flops and two packed lanes per instruction)
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9   # 256 CUs x 64 fp32 lanes/clk x 2.4 GHz (non-packed)
 # the largest single-GPU workload: the million-token Mamba-1 layer scan
 HEADLINE = "long_1m"
@@ -382,15 +385,30 @@ def read_traffic(workload, kernel):
     return float(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None
 
 
-def read_valu(workload, kernel):
+def read_valu(workload, kernel, launch_ms=None, updates=None):
     """VALU lane-instructions per state update and VALU busy at the measured
-    clock, from the same committed summary, or None."""
+    clock, from the same committed summary, or None.  With this run's launch
+    time and the call's state updates, also the lane-instruction rate it
+    implies against the VALU peak (the kernel's other roofline)."""
     kv = read_profile(workload, kernel)
     out = {}
     for k in ("valu_lane_ops_per_update", "valu_busy_at_measured_clock", "measured_clock_ghz"):
         if k in kv:
             out[k] = float(kv[k])
+    if out and launch_ms and updates and "valu_lane_ops_per_update" in out:
+        rate = out["valu_lane_ops_per_update"] * updates / (launch_ms * 1e-3)
+        out.update({"achieved_lane_ops_per_s": rate, "peak_lane_ops_per_s": VALU_PEAK_LANE_OPS,
+                    "frac": rate / VALU_PEAK_LANE_OPS})
     return out or None
+
+
+def read_call_traffic(workload, kernel):
+    """HBM bytes of the whole call (every kernel, counters scaled as for the
+    dominant kernel) from the dominant kernel's committed summary, or None."""
+    kv = read_profile(workload, kernel)
+    if "call_hbm_bytes" not in kv:
+        return None
+    return {"bytes": float(kv["call_hbm_bytes"]), "over_algorithmic": float(kv["call_traffic_over_algorithmic"])}
 
 
 def cpu_baseline(name, seed, min_s=10.0, max_s=30.0):
@@ -484,7 +502,9 @@ def main():
         r["dominant_kernel"] = {"name": kn, "avg_ms": kk["avg_ms"],
                                 "gbs": r["algorithmic_bytes"] / (kk["avg_ms"] * 1e-3) / 1e9,
                                 "frac": r["algorithmic_bytes"] / (kk["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                "traffic": read_traffic(name, kn), "valu": read_valu(name, kn)}
+                                "traffic": read_traffic(name, kn),
+                                "valu": read_valu(name, kn, kk["avg_ms"], r["updates_per_step"]),
+                                "call_traffic": read_call_traffic(name, kn)}
         extras[name] = r
 
     kname, k = dominant_kernel(head)
@@ -519,11 +539,19 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kname, "avg_launch_ms": avg_ms, "launches": k["launches"],
                      "bytes_per_launch": head["algorithmic_bytes"],
+                     "traffic_over_algorithmic": None if traffic is None else traffic / head["algorithmic_bytes"],
                      # the whole call (every kernel and the gaps between them)
                      "whole_call": {"achieved": head["hbm_gbs"], "frac": head["hbm_frac_of_peak"],
-                                    "ms": head["ms_per_step"]},
+                                    "ms": head["ms_per_step"],
+                                    "traffic": read_call_traffic(args.workload, kname)},
                      "kernels": {n: v["avg_ms"] for n, v in head["kernels"].items()},
-                     "valu": read_valu(args.workload, kname)},
+                     # the same kernel against its other ceiling, the VALU issue rate
+                     "valu": read_valu(args.workload, kname, avg_ms, head["updates_per_step"]),
+                     "summary_pass": ({"traffic": read_traffic(args.workload, "m1_scan_summary"),
+                                       "valu": read_valu(args.workload, "m1_scan_summary",
+                                                         head["kernels"]["m1_scan_summary"]["avg_ms"],
+                                                         head["updates_per_step"])}
+                                      if "m1_scan_summary" in head["kernels"] else None)},
         "workloads": {args.workload: head, **extras},
         "library": ss.version(),
     }
