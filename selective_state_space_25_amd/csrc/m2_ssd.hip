@@ -91,7 +91,6 @@ __device__ __forceinline__ bf16x8 cat(s16x4 a, s16x4 b) {
     const s16x8 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, r);
 }
-__device__ __forceinline__ s16x4 ld4(const uint16_t* p) { return *reinterpret_cast<const s16x4*>(p); }
 
 // Transposing LDS load.  Within each group of 16 lanes, lane a passes the
 // address of 4 consecutive elements; lane i receives element i % 4 of the
@@ -107,6 +106,25 @@ __device__ __forceinline__ s16x4 ld_tr(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 ld_col8(const uint16_t* m, int rs, int r0, int c0, int lane) {
     const int g = lane >> 4, a = lane & 15;
     const uint16_t* p = m + (r0 + 8 * g + (a >> 2)) * rs + c0 + 4 * (a & 3);
+    return cat(ld_tr(p), ld_tr(p + 4 * rs));
+}
+
+// B and C rows sit in LDS with the state index permuted in 4-element
+// pieces inside each group of 32: pieces 0..7 at positions 0, 2, 4, 6, 1, 3,
+// 5, 7.  The C operand of C S takes pieces p and p + 4 of a group (the
+// order that matches the state's accumulator rows), which are then one
+// contiguous 16-byte read instead of two 8-byte reads from 16 rows (2-way
+// bank conflicts); the contractions over n pair B and C under the same
+// permutation, and the transposed B reads address their pieces through it.
+__device__ __forceinline__ int npos(int n) {
+    const int pc = (n & 31) >> 2;
+    return (n & ~31) + 4 * (pc < 4 ? 2 * pc : 2 * pc - 7) + (n & 3);
+}
+
+// As ld_col8 over a B row block stored with npos: columns c0 .. c0 + 15.
+__device__ __forceinline__ bf16x8 ld_col8_n(const uint16_t* m, int rs, int r0, int c0, int lane) {
+    const int g = lane >> 4, a = lane & 15;
+    const uint16_t* p = m + (r0 + 8 * g + (a >> 2)) * rs + npos(c0 + 4 * (a & 3));
     return cat(ld_tr(p), ld_tr(p + 4 * rs));
 }
 
@@ -275,8 +293,11 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
         *reinterpret_cast<u32x4*>(&sm.zs[rt][8 * rq]) = r.z;
 #pragma unroll
         for (int q = 0; q < NBC; ++q) {
-            *reinterpret_cast<u32x4*>(&sm.Bs[rt][8 * (NBC * rq + q)]) = r.b[q];
-            *reinterpret_cast<u32x4*>(&sm.Cs[rt][8 * (NBC * rq + q)]) = r.c[q];
+            const int n0 = 8 * (NBC * rq + q);
+            *reinterpret_cast<uint2*>(&sm.Bs[rt][npos(n0)]) = make_uint2(r.b[q].x, r.b[q].y);
+            *reinterpret_cast<uint2*>(&sm.Bs[rt][npos(n0 + 4)]) = make_uint2(r.b[q].z, r.b[q].w);
+            *reinterpret_cast<uint2*>(&sm.Cs[rt][npos(n0)]) = make_uint2(r.c[q].x, r.c[q].y);
+            *reinterpret_cast<uint2*>(&sm.Cs[rt][npos(n0 + 4)]) = make_uint2(r.c[q].z, r.c[q].w);
         }
     };
 
@@ -314,10 +335,10 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             Yacc[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint16_t* crow = &sm.Cs[16 * tb + li][nb0 + 4 * lg];
+            const uint16_t* crow = &sm.Cs[16 * tb + li][nb0 + 8 * lg];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 cv = cat(ld4(crow + 32 * ks), ld4(crow + 32 * ks + 16));
+                const bf16x8 cv = ld8(crow + 32 * ks);
                 Yacc[tb] = mfma(cv, Sh[ks], Yacc[tb]);
                 Yacc[tb] = mfma(cv, Sl[ks], Yacc[tb]);
             }
@@ -431,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     // B^T operand: row n = nb0 + 16 j + li, k = s
-                    const bf16x8 bt = ld_col8(&sm.Bs[0][0], kRowN, 32 * ks, nb0 + 16 * j, lane);
+                    const bf16x8 bt = ld_col8_n(&sm.Bs[0][0], kRowN, 32 * ks, nb0 + 16 * j, lane);
                     S[j] = mfma(bt, wh, S[j]);
                     S[j] = mfma(bt, wl, S[j]);
                 }
