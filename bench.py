@@ -29,7 +29,7 @@ VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9   # 256 CUs x 64 fp32 lanes/clk x 2.4 GHz (non-packed)
 # the largest single-GPU workload: the million-token Mamba-1 layer scan
 HEADLINE = "long_1m"
-EXTRA = ["mamba130m_l2k", "mamba2p8b_l8k", "mamba2p8b_l8k_alog", "mamba2_mh"]
+EXTRA = ["mamba130m_l2k", "mamba2p8b_l8k", "mamba2p8b_l8k_alog", "long_1m_shard8", "mamba2_mh"]
 
 
 def parse():

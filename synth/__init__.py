@@ -68,6 +68,10 @@ WORKLOADS = {
     "long_1m": Workload("long_1m", "m1", batch=1, seqlen=1 << 20, dstate=16, dtype=torch.bfloat16,
                         dim=2048, a_kind="s4d_jitter",
                         note="million-token scan: d_inner 2048, d_state 16, batch 1, L 2^20"),
+    "long_1m_shard8": Workload("long_1m_shard8", "m1", batch=1, seqlen=1 << 20, dstate=16, dtype=torch.bfloat16,
+                               dim=256, a_kind="s4d_jitter",
+                               note="one GPU's share of the million-token layer split 8 ways by channel: "
+                                    "d_inner 256, d_state 16, batch 1, L 2^20"),
     "mamba2p8b_l8k_alog": Workload("mamba2p8b_l8k_alog", "m1", batch=4, seqlen=8192, dstate=16,
                                    dtype=torch.bfloat16, dim=5120, a_kind="alog",
                                    note="Mamba-2.8b-shaped layer with A = -exp(A_log) (no exact S4D-real "

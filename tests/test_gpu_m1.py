@@ -252,7 +252,7 @@ def test_isolated_zero_inputs(gpu, monkeypatch, chunks):
 
 
 @pytest.mark.parametrize("workload,nrows", [("mamba130m_l2k", 48), ("mamba2p8b_l8k", 48), ("mamba2p8b_l8k_alog", 48),
-                                            ("long_1m", 6)])
+                                            ("long_1m", 6), ("long_1m_shard8", 6)])
 def test_full_size_workloads_sampled(gpu, workload, nrows):
     """The benchmark's workloads at full size, in the launch plan the
     benchmark uses; sampled rows (first, last, random) against the oracle."""
