@@ -210,3 +210,31 @@ def test_full_size_sampled(gpu, name):
     _check_grads(got, ref, names=("dB", "dC"))
     del got, masked, inp, dout
     torch.cuda.empty_cache()
+
+
+def test_maximum_seqlen_sampled(gpu):
+    """The longest sequence the backward accepts (2^22 tokens, 32-bit byte
+    offsets from per-workgroup bases): per-row and per-channel gradients of
+    sampled channels exact from the oracle on those channels, dB and dC
+    from a run with dout zero outside the sample (as in the full-size
+    test above)."""
+    L = 1 << 22
+    inp, dout = _case(1, 64, 16, L, torch.bfloat16, seed=22)
+    chans = [0, 37, 63]
+    idx = torch.tensor(chans, device=DEV)
+    sub = {k: (None if v is None else
+               v.index_select(1, idx).contiguous() if k in ("u", "delta", "z") else
+               v.index_select(0, idx).contiguous() if k in ("A", "D", "delta_bias") else v)
+           for k, v in inp.items()}
+    print(f"[bwd max seqlen] B=1 D=64 L={L}", flush=True)
+    ref = _oracle(sub, dout.index_select(1, idx))
+    got = _gpu(inp, dout)
+    got = {k: (v.index_select(1, idx) if k in ("du", "ddelta", "dz") else v) for k, v in got.items()}
+    _check_grads(got, ref, names=("du", "ddelta", "dz", "dA", "dD", "ddelta_bias"), chans=chans)
+    del got
+    masked = torch.zeros_like(dout)
+    masked[:, idx] = dout[:, idx]
+    got = _gpu(inp, masked)
+    _check_grads(got, ref, names=("dB", "dC"))
+    del got, masked, inp, dout
+    torch.cuda.empty_cache()

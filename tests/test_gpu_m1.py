@@ -269,3 +269,22 @@ def test_full_size_workloads_sampled(gpu, workload, nrows):
     check_close(host(last[idx_b, idx_d]).double().numpy(), lr, TOL_BF16, f"{workload} last_state")
     del inp, y, last
     torch.cuda.empty_cache()
+
+
+def test_maximum_seqlen_sampled(gpu):
+    """The longest sequence the forward accepts (2^24 - 1 tokens: the 32-bit
+    byte offsets of the row copies and of the y stores near their limit),
+    with a ragged tail and a partial 64-channel block, in the plan the
+    library picks (over a thousand chunks, the carry scan): sampled rows
+    against the oracle over the whole length, and the final state."""
+    L = (1 << 24) - 1
+    inp = _inputs(1, 70, 16, L, torch.bfloat16, seed=24)
+    print(f"[max seqlen] B=1 D=70 L={L}", flush=True)
+    y, last = _run(inp)
+    rows = [(0, 0), (0, 63), (0, 69)]
+    yr, lr = oracle_m1_rows(inp, rows)
+    idx = torch.tensor([d for _, d in rows], device=DEV)
+    check_close(host(y[0].index_select(0, idx)).double().numpy(), yr, TOL_BF16, "y")
+    check_close(host(last[0].index_select(0, idx)).double().numpy(), lr, TOL_BF16, "last_state")
+    del inp, y, last, yr
+    torch.cuda.empty_cache()
