@@ -161,3 +161,23 @@ def test_chunked_mfma_form_edge_cases(gpu, case):
                        h0=None if h0 is None else host(h0))
     check_close(host(y).double().numpy(), yr, tol_out_bf16(TOL_BF16) if out_dtype else TOL_BF16, "y")
     check_close(host(last).double().numpy(), lr, TOL_BF16, "last_state")
+
+
+@pytest.mark.parametrize("ssd", ["1", "0"])
+def test_long_sequence_sampled(gpu, monkeypatch, ssd):
+    """A million-token sequence with a ragged last chunk through the chunked
+    matrix form (16,385 chunks walked by one workgroup per head) and through
+    the recurrent form: sampled heads against the oracle over the whole
+    length, and their final states."""
+    monkeypatch.setenv("SELSCAN_M2_SSD", ssd)
+    L = (1 << 20) + 37
+    inp = _inputs(1, L, 4, 64, 1, 64, torch.bfloat16, seed=20)
+    print(f"[m2 long] ssd={ssd} L={L}", flush=True)
+    y, last = _run(inp)
+    units = [(0, 0), (0, 3)]
+    yr, lr = oracle_m2_units(inp, units)
+    for i, (b, h) in enumerate(units):
+        check_close(host(y[b, :, h]).double().numpy(), yr[i], TOL_BF16, f"y unit {(b, h)}")
+        check_close(host(last[b, h]).double().numpy(), lr[i], TOL_BF16, f"last unit {(b, h)}")
+    del inp, y, last, yr
+    torch.cuda.empty_cache()
