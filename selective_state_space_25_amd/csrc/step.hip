@@ -99,9 +99,9 @@ __global__ __launch_bounds__(256) void m1_step_kernel(StepArgs a) {
         hv[i] = __builtin_fmaf(fast_exp2(w * Av[i]), hv[i], x * Bv[i]);
         acc = __builtin_fmaf(Cv[i], hv[i], acc);
     }
+    if (ok) *st = h;
     acc = group_sum<Q>(acc);
     if (!ok) return;
-    *st = h;
     if (qi == 0) {
         float yv = a.D ? __builtin_fmaf(a.D[d], uu, acc) : acc;
         if (a.z) yv *= silu(ld1(reinterpret_cast<const Tin*>(a.z), row));
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void m1_step_rows_kernel(StepArgs a) {
 }
 
 // Mamba-2: row = (batch, head, channel), scalar A per head, B/C per group.
-template <typename Tin, typename Tout, bool SP, int Q>
+template <typename Tin, typename Tout, bool SP, int Q, int E>
 __global__ __launch_bounds__(256) void m2_step_kernel(StepArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t rows = a.batch * a.H * a.P;
@@ -153,34 +153,42 @@ __global__ __launch_bounds__(256) void m2_step_kernel(StepArgs a) {
     const Tin* DT = reinterpret_cast<const Tin*>(a.delta);
     const Tin* Bm = reinterpret_cast<const Tin*>(a.B) + (b * a.G + grp) * N;
     const Tin* Cm = reinterpret_cast<const Tin*>(a.C) + (b * a.G + grp) * N;
+    float4* st = reinterpret_cast<float4*>(a.state + row * N) + qi * (E / 4);
+    float4 s[E / 4];
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) s[k] = st[k];
     const float xx = ld1(X, row);
     const float w = SP ? delta_log2<true>(ld1(DT, bh), a.bias ? a.bias[h] : 0.0f)
                        : delta_log2<false>(ld1(DT, bh), a.bias ? a.bias[h] : 0.0f);
     const float dA = fast_exp2(w * a.A[h]);
     const float x = (w * kLn2) * xx;
     float acc = 0.0f;
-    float4* st = reinterpret_cast<float4*>(a.state + row * N) + qi;
-    float4 s = *st;
-    float* sv = reinterpret_cast<float*>(&s);
-    float Bv[4], Cv[4];
+    float* sv = reinterpret_cast<float*>(&s[0]);
+    float Bv[E], Cv[E];
     if (a.vec) {
-        ld4(Bm + 4 * qi, Bv);
-        ld4(Cm + 4 * qi, Cv);
+#pragma unroll
+        for (int k = 0; k < E / 4; ++k) {
+            ld4(Bm + E * qi + 4 * k, Bv + 4 * k);
+            ld4(Cm + E * qi + 4 * k, Cv + 4 * k);
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Bv[i] = ld1(Bm, 4 * qi + i);
-            Cv[i] = ld1(Cm, 4 * qi + i);
+        for (int i = 0; i < E; ++i) {
+            Bv[i] = ld1(Bm, E * qi + i);
+            Cv[i] = ld1(Cm, E * qi + i);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < E; ++i) {
         sv[i] = __builtin_fmaf(dA, sv[i], x * Bv[i]);
         acc = __builtin_fmaf(Cv[i], sv[i], acc);
     }
+    if (ok) {
+#pragma unroll
+        for (int k = 0; k < E / 4; ++k) st[k] = s[k];
+    }
     acc = group_sum<Q>(acc);
     if (!ok) return;
-    *st = s;
     if (qi == 0) {
         float yv = a.D ? __builtin_fmaf(a.D[h], xx, acc) : acc;
         if (a.z) yv *= silu(ld1(reinterpret_cast<const Tin*>(a.z), row));
@@ -194,11 +202,20 @@ hipError_t launch_q(const StepArgs& a, int64_t rows, hipStream_t stream, bool ma
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     if (mamba2) {
         KTime kt("m2_step", stream);
-        hipLaunchKernelGGL((m2_step_kernel<Tin, Tout, SP, Q>), dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((m2_step_kernel<Tin, Tout, SP, Q, 4>), dim3(blocks), dim3(256), 0, stream, a);
     } else {
         KTime kt("m1_step", stream);
         hipLaunchKernelGGL((m1_step_kernel<Tin, Tout, SP, Q>), dim3(blocks), dim3(256), 0, stream, a);
     }
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout, bool SP, int Q>
+hipError_t launch_q8(const StepArgs& a, int64_t rows, hipStream_t stream) {
+    const int64_t threads = rows * Q;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    KTime kt("m2_step", stream);
+    hipLaunchKernelGGL((m2_step_kernel<Tin, Tout, SP, Q, 8>), dim3(blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -210,8 +227,10 @@ hipError_t launch_sp(const StepArgs& a, hipStream_t stream, bool mamba2) {
         case 8: return launch_q<Tin, Tout, SP, 2>(a, rows, stream, mamba2);
         case 16: return launch_q<Tin, Tout, SP, 4>(a, rows, stream, mamba2);
         case 32: return launch_q<Tin, Tout, SP, 8>(a, rows, stream, mamba2);
-        case 64: return launch_q<Tin, Tout, SP, 16>(a, rows, stream, mamba2);
-        case 128: return launch_q<Tin, Tout, SP, 32>(a, rows, stream, mamba2);
+        case 64: if (mamba2) return launch_q8<Tin, Tout, SP, 8>(a, rows, stream);
+                 return launch_q<Tin, Tout, SP, 16>(a, rows, stream, mamba2);
+        case 128: if (mamba2) return launch_q8<Tin, Tout, SP, 16>(a, rows, stream);
+                  return launch_q<Tin, Tout, SP, 32>(a, rows, stream, mamba2);
         default:
             if (mamba2 || a.N < 1 || a.N > 16) return hipErrorInvalidValue;
             {

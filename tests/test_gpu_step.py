@@ -161,6 +161,22 @@ def test_step_does_not_touch_other_rows(gpu):
     assert torch.equal(host(big[:, 5]), torch.full((1, 16), 7.0))
 
 
+@pytest.mark.parametrize("N", [64, 128])
+def test_m2_step_does_not_touch_other_rows(gpu, N):
+    """Mamba-2 rows (eight states per thread here) past the last one of a
+    partly filled block are not written: the state is followed by a guard."""
+    inp = synth.m2_inputs(1, 1, 3, 5, 1, N, torch.float32, seed=97, device=DEV)
+    rows = 3 * 5
+    buf = torch.full(((rows + 3) * N,), 7.0, dtype=torch.float32, device=DEV)
+    state = buf[:rows * N].view(1, 3, 5, N)
+    state.zero_()
+    sl = lambda k: inp[k][:, 0].contiguous()
+    ss.mamba2_step(state, sl("x"), sl("dt"), inp["A"], sl("B"), sl("C"), inp["D"], sl("z"), inp["dt_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(host(buf[rows * N:]), torch.full((3 * N,), 7.0))
+    assert not torch.equal(host(state), torch.zeros((1, 3, 5, N)))
+
+
 @pytest.mark.parametrize("mamba2", [False, True])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_step_with_unaligned_b_c(gpu, mamba2, dtype):
