@@ -468,7 +468,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; every box here has one GPU)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
