@@ -318,6 +318,20 @@ def time_backward(name, steps, device, warmup=2, seed=0):
     return res
 
 
+def time_abi_host(calls=200):
+    """Host time per decode call through the C ABI alone: the native harness
+    built beside the library (abi_bench) calls the step entry points back to
+    back from C++.  None when it is not built."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "selective_state_space_25_amd", "abi_bench")
+    if not os.path.exists(exe):
+        return None
+    r = subprocess.run([exe, str(calls)], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip()[-300:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def copy_calibration(device, gib):
     """Kernels of known traffic for scaling the HBM byte counters: a plain copy
     (torch.neg over fp32, reads and writes `gib` GiB) and a read of the first
@@ -556,6 +570,7 @@ def main():
         "library": ss.version(),
     }
     line["decode"] = {n: time_decode(n, 200, device) for n in ("mamba2p8b_l8k", "mamba2_mh")}
+    line["decode"]["c_abi_host_us_per_call"] = time_abi_host()
     line["conv1d"] = time_conv1d("mamba2p8b_l8k", 10, device)
     line["backward"] = {n: time_backward(n, 5 if n != "long_1m" else 3, device)
                         for n in ("mamba130m_l2k", "mamba2p8b_l8k", "long_1m")}

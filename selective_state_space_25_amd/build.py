@@ -25,6 +25,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libselscan.so")
+ABI_BENCH = os.path.join(HERE, "abi_bench")   # host cost of the decode entry points, timed from C++
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["selscan.cpp", "timing.cpp", "m1_scan.hip", "m2_scan.hip", "m2_ssd.hip", "step.hip", "conv1d.hip", "m1_bwd.hip", "noalloc.hip"]
 ARCH = os.environ.get("SELSCAN_ARCH", "gfx950")
@@ -87,6 +88,14 @@ def build(verbose: bool = True) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.run(cmd, check=True, capture_output=True)
     os.replace(tmp, LIB)
+    # the native decode timing harness, linked against the library beside it
+    tmp = ABI_BENCH + ".tmp"
+    cmd = [hipcc(), "-O2", "-std=c++17", "-I", INCLUDE, os.path.join(CSRC, "abi_bench.cpp"), "-o", tmp,
+           "-L", HERE, "-lselscan", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("building abi_bench failed:\n" + r.stderr)
+    os.replace(tmp, ABI_BENCH)
     if verbose:
         print(f"built {LIB}")
     return LIB
