@@ -164,6 +164,7 @@ hipError_t launch_conv1d(const ConvArgs& a, int in_bf16, int out_bf16, hipStream
 hipError_t launch_m2(const M2Args& a, int in_bf16, int out_bf16, hipStream_t stream);
 // Chunked matrix (SSD) form on MFMA for bf16 inputs, P = 64, N in {64, 128}.
 bool m2_ssd_supported(const M2Args& a, int in_bf16);
-hipError_t launch_m2_ssd(const M2Args& a, int out_bf16, hipStream_t stream);
+// ws: 1 = warp-specialised kernel (state waves and chunk waves), 0 = every wave in every phase
+hipError_t launch_m2_ssd(const M2Args& a, int out_bf16, int ws, hipStream_t stream);
 
 }  // namespace selscan

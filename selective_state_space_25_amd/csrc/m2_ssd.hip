@@ -22,16 +22,22 @@
 // 2^-16.  bf16 inputs, P = 64 and N in {64, 128} only; other shapes use the
 // recurrent kernel.
 //
-// The eight waves share every step.  Wave w holds the state rows of one
-// half of n (w / 4) for 16 columns (w % 4) in accumulator tiles, and
-// computes its part of C S (straight from those registers), of M X and of
-// the state update; two LDS buffers collect the two halves' parts of Y.
-// Every thread also stages an eighth of a token's inputs, builds M tiles,
-// splits the weighted x, prepares the gate and writes y.  Chunk inputs stay
-// in LDS in their memory layout ([token][channel] rows); operands that need
-// the other orientation are read with the transposing LDS load
-// (ds_read_b64_tr_b16), which hands each lane four consecutive rows of one
-// column.  Global memory is read and written through buffer descriptors
+// Two kernels share this arithmetic:
+//  - m2_ssd_ws_kernel (the default) splits the roles: four state waves hold
+//    the state and compute C S, the gate and y, and the state update; four
+//    chunk waves build M and M X and stage the inputs one chunk ahead, with
+//    one barrier per chunk between the groups (see its comment);
+//  - m2_ssd_kernel has every wave take part in every step, with four
+//    barrier-separated phases per chunk.  Wave w holds the state rows of one
+//    half of n (w / 4) for 16 columns (w % 4) in accumulator tiles, and
+//    computes its part of C S (straight from those registers), of M X and of
+//    the state update; two LDS buffers collect the two halves' parts of Y.
+//    Every thread also stages an eighth of a token's inputs, builds M tiles,
+//    splits the weighted x, prepares the gate and writes y.
+// Chunk inputs stay in LDS in their memory layout ([token][channel] rows);
+// operands that need the other orientation are read with the transposing LDS
+// load (ds_read_b64_tr_b16), which hands each lane four consecutive rows of
+// one column.  Global memory is read and written through buffer descriptors
 // bounded at the last token, so tokens past L load as zero and their stores
 // are dropped by the hardware: every chunk issues the same memory
 // operations.
@@ -475,14 +481,383 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Warp-specialised form.  Waves 0..3 ("state waves") each hold the state of
+// one 16-column p-tile for every n; per chunk they compute 2^cum C S, the gate
+// silu(z) and D x silu(z) of their outputs, y of the chunk before (adding the
+// chunk waves' M X), and the state update, with the weighted x built on the
+// fly from x and the decay weights.  Waves 4..7 ("chunk waves") each own one
+// 16-token t-tile: they build their rows of M in registers (no LDS round
+// trip) and M X, and stage the inputs.  The two groups meet at one barrier
+// per chunk: in iteration c the state waves finish y of chunk c - 1 and work
+// on chunk c while the chunk waves compute M X of chunk c and stage chunk
+// c + 1.  Every LDS array the groups exchange is double-buffered by chunk
+// parity, so the matrix-core work of one group overlaps the vector and LDS
+// work of the other instead of all waves running the same phase at once.
+// The gate sits with the state waves because the chunk waves, whose t-tiles
+// carry unequal shares of M (one to four 16x16 tiles), set the pace.
+//
+// Both groups work in the transposed orientation where that puts a lane's
+// values in the layout its consumer needs: C S and M X are computed as
+// (S^T C^T) and (X^T M^T), whose accumulators give each lane one token and
+// four consecutive channels p, the row-major order of y.
+
+// MFMA operand with k running down a row-major matrix in the permuted order
+// of an accumulator's rows: lane l = 16 g + i gets rows r0 + 4 g .. + 3, then
+// r0 + 16 + 4 g .. + 3, of column c0 + i (k-step over two 16-row tiles).
+__device__ __forceinline__ bf16x8 ld_col8_acc(const uint16_t* m, int rs, int r0, int c0, int lane) {
+    const int g = lane >> 4, a = lane & 15;
+    const uint16_t* p = m + (r0 + 4 * g + (a >> 2)) * rs + c0 + 4 * (a & 3);
+    return cat(ld_tr(p), ld_tr(p + 16 * rs));
+}
+
+template <int N>
+struct WsSmem {
+    static constexpr int kRowN = N + 8;
+    uint16_t Bs[2][kQ][kRowN];    // B, [s][n] (n permuted by npos)
+    uint16_t Cs[2][kQ][kRowN];    // C, [t][n] (n permuted by npos)
+    uint16_t xs[2][kQ][kRowX];    // x, [s][p]
+    uint16_t zs[2][kQ][kRowX];    // z, [t][p]
+    float Yc[2][kQ][kRowY];       // M X of the chunk, [t][p]
+    float dl[2][kQ];              // Delta
+    float cum[2][kQ];             // inclusive prefix of w A within the chunk
+    float wts[2][kQ];             // 2^(cum_last - cum_s) Delta_s
+    float ecum[2][kQ];            // 2^cum_t
+};
+
+// A chunk wave thread's quarter of one token's inputs, fetched a chunk ahead.
+template <int N>
+struct WsRegs {
+    static constexpr int kBC = N / 32;   // 16-byte pieces of a quarter B (or C) row
+    u32x4 x[2], z[2];
+    u32x4 b[kBC], c[kBC];
+    unsigned short dt;
+};
+
+template <typename Tout, int N, bool SP>
+__global__ __launch_bounds__(kThreads) void m2_ssd_ws_kernel(M2Args a) {
+    constexpr int NT = N / 16;               // 16-row state tiles per state wave
+    constexpr int KS = N / 32;               // k-steps over n
+    constexpr int NBC = WsRegs<N>::kBC;
+    constexpr int kRowN = WsSmem<N>::kRowN;
+    __shared__ __attribute__((aligned(16))) WsSmem<N> sm;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the roles branch on it
+    const int lane = tid & 63;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / a.H;
+    const int64_t h = bh - b * a.H;
+    const int64_t grp = h / (a.H / a.G);
+    const int64_t L = a.L;
+    const int64_t H = a.H, G = a.G;
+    const int64_t nch = (L + kQ - 1) / kQ;
+    const uint16_t* Z = reinterpret_cast<const uint16_t*>(a.z);
+
+    if (wave < 4) {
+        // ---------------- state waves: p-tile `wave`, every n ----------------
+        // A lane's outputs: token 16 tb + li, channels 16 pt + 4 lg .. + 3,
+        // for the four t-tiles tb.
+        const int pt = wave;
+        const int pcol = 16 * pt + li;
+        const bool has_z = Z != nullptr;
+        const float Dh = a.D ? a.D[h] : 0.0f;
+        Tout* Yg = reinterpret_cast<Tout*>(a.y);
+        const int64_t sy = H * kPd * (int64_t)sizeof(Tout);
+        // state tile j: rows n = 16 j + 4 lg + q, column pcol
+        f32x4 S[NT];
+        bf16x8 Sh[KS], Sl[KS];   // S^T as A operands (k-step ks: tiles 2 ks, 2 ks + 1)
+        auto split_state = [&]() {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float v = S[2 * ks + (j >> 2)][j & 3];
+                    const __bf16 hv = (__bf16)v;
+                    Sh[ks][j] = hv;
+                    Sl[ks][j] = (__bf16)(v - (float)hv);
+                }
+            }
+        };
+        // chunk c - 1 carried across the barrier: 2^cum C S, silu(z), D x silu(z)
+        f32x4 Ye[4];
+        float eg[16], edg[16];
+        // y of chunk c (M X from buffer cb), for c = -1 too through an empty
+        // descriptor that drops the stores
+        auto fin = [&](int64_t c, int cb) {
+            const int64_t t0 = c * kQ;
+            const int64_t rows = c < 0 ? 0 : L - t0 < kQ ? L - t0 : kQ;
+            const auto ry = rows_rsrc(Yg + ((b * L + t0) * H + h) * kPd, rows, sy, kPd * (int)sizeof(Tout));
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + li;
+                const f32x4 yi = *reinterpret_cast<const f32x4*>(&sm.Yc[cb][t][16 * pt + 4 * lg]);
+                float yv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    yv[q] = __builtin_fmaf(yi[q] + Ye[tb][q], eg[4 * tb + q], edg[4 * tb + q]);
+                const int yo = (int)(t * sy) + (16 * pt + 4 * lg) * (int)sizeof(Tout);
+                if constexpr (sizeof(Tout) == 4) {
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(yv[0]), __float_as_uint(yv[1]),
+                                                                 __float_as_uint(yv[2]), __float_as_uint(yv[3])},
+                                                           ry, yo, 0, 0);
+                } else {
+                    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])}, ry, yo, 0, 0);
+                }
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                S[j][q] = a.h0 ? a.h0[(bh * kPd + pcol) * N + 16 * j + 4 * lg + q] : 0.0f;
+        split_state();
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) Ye[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) eg[i] = edg[i] = 0.0f;
+        lds_barrier();   // chunk 0 staged
+
+        for (int64_t c = 0; c < nch; ++c) {
+            const int cb = (int)(c & 1);
+            fin(c - 1, cb ^ 1);
+            // (S^T C^T)[p, t] 2^cum_t for each t-tile
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                const uint16_t* crow = &sm.Cs[cb][16 * tb + li][8 * lg];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 cv = ld8(crow + 32 * ks);
+                    acc = mfma(Sh[ks], cv, acc);
+                    acc = mfma(Sl[ks], cv, acc);
+                }
+                Ye[tb] = acc * sm.ecum[cb][16 * tb + li];
+            }
+            // the gate of the lane's outputs
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + li;
+                const uint2 xw = *reinterpret_cast<const uint2*>(&sm.xs[cb][t][16 * pt + 4 * lg]);
+                const uint2 zw = *reinterpret_cast<const uint2*>(&sm.zs[cb][t][16 * pt + 4 * lg]);
+                const float xq[4] = {bf16lo(xw.x), bf16hi(xw.x), bf16lo(xw.y), bf16hi(xw.y)};
+                const float zq[4] = {bf16lo(zw.x), bf16hi(zw.x), bf16lo(zw.y), bf16hi(zw.y)};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // a select, not a branch: a branch per value would also
+                    // serialise the LDS reads around it (the empty asm keeps
+                    // the compiler from moving silu into one)
+                    float sz = silu_scaled(zq[q], 1.0f);
+                    asm volatile("" : "+v"(sz));
+                    const float gz = has_z ? sz : 1.0f;
+                    eg[4 * tb + q] = gz;
+                    edg[4 * tb + q] = Dh * xq[q] * gz;
+                }
+            }
+            // S = 2^cum_last S + B^T diag(w) X, the weighted x split as it is read
+            const float dec = sm.ecum[cb][kQ - 1];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) S[j] *= dec;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 xv = ld_col8(&sm.xs[cb][0][0], kRowX, 32 * ks, 16 * pt, lane);
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wts[cb][32 * ks + 8 * lg]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wts[cb][32 * ks + 8 * lg + 4]);
+                bf16x8 wh, wl;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float v = (float)xv[j] * (j < 4 ? w0[j] : w1[j - 4]);
+                    const __bf16 vh = (__bf16)v;
+                    wh[j] = vh;
+                    wl[j] = (__bf16)(v - (float)vh);
+                }
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    // B^T operand: row n = 16 j + li, k = s
+                    const bf16x8 bt = ld_col8_n(&sm.Bs[cb][0][0], kRowN, 32 * ks, 16 * j, lane);
+                    S[j] = mfma(bt, wh, S[j]);
+                    S[j] = mfma(bt, wl, S[j]);
+                }
+            }
+            split_state();
+            lds_barrier();
+        }
+        fin(nch - 1, (int)((nch - 1) & 1));
+        if (a.last) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a.last[(bh * kPd + pcol) * N + 16 * j + 4 * lg + q] = S[j][q];
+        }
+        return;
+    }
+
+    // ---------------- chunk waves: t-tile `wave - 4` --------------------------
+    const int tb = wave - 4;
+    const int t = 16 * tb + li;              // this lane's token within a chunk
+    const int ct = tid - 256;
+    const int rt = ct >> 2, rq = ct & 3;     // staging: token, quarter of a row
+    const float Ah = a.A[h];
+    const float bias_l = (a.dt_bias ? a.dt_bias[h] : 0.0f) * kLog2e;
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
+    const uint16_t* DT = reinterpret_cast<const uint16_t*>(a.dt);
+    const uint16_t* Bg = reinterpret_cast<const uint16_t*>(a.B);
+    const uint16_t* Cg = reinterpret_cast<const uint16_t*>(a.C);
+    const int64_t sx = H * kPd * 2, sbc = G * N * 2, sd = H * 2;
+
+    auto fetch = [&](int64_t t0, WsRegs<N>& r) {
+        const int64_t rows = L - t0 < kQ ? L - t0 : kQ;
+        if (wave == 4) {
+            const auto rd = rows_rsrc(DT + (b * L + t0) * H + h, rows, sd, 2);
+            r.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)(lane * sd), 0, 0);
+        }
+        const int64_t xo = ((b * L + t0) * H + h) * kPd;
+        const auto rx = rows_rsrc(X + xo, rows, sx, kPd * 2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            r.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(rt * sx) + 32 * rq + 16 * i, 0, 0);
+        if (Z) {
+            const auto rz = rows_rsrc(Z + xo, rows, sx, kPd * 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                r.z[i] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)(rt * sx) + 32 * rq + 16 * i, 0, 0);
+        }
+        const int64_t bo = ((b * L + t0) * G + grp) * N;
+        const auto rb = rows_rsrc(Bg + bo, rows, sbc, N * 2);
+        const auto rc = rows_rsrc(Cg + bo, rows, sbc, N * 2);
+#pragma unroll
+        for (int q = 0; q < NBC; ++q) {
+            r.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(rt * sbc) + 16 * (NBC * rq + q), 0, 0);
+            r.c[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(rt * sbc) + 16 * (NBC * rq + q), 0, 0);
+        }
+    };
+    // Delta, the in-chunk prefix of the log2 decay and the per-token factors
+    // of the chunk at t0 (tokens past L: Delta 0, decay 1, no input)
+    auto prefix = [&](int64_t t0, unsigned short dt, int buf) {
+        float wv = 0.0f;
+        if (t0 + lane < L) {
+            const float vl = __builtin_fmaf(bf16_to_f32(dt), kLog2e, bias_l);
+            wv = SP ? softplus_log2(vl) : vl;
+        }
+        float cs = wv * Ah;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float up = __shfl_up(cs, o, 64);
+            if (lane >= o) cs += up;
+        }
+        const float last = __shfl(cs, 63, 64);
+        const float dlv = wv * kLn2;
+        sm.dl[buf][lane] = dlv;
+        sm.cum[buf][lane] = cs;
+        sm.ecum[buf][lane] = fast_exp2(cs);
+        sm.wts[buf][lane] = fast_exp2(last - cs) * dlv;
+    };
+    auto stage = [&](const WsRegs<N>& r, int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<u32x4*>(&sm.xs[buf][rt][16 * rq + 8 * i]) = r.x[i];
+            *reinterpret_cast<u32x4*>(&sm.zs[buf][rt][16 * rq + 8 * i]) = r.z[i];
+        }
+#pragma unroll
+        for (int q = 0; q < NBC; ++q) {
+            const int n0 = 8 * (NBC * rq + q);
+            *reinterpret_cast<uint2*>(&sm.Bs[buf][rt][npos(n0)]) = make_uint2(r.b[q].x, r.b[q].y);
+            *reinterpret_cast<uint2*>(&sm.Bs[buf][rt][npos(n0 + 4)]) = make_uint2(r.b[q].z, r.b[q].w);
+            *reinterpret_cast<uint2*>(&sm.Cs[buf][rt][npos(n0)]) = make_uint2(r.c[q].x, r.c[q].y);
+            *reinterpret_cast<uint2*>(&sm.Cs[buf][rt][npos(n0 + 4)]) = make_uint2(r.c[q].z, r.c[q].w);
+        }
+    };
+
+    // (X^T M^T)[p, t] of chunk buffer cb for t-tile TB, into Yc.  The rows of
+    // M^T come from the MFMA (B C^T) in the accumulator layout (lane: column
+    // t, rows s = 16 sb + 4 lg + q), which is the B operand of the product with
+    // k = s permuted to match; X^T is read in the same order.
+    auto prep = [&](auto tbc, int cb) {
+        constexpr int TB = decltype(tbc)::value;
+        constexpr int KX = TB / 2 + 1;   // 32-token k-steps of M X
+        bf16x8 cop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) cop[ks] = ld8(&sm.Cs[cb][t][32 * ks + 8 * lg]);
+        const float ctv = sm.cum[cb][t];
+        bf16x8 mh[KX], ml[KX];
+#pragma unroll
+        for (int sb = 0; sb < 2 * KX; ++sb) {
+            float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (sb <= TB) {
+                f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) g = mfma(ld8(&sm.Bs[cb][16 * sb + li][32 * ks + 8 * lg]), cop[ks], g);
+                const int s0 = 16 * sb + 4 * lg;
+                const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[cb][s0]);
+                const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dl[cb][s0]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    m[q] = (sb < TB || s0 + q <= t) ? g[q] * fast_exp2(ctv - cs[q]) * ds[q] : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const __bf16 hv = (__bf16)m[q];
+                mh[sb >> 1][4 * (sb & 1) + q] = hv;
+                ml[sb >> 1][4 * (sb & 1) + q] = (__bf16)(m[q] - (float)hv);
+            }
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            f32x4 yi = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KX; ++ks) {
+                const bf16x8 xa = ld_col8_acc(&sm.xs[cb][0][0], kRowX, 32 * ks, 16 * pt, lane);
+                yi = mfma(xa, mh[ks], yi);
+                yi = mfma(xa, ml[ks], yi);
+            }
+            *reinterpret_cast<f32x4*>(&sm.Yc[cb][t][16 * pt + 4 * lg]) = yi;
+        }
+    };
+
+    WsRegs<N> cr;
+    cr.z[0] = cr.z[1] = u32x4{0u, 0u, 0u, 0u};
+    fetch(0, cr);
+    if (wave == 4) prefix(0, cr.dt, 0);
+    stage(cr, 0);
+    fetch(kQ, cr);
+    lds_barrier();
+
+    for (int64_t c = 0; c < nch; ++c) {
+        const int64_t t0 = c * kQ;
+        const int cb = (int)(c & 1);
+        switch (tb) {
+            case 0: prep(std::integral_constant<int, 0>{}, cb); break;
+            case 1: prep(std::integral_constant<int, 1>{}, cb); break;
+            case 2: prep(std::integral_constant<int, 2>{}, cb); break;
+            default: prep(std::integral_constant<int, 3>{}, cb); break;
+        }
+        // chunk c + 1 into the other buffer (its prefix from wave 4), then
+        // request chunk c + 2
+        stage(cr, cb ^ 1);
+        if (wave == 4 && c + 1 < nch) prefix(t0 + kQ, cr.dt, cb ^ 1);
+        fetch(t0 + 2 * kQ, cr);
+        lds_barrier();
+    }
+}
+
 template <typename Tout, int N>
-hipError_t launch_n(const M2Args& a, hipStream_t stream) {
+hipError_t launch_n(const M2Args& a, int ws, hipStream_t stream) {
     const unsigned blocks = (unsigned)(a.batch * a.H);
     KTime kt("m2_ssd", stream);
-    if (a.softplus)
+    if (ws) {
+        if (a.softplus)
+            hipLaunchKernelGGL((m2_ssd_ws_kernel<Tout, N, true>), dim3(blocks), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((m2_ssd_ws_kernel<Tout, N, false>), dim3(blocks), dim3(kThreads), 0, stream, a);
+    } else if (a.softplus) {
         hipLaunchKernelGGL((m2_ssd_kernel<Tout, N, true>), dim3(blocks), dim3(kThreads), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL((m2_ssd_kernel<Tout, N, false>), dim3(blocks), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -496,9 +871,9 @@ bool m2_ssd_supported(const M2Args& a, int in_bf16) {
            chunk_x < (int64_t(1) << 31) && chunk_b < (int64_t(1) << 31);
 }
 
-hipError_t launch_m2_ssd(const M2Args& a, int out_bf16, hipStream_t stream) {
-    if (a.N == 128) return out_bf16 ? launch_n<uint16_t, 128>(a, stream) : launch_n<float, 128>(a, stream);
-    return out_bf16 ? launch_n<uint16_t, 64>(a, stream) : launch_n<float, 64>(a, stream);
+hipError_t launch_m2_ssd(const M2Args& a, int out_bf16, int ws, hipStream_t stream) {
+    if (a.N == 128) return out_bf16 ? launch_n<uint16_t, 128>(a, ws, stream) : launch_n<float, 128>(a, ws, stream);
+    return out_bf16 ? launch_n<uint16_t, 64>(a, ws, stream) : launch_n<float, 64>(a, ws, stream);
 }
 
 }  // namespace selscan

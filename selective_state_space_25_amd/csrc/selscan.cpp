@@ -406,11 +406,12 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* s, const void* 
         if (env_int("SELSCAN_M2_SSD", 1) != 0 && selscan::m2_ssd_supported(a, in_bf16) && aligned16(x) &&
             aligned16(B) && aligned16(C)) {
             // chunked matrix form on MFMA; needs no workspace
+            const int ws_form = env_int("SELSCAN_M2_SSD_WS", 1) != 0;
             if (log_plans())
-                std::fprintf(stderr, "[selscan] m2 ssd B=%lld L=%lld H=%lld P=%lld G=%lld N=%lld\n",
+                std::fprintf(stderr, "[selscan] m2 ssd B=%lld L=%lld H=%lld P=%lld G=%lld N=%lld ws=%d\n",
                              (long long)s->batch, (long long)s->seqlen, (long long)s->nheads, (long long)s->headdim,
-                             (long long)s->ngroups, (long long)s->dstate);
-            hipError_t e = selscan::launch_m2_ssd(a, out_bf16, hs);
+                             (long long)s->ngroups, (long long)s->dstate, ws_form);
+            hipError_t e = selscan::launch_m2_ssd(a, out_bf16, ws_form, hs);
             if (e != hipSuccess)
                 return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
             return ok();

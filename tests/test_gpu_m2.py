@@ -133,14 +133,18 @@ def test_full_size_workload_sampled(gpu):
         check_close(host(last[b, h]).double().numpy(), lr[i], TOL_BF16, f"last unit {(b, h)}")
 
 
+@pytest.mark.parametrize("form", ["split_roles", "shared_phases"])
 @pytest.mark.parametrize("case", ["h0_n128_g2", "h0_n128_g2_bf16_out", "h0_single_token", "no_softplus",
-                                  "group_per_head", "ragged_many_heads"])
-def test_chunked_mfma_form_edge_cases(gpu, case):
-    """The chunked matrix form (bf16 inputs, headdim 64, N 64 or 128) on an
-    initial state, a single token, softplus off, one group per head and a
-    ragged length over several batches and heads, against the oracle."""
-    N = 64 if case in ("group_per_head", "h0_single_token") else 128
-    L = {"h0_single_token": 1, "ragged_many_heads": 197}.get(case, 333)
+                                  "group_per_head", "ragged_many_heads", "h0_n64_two_chunks"])
+def test_chunked_mfma_form_edge_cases(gpu, monkeypatch, case, form):
+    """The chunked matrix form (bf16 inputs, headdim 64, N 64 or 128), in
+    both of its kernels (state and chunk waves with split roles, the default;
+    all waves in every phase), on an initial state, a single token, softplus
+    off, one group per head and a ragged length over several batches and
+    heads, against the oracle."""
+    monkeypatch.setenv("SELSCAN_M2_SSD_WS", "1" if form == "split_roles" else "0")
+    N = 64 if case in ("group_per_head", "h0_single_token", "h0_n64_two_chunks") else 128
+    L = {"h0_single_token": 1, "ragged_many_heads": 197, "h0_n64_two_chunks": 128}.get(case, 333)
     batch, H, G = (3, 6, 3) if case == "ragged_many_heads" else (2, 4, 4 if case == "group_per_head" else 2)
     inp = _inputs(batch, L, H, 64, G, N, torch.bfloat16, seed=len(case))
     softplus = case != "no_softplus"
