@@ -122,6 +122,7 @@ struct M2Args {
     int64_t chunk;
     int chunks;
     int softplus;
+    int xcd_units;    // chunked matrix form: place the units of one batch on one XCD
 };
 
 int m2_waves_per_block(int64_t N);

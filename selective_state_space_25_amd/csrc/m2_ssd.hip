@@ -567,7 +567,12 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_ws_kernel(M2Args a) {
     const int lane = tid & 63;
     const int li = lane & 15;
     const int lg = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    // (batch, head) unit: workgroups are dealt to the 8 XCDs round-robin by
+    // id, so unit id % 8 * (units / 8) + id / 8 puts consecutive units, the
+    // heads of one batch that share its B and C, on one XCD and its L2
+    const int64_t nbh = a.batch * a.H;
+    const int64_t bh = (a.xcd_units && nbh % 8 == 0) ? (int64_t)(blockIdx.x % 8) * (nbh / 8) + blockIdx.x / 8
+                                                     : (int64_t)blockIdx.x;
     const int64_t b = bh / a.H;
     const int64_t h = bh - b * a.H;
     const int64_t grp = h / (a.H / a.G);

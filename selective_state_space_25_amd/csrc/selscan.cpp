@@ -407,6 +407,7 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* s, const void* 
             aligned16(B) && aligned16(C)) {
             // chunked matrix form on MFMA; needs no workspace
             const int ws_form = env_int("SELSCAN_M2_SSD_WS", 1) != 0;
+            a.xcd_units = env_int("SELSCAN_M2_XCD_UNITS", 1) != 0;
             if (log_plans())
                 std::fprintf(stderr, "[selscan] m2 ssd B=%lld L=%lld H=%lld P=%lld G=%lld N=%lld ws=%d\n",
                              (long long)s->batch, (long long)s->seqlen, (long long)s->nheads, (long long)s->headdim,
