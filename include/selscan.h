@@ -233,6 +233,15 @@ size_t selscan_mamba2_workspace_bytes(const selscan_m2_shape_t* shape);
  *   dt_bias    [H]           fp32       NULL = 0
  *   y          [B, L, H, P]  out_dtype  (written)
  *   last_state [B, H, P, N]  fp32       (written); NULL = skip
+ *
+ * Two forms compute it.  bf16 inputs with P = 64, N in {64, 128} and x, B, C
+ * on 16-byte boundaries take the chunked matrix form named in the README's
+ * Mamba-2 section (64-token chunks, the products on the matrix cores in bf16
+ * with fp32 accumulation; the fp32 operands -- the intra-chunk matrix, the
+ * state and the weighted x -- enter as bf16 pairs, relative error near
+ * 2^-16, and sums run in another order than the recurrence's); every other
+ * shape takes the recurrent form in fp32 (whose chunk carries on long
+ * sequences are what selscan_mamba2_workspace_bytes sizes).
  */
 selscan_status_t selscan_mamba2_fwd(const selscan_m2_shape_t* shape,
                                     const void* x, const void* dt, const float* A,
