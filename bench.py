@@ -351,6 +351,29 @@ def copy_calibration(device, gib):
     return n * 4
 
 
+def time_copy(device, gib=1.0, reps=10):
+    """Achievable HBM bandwidth for context: a plain device copy of `gib` GiB
+    (fp32, read once and written once), timed with events on the current
+    stream; GB/s counts the bytes read plus the bytes written."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    st = torch.cuda.current_stream(device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(device)
+    e0.record(st)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(st)
+    torch.cuda.synchronize(device)
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"bytes": 2 * n * 4, "ms": ms, "gbs": 2 * n * 4 / (ms * 1e-3) / 1e9}
+
+
 def decay_path(w):
     """Which Mamba-1 decay path the workload's A takes: "structured" when every
     row has A[d, n] == fl32((n + 1) A[d, 0]) (one exponential per token),
@@ -569,6 +592,10 @@ def main():
         "workloads": {args.workload: head, **extras},
         "library": ss.version(),
     }
+    # the bandwidth a plain copy reaches on this GPU, next to the peak
+    copy = time_copy(device)
+    line["roofline"]["copy"] = {"gbs": copy["gbs"], "kernel_frac_of_copy": achieved / copy["gbs"],
+                                "call_frac_of_copy": head["hbm_gbs"] / copy["gbs"]}
     line["decode"] = {n: time_decode(n, 200, device) for n in ("mamba2p8b_l8k", "mamba2_mh")}
     line["decode"]["c_abi_host_us_per_call"] = time_abi_host()
     line["conv1d"] = time_conv1d("mamba2p8b_l8k", 10, device)
