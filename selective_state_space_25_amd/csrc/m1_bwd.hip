@@ -997,7 +997,10 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
         fetch(tile > 0 ? tile - 1 : 0);   // unconditional: no branch around the loads
 
         // recompute the tile's states
-        float hs[kT][4];
+        // the tile's states and decays, kept for the adjoint sweep (the
+        // decays are not computed twice: 64 registers, which the two waves
+        // per SIMD leave free)
+        float hs[kT][4], as[kT][4];
         {
             float h[4] = {ck[0], ck[1], ck[2], ck[3]};
 #pragma unroll
@@ -1005,11 +1008,10 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
                 const float dt = sm.dt[c.r][j], dtu = sm.dtu[c.r][j];
                 const float4 Bv = *reinterpret_cast<const float4*>(&sm.B[j][4 * c.q]);
                 const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
-                float at[4];
-                decay4<ST>(c, dt, at);
+                decay4<ST>(c, dt, as[j]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    h[i] = __builtin_fmaf(at[i], h[i], dtu * bb[i]);
+                    h[i] = __builtin_fmaf(as[j][i], h[i], dtu * bb[i]);
                     hs[j][i] = h[i];
                 }
             }
@@ -1024,12 +1026,10 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
             const float cc[4] = {Cv.x, Cv.y, Cv.z, Cv.w};
             float sLB = 0.0f, sLAq = 0.0f, sCh = 0.0f;
             float v[8];
-            float ats[4];
-            decay4<ST>(c, dt, ats);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float hp = j > 0 ? hs[j - 1][i] : ck[i];
-                const float at = ats[i];
+                const float at = as[j][i];
                 const float lam = __builtin_fmaf(dy, cc[i], lamn[i]);
                 const float tq = lam * at * hp;
                 sLB = __builtin_fmaf(lam, bb[i], sLB);
