@@ -494,10 +494,49 @@ def cpu_baseline(name, seed, min_s=10.0, max_s=30.0):
         elapsed += one(rows_b)
         passes += 1
     upd = passes * rows_b * nd * nl * nn
-    return {"value": upd / elapsed, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
-            "sample": f"{passes} pass(es) over {rows_b} of {nb} batch elements of {what} "
-                      f"({rows_b * nd} (batch, channel) rows, full L={nl}, N={nn}), "
-                      f"fp64 with {cores} OpenMP threads, {elapsed:.1f} s of oracle time",
+    res = {"value": upd / elapsed, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+           "sample": f"{passes} pass(es) over {rows_b} of {nb} batch elements of {what} "
+                     f"({rows_b * nd} (batch, channel) rows, full L={nl}, N={nn}), "
+                     f"fp64 with {cores} OpenMP threads, {elapsed:.1f} s of oracle time",
+           "seconds": elapsed, "per_core": upd / elapsed / cores, "cpu_model": cpu_model()}
+    res["one_core"] = one_core_baseline(seed)
+    oracle.set_threads(cores)
+    return res
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None where absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def one_core_baseline(seed, min_s=2.0):
+    """The oracle on one thread, for scaling context: one batch element of the
+    Mamba-130m-shaped layer (1536 channels x 2048 tokens, N 16), repeated
+    until `min_s` seconds have run."""
+    import numpy as np
+    import synth
+    import oracle
+
+    w = synth.WORKLOADS["mamba130m_l2k"]
+    inp = synth.m1_inputs(1, w.dim, w.dstate, w.seqlen, w.dtype, w.a_kind, seed=seed, device="cpu")
+    f64 = {k: (None if v is None else np.ascontiguousarray(v.double().numpy())) for k, v in inp.items()}
+    oracle.set_threads(1)
+    passes, elapsed = 0, 0.0
+    while elapsed < min_s or passes == 0:
+        t = time.perf_counter()
+        oracle.m1(f64["u"], f64["delta"], f64["A"], f64["B"], f64["C"], f64["D"], f64["z"], f64["delta_bias"])
+        elapsed += time.perf_counter() - t
+        passes += 1
+    upd = passes * w.dim * w.seqlen * w.dstate
+    return {"value": upd / elapsed, "unit": "state-updates/s", "cores": 1,
+            "sample": f"{passes} pass(es) over batch element 0 of mamba130m_l2k (1536 channels, L=2048, N=16)",
             "seconds": elapsed}
 
 
@@ -603,6 +642,7 @@ def main():
                         for n in ("mamba130m_l2k", "mamba2p8b_l8k", "long_1m")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
+        line["cpu_baseline"]["gpu_over_cpu"] = line["value"] / line["cpu_baseline"]["value"]
     print(json.dumps(line))
 
 

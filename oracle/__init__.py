@@ -59,6 +59,8 @@ def _load():
             lib.oracle_conv1d_f64.argtypes = [i64] * 4 + [dp] * 3 + [ctypes.c_int, dp]
             lib.oracle_conv1d_f64.restype = ctypes.c_int
             lib.oracle_version.restype = ctypes.c_char_p
+            lib.oracle_set_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_threads.restype = None
             _lib = lib
     return _lib
 
@@ -82,9 +84,11 @@ def _ptr(a):
 
 
 def set_threads(n: int | None) -> None:
-    """Set the OpenMP thread count used by later oracle calls."""
+    """Set the OpenMP thread count used by later oracle calls (from this
+    Python thread)."""
     if n is not None:
         os.environ["OMP_NUM_THREADS"] = str(int(n))
+        _load().oracle_set_threads(int(n))
 
 
 def m1(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None):

@@ -38,6 +38,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <omp.h>
 
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
@@ -50,6 +51,13 @@ static double sp64(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x
 static double silu64(double z) { return z / (1.0 + exp(-z)); }
 
 const char* oracle_version(void) { return "selscan-oracle fp64 1"; }
+
+/* Number of threads of the calling thread's later parallel regions (the
+ * timing of the oracle picks it; OMP_NUM_THREADS is read only once, when the
+ * OpenMP runtime starts).  Values below 1 are ignored. */
+void oracle_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+}
 
 /*
  * Mamba-1 selective scan, one channel row at a time.
