@@ -97,6 +97,18 @@ def test_deterministic(gpu):
     assert torch.equal(y0, y1) and torch.equal(l0, l1)
 
 
+@pytest.mark.parametrize("N,G", [(128, 2), (64, 4)])
+def test_xcd_unit_order_is_a_permutation(gpu, monkeypatch, N, G):
+    """The chunked matrix form's placement of (batch, head) units on the
+    XCDs (16 units, a multiple of 8) only reorders the workgroups: y and the
+    final state are bitwise those of the linear order, and match the oracle."""
+    inp = _inputs(2, 200, 8, 64, G, N, torch.bfloat16, seed=N + G)
+    y1, l1 = _full_compare(inp)
+    monkeypatch.setenv("SELSCAN_M2_XCD_UNITS", "0")
+    y0, l0 = _run(inp)
+    assert torch.equal(y0, y1) and torch.equal(l0, l1)
+
+
 def test_causality_bitwise(gpu, monkeypatch):
     monkeypatch.setenv("SELSCAN_M2_CHUNKS", "3")
     inp = _inputs(1, 300, 4, 64, 1, 64, torch.bfloat16, seed=3)
