@@ -70,14 +70,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 // device (cached like device_cus()); later calls only read the current device.
 selscan_status_t device_check() {
     static std::mutex mu;
-    static signed char verdict[64] = {0};   // 0 unknown, 1 gfx950, -1 other
+    static signed char arch_state[64] = {0};   // 0 unknown, 1 gfx950, -1 other
     static std::string other[64];
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(SELSCAN_ERR_NO_DEVICE, "no HIP device available");
     if (dev < 64) {
         std::lock_guard<std::mutex> lk(mu);
-        if (verdict[dev] == 1) return SELSCAN_OK;
-        if (verdict[dev] == -1)
+        if (arch_state[dev] == 1) return SELSCAN_OK;
+        if (arch_state[dev] == -1)
             return fail(SELSCAN_ERR_NO_DEVICE, "libselscan is built for gfx950, device is " + other[dev]);
     }
     hipDeviceProp_t prop;
@@ -86,7 +86,7 @@ selscan_status_t device_check() {
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     if (dev < 64) {
         std::lock_guard<std::mutex> lk(mu);
-        verdict[dev] = ok ? 1 : -1;
+        arch_state[dev] = ok ? 1 : -1;
         if (!ok) other[dev] = prop.gcnArchName;
     }
     if (!ok)
