@@ -494,8 +494,10 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_kernel(M2Args a) {
 // c + 1.  Every LDS array the groups exchange is double-buffered by chunk
 // parity, so the matrix-core work of one group overlaps the vector and LDS
 // work of the other instead of all waves running the same phase at once.
-// The gate sits with the state waves because the chunk waves, whose t-tiles
-// carry unequal shares of M (one to four 16x16 tiles), set the pace.
+// The state waves' path is the longer one; the gate still sits with them,
+// because staged from the chunk waves (as silu(z) in fp32) it made the chunk
+// wave of t-tile 3, which carries the largest share of M (four 16x16 tiles
+// against one for t-tile 0), the slower side of the barrier.
 //
 // Both groups work in the transposed orientation where that puts a lane's
 // values in the layout its consumer needs: C S and M X are computed as
@@ -718,8 +720,8 @@ __global__ __launch_bounds__(kThreads) void m2_ssd_ws_kernel(M2Args a) {
     // ---------------- chunk waves: t-tile `wave - 4` --------------------------
     const int tb = wave - 4;
     const int t = 16 * tb + li;              // this lane's token within a chunk
-    // issue priority over the state wave sharing the SIMD: the chunk wave of
-    // t-tile 3 sets the pace of the barrier (measured: about 1.5 % less time)
+    // issue priority over the state wave sharing the SIMD (measured: about
+    // 1.5 % less time)
     __builtin_amdgcn_s_setprio(3);
     const int ct = tid - 256;
     const int rt = ct >> 2, rq = ct & 3;     // staging: token, quarter of a row
