@@ -84,8 +84,8 @@ struct BwdArgs {
     float* pD;      // [rows, G]
     float* pbias;   // [rows, G]
     float* part;    // [dim / 64, batch, L, 32] per-channel-block dB (16) and dC (16)
-    float* ckz;     // [rows, tiles, 16] state entering every tile (m1_bwd_tile() tokens) from the chunk's zero start
-    float* wck;     // [rows, tiles] sum of Delta from the chunk's start to the same tokens
+    float* ckz;     // [batch, tiles, dim, 16] state entering every tile (m1_bwd_tile() tokens) from the chunk's zero start
+    float* wck;     // [batch, tiles, dim] sum of Delta from the chunk's start to the same tokens
     float* bcq;     // [batch, L, 32] fp32 records of B and C (the lane-per-channel summary pass)
     int lane_sum;   // the summary pass runs one channel per lane (rows 16-byte aligned)
     int chunk_img;  // the chunk pass reads 32-token row images (lane_sum, bf16 inputs, L and chunk multiples of 32)

@@ -135,10 +135,19 @@ struct Span {
     }
 };
 
+// Checkpoint record of (batch b, tile, channel d), tile-major: the records of
+// consecutive channels at one tile are adjacent, so a block's checkpoint
+// stores and loads of one tile cover one contiguous run (with the rows of a
+// long sequence a power-of-two stride apart, a row-major layout sent every
+// lane's store to its own far-apart line).
+__device__ __forceinline__ int64_t ck_cell(const BwdArgs& a, int64_t b, int tile, int64_t d) {
+    return (b * ((a.L + kT - 1) / kT) + tile) * a.dim + d;
+}
+
 struct Blk {
     int64_t b, cb, g, row0;       // row0 = b dim + 64 cb
     int t0, t_end, tiles, rows;   // rows: channels of this block below dim
-    int L, TL;                    // tokens; tiles per row
+    int L;                        // tokens
 };
 
 __device__ __forceinline__ Blk blk(const BwdArgs& a) {
@@ -150,7 +159,6 @@ __device__ __forceinline__ Blk blk(const BwdArgs& a) {
     k.cb = rb - k.b * nbc;
     k.row0 = k.b * a.dim + k.cb * kCh;
     k.L = (int)a.L;
-    k.TL = (k.L + kT - 1) / kT;
     k.t0 = (int)(k.g * a.chunk);
     k.t_end = min(k.L, k.t0 + (int)a.chunk);
     k.tiles = (k.t_end - k.t0 + kT - 1) / kT;
@@ -314,10 +322,6 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
     const int tile0 = k.t0 / kT;
     const bool bc_thread = tid < kT * kSt;
     const int bj = (tid >> 4) & (kT - 1), bn = tid & 15;
-    // the block's rows of the checkpoints (at most 64 rows x 2^19 tiles x 64 bytes)
-    const Span ckz(a.ckz + k.row0 * k.TL * kSt, (uint32_t)k.rows * (uint32_t)k.TL * (kSt * 4));
-    const Span wck(a.wck + k.row0 * k.TL, (uint32_t)k.rows * (uint32_t)k.TL * 4);
-    const uint32_t ckrow = (uint32_t)c.rc * (uint32_t)k.TL;
 
     float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float W = 0.0f;
@@ -336,9 +340,9 @@ __device__ __forceinline__ void summary_body(const BwdArgs& a, SumSmem& sm) {
         }
         if (bc_thread) sm.bc[pb][bj][bn] = bc_valid(a, k, tt0) ? f32_of(r.bv) : 0.0f;
         {
-            const uint32_t ct = ckrow + (uint32_t)(tile0 + tile);
-            ckz.st4(c.ok, (ct * 4 + c.q) * 16, h);
-            wck.st(c.ok && c.q == 0, ct * 4, W);
+            const int64_t ct = ck_cell(a, k.b, tile0 + tile, k.cb * kCh);
+            Span(a.ckz + ct * kSt, (uint32_t)k.rows * (kSt * 4)).st4(c.ok, (uint32_t)(c.rc * 4 + c.q) * 16, h);
+            Span(a.wck + ct, (uint32_t)k.rows * 4).st(c.ok && c.q == 0, (uint32_t)c.rc * 4, W);
         }
         lds_barrier();
         // unconditional (the last tile re-fetches itself): no branch around the loads
@@ -526,7 +530,6 @@ __device__ __forceinline__ void body(const BwdArgs& a, uint4* lds) {
     const int t0 = (int)(g * a.chunk);
     const int t_end = min(L, t0 + (int)a.chunk);
     const int t_full = t0 + ((t_end - t0) / kTile) * kTile;
-    const int TL = (L + kT - 1) / kT;
     const int ls = rows::lane_slot(lane);
 
     float Al2[kSt];
@@ -542,18 +545,18 @@ __device__ __forceinline__ void body(const BwdArgs& a, uint4* lds) {
     const Tout* grow0 = reinterpret_cast<const Tout*>(a.dout) + row0 * a.L;
     const int64_t ro = (int64_t)rc * a.L;   // this lane's row within the block's rows
 
-    // checkpoints: the state entering tile t / kT and the sum of Delta before it
-    const Span ckz(a.ckz + row0 * TL * kSt, (uint32_t)(last + 1) * (uint32_t)TL * (kSt * 4));
-    const Span wck(a.wck + row0 * TL, (uint32_t)(last + 1) * (uint32_t)TL * 4);
     float h[kSt];
 #pragma unroll
     for (int n = 0; n < kSt; ++n) h[n] = 0.0f;
     float W = 0.0f;
+    // checkpoints: the state entering tile t / kT and the sum of Delta before
+    // it; the block's 64 records of one tile are contiguous
     auto ckpt = [&](int t) {
-        const uint32_t ct = (uint32_t)rc * (uint32_t)TL + (uint32_t)(t / kT);
+        const int64_t ct = ck_cell(a, b, t / kT, d0);
+        const Span ckz(a.ckz + ct * kSt, (uint32_t)(last + 1) * (kSt * 4));
 #pragma unroll
-        for (int q = 0; q < kSt / 4; ++q) ckz.st4(row_ok, (ct * kSt + 4 * q) * 4, &h[4 * q]);
-        wck.st(row_ok, ct * 4, W);
+        for (int q = 0; q < kSt / 4; ++q) ckz.st4(row_ok, (uint32_t)(rc * kSt + 4 * q) * 4, &h[4 * q]);
+        Span(a.wck + ct, (uint32_t)(last + 1) * 4).st(row_ok, (uint32_t)rc * 4, W);
     };
     auto fwd_token = [&](float dl, float uu, const float* Bp) {
         float dd;
@@ -827,9 +830,6 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
     const int64_t cell0 = k.row0 * G * kSt;
     const bool bc_thread = tid < kT * kSt;
     const int bj = (tid >> 4) & (kT - 1), bn = tid & 15;
-    const float* ckz = a.ckz + k.row0 * k.TL * kSt;
-    const float* wck = a.wck + k.row0 * k.TL;
-    const uint32_t ckrow = (uint32_t)c.rc * (uint32_t)k.TL;
 
     // state entering the chunk and adjoint entering it from the right
     // (c.rc is clamped in bounds: loads are unconditional, results masked)
@@ -865,9 +865,9 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
     float wc;
     auto fetch = [&](int tile) {   // c.rc is clamped in bounds
         if constexpr (!RI) fetch_raw<Tin, Tout, true, true, true, true>(a, k, p, in, k.t0 + tile * kT, r);
-        const uint32_t ct = ckrow + (uint32_t)(tile0 + tile);
-        zck = ldo(reinterpret_cast<const float4*>(ckz), ct * 4 + c.q);
-        wc = ldo(wck, ct);
+        const int64_t ct = ck_cell(a, k.b, tile0 + tile, k.cb * kCh);
+        zck = ldo(reinterpret_cast<const float4*>(a.ckz + ct * kSt), (uint32_t)c.rc * 4 + c.q);
+        wc = ldo(a.wck + ct, (uint32_t)c.rc);
     };
     // image q covers tokens t0 + 32q .. t0 + 32q + 31 (tiles 2q, 2q + 1)
     const int img_last = (int)min<int64_t>(kCh, a.dim - k.cb * kCh) - 1;
