@@ -901,8 +901,11 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
     // prefetch: the first tile then finds the same memory operations in
     // flight as every later one (prefetch, then stores), and the compiler's
     // wait for the prefetch need not cover the previous tile's stores.
+    // (With row images every tile is whole, and a producer thread's kPT
+    // tokens, consecutive and 16-byte aligned, go out as one store per tensor.)
+    constexpr int kGradSt = RI ? 1 : kPT;
 #pragma unroll
-    for (int jj = 0; jj < kPT; ++jj) {
+    for (int jj = 0; jj < kGradSt; ++jj) {
         du.st(false, 0, 0.0f);
         ddelta.st(false, 0, 0.0f);
         dz.st(false, 0, 0.0f);
@@ -1054,20 +1057,34 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
         lds_barrier();
 
         // per-channel outputs (producer mapping)
+        float gu[kPT], gd[kPT], gz[kPT];
 #pragma unroll
         for (int jj = 0; jj < kPT; ++jj) {
             const int j = p.pj + jj;
-            const int t = tt0 + j;
-            const bool ok = p.ok && t < k.t_end;
+            const bool ok = p.ok && tt0 + j < k.t_end;
             const float sLB = sm.sLB[p.pr][j], sLAq = sm.sLAq[p.pr][j], sCh = sm.sCh[p.pr][j];
             const float dt = sm.dt[p.pr][j], dy = sm.dy[p.pr][j], uu = sm.u[p.pr][j];
-            const uint32_t o = (p.off + (uint32_t)t) * 4;
-            du.st(ok, o, __builtin_fmaf(dt, sLB, p.D * dy));
-            const float dx = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd[p.pr][j];
-            ddelta.st(ok, o, dx);
-            dz.st(ok, o, __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j]);
+            gu[jj] = __builtin_fmaf(dt, sLB, p.D * dy);
+            gd[jj] = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd[p.pr][j];
+            gz[jj] = __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j];
             dD_acc += ok ? dy * uu : 0.0f;
-            dbias_acc += ok ? dx : 0.0f;
+            dbias_acc += ok ? gd[jj] : 0.0f;
+        }
+        if constexpr (RI) {
+            const uint32_t o = (p.off + (uint32_t)(tt0 + p.pj)) * 4;
+            du.st4(p.ok, o, gu);
+            ddelta.st4(p.ok, o, gd);
+            dz.st4(p.ok, o, gz);
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < kPT; ++jj) {
+                const int t = tt0 + p.pj + jj;
+                const bool ok = p.ok && t < k.t_end;
+                const uint32_t o = (p.off + (uint32_t)t) * 4;
+                du.st(ok, o, gu[jj]);
+                ddelta.st(ok, o, gd[jj]);
+                dz.st(ok, o, gz[jj]);
+            }
         }
 #pragma unroll
         for (int jh = 0; jh < kT / kRT; ++jh) {   // dB, dC partials of this channel block: thread = (token j, value v)

@@ -10,6 +10,8 @@ and at most ~1e4 accumulated roundings the error stays below ~1e-3 of the
 typical size (rms) of that gradient even where its terms cancel, and below
 1e-4 relative where they do not.  Hence |gpu - ref| <= 1e-3 rms(ref) +
 1e-4 |ref| per element."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -155,6 +157,32 @@ def test_gradients_are_reproducible_bit_for_bit(gpu):
     b = _gpu(inp, dout)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_unaligned_gradient_outputs(gpu):
+    """du, ddelta and dz 4 bytes off a 16-byte boundary (possible for callers
+    of the C ABI, not through this binding) take the chunk pass that stores
+    one value at a time; the gradients are bitwise those of aligned outputs."""
+    inp, dout = _case(2, 100, 16, 1024, torch.bfloat16, seed=13)
+    ref = _gpu(inp, dout)
+    batch, dim, L = inp["u"].shape
+
+    def shifted(shape):   # contiguous, data pointer 4 bytes past an allocation
+        return torch.zeros(int(np.prod(shape)) + 1, dtype=torch.float32, device=DEV)[1:].view(shape)
+
+    g = {k: shifted(tuple(v.shape)) if k in ("du", "ddelta", "dz") else torch.zeros_like(v) for k, v in ref.items()}
+    assert g["du"].data_ptr() % 16 == 4
+    s = ss.Shape(batch, dim, inp["A"].shape[1], L, ss._dtype_code(inp["u"]), ss._dtype_code(dout), None, 0)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    gp = lambda k: g[k].data_ptr() if k in g else None
+    ss._check(ss.lib().selscan_bwd(
+        ctypes.byref(s), ptr(inp["u"]), ptr(inp["delta"]), ptr(inp["A"]), ptr(inp["B"]), ptr(inp["C"]),
+        ptr(inp.get("D")), ptr(inp.get("z")), ptr(inp.get("delta_bias")), 1, None, ptr(dout),
+        gp("du"), gp("ddelta"), gp("dA"), gp("dB"), gp("dC"), gp("dD"), gp("dz"), gp("ddelta_bias"), None,
+        torch.cuda.current_stream(DEV).cuda_stream))
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(g[k], ref[k]), k
 
 
 def test_gradient_matches_the_forward_by_directional_derivative(gpu):
