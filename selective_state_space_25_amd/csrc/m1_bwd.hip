@@ -752,12 +752,22 @@ __global__ __launch_bounds__(256) void m1_bwd_carry_kernel(BwdArgs a) {
     }
 }
 
+// Per-channel values of a tile, [channel][token] with the token index XORed
+// by bits 1-2 of the channel.  Of 32 lanes the producer mapping touches 8
+// channels at 4 consecutive tokens each, the adjoint lanes 8 channels at one
+// token: with this layout either set falls in 32 distinct banks (a padded
+// row pitch of 17 left the producer's accesses 2-way conflicted).
+struct TileVals {
+    float v[kCh * kT];
+    __device__ __forceinline__ float& operator()(int r, int j) { return v[r * kT + (j ^ ((r >> 1) & 3))]; }
+};
+
 struct ChunkSmem {
-    float dt[kCh][kPad], dtu[kCh][kPad], dy[kCh][kPad];   // read by the adjoint lanes
-    float u[kCh][kPad], dd[kCh][kPad], zf[kCh][kPad];     // kept for the output pass
+    TileVals dt, dtu, dy;   // read by the adjoint lanes
+    TileVals u, dd, zf;     // kept for the output pass
     alignas(16) float B[kT][kSt];   // read as float4
     alignas(16) float C[kT][kSt];
-    float sLB[kCh][kPad], sLAq[kCh][kPad], sCh[kCh][kPad];
+    TileVals sLB, sLAq, sCh;
     float red[kWaves][kT][2 * kSt];                       // per wave: dB[16], dC[16] per token
 };
 
@@ -966,12 +976,12 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
                 dy = g * zz * sg;
                 zf = g * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
             }
-            sm.dt[p.pr][j] = ok ? dt : 0.0f;
-            sm.dtu[p.pr][j] = ok ? dt * uu : 0.0f;
-            sm.dy[p.pr][j] = ok ? dy : 0.0f;
-            sm.u[p.pr][j] = uu;
-            sm.dd[p.pr][j] = dd;
-            sm.zf[p.pr][j] = zf;
+            sm.dt(p.pr, j) = ok ? dt : 0.0f;
+            sm.dtu(p.pr, j) = ok ? dt * uu : 0.0f;
+            sm.dy(p.pr, j) = ok ? dy : 0.0f;
+            sm.u(p.pr, j) = uu;
+            sm.dd(p.pr, j) = dd;
+            sm.zf(p.pr, j) = zf;
         }
         if (bc_thread) {
             const bool ok = bc_valid(a, k, tt0);
@@ -1008,7 +1018,7 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
             float h[4] = {ck[0], ck[1], ck[2], ck[3]};
 #pragma unroll
             for (int j = 0; j < kT; ++j) {
-                const float dt = sm.dt[c.r][j], dtu = sm.dtu[c.r][j];
+                const float dt = sm.dt(c.r, j), dtu = sm.dtu(c.r, j);
                 const float4 Bv = *reinterpret_cast<const float4*>(&sm.B[j][4 * c.q]);
                 const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
                 decay4<ST>(c, dt, as[j]);
@@ -1022,7 +1032,7 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
         // adjoint back through the tile
 #pragma unroll
         for (int j = kT - 1; j >= 0; --j) {
-            const float dt = sm.dt[c.r][j], dtu = sm.dtu[c.r][j], dy = sm.dy[c.r][j];
+            const float dt = sm.dt(c.r, j), dtu = sm.dtu(c.r, j), dy = sm.dy(c.r, j);
             const float4 Bv = *reinterpret_cast<const float4*>(&sm.B[j][4 * c.q]);
             const float4 Cv = *reinterpret_cast<const float4*>(&sm.C[j][4 * c.q]);
             const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
@@ -1047,9 +1057,9 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
             sLAq = sum_q(sLAq);
             sCh = sum_q(sCh);
             if (c.q == 0) {
-                sm.sLB[c.r][j] = sLB;
-                sm.sLAq[c.r][j] = sLAq;
-                sm.sCh[c.r][j] = sCh;
+                sm.sLB(c.r, j) = sLB;
+                sm.sLAq(c.r, j) = sLAq;
+                sm.sCh(c.r, j) = sCh;
             }
             const float s = reduce_bc(v, c.rr);
             if (writer) sm.red[c.w][j][vidx] = s;
@@ -1062,11 +1072,11 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
         for (int jj = 0; jj < kPT; ++jj) {
             const int j = p.pj + jj;
             const bool ok = p.ok && tt0 + j < k.t_end;
-            const float sLB = sm.sLB[p.pr][j], sLAq = sm.sLAq[p.pr][j], sCh = sm.sCh[p.pr][j];
-            const float dt = sm.dt[p.pr][j], dy = sm.dy[p.pr][j], uu = sm.u[p.pr][j];
+            const float sLB = sm.sLB(p.pr, j), sLAq = sm.sLAq(p.pr, j), sCh = sm.sCh(p.pr, j);
+            const float dt = sm.dt(p.pr, j), dy = sm.dy(p.pr, j), uu = sm.u(p.pr, j);
             gu[jj] = __builtin_fmaf(dt, sLB, p.D * dy);
-            gd[jj] = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd[p.pr][j];
-            gz[jj] = __builtin_fmaf(p.D, uu, sCh) * sm.zf[p.pr][j];
+            gd[jj] = __builtin_fmaf(uu, sLB, sLAq * kLn2) * sm.dd(p.pr, j);
+            gz[jj] = __builtin_fmaf(p.D, uu, sCh) * sm.zf(p.pr, j);
             dD_acc += ok ? dy * uu : 0.0f;
             dbias_acc += ok ? gd[jj] : 0.0f;
         }
