@@ -772,31 +772,28 @@ struct ChunkSmem {
 };
 
 // One lane's 8 values (dB of states 4q..4q+3, then dC) summed over the wave's
-// 16 channels.  Returns the lane's share: value k = 2 rr + (lane >= 32), i.e.
-// kind k >> 2 (0 = dB, 1 = dC) of state 4q + (k & 3); every value is held by
-// two lanes, one in DPP row 0 or 2 and one in DPP row 1 or 3.
-__device__ __forceinline__ float reduce_bc(const float* v, int rr) {
-    const bool hi2 = rr & 2, hi1 = rr & 1;
-    float u4[4];
+// 16 channels (lane bits 0, 1: rr; bits 4, 5: the DPP row), scattered as
+// they are summed: the half swap (bit 5) leaves dB in lanes 0..31 and dC in
+// lanes 32..63, the row swap (bit 4) keeps states 4q + 2 b4 + {0, 1}, the
+// quad exchange (bit 1) one of them, and bit 0 is summed last.  Returns kind
+// b5 (0 = dB, 1 = dC) of state 4q + 2 b4 + b1, held by lanes l and l ^ 1.
+// The swaps exchange values without a select per value: 16 instructions.
+__device__ __forceinline__ float reduce_bc(const float* v, bool b1) {
+    float u[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const float keep = hi2 ? v[m + 4] : v[m];
-        const float send = hi2 ? v[m] : v[m + 4];
-        u4[m] = keep + dpp<kQuadX2>(send);          // channels rr, rr ^ 2
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 4]), false, false);
+        u[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
     }
-    float w2[2];
+    float w[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        const float keep = hi1 ? u4[m + 2] : u4[m];
-        const float send = hi1 ? u4[m] : u4[m + 2];
-        w2[m] = keep + dpp<kQuadX1>(send);          // channels rr, rr ^ 1
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[m]), __float_as_uint(u[m + 2]), false, false);
+        w[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
     }
-    // lanes 0..31 take w2[0] summed with lanes 32..63, lanes 32..63 take w2[1]
-    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(w2[0]), __float_as_uint(w2[1]), false, false);
-    const float x = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-    // DPP rows 0 + 1 and 2 + 3
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const float keep = b1 ? w[1] : w[0], send = b1 ? w[0] : w[1];
+    const float x = keep + dpp<kQuadX2>(send);
+    return x + dpp<kQuadX1>(x);
 }
 
 // Row images for the chunk pass (bf16 inputs, rows on 16-byte boundaries,
@@ -865,9 +862,9 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
     float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float dD_acc = 0.0f, dbias_acc = 0.0f;
     // identity of this lane's dB/dC share
-    const int kk = 2 * c.rr + (c.l >= 32 ? 1 : 0);
-    const int vidx = (kk >> 2) * kSt + 4 * c.q + (kk & 3);
-    const bool writer = (c.l & 16) == 0;
+    const bool b1 = (c.l >> 1) & 1;
+    const int vidx = (c.l >> 5) * kSt + 4 * c.q + 2 * ((c.l >> 4) & 1) + (int)b1;
+    const bool writer = (c.l & 1) == 0;
 
     // prefetched inputs of the next tile (processed from the last)
     Raw<Tin, Tout> r;
@@ -1061,7 +1058,7 @@ __device__ __forceinline__ void chunk_body(const BwdArgs& a, ChunkSmem& sm, ImgS
                 sm.sLAq(c.r, j) = sLAq;
                 sm.sCh(c.r, j) = sCh;
             }
-            const float s = reduce_bc(v, c.rr);
+            const float s = reduce_bc(v, b1);
             if (writer) sm.red[c.w][j][vidx] = s;
         }
         lds_barrier();
