@@ -56,6 +56,8 @@ def _load():
             lib.oracle_m2_f64.restype = ctypes.c_int
             lib.oracle_m1_bwd_f64.argtypes = [i64] * 4 + [dp] * 8 + [ctypes.c_int] + [dp] * 11
             lib.oracle_m1_bwd_f64.restype = ctypes.c_int
+            lib.oracle_m2_bwd_f64.argtypes = [i64] * 6 + [dp] * 8 + [ctypes.c_int] + [dp] * 11
+            lib.oracle_m2_bwd_f64.restype = ctypes.c_int
             lib.oracle_conv1d_f64.argtypes = [i64] * 4 + [dp] * 3 + [ctypes.c_int, dp]
             lib.oracle_conv1d_f64.restype = ctypes.c_int
             lib.oracle_version.restype = ctypes.c_char_p
@@ -176,6 +178,37 @@ def m1_bwd(u, delta, A, B, C, D, z, delta_bias, dout, softplus=True, h0=None):
                                    _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]))
     if rc != 0:
         raise RuntimeError(f"oracle_m1_bwd_f64 failed with status {rc}")
+    return g
+
+
+def m2_bwd(x, dt, A, B, C, D, z, dt_bias, dout, softplus=True, h0=None):
+    """Gradients of the Mamba-2 scan output (gated by silu(z)) in fp64 from
+    the initial state h0 [batch, nheads, headdim, N] (None = zero).  Returns a
+    dict: dx, dz [batch, L, nheads, headdim]; ddt [batch, L, nheads]; dA, dD,
+    ddt_bias [nheads]; dB, dC [batch, L, ngroups, N]; dh0 [batch, nheads,
+    headdim, N]."""
+    x = _f64(x)
+    nb, nl, nh, np_ = x.shape
+    B = _f64(B)
+    ng, nn = B.shape[2], B.shape[3]
+    dt = _f64(dt, (nb, nl, nh))
+    A = _f64(A, (nh,))
+    C = _f64(C, (nb, nl, ng, nn))
+    D = _f64(D, (nh,))
+    z = _f64(z, (nb, nl, nh, np_))
+    dt_bias = _f64(dt_bias, (nh,))
+    h0 = _f64(h0, (nb, nh, np_, nn))
+    dout = _f64(dout, (nb, nl, nh, np_))
+    g = {k: np.empty(s, np.float64) for k, s in (("dx", (nb, nl, nh, np_)), ("ddt", (nb, nl, nh)), ("dA", (nh,)),
+                                                  ("dB", (nb, nl, ng, nn)), ("dC", (nb, nl, ng, nn)), ("dD", (nh,)),
+                                                  ("dz", (nb, nl, nh, np_)), ("ddt_bias", (nh,)),
+                                                  ("dh0", (nb, nh, np_, nn)))}
+    rc = _load().oracle_m2_bwd_f64(nb, nl, nh, np_, ng, nn, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(z), _ptr(dt_bias), int(bool(softplus)), _ptr(h0), _ptr(dout),
+                                   _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                   _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]), _ptr(g["dh0"]))
+    if rc != 0:
+        raise RuntimeError(f"oracle_m2_bwd_f64 failed with status {rc}")
     return g
 
 

@@ -313,3 +313,109 @@ int oracle_m1_bwd_f64(int64_t nb, int64_t nd, int64_t nn, int64_t nl, const doub
     free(h); free(lam); free(dl);
     return ORACLE_OK;
 }
+
+/*
+ * Gradients of the Mamba-2 (multi-head) scan (reverse-mode, fp64).  The
+ * forward is oracle_m2_f64: per (batch b, head hh, channel p), with the
+ * group g = hh / (nh / ng) of the head,
+ *   Delta_t = sp(dt[b,t,hh] + dtb[hh]),  a_t = exp(Delta_t A[hh]),
+ *   h_t[n]  = a_t h_{t-1}[n] + Delta_t B[b,t,g,n] x[b,t,hh,p],
+ *   out_t   = (sum_n C[b,t,g,n] h_t[n] + D[hh] x[b,t,hh,p]) * silu(z[b,t,hh,p]),
+ * i.e. the Mamba-1 recurrence with one scalar decay per (token, head) and B,
+ * C shared by the heads of a group (README section "Mamba-2"; skill page
+ * "model-architecture-mamba").  Given dout = d loss / d out, the adjoint of
+ * the state runs backward in time exactly as for Mamba-1,
+ *   lam_t[n] = dy_t C_t[n] + a_{t+1} lam_{t+1}[n],
+ * and the gradients that the Mamba-2 sharing ties together are sums: ddt
+ * over the channels p of the head, dA, dD, ddt_bias over everything but the
+ * head, dB and dC over the heads of the group and their channels.
+ * Outputs (all written, fp64): dx, dz [nb,nl,nh,np]; ddt [nb,nl,nh];
+ * dA, dD, ddtb [nh]; dB, dC [nb,nl,ng,nn]; dh0 [nb,nh,np,nn] when non-NULL
+ * (dh0 = a_0 lam_0).  z, D, dtb, h0 may be NULL.  Units run one after
+ * another, so every sum is a plain sequential sum.
+ */
+int oracle_m2_bwd_f64(int64_t nb, int64_t nl, int64_t nh, int64_t np, int64_t ng, int64_t nn,
+                      const double* x, const double* dt, const double* A, const double* Bm, const double* Cm,
+                      const double* Dv, const double* z, const double* dtb, int softplus, const double* h0,
+                      const double* dout, double* dx, double* ddt, double* dA, double* dBm, double* dCm,
+                      double* dD, double* dz, double* ddtb, double* dh0) {
+    if (nb < 1 || nl < 1 || nh < 1 || np < 1 || ng < 1 || nn < 1 || nh % ng != 0) return ORACLE_BAD_ARG;
+    if (!x || !dt || !A || !Bm || !Cm || !dout || !dx || !ddt || !dA || !dBm || !dCm || !dD || !dz || !ddtb)
+        return ORACLE_BAD_ARG;
+    double* h = (double*)malloc(sizeof(double) * (size_t)(nl + 1) * (size_t)nn);   /* h_{-1} .. h_{L-1} */
+    double* lam = (double*)malloc(sizeof(double) * (size_t)nn);
+    double* dl = (double*)malloc(sizeof(double) * (size_t)nl);
+    if (!h || !lam || !dl) {
+        free(h); free(lam); free(dl);
+        return ORACLE_NO_MEM;
+    }
+    const int64_t hpg = nh / ng;
+    for (int64_t i = 0; i < nh; ++i) { dA[i] = 0.0; dD[i] = 0.0; ddtb[i] = 0.0; }
+    for (int64_t i = 0; i < nb * nl * nh; ++i) ddt[i] = 0.0;
+    for (int64_t i = 0; i < nb * nl * ng * nn; ++i) { dBm[i] = 0.0; dCm[i] = 0.0; }
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t hh = 0; hh < nh; ++hh) {
+            const int64_t g = hh / hpg;
+            for (int64_t t = 0; t < nl; ++t) {
+                const double v = dt[(b * nl + t) * nh + hh] + (dtb ? dtb[hh] : 0.0);
+                dl[t] = softplus ? sp64(v) : v;
+            }
+            for (int64_t p = 0; p < np; ++p) {
+                const int64_t unit = (b * nh + hh) * np + p;
+                /* forward, keeping every state */
+                for (int64_t n = 0; n < nn; ++n) h[n] = h0 ? h0[unit * nn + n] : 0.0;
+                for (int64_t t = 0; t < nl; ++t) {
+                    const double a = exp(dl[t] * A[hh]);
+                    const double xt = x[((b * nl + t) * nh + hh) * np + p];
+                    const double* Bt = Bm + ((b * nl + t) * ng + g) * nn;
+                    for (int64_t n = 0; n < nn; ++n) h[(t + 1) * nn + n] = a * h[t * nn + n] + dl[t] * Bt[n] * xt;
+                }
+                /* backward */
+                for (int64_t n = 0; n < nn; ++n) lam[n] = 0.0;
+                for (int64_t t = nl - 1; t >= 0; --t) {
+                    const int64_t e = ((b * nl + t) * nh + hh) * np + p;
+                    const double xt = x[e];
+                    const double* Bt = Bm + ((b * nl + t) * ng + g) * nn;
+                    const double* Ct = Cm + ((b * nl + t) * ng + g) * nn;
+                    double* dBt = dBm + ((b * nl + t) * ng + g) * nn;
+                    double* dCt = dCm + ((b * nl + t) * ng + g) * nn;
+                    double y = Dv ? Dv[hh] * xt : 0.0;
+                    for (int64_t n = 0; n < nn; ++n) y += Ct[n] * h[(t + 1) * nn + n];
+                    double dy = dout[e];
+                    if (z) {
+                        const double zz = z[e];
+                        const double sg = 1.0 / (1.0 + exp(-zz));
+                        dz[e] = dout[e] * y * sg * (1.0 + zz * (1.0 - sg));
+                        dy = dout[e] * zz * sg;
+                    } else {
+                        dz[e] = 0.0;
+                    }
+                    double dxt = Dv ? dy * Dv[hh] : 0.0;
+                    if (Dv) dD[hh] += dy * xt;
+                    const double a = exp(dl[t] * A[hh]);
+                    double ddl = 0.0;
+                    for (int64_t n = 0; n < nn; ++n) {
+                        /* lam_t = dy C_t + a_{t+1} lam_{t+1}; lam[] holds a_{t+1} lam_{t+1} */
+                        const double l = dy * Ct[n] + lam[n];
+                        const double hp = h[t * nn + n];
+                        dCt[n] += dy * h[(t + 1) * nn + n];
+                        dBt[n] += l * dl[t] * xt;
+                        dxt += l * dl[t] * Bt[n];
+                        ddl += l * (Bt[n] * xt + A[hh] * a * hp);
+                        dA[hh] += l * dl[t] * a * hp;
+                        lam[n] = a * l;   /* a_t lam_t, carried to token t-1 */
+                    }
+                    dx[e] = dxt;
+                    const double v = dt[(b * nl + t) * nh + hh] + (dtb ? dtb[hh] : 0.0);
+                    const double dv = softplus ? ddl / (1.0 + exp(-v)) : ddl;   /* sp'(v) = sigmoid(v) */
+                    ddt[(b * nl + t) * nh + hh] += dv;
+                    if (dtb) ddtb[hh] += dv;
+                }
+                if (dh0)
+                    for (int64_t n = 0; n < nn; ++n) dh0[unit * nn + n] = lam[n];
+            }
+        }
+    }
+    free(h); free(lam); free(dl);
+    return ORACLE_OK;
+}

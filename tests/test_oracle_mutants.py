@@ -40,6 +40,11 @@ MUTANTS = {
                               "dCm[(b * nn + n) * nl + t] += dy * h[t * nn + n];"),
     "bwd_h0_ignored": ("/* forward, keeping every state */\n            for (int64_t n = 0; n < nn; ++n) h[n] = h0 ? h0[row * nn + n] : 0.0;",
                        "/* forward, keeping every state */\n            for (int64_t n = 0; n < nn; ++n) h[n] = 0.0;"),
+    "m2_bwd_db_one_head": ("dBt[n] += l * dl[t] * xt;", "if (hh % hpg == 0) dBt[n] += l * dl[t] * xt;"),
+    "m2_bwd_ddt_last_channel": ("ddt[(b * nl + t) * nh + hh] += dv;", "ddt[(b * nl + t) * nh + hh] = dv;"),
+    "m2_bwd_adjoint_undecayed": ("lam[n] = a * l;   /* a_t lam_t, carried to token t-1 */\n                    }\n                    dx[e] = dxt;",
+                                 "lam[n] = l;   /* a_t lam_t, carried to token t-1 */\n                    }\n                    dx[e] = dxt;"),
+    "m2_bwd_da_no_delta": ("dA[hh] += l * dl[t] * a * hp;", "dA[hh] += l * a * hp;"),
     "conv_kernel_reversed": ("if (s >= 0) acc += w[d * nk + k] * xr[s];", "if (s >= 0) acc += w[d * nk + (nk - 1 - k)] * xr[s];"),
     "conv_offset": ("const int64_t s = t - (nk - 1) + k;", "const int64_t s = t - nk + k;"),
 }

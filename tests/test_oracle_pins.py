@@ -552,3 +552,87 @@ def test_backward_matches_finite_differences(softplus, gate_skip_bias):
         np.testing.assert_allclose(g[gname], fd, rtol=2e-6, atol=2e-7, err_msg=gname)
     if not gate_skip_bias:
         assert np.all(g["dD"] == 0) and np.all(g["dz"] == 0) and np.all(g["ddelta_bias"] == 0)
+
+
+# ---- gradients of the Mamba-2 scan ----------------------------------------
+# oracle_m2_bwd_f64 is pinned the same way, to central finite differences of
+# the (pinned) Mamba-2 forward oracle.  Two groups of two heads make every
+# sum that Mamba-2's sharing implies visible: ddt over a head's channels,
+# dA/dD/ddt_bias over batches, tokens and channels, dB/dC over the heads of
+# a group and their channels (a sum over the wrong heads, or one head only,
+# moves dB and dC away from the differences).
+
+def _loss_m2(inp, dout, softplus):
+    y, _ = oracle.m2(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["dt_bias"],
+                     softplus=softplus, h0=inp["h0"])
+    return float(np.sum(y * dout))
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("gate_skip_bias", [True, False])
+def test_m2_backward_matches_finite_differences(softplus, gate_skip_bias):
+    rng = np.random.default_rng(41 + int(softplus) + 2 * int(gate_skip_bias))
+    nb, nl, nh, npd, ng, nn = 2, 6, 4, 2, 2, 3
+    inp = {
+        "x": rng.standard_normal((nb, nl, nh, npd)),
+        "dt": rng.standard_normal((nb, nl, nh)) * 0.5 + (0.0 if softplus else 1.0),
+        "A": -rng.uniform(0.2, 2.0, nh),
+        "B": rng.standard_normal((nb, nl, ng, nn)),
+        "C": rng.standard_normal((nb, nl, ng, nn)),
+        "D": rng.standard_normal(nh) if gate_skip_bias else None,
+        "z": rng.standard_normal((nb, nl, nh, npd)) if gate_skip_bias else None,
+        "dt_bias": rng.standard_normal(nh) * 0.3 if gate_skip_bias else None,
+        "h0": rng.standard_normal((nb, nh, npd, nn)) if gate_skip_bias else None,
+    }
+    dout = rng.standard_normal((nb, nl, nh, npd))
+    g = oracle.m2_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["dt_bias"], dout,
+                      softplus=softplus, h0=inp["h0"])
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "dt_bias": "ddt_bias",
+             "h0": "dh0"}
+    eps = 1e-6
+    for name, gname in names.items():
+        if inp[name] is None:
+            continue
+        fd = np.zeros_like(inp[name])
+        for idx in np.ndindex(*inp[name].shape):
+            plus = {k: (None if v is None else v.copy()) for k, v in inp.items()}
+            minus = {k: (None if v is None else v.copy()) for k, v in inp.items()}
+            plus[name][idx] += eps
+            minus[name][idx] -= eps
+            fd[idx] = (_loss_m2(plus, dout, softplus) - _loss_m2(minus, dout, softplus)) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=2e-6, atol=2e-7, err_msg=gname)
+    if not gate_skip_bias:
+        assert np.all(g["dD"] == 0) and np.all(g["dz"] == 0) and np.all(g["ddt_bias"] == 0)
+
+
+def test_m2_backward_equals_broadcast_m1_backward():
+    """One head per group and headdim channels that are Mamba-1 channels with
+    A[d, n] = A[head] and delta[d, t] = dt[t, head]: the Mamba-2 gradients are
+    the Mamba-1 ones, summed over a head's channels for dt, A, D and bias."""
+    rng = np.random.default_rng(7)
+    nb, nl, nh, npd, nn = 1, 5, 2, 3, 4
+    x = rng.standard_normal((nb, nl, nh, npd))
+    dt = rng.standard_normal((nb, nl, nh)) * 0.5
+    A = -rng.uniform(0.2, 2.0, nh)
+    B = rng.standard_normal((nb, nl, nh, nn))
+    C = rng.standard_normal((nb, nl, nh, nn))
+    D = rng.standard_normal(nh)
+    z = rng.standard_normal((nb, nl, nh, npd))
+    bias = rng.standard_normal(nh) * 0.3
+    dout = rng.standard_normal((nb, nl, nh, npd))
+    g2 = oracle.m2_bwd(x, dt, A, B, C, D, z, bias, dout)
+    for hh in range(nh):
+        u1 = np.transpose(x[:, :, hh, :], (0, 2, 1))                        # [nb, P, L]
+        d1 = np.repeat(np.transpose(dt[:, :, hh:hh + 1], (0, 2, 1)), npd, axis=1)
+        g1 = oracle.m1_bwd(u1, d1, np.full((npd, nn), A[hh]), np.transpose(B[:, :, hh, :], (0, 2, 1)),
+                           np.transpose(C[:, :, hh, :], (0, 2, 1)), np.full(npd, D[hh]),
+                           np.transpose(z[:, :, hh, :], (0, 2, 1)), np.full(npd, bias[hh]),
+                           np.transpose(dout[:, :, hh, :], (0, 2, 1)))
+        np.testing.assert_allclose(g2["dx"][:, :, hh, :], np.transpose(g1["du"], (0, 2, 1)), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2["dz"][:, :, hh, :], np.transpose(g1["dz"], (0, 2, 1)), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2["ddt"][:, :, hh], g1["ddelta"].sum(axis=1), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2["dA"][hh], g1["dA"].sum(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2["dD"][hh], g1["dD"].sum(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2["ddt_bias"][hh], g1["ddelta_bias"].sum(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2["dB"][:, :, hh, :], np.transpose(g1["dB"], (0, 2, 1)), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g2["dC"][:, :, hh, :], np.transpose(g1["dC"], (0, 2, 1)), rtol=1e-12, atol=1e-13)
