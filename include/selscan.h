@@ -257,6 +257,50 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* shape,
                                        const void* z, const float* dt_bias, int softplus,
                                        const float* h0, void* y, float* last_state, void* stream);
 
+/* Bytes of workspace selscan_mamba2_bwd needs for `shape` (0 on a bad
+ * shape): per (batch, head) the state entering every 8-token tile
+ * (64 x N fp32 each) and the head's share of dB and dC (2 x L x N fp32). */
+size_t selscan_mamba2_bwd_workspace_bytes(const selscan_m2_shape_t* shape);
+
+/*
+ * Gradients of the Mamba-2 scan (training; reverse mode through the
+ * multi-head recurrence of the README's "Mamba-2" section: one scalar decay
+ * per token and head, B and C shared by the heads of a group).  For
+ * out = selscan_mamba2_fwd_h0(...) and dout = d loss / d out, writes the
+ * gradient of the loss with respect to every input; the states are
+ * recomputed from the inputs (the recurrence in fp32, states entering every
+ * 8-token tile kept in the workspace).
+ *   x .. softplus, h0   as for selscan_mamba2_fwd_h0 (h0 NULL = zero state)
+ *   dout        [B, L, H, P]  out_dtype   gradient of the output
+ *   dx          [B, L, H, P]  fp32        (written)
+ *   ddt         [B, L, H]     fp32        (written; with respect to dt itself,
+ *                                         before bias and softplus)
+ *   dA          [H]           fp32        (written)
+ *   dB, dC      [B, L, G, N]  fp32        (written; summed over the heads of
+ *                                         each group and their channels)
+ *   dD          [H]           fp32        (written; NULL = skip; 0 when D is NULL)
+ *   dz          [B, L, H, P]  fp32        (written; required when z is given,
+ *                                         ignored otherwise)
+ *   ddt_bias    [H]           fp32        (written; NULL = skip; 0 when dt_bias
+ *                                         is NULL)
+ *   dh0         [B, H, P, N]  fp32        (written; NULL = skip)
+ * headdim P = 64 only (SELSCAN_ERR_UNSUPPORTED otherwise); N in
+ * {16, 32, 64, 128}.  Gradients must not alias inputs or each other.  Sums
+ * over heads, channels, batches and time run in a fixed order: results are
+ * reproducible bit for bit.  shape->workspace as for selscan_mamba2_fwd,
+ * sized by selscan_mamba2_bwd_workspace_bytes.  Errors as for
+ * selscan_mamba2_fwd, plus SELSCAN_ERR_INVALID_ARG for a NULL required
+ * gradient.
+ */
+selscan_status_t selscan_mamba2_bwd(const selscan_m2_shape_t* shape,
+                                    const void* x, const void* dt, const float* A,
+                                    const void* B, const void* C, const float* D,
+                                    const void* z, const float* dt_bias, int softplus,
+                                    const float* h0, const void* dout,
+                                    float* dx, float* ddt, float* dA, float* dB, float* dC,
+                                    float* dD, float* dz, float* ddt_bias, float* dh0,
+                                    void* stream);
+
 /*
  * Mamba-2 one-token update.  shape: batch, nheads H, headdim P, ngroups G,
  * dstate N in {16, 32, 64, 128}, dtypes; seqlen and workspace ignored.

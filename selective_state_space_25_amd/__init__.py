@@ -49,6 +49,7 @@ _lib = None
 EXPORTED = ("selscan_fwd", "selscan_mamba2_fwd", "selscan_workspace_bytes", "selscan_mamba2_workspace_bytes",
             "selscan_fwd_h0", "selscan_mamba2_fwd_h0", "selscan_step", "selscan_mamba2_step", "selscan_conv1d",
             "selscan_bwd", "selscan_bwd_workspace_bytes", "selscan_fwd_noalloc",
+            "selscan_mamba2_bwd", "selscan_mamba2_bwd_workspace_bytes",
             "selscan_last_error", "selscan_version", "selscan_timing_enable", "selscan_timing_collect")
 
 
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
         L.selscan_conv1d.restype = i32
         L.selscan_bwd.argtypes = [ctypes.POINTER(Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp] + [fp] * 9 + [vp]
         L.selscan_bwd.restype = i32
+        L.selscan_mamba2_bwd.argtypes = [ctypes.POINTER(M2Shape), vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp] + \
+            [fp] * 9 + [vp]
+        L.selscan_mamba2_bwd.restype = i32
+        L.selscan_mamba2_bwd_workspace_bytes.argtypes = [ctypes.POINTER(M2Shape)]
+        L.selscan_mamba2_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
         L.selscan_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.selscan_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
@@ -410,6 +416,58 @@ def mamba2_step(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus=Tr
         _ptr(z, "z", (batch, H, P), dtp, dev), _ptr(dt_bias, "dt_bias", (H,), torch.float32, dev),
         int(bool(softplus)), _ptr(out, "out", (batch, H, P), odt, dev), _stream_handle(dev)))
     return out
+
+
+def mamba2_bwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dout=None, softplus=True, h0=None,
+               want_dh0=False, workspace=None):
+    """Gradients of the Mamba-2 scan on the GPU (headdim 64).
+
+    Inputs as for mamba2_fwd; dout [batch, L, nheads, headdim] (float32 or
+    bfloat16) is the gradient of the loss with respect to y.  Returns a dict
+    of float32 tensors: dx, dz (when z is given) [batch, L, nheads, headdim];
+    ddt [batch, L, nheads]; dA [nheads]; dB, dC [batch, L, ngroups, N]; dD
+    (when D is given) and ddt_bias (when dt_bias is given) [nheads]; dh0
+    [batch, nheads, headdim, N] (when h0 is given or want_dh0).
+    """
+    torch = _torch()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("selscan.mamba2_bwd needs tensors on a GPU device")
+    if dout is None:
+        raise ValueError("dout is required")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dt_ = x.dtype
+    f32 = torch.float32
+    new = lambda *shape: torch.empty(shape, dtype=f32, device=dev)
+    g = {"dx": new(batch, L, H, P), "ddt": new(batch, L, H), "dA": new(H), "dB": new(batch, L, G, N),
+         "dC": new(batch, L, G, N)}
+    if z is not None:
+        g["dz"] = new(batch, L, H, P)
+    if D is not None:
+        g["dD"] = new(H)
+    if dt_bias is not None:
+        g["ddt_bias"] = new(H)
+    if h0 is not None or want_dh0:
+        g["dh0"] = new(batch, H, P, N)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    s = M2Shape(batch, L, H, P, G, N, _dtype_code(x), _dtype_code(dout), ws_ptr, ws_bytes)
+    gp = lambda k: g[k].data_ptr() if k in g else None
+    _check(lib().selscan_mamba2_bwd(
+        ctypes.byref(s), _ptr(x, "x", (batch, L, H, P), dt_, dev), _ptr(dt, "dt", (batch, L, H), dt_, dev),
+        _ptr(A, "A", (H,), f32, dev), _ptr(B, "B", (batch, L, G, N), dt_, dev), _ptr(C, "C", (batch, L, G, N), dt_, dev),
+        _ptr(D, "D", (H,), f32, dev), _ptr(z, "z", (batch, L, H, P), dt_, dev),
+        _ptr(dt_bias, "dt_bias", (H,), f32, dev), int(bool(softplus)),
+        _ptr(h0, "h0", (batch, H, P, N), f32, dev), _ptr(dout, "dout", (batch, L, H, P), None, dev),
+        gp("dx"), gp("ddt"), gp("dA"), gp("dB"), gp("dC"), gp("dD"), gp("dz"), gp("ddt_bias"), gp("dh0"),
+        _stream_handle(dev)))
+    return g
+
+
+def mamba2_bwd_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype=BF16, out_dtype=None) -> int:
+    s = M2Shape(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype, in_dtype if out_dtype is None else out_dtype,
+                None, 0)
+    return int(lib().selscan_mamba2_bwd_workspace_bytes(ctypes.byref(s)))
 
 
 def mamba2_workspace_bytes(batch, seqlen, nheads, headdim, ngroups, dstate, in_dtype=BF16, out_dtype=None) -> int:

@@ -27,7 +27,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libselscan.so")
 ABI_BENCH = os.path.join(HERE, "abi_bench")   # host cost of the decode entry points, timed from C++
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["selscan.cpp", "timing.cpp", "m1_scan.hip", "m2_scan.hip", "m2_ssd.hip", "step.hip", "conv1d.hip", "m1_bwd.hip", "noalloc.hip"]
+SOURCES = ["selscan.cpp", "timing.cpp", "m1_scan.hip", "m2_scan.hip", "m2_ssd.hip", "step.hip", "conv1d.hip", "m1_bwd.hip", "m2_bwd.hip", "noalloc.hip"]
 ARCH = os.environ.get("SELSCAN_ARCH", "gfx950")
 
 

@@ -127,6 +127,32 @@ struct M2Args {
 
 int m2_waves_per_block(int64_t N);
 
+// Mamba-2 gradients (recurrent form, headdim 64).  Tensors as in selscan.h;
+// ck, pB, pC, pA, pD, pbias point into the workspace (m2_bwd_carve).
+struct M2BwdArgs {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* dt_bias;
+    const float* h0;
+    const void* dout;
+    float *dx, *ddt, *dA, *dB, *dC, *dD, *dz, *ddt_bias, *dh0;
+    float* ck;        // [batch*H, tiles, N/16, 64, 16] states entering each 8-token tile
+    float* pB;        // [batch*H, L, N] per-head dB
+    float* pC;        // [batch*H, L, N] per-head dC
+    float *pA, *pD, *pbias;   // [batch*H] per-(batch, head) sums
+    int64_t batch, L, H, G, N;
+    int softplus;
+    int in_bf16;
+};
+size_t m2_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t N);
+void m2_bwd_carve(M2BwdArgs& a, void* ws);
+hipError_t launch_m2_bwd(const M2BwdArgs& a, int in_bf16, int out_bf16, hipStream_t stream);
+
 // One-token state update (decoding), both variants.  Mamba-1: u, delta, z, y
 // [batch, dim]; B, C [batch, N]; A [dim, N]; D, bias [dim]; state
 // [batch, dim, N].  Mamba-2: u = x, z, y [batch, H, P]; delta = dt

@@ -1,0 +1,498 @@
+// m2_bwd.hip -- gradients of the Mamba-2 (multi-head) selective scan, gfx950.
+//
+// The forward is the Mamba-2 layer of the Mamba README (section "Mamba-2";
+// skill page "model-architecture-mamba": heads, headdim, d_state, groups):
+// per (batch b, head h, channel p) the Mamba-1 recurrence of section 2.2 of
+// the "Understanding Mamba and Selective State Space Models (SSMs)" blog
+// with one scalar decay per (token, head) and B, C shared by the heads of a
+// group g = h / (H / G):
+//
+//   Delta_t = softplus(dt_t + bias_h),  a_t = exp(Delta_t A_h)
+//   h_t[n]  = a_t h_{t-1}[n] + Delta_t x_t[p] B_t[n]
+//   out_t   = (sum_n C_t[n] h_t[n] + D_h x_t[p]) silu(z_t[p])
+//
+// Reverse mode, with dy_t = dout_t silu(z_t) and the state's adjoint
+// lam_t[n] = dy_t C_t[n] + a_{t+1} lam_{t+1}[n] running backward in time:
+//
+//   dx_t[p]   = Delta_t sum_n lam_t[n] B_t[n] + D_h dy_t
+//   dDelta_t  = sum_{p,n} lam_t (x_t B_t + A_h a_t h_{t-1})
+//   dA_h      = sum_t Delta_t a_t sum_{p,n} lam_t h_{t-1}
+//   dB_t[n]   = sum_{h in g, p} lam_t[n] Delta_t x_t[p]
+//   dC_t[n]   = sum_{h in g, p} dy_t[p] h_t[n]
+//   dz_t      = dout_t y_t silu'(z_t),  dD_h = sum dy x,  dh0 = a_0 lam_0
+//
+// Work layout: one workgroup per (batch, head), N / 16 waves; wave w holds
+// states n = 16 w .. 16 w + 15 of all 64 channels, lane = channel p.
+//  - checkpoint pass: the forward recurrence, storing every 8th state (the
+//    state entering each 8-token tile) to the workspace;
+//  - adjoint pass: tiles from the last, each recomputing its 8 tokens'
+//    states from the tile's checkpoint into registers, then running the
+//    adjoint back through them.  Sums over n (dx, dDelta) go over the 16
+//    states in a lane and the waves through LDS; sums over p (dB, dC) are
+//    reduced across the lanes with permlane swaps and DPP row sums and
+//    stored per head;
+//  - reduce: dB, dC over the heads of a group, dA, dD, dbias over batches,
+//    in a fixed order (results are reproducible bit for bit).
+#include "device_math.hpp"
+#include "kernels.hpp"
+
+namespace selscan {
+
+namespace {
+
+constexpr int kT2 = 8;   // tokens per tile (and per checkpoint)
+constexpr int kP = 64;   // headdim = lanes
+
+template <typename T> __device__ __forceinline__ float ldf(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ldf<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kRor4 = 0x124, kRor8 = 0x128, kQuadX1 = 0xB1, kQuadX2 = 0x4E;
+
+// sum over the 16 lanes of a DPP row, in every lane of the row
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<kRor8>(v);
+    v += dpp<kRor4>(v);
+    v += dpp<kQuadX2>(v);
+    return v + dpp<kQuadX1>(v);
+}
+
+// sum over the 64 lanes of the wave, in every lane
+__device__ __forceinline__ float wave_sum(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    return row_sum(v);
+}
+
+// Sums over the 64 lanes of 16 per-lane values v[0..15].  Returns, in lane l
+// with i = l % 16 < 4, the sum of value 4 (l / 16) + i (other lanes: junk).
+// permlane32 swaps pair value m with m + 8 (lower half keeps m), permlane16
+// swaps pair m with m + 4 (rows 0..3 then hold values 4r .. 4r + 3, each
+// summed over the 4 rows' lanes at the same place), and row sums finish.
+__device__ __forceinline__ float reduce16(const float* v) {
+    float u[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 8]), false, false);
+        u[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+    float x[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[m]), __float_as_uint(u[m + 4]), false, false);
+        x[m] = row_sum(__uint_as_float(s[0]) + __uint_as_float(s[1]));
+    }
+    const int i = threadIdx.x & 3;
+    const float lo = (i & 1) ? x[1] : x[0], hi = (i & 1) ? x[3] : x[2];
+    return (i & 2) ? hi : lo;
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Delta / ln2 of a token (log2 units) and the softplus derivative sigmoid(v).
+template <bool SP>
+__device__ __forceinline__ float w_of(float v, float& deriv) {
+    if (!SP) {
+        deriv = 1.0f;
+        return v * kLog2e;
+    }
+    const float e = fast_exp2(-fabsf(v) * kLog2e);   // exp(-|v|)
+    const float r = fast_rcp(1.0f + e);
+    deriv = v >= 0.0f ? r : e * r;
+    return softplus_log2(v * kLog2e);
+}
+
+// Per-tile token constants staged by threads 0..7: Delta, a = exp(Delta A)
+// and the softplus derivative; tokens past L get Delta = 0, a = 1 (an
+// identity step).
+template <bool SP>
+__device__ __forceinline__ void stage_tok(const M2BwdArgs& a, int64_t b, int64_t h, float Ah, float biash, int64_t t0,
+                                          float* Dl, float* Aa, float* Dv) {
+    const int j = threadIdx.x;
+    if (j >= kT2) return;
+    const int64_t t = t0 + j;
+    float dl = 0.0f, av = 1.0f, dv = 0.0f;
+    if (t < a.L) {
+        const float v = (a.in_bf16 ? ldf(reinterpret_cast<const uint16_t*>(a.dt), (b * a.L + t) * a.H + h)
+                                   : ldf(reinterpret_cast<const float*>(a.dt), (b * a.L + t) * a.H + h)) + biash;
+        const float w = w_of<SP>(v, dv);
+        dl = w * kLn2;
+        av = fast_exp2(w * Ah);
+    }
+    Dl[j] = dl;
+    Aa[j] = av;
+    Dv[j] = dv;
+}
+
+// A tile's B (and C) rows of the group, fp32, zero past L.
+template <typename Tin, int N>
+__device__ __forceinline__ void stage_bc(const M2BwdArgs& a, int64_t b, int64_t g, int64_t t0, float (*Bs)[N],
+                                         float (*Cs)[N]) {
+    const Tin* Bp = reinterpret_cast<const Tin*>(a.B);
+    const Tin* Cp = reinterpret_cast<const Tin*>(a.C);
+    for (int e = threadIdx.x; e < kT2 * N; e += blockDim.x) {
+        const int j = e / N, n = e - j * N;
+        const int64_t t = t0 + j;
+        const int64_t i = ((b * a.L + t) * a.G + g) * N + n;
+        const bool ok = t < a.L;
+        Bs[j][n] = ok ? ldf(Bp, i) : 0.0f;
+        if (Cs) Cs[j][n] = ok ? ldf(Cp, i) : 0.0f;
+    }
+}
+
+// ---------------- checkpoint pass -------------------------------------------
+template <typename Tin, int NW, bool SP>
+__global__ __launch_bounds__(64 * NW) void m2_bwd_ck_kernel(M2BwdArgs a) {
+    constexpr int N = 16 * NW;
+    __shared__ float Bs[2][kT2][N];
+    __shared__ float Dl[2][kT2], Aa[2][kT2], Dv[2][kT2];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int64_t bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
+    const float Ah = a.A[h], biash = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const Tin* X = reinterpret_cast<const Tin*>(a.x);
+    const int64_t ntiles = (a.L + kT2 - 1) / kT2;
+    float hs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hs[i] = a.h0 ? a.h0[(bh * kP + lane) * N + 16 * w + i] : 0.0f;
+    stage_bc<Tin, N>(a, b, g, 0, Bs[0], nullptr);
+    stage_tok<SP>(a, b, h, Ah, biash, 0, Dl[0], Aa[0], Dv[0]);
+    lds_barrier();
+    for (int64_t k = 0; k < ntiles; ++k) {
+        const int buf = (int)(k & 1);
+        float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16) + lane * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = make_float4(hs[4 * q], hs[4 * q + 1], hs[4 * q + 2], hs[4 * q + 3]);
+        if (k + 1 < ntiles) {
+            stage_bc<Tin, N>(a, b, g, (k + 1) * kT2, Bs[buf ^ 1], nullptr);
+            stage_tok<SP>(a, b, h, Ah, biash, (k + 1) * kT2, Dl[buf ^ 1], Aa[buf ^ 1], Dv[buf ^ 1]);
+        }
+        float xv[kT2];
+#pragma unroll
+        for (int j = 0; j < kT2; ++j) {
+            const int64_t t = k * kT2 + j;
+            xv[j] = t < a.L ? ldf(X, ((b * a.L + t) * a.H + h) * kP + lane) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kT2; ++j) {
+            const float xw = Dl[buf][j] * xv[j], av = Aa[buf][j];
+            const float4* br = reinterpret_cast<const float4*>(&Bs[buf][j][16 * w]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 bb = br[q];
+                hs[4 * q] = __builtin_fmaf(av, hs[4 * q], xw * bb.x);
+                hs[4 * q + 1] = __builtin_fmaf(av, hs[4 * q + 1], xw * bb.y);
+                hs[4 * q + 2] = __builtin_fmaf(av, hs[4 * q + 2], xw * bb.z);
+                hs[4 * q + 3] = __builtin_fmaf(av, hs[4 * q + 3], xw * bb.w);
+            }
+        }
+        lds_barrier();
+    }
+}
+
+// ---------------- adjoint pass ----------------------------------------------
+template <int NW>
+struct BwdSmem {
+    static constexpr int N = 16 * NW;
+    alignas(16) float Bs[kT2][N];
+    alignas(16) float Cs[kT2][N];
+    float Dl[kT2], Aa[kT2], Dv[kT2];
+    float xs[kT2][kP], dys[kT2][kP], xws[kT2][kP];
+    float ycp[NW][kT2][kP], dxp[NW][kT2][kP], s1p[NW][kT2][kP];
+    float red[3][NW];
+};
+
+template <typename Tin, typename Tout, int NW, bool SP>
+__global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
+    constexpr int N = 16 * NW;
+    constexpr int kPer = (kT2 + NW - 1) / NW;   // (token, channel) pairs per thread per tile
+    __shared__ BwdSmem<NW> sm;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int64_t bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
+    const float Ah = a.A[h], biash = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    const Tin* X = reinterpret_cast<const Tin*>(a.x);
+    const Tin* Z = reinterpret_cast<const Tin*>(a.z);
+    const Tout* DO = reinterpret_cast<const Tout*>(a.dout);
+    const int64_t ntiles = (a.L + kT2 - 1) / kT2;
+
+    float lam[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lam[i] = 0.0f;
+    float accD = 0.0f, accA = 0.0f, accBias = 0.0f;
+
+    for (int64_t k = ntiles - 1; k >= 0; --k) {
+        const int64_t t0 = k * kT2;
+        // stage the tile: B, C rows, token constants, and per (token, channel)
+        // x, dy = dout silu(z) (or dout) and Delta x
+        stage_bc<Tin, N>(a, b, g, t0, sm.Bs, sm.Cs);
+        stage_tok<SP>(a, b, h, Ah, biash, t0, sm.Dl, sm.Aa, sm.Dv);
+        lds_barrier();   // Dl is read below
+        float dor[kPer], zr[kPer];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int j = w + m * NW;
+            dor[m] = 0.0f;
+            zr[m] = 0.0f;
+            if (j < kT2) {
+                const int64_t t = t0 + j;
+                const bool ok = t < a.L;
+                const int64_t e = ((b * a.L + t) * a.H + h) * kP + lane;
+                const float xv = ok ? ldf(X, e) : 0.0f;
+                const float dv = ok ? ldf(DO, e) : 0.0f;
+                float dy = dv;
+                if (Z) {
+                    const float zz = ok ? ldf(Z, e) : 0.0f;
+                    zr[m] = zz;
+                    dy = dv * silu_scaled(zz, 1.0f);
+                }
+                dor[m] = dv;
+                sm.xs[j][lane] = xv;
+                sm.dys[j][lane] = dy;
+                sm.xws[j][lane] = sm.Dl[j] * xv;
+            }
+        }
+        lds_barrier();
+
+        // this wave's states at the tile's tokens, from its checkpoint
+        float hc[16];
+        {
+            const float4* src =
+                reinterpret_cast<const float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16) + lane * 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = src[q];
+                hc[4 * q] = v.x; hc[4 * q + 1] = v.y; hc[4 * q + 2] = v.z; hc[4 * q + 3] = v.w;
+            }
+        }
+        float hs[kT2][16];
+#pragma unroll
+        for (int j = 0; j < kT2; ++j) {
+            const float xw = sm.xws[j][lane], av = sm.Aa[j];
+            const float4* br = reinterpret_cast<const float4*>(&sm.Bs[j][16 * w]);
+            const float4* cr = reinterpret_cast<const float4*>(&sm.Cs[j][16 * w]);
+            float yc = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 bb = br[q], cc = cr[q];
+                const float bq[4] = {bb.x, bb.y, bb.z, bb.w}, cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * q + r;
+                    hs[j][i] = __builtin_fmaf(av, j ? hs[j - 1][i] : hc[i], xw * bq[r]);
+                    yc = __builtin_fmaf(cq[r], hs[j][i], yc);
+                }
+            }
+            sm.ycp[w][j][lane] = yc;
+        }
+
+        // the adjoint back through the tile
+#pragma unroll
+        for (int j = kT2 - 1; j >= 0; --j) {
+            const int64_t t = t0 + j;
+            const float dy = sm.dys[j][lane], xw = sm.xws[j][lane], av = sm.Aa[j];
+            const float4* br = reinterpret_cast<const float4*>(&sm.Bs[j][16 * w]);
+            const float4* cr = reinterpret_cast<const float4*>(&sm.Cs[j][16 * w]);
+            float vB[16], vC[16];
+            float dxs = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 bb = br[q], cc = cr[q];
+                const float bq[4] = {bb.x, bb.y, bb.z, bb.w}, cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * q + r;
+                    const float l = __builtin_fmaf(dy, cq[r], lam[i]);
+                    const float hp = j ? hs[j - 1][i] : hc[i];
+                    vC[i] = dy * hs[j][i];
+                    vB[i] = l * xw;
+                    dxs = __builtin_fmaf(l, bq[r], dxs);
+                    s1 = __builtin_fmaf(l, hp, s1);
+                    lam[i] = av * l;
+                }
+            }
+            sm.dxp[w][j][lane] = dxs;
+            sm.s1p[w][j][lane] = s1;
+            const float sB = reduce16(vB);
+            const float sC = reduce16(vC);
+            if ((lane & 15) < 4 && t < a.L) {
+                const int64_t o = (bh * a.L + t) * N + 16 * w + 4 * (lane >> 4) + (lane & 3);
+                a.pB[o] = sB;
+                a.pC[o] = sC;
+            }
+        }
+        lds_barrier();
+
+        // per (token, channel): dx, dz, and the token's dDelta (a wave per token)
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int j = w + m * NW;
+            if (j >= kT2) continue;   // uniform per wave
+            const int64_t t = t0 + j;
+            const bool ok = t < a.L;
+            float dxsum = 0.0f, s1sum = 0.0f, ycs = 0.0f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                dxsum += sm.dxp[v][j][lane];
+                s1sum += sm.s1p[v][j][lane];
+                ycs += sm.ycp[v][j][lane];
+            }
+            const float xv = sm.xs[j][lane], dy = sm.dys[j][lane];
+            const float dl = sm.Dl[j], av = sm.Aa[j];
+            const int64_t e = ((b * a.L + t) * a.H + h) * kP + lane;
+            if (ok) a.dx[e] = __builtin_fmaf(dl, dxsum, Dh * dy);
+            if (Z && ok) {
+                const float zz = zr[m];
+                const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+                const float yc = __builtin_fmaf(Dh, xv, ycs);
+                a.dz[e] = dor[m] * yc * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+            }
+            accD = __builtin_fmaf(dy, xv, accD);
+            accA = __builtin_fmaf(dl * av, s1sum, accA);
+            const float ddl = wave_sum(__builtin_fmaf(xv, dxsum, Ah * av * s1sum));
+            if (lane == 0 && ok) {
+                const float dv = ddl * sm.Dv[j];
+                a.ddt[(b * a.L + t) * a.H + h] = dv;
+                accBias += dv;
+            }
+        }
+        lds_barrier();   // the tile's LDS is restaged next
+    }
+
+    if (a.dh0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a.dh0[(bh * kP + lane) * N + 16 * w + i] = lam[i];
+    }
+    // the workgroup's shares of dD, dA, dbias
+    accD = wave_sum(accD);
+    accA = wave_sum(accA);
+    if (lane == 0) {
+        sm.red[0][w] = accD;
+        sm.red[1][w] = accA;
+        sm.red[2][w] = accBias;
+    }
+    lds_barrier();
+    if (tid < 3) {
+        float s = 0.0f;
+        for (int v = 0; v < NW; ++v) s += sm.red[tid][v];
+        (tid == 0 ? a.pD : tid == 1 ? a.pA : a.pbias)[bh] = s;
+    }
+}
+
+// dB, dC: sums of the per-head partials over the heads of each group, one
+// thread per (batch, token, group, n).
+__global__ __launch_bounds__(256) void m2_bwd_bc_reduce_kernel(M2BwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = a.batch * a.L * a.G * a.N;
+    if (i >= total) return;
+    const int64_t n = i % a.N, r = i / a.N, g = r % a.G, bt = r / a.G, t = bt % a.L, b = bt / a.L;
+    const int64_t hpg = a.H / a.G;
+    float sB = 0.0f, sC = 0.0f;
+    for (int64_t hh = g * hpg; hh < (g + 1) * hpg; ++hh) {
+        const int64_t o = ((b * a.H + hh) * a.L + t) * a.N + n;
+        sB += a.pB[o];
+        sC += a.pC[o];
+    }
+    a.dB[i] = sB;
+    a.dC[i] = sC;
+}
+
+// dA, dD, dbias: sums over batches of the per-(batch, head) partials.
+__global__ __launch_bounds__(64) void m2_bwd_param_reduce_kernel(M2BwdArgs a) {
+    const int64_t h = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (h >= a.H) return;
+    float sA = 0.0f, sD = 0.0f, sb = 0.0f;
+    for (int64_t b = 0; b < a.batch; ++b) {
+        sA += a.pA[b * a.H + h];
+        sD += a.pD[b * a.H + h];
+        sb += a.pbias[b * a.H + h];
+    }
+    a.dA[h] = sA;
+    if (a.dD) a.dD[h] = a.D ? sD : 0.0f;
+    if (a.ddt_bias) a.ddt_bias[h] = a.dt_bias ? sb : 0.0f;
+}
+
+template <typename Tin, typename Tout, int NW>
+hipError_t launch_nw(const M2BwdArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.batch * a.H)), block(64 * NW);
+    {
+        KTime kt("m2_bwd_checkpoint", stream);
+        if (a.softplus)
+            hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, false>), grid, block, 0, stream, a);
+    }
+    {
+        KTime kt("m2_bwd_adjoint", stream);
+        if (a.softplus)
+            hipLaunchKernelGGL((m2_bwd_kernel<Tin, Tout, NW, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((m2_bwd_kernel<Tin, Tout, NW, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_dt(const M2BwdArgs& a, hipStream_t stream) {
+    switch (a.N) {
+        case 16: return launch_nw<Tin, Tout, 1>(a, stream);
+        case 32: return launch_nw<Tin, Tout, 2>(a, stream);
+        case 64: return launch_nw<Tin, Tout, 4>(a, stream);
+        default: return launch_nw<Tin, Tout, 8>(a, stream);
+    }
+}
+
+}  // namespace
+
+size_t m2_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t N) {
+    const int64_t ntiles = (L + kT2 - 1) / kT2;
+    const int64_t ck = batch * H * ntiles * kP * N;      // checkpoints
+    const int64_t part = 2 * batch * H * L * N;          // per-head dB, dC
+    const int64_t par = 3 * batch * H;                   // per-(batch, head) dD, dA, dbias
+    return (size_t)(ck + part + par + 64) * sizeof(float);
+}
+
+void m2_bwd_carve(M2BwdArgs& a, void* ws) {
+    float* p = static_cast<float*>(ws);
+    const int64_t ntiles = (a.L + kT2 - 1) / kT2;
+    a.ck = p;
+    p += a.batch * a.H * ntiles * kP * a.N;
+    a.pB = p;
+    p += a.batch * a.H * a.L * a.N;
+    a.pC = p;
+    p += a.batch * a.H * a.L * a.N;
+    a.pA = p;
+    a.pD = p + a.batch * a.H;
+    a.pbias = p + 2 * a.batch * a.H;
+}
+
+hipError_t launch_m2_bwd(const M2BwdArgs& a, int in_bf16, int out_bf16, hipStream_t stream) {
+    hipError_t e;
+    if (in_bf16)
+        e = out_bf16 ? launch_dt<uint16_t, uint16_t>(a, stream) : launch_dt<uint16_t, float>(a, stream);
+    else
+        e = out_bf16 ? launch_dt<float, uint16_t>(a, stream) : launch_dt<float, float>(a, stream);
+    if (e != hipSuccess) return e;
+    {
+        KTime kt("m2_bwd_bc_reduce", stream);
+        const int64_t total = a.batch * a.L * a.G * a.N;
+        hipLaunchKernelGGL(m2_bwd_bc_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
+    }
+    {
+        KTime kt("m2_bwd_param_reduce", stream);
+        hipLaunchKernelGGL(m2_bwd_param_reduce_kernel, dim3((unsigned)((a.H + 63) / 64)), dim3(64), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace selscan

@@ -527,6 +527,65 @@ selscan_status_t selscan_bwd(const selscan_shape_t* s, const void* u, const void
     }
 }
 
+// Mamba-2 gradients: the recurrent form with lane = channel needs headdim 64.
+selscan_status_t check_m2_bwd_shape(const selscan_m2_shape_t* s) {
+    selscan_status_t st = check_m2_shape(s);
+    if (st != SELSCAN_OK) return st;
+    if (s->headdim != 64) return fail(SELSCAN_ERR_UNSUPPORTED, "Mamba-2 gradients support headdim 64");
+    if (s->batch * s->nheads > 0x7fffffff) return fail(SELSCAN_ERR_UNSUPPORTED, "too many (batch, head) units");
+    if (s->batch * s->seqlen * s->ngroups * s->dstate > (int64_t)0xffffffff * 256)
+        return fail(SELSCAN_ERR_UNSUPPORTED, "too many dB/dC elements for one launch");
+    return SELSCAN_OK;
+}
+
+size_t selscan_mamba2_bwd_workspace_bytes(const selscan_m2_shape_t* s) {
+    if (check_m2_bwd_shape(s) != SELSCAN_OK) return 0;
+    return selscan::m2_bwd_workspace_bytes(s->batch, s->seqlen, s->nheads, s->dstate);
+}
+
+selscan_status_t selscan_mamba2_bwd(const selscan_m2_shape_t* s, const void* x, const void* dt, const float* A,
+                                    const void* B, const void* C, const float* D, const void* z,
+                                    const float* dt_bias, int softplus, const float* h0, const void* dout,
+                                    float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD, float* dz,
+                                    float* ddt_bias, float* dh0, void* stream) {
+    try {
+        selscan_status_t st = check_m2_bwd_shape(s);
+        if (st != SELSCAN_OK) return st;
+        if (!x || !dt || !A || !B || !C || !dout)
+            return fail(SELSCAN_ERR_INVALID_ARG, "x, dt, A, B, C and dout must be non-NULL");
+        if (!dx || !ddt || !dA || !dB || !dC)
+            return fail(SELSCAN_ERR_INVALID_ARG, "dx, ddt, dA, dB and dC must be non-NULL");
+        if (z && !dz) return fail(SELSCAN_ERR_INVALID_ARG, "dz must be non-NULL when z is given");
+        if (softplus != 0 && softplus != 1) return fail(SELSCAN_ERR_INVALID_ARG, "softplus must be 0 or 1");
+        st = device_check();
+        if (st != SELSCAN_OK) return st;
+        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        Scratch ws;
+        st = ws.get(s->workspace, s->workspace_bytes,
+                    selscan::m2_bwd_workspace_bytes(s->batch, s->seqlen, s->nheads, s->dstate), hs);
+        if (st != SELSCAN_OK) return st;
+        selscan::M2BwdArgs a{};
+        a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.dt_bias = dt_bias; a.h0 = h0;
+        a.dout = dout;
+        a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz; a.ddt_bias = ddt_bias;
+        a.dh0 = dh0;
+        a.batch = s->batch; a.L = s->seqlen; a.H = s->nheads; a.G = s->ngroups; a.N = s->dstate;
+        a.softplus = softplus;
+        a.in_bf16 = s->in_dtype == SELSCAN_BF16;
+        selscan::m2_bwd_carve(a, ws.ptr);
+        if (log_plans())
+            std::fprintf(stderr, "[selscan] m2 bwd B=%lld L=%lld H=%lld G=%lld N=%lld ws=%zu\n", (long long)s->batch,
+                         (long long)s->seqlen, (long long)s->nheads, (long long)s->ngroups, (long long)s->dstate,
+                         selscan::m2_bwd_workspace_bytes(s->batch, s->seqlen, s->nheads, s->dstate));
+        hipError_t e = selscan::launch_m2_bwd(a, a.in_bf16, s->out_dtype == SELSCAN_BF16, hs);
+        ws.release();
+        if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return ok();
+    } catch (...) {
+        return fail(SELSCAN_ERR_LAUNCH, "unexpected host exception");
+    }
+}
+
 selscan_status_t selscan_mamba2_step(const selscan_m2_shape_t* s, float* state, const void* x, const void* dt,
                                      const float* A, const void* B, const void* C, const float* D, const void* z,
                                      const float* dt_bias, int softplus, void* y, void* stream) {

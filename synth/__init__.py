@@ -200,6 +200,17 @@ def m1_dout(batch, dim, seqlen, dtype=torch.bfloat16, seed=0, device="cpu"):
     return _normal((batch, dim, seqlen), seed, "dout", dtype, torch.device(device))
 
 
+def m2_dout(batch, seqlen, nheads, headdim, dtype=torch.float32, seed=0, device="cpu"):
+    """Gradient of a loss with respect to a Mamba-2 scan's output: standard
+    normal [batch, seqlen, nheads, headdim], drawn like the inputs."""
+    return _normal((batch, seqlen, nheads, headdim), seed, "dout", dtype, torch.device(device))
+
+
+def m2_state(batch, nheads, headdim, dstate, seed=0, device="cpu"):
+    """A Mamba-2 state [batch, nheads, headdim, dstate] fp32, standard normal."""
+    return _normal((batch, nheads, headdim, dstate), seed, "h0", torch.float32, torch.device(device))
+
+
 def m1_state(batch, dim, dstate, seed=0, device="cpu"):
     """A Mamba-1 state [batch, dim, dstate] fp32, standard normal."""
     return _normal((batch, dim, dstate), seed, "h0", torch.float32, torch.device(device))

@@ -222,3 +222,36 @@ def test_bwd_workspace_size():
     assert n % 256 == 0
     assert n >= 3 * 2 * 32 * 1000 * 4
     assert ss.lib().selscan_bwd_workspace_bytes(ctypes.byref(_m1(dstate=17))) == 0
+
+
+def _m2(**kw):
+    base = dict(batch=1, seqlen=16, nheads=2, headdim=64, ngroups=1, dstate=32, in_dtype=ss.BF16, out_dtype=ss.F32)
+    base.update(kw)
+    return ss.M2Shape(base["batch"], base["seqlen"], base["nheads"], base["headdim"], base["ngroups"],
+                      base["dstate"], base["in_dtype"], base["out_dtype"], None, 0)
+
+
+def _m2_bwd(s, z=None, dz=None, dx=FAKE, softplus=1):
+    return ss.lib().selscan_mamba2_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, z, None, softplus, None,
+                                       FAKE, dx, FAKE, FAKE, FAKE, FAKE, None, dz, None, None, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("headdim", 32, ss.ERR_UNSUPPORTED), ("headdim", 128, ss.ERR_UNSUPPORTED), ("dstate", 24, ss.ERR_UNSUPPORTED),
+    ("ngroups", 3, ss.ERR_INVALID_ARG), ("seqlen", 0, ss.ERR_INVALID_ARG)])
+def test_m2_bwd_bad_shape_rejected(field, value, status):
+    assert _m2_bwd(_m2(**{field: value})) == status
+
+
+def test_m2_bwd_argument_checks():
+    assert _m2_bwd(_m2(), dx=None) == ss.ERR_INVALID_ARG
+    assert _m2_bwd(_m2(), z=FAKE, dz=None) == ss.ERR_INVALID_ARG
+    assert "dz" in ss.last_error()
+    assert _m2_bwd(_m2(), softplus=2) == ss.ERR_INVALID_ARG
+
+
+def test_m2_bwd_workspace_size():
+    # the state entering every 8-token tile and the per-head dB/dC
+    n = ss.mamba2_bwd_workspace_bytes(2, 100, 4, 64, 1, 128)
+    assert n >= (2 * 4 * 13 * 64 * 128 + 2 * 2 * 4 * 100 * 128) * 4
+    assert ss.mamba2_bwd_workspace_bytes(2, 100, 4, 32, 1, 128) == 0
