@@ -282,20 +282,28 @@ def time_conv1d(name, steps, device, width=4):
 
 
 def time_backward(name, steps, device, warmup=2, seed=0):
-    """Mamba-1 gradients (selscan_bwd: every input's gradient from dout) on a
-    workload's full shape, fp32 dout and gradients, workspace preallocated."""
+    """Gradients (selscan_bwd / selscan_mamba2_bwd: every input's gradient
+    from dout) on a workload's full shape, fp32 dout and gradients, workspace
+    preallocated."""
     import torch
     import selective_state_space_25_amd as ss
     import synth
 
     w = synth.WORKLOADS[name]
     inp = synth.workload_inputs(w, seed=seed, device=device)
-    dout = synth.m1_dout(w.batch, w.dim, w.seqlen, torch.float32, seed=seed, device=device)
     code = ss.BF16 if w.dtype == torch.bfloat16 else ss.F32
-    ws = torch.empty(ss.bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, code, ss.F32),
-                     dtype=torch.uint8, device=device)
-    f = lambda: ss.bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                       inp["delta_bias"], dout, softplus=True, workspace=ws)
+    if w.kind == "m1":
+        dout = synth.m1_dout(w.batch, w.dim, w.seqlen, torch.float32, seed=seed, device=device)
+        ws = torch.empty(ss.bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, code, ss.F32),
+                         dtype=torch.uint8, device=device)
+        f = lambda: ss.bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                           inp["delta_bias"], dout, softplus=True, workspace=ws)
+    else:
+        dout = synth.m2_dout(w.batch, w.seqlen, w.nheads, w.headdim, torch.float32, seed=seed, device=device)
+        ws = torch.empty(ss.mamba2_bwd_workspace_bytes(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
+                                                       code, ss.F32), dtype=torch.uint8, device=device)
+        f = lambda: ss.mamba2_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                  inp["dt_bias"], dout, softplus=True, workspace=ws)
     for _ in range(warmup):
         f()
     torch.cuda.synchronize(device)
@@ -647,7 +655,7 @@ def main():
     line["decode"]["c_abi_host_us_per_call"] = time_abi_host()
     line["conv1d"] = time_conv1d("mamba2p8b_l8k", 10, device)
     line["backward"] = {n: time_backward(n, 5 if n != "long_1m" else 3, device)
-                        for n in ("mamba130m_l2k", "mamba2p8b_l8k", "long_1m")}
+                        for n in ("mamba130m_l2k", "mamba2p8b_l8k", "long_1m", "mamba2_mh")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.seed)
         line["cpu_baseline"]["gpu_over_cpu"] = line["value"] / line["cpu_baseline"]["value"]

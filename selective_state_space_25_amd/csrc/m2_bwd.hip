@@ -113,41 +113,64 @@ __device__ __forceinline__ float w_of(float v, float& deriv) {
     return softplus_log2(v * kLog2e);
 }
 
-// Per-tile token constants staged by threads 0..7: Delta, a = exp(Delta A)
-// and the softplus derivative; tokens past L get Delta = 0, a = 1 (an
-// identity step).
+// Delta, a = exp(Delta A) and the softplus derivative of one token from its
+// raw dt (tokens past L: Delta = 0, a = 1, an identity step).
 template <bool SP>
-__device__ __forceinline__ void stage_tok(const M2BwdArgs& a, int64_t b, int64_t h, float Ah, float biash, int64_t t0,
-                                          float* Dl, float* Aa, float* Dv) {
-    const int j = threadIdx.x;
-    if (j >= kT2) return;
-    const int64_t t = t0 + j;
-    float dl = 0.0f, av = 1.0f, dv = 0.0f;
-    if (t < a.L) {
-        const float v = (a.in_bf16 ? ldf(reinterpret_cast<const uint16_t*>(a.dt), (b * a.L + t) * a.H + h)
-                                   : ldf(reinterpret_cast<const float*>(a.dt), (b * a.L + t) * a.H + h)) + biash;
-        const float w = w_of<SP>(v, dv);
+__device__ __forceinline__ void tok_consts(float dtv, bool ok, float Ah, float biash, float& dl, float& av,
+                                           float& dv) {
+    dl = 0.0f;
+    av = 1.0f;
+    dv = 0.0f;
+    if (ok) {
+        const float w = w_of<SP>(dtv + biash, dv);
         dl = w * kLn2;
         av = fast_exp2(w * Ah);
     }
-    Dl[j] = dl;
-    Aa[j] = av;
-    Dv[j] = dv;
 }
 
-// A tile's B (and C) rows of the group, fp32, zero past L.
-template <typename Tin, int N>
-__device__ __forceinline__ void stage_bc(const M2BwdArgs& a, int64_t b, int64_t g, int64_t t0, float (*Bs)[N],
-                                         float (*Cs)[N]) {
+// One tile's global inputs held in registers while the tile before it is
+// computed: this thread's two of the tile's 8 x N B (and C) values, the raw
+// dt of its tokens, and x (dout, z) of its (token, channel) pairs.  Thread
+// `tid` takes B/C elements e = tid and tid + 64 NW of the tile (token e / N,
+// state e % N) and pairs (w + m NW, lane).
+template <int NW>
+struct TileRegs {
+    static constexpr int kPer = (kT2 + NW - 1) / NW;
+    float b[2], c[2];
+    float dt[kPer], x[kPer], dout[kPer], z[kPer];
+};
+
+template <typename Tin, typename Tout, int NW, bool BWD>
+__device__ __forceinline__ void load_tile(const M2BwdArgs& a, int64_t b, int64_t h, int64_t g, int64_t t0,
+                                          TileRegs<NW>& r) {
+    constexpr int N = 16 * NW;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const Tin* Bp = reinterpret_cast<const Tin*>(a.B);
     const Tin* Cp = reinterpret_cast<const Tin*>(a.C);
-    for (int e = threadIdx.x; e < kT2 * N; e += blockDim.x) {
+    const Tin* X = reinterpret_cast<const Tin*>(a.x);
+    const Tin* DT = reinterpret_cast<const Tin*>(a.dt);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = tid + q * 64 * NW;
         const int j = e / N, n = e - j * N;
         const int64_t t = t0 + j;
         const int64_t i = ((b * a.L + t) * a.G + g) * N + n;
         const bool ok = t < a.L;
-        Bs[j][n] = ok ? ldf(Bp, i) : 0.0f;
-        if (Cs) Cs[j][n] = ok ? ldf(Cp, i) : 0.0f;
+        r.b[q] = ok ? ldf(Bp, i) : 0.0f;
+        if (BWD) r.c[q] = ok ? ldf(Cp, i) : 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < TileRegs<NW>::kPer; ++m) {
+        const int j = w + m * NW;
+        const int64_t t = t0 + j;
+        const bool ok = j < kT2 && t < a.L;
+        const int64_t e = ((b * a.L + t) * a.H + h) * kP + lane;
+        r.dt[m] = ok ? ldf(DT, (b * a.L + t) * a.H + h) : 0.0f;
+        r.x[m] = ok ? ldf(X, e) : 0.0f;
+        if (BWD) {
+            r.dout[m] = ok ? ldf(reinterpret_cast<const Tout*>(a.dout), e) : 0.0f;
+            r.z[m] = (ok && a.z) ? ldf(reinterpret_cast<const Tin*>(a.z), e) : 0.0f;
+        }
     }
 }
 
@@ -155,37 +178,45 @@ __device__ __forceinline__ void stage_bc(const M2BwdArgs& a, int64_t b, int64_t 
 template <typename Tin, int NW, bool SP>
 __global__ __launch_bounds__(64 * NW) void m2_bwd_ck_kernel(M2BwdArgs a) {
     constexpr int N = 16 * NW;
-    __shared__ float Bs[2][kT2][N];
-    __shared__ float Dl[2][kT2], Aa[2][kT2], Dv[2][kT2];
+    constexpr int kPer = TileRegs<NW>::kPer;
+    __shared__ alignas(16) float Bs[2][kT2][N];
+    __shared__ float xws[2][kT2][kP], Aa[2][kT2];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int64_t bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
     const float Ah = a.A[h], biash = a.dt_bias ? a.dt_bias[h] : 0.0f;
-    const Tin* X = reinterpret_cast<const Tin*>(a.x);
     const int64_t ntiles = (a.L + kT2 - 1) / kT2;
     float hs[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) hs[i] = a.h0 ? a.h0[(bh * kP + lane) * N + 16 * w + i] : 0.0f;
-    stage_bc<Tin, N>(a, b, g, 0, Bs[0], nullptr);
-    stage_tok<SP>(a, b, h, Ah, biash, 0, Dl[0], Aa[0], Dv[0]);
+    // a tile's inputs into LDS buffer `buf`: B, a per token, Delta x per pair
+    auto put = [&](const TileRegs<NW>& r, int64_t t0, int buf) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) (&Bs[buf][0][0])[tid + q * 64 * NW] = r.b[q];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int j = w + m * NW;
+            if (j < kT2) {
+                float dl, av, dv;
+                tok_consts<SP>(r.dt[m], t0 + j < a.L, Ah, biash, dl, av, dv);
+                xws[buf][j][lane] = dl * r.x[m];
+                if (lane == 0) Aa[buf][j] = av;
+            }
+        }
+    };
+    TileRegs<NW> nx;
+    load_tile<Tin, Tin, NW, false>(a, b, h, g, 0, nx);
+    put(nx, 0, 0);
     lds_barrier();
     for (int64_t k = 0; k < ntiles; ++k) {
         const int buf = (int)(k & 1);
+        // the next tile's loads stay in flight over this tile's arithmetic
+        if (k + 1 < ntiles) load_tile<Tin, Tin, NW, false>(a, b, h, g, (k + 1) * kT2, nx);
         float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16) + lane * 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[q] = make_float4(hs[4 * q], hs[4 * q + 1], hs[4 * q + 2], hs[4 * q + 3]);
-        if (k + 1 < ntiles) {
-            stage_bc<Tin, N>(a, b, g, (k + 1) * kT2, Bs[buf ^ 1], nullptr);
-            stage_tok<SP>(a, b, h, Ah, biash, (k + 1) * kT2, Dl[buf ^ 1], Aa[buf ^ 1], Dv[buf ^ 1]);
-        }
-        float xv[kT2];
 #pragma unroll
         for (int j = 0; j < kT2; ++j) {
-            const int64_t t = k * kT2 + j;
-            xv[j] = t < a.L ? ldf(X, ((b * a.L + t) * a.H + h) * kP + lane) : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < kT2; ++j) {
-            const float xw = Dl[buf][j] * xv[j], av = Aa[buf][j];
+            const float xw = xws[buf][j][lane], av = Aa[buf][j];
             const float4* br = reinterpret_cast<const float4*>(&Bs[buf][j][16 * w]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -196,6 +227,8 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_ck_kernel(M2BwdArgs a) {
                 hs[4 * q + 3] = __builtin_fmaf(av, hs[4 * q + 3], xw * bb.w);
             }
         }
+        // buffer buf ^ 1 was last read in iteration k - 1, before its barrier
+        if (k + 1 < ntiles) put(nx, (k + 1) * kT2, buf ^ 1);
         lds_barrier();
     }
 }
@@ -207,7 +240,7 @@ struct BwdSmem {
     alignas(16) float Bs[kT2][N];
     alignas(16) float Cs[kT2][N];
     float Dl[kT2], Aa[kT2], Dv[kT2];
-    float xs[kT2][kP], dys[kT2][kP], xws[kT2][kP];
+    float xs[kT2][kP], dys[kT2][kP], xws[kT2][kP], zs[kT2][kP], dos[kT2][kP];
     float ycp[NW][kT2][kP], dxp[NW][kT2][kP], s1p[NW][kT2][kP];
     float red[3][NW];
 };
@@ -215,15 +248,13 @@ struct BwdSmem {
 template <typename Tin, typename Tout, int NW, bool SP>
 __global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
     constexpr int N = 16 * NW;
-    constexpr int kPer = (kT2 + NW - 1) / NW;   // (token, channel) pairs per thread per tile
+    constexpr int kPer = TileRegs<NW>::kPer;
     __shared__ BwdSmem<NW> sm;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int64_t bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
     const float Ah = a.A[h], biash = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float Dh = a.D ? a.D[h] : 0.0f;
-    const Tin* X = reinterpret_cast<const Tin*>(a.x);
-    const Tin* Z = reinterpret_cast<const Tin*>(a.z);
-    const Tout* DO = reinterpret_cast<const Tout*>(a.dout);
+    const bool has_z = a.z != nullptr;
     const int64_t ntiles = (a.L + kT2 - 1) / kT2;
 
     float lam[16];
@@ -231,50 +262,57 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
     for (int i = 0; i < 16; ++i) lam[i] = 0.0f;
     float accD = 0.0f, accA = 0.0f, accBias = 0.0f;
 
+    TileRegs<NW> nx;
+    float4 ckn[4];
+    auto load_ck = [&](int64_t k) {
+        const float4* src =
+            reinterpret_cast<const float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16) + lane * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ckn[q] = src[q];
+    };
+    load_tile<Tin, Tout, NW, true>(a, b, h, g, (ntiles - 1) * kT2, nx);
+
     for (int64_t k = ntiles - 1; k >= 0; --k) {
         const int64_t t0 = k * kT2;
-        // stage the tile: B, C rows, token constants, and per (token, channel)
-        // x, dy = dout silu(z) (or dout) and Delta x
-        stage_bc<Tin, N>(a, b, g, t0, sm.Bs, sm.Cs);
-        stage_tok<SP>(a, b, h, Ah, biash, t0, sm.Dl, sm.Aa, sm.Dv);
-        lds_barrier();   // Dl is read below
-        float dor[kPer], zr[kPer];
+        // the tile's checkpoint, requested before the LDS staging below
+        load_ck(k);
+        // the tile's inputs, loaded during the tile after it, into LDS: B, C
+        // rows, token constants, and per (token, channel) x, dout, z,
+        // dy = dout silu(z) (or dout) and Delta x
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            (&sm.Bs[0][0])[tid + q * 64 * NW] = nx.b[q];
+            (&sm.Cs[0][0])[tid + q * 64 * NW] = nx.c[q];
+        }
 #pragma unroll
         for (int m = 0; m < kPer; ++m) {
             const int j = w + m * NW;
-            dor[m] = 0.0f;
-            zr[m] = 0.0f;
             if (j < kT2) {
-                const int64_t t = t0 + j;
-                const bool ok = t < a.L;
-                const int64_t e = ((b * a.L + t) * a.H + h) * kP + lane;
-                const float xv = ok ? ldf(X, e) : 0.0f;
-                const float dv = ok ? ldf(DO, e) : 0.0f;
-                float dy = dv;
-                if (Z) {
-                    const float zz = ok ? ldf(Z, e) : 0.0f;
-                    zr[m] = zz;
-                    dy = dv * silu_scaled(zz, 1.0f);
+                float dl, av, dv;
+                tok_consts<SP>(nx.dt[m], t0 + j < a.L, Ah, biash, dl, av, dv);
+                if (lane == 0) {
+                    sm.Dl[j] = dl;
+                    sm.Aa[j] = av;
+                    sm.Dv[j] = dv;
                 }
-                dor[m] = dv;
-                sm.xs[j][lane] = xv;
-                sm.dys[j][lane] = dy;
-                sm.xws[j][lane] = sm.Dl[j] * xv;
+                const float zz = nx.z[m];
+                sm.xs[j][lane] = nx.x[m];
+                sm.dos[j][lane] = nx.dout[m];
+                sm.zs[j][lane] = zz;
+                sm.dys[j][lane] = has_z ? nx.dout[m] * silu_scaled(zz, 1.0f) : nx.dout[m];
+                sm.xws[j][lane] = dl * nx.x[m];
             }
+        }
+        float hc[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hc[4 * q] = ckn[q].x; hc[4 * q + 1] = ckn[q].y; hc[4 * q + 2] = ckn[q].z; hc[4 * q + 3] = ckn[q].w;
         }
         lds_barrier();
+        // the next tile's loads stay in flight over this tile's arithmetic
+        if (k > 0) load_tile<Tin, Tout, NW, true>(a, b, h, g, (k - 1) * kT2, nx);
 
         // this wave's states at the tile's tokens, from its checkpoint
-        float hc[16];
-        {
-            const float4* src =
-                reinterpret_cast<const float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16) + lane * 16);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = src[q];
-                hc[4 * q] = v.x; hc[4 * q + 1] = v.y; hc[4 * q + 2] = v.z; hc[4 * q + 3] = v.w;
-            }
-        }
         float hs[kT2][16];
 #pragma unroll
         for (int j = 0; j < kT2; ++j) {
@@ -351,11 +389,11 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
             const float dl = sm.Dl[j], av = sm.Aa[j];
             const int64_t e = ((b * a.L + t) * a.H + h) * kP + lane;
             if (ok) a.dx[e] = __builtin_fmaf(dl, dxsum, Dh * dy);
-            if (Z && ok) {
-                const float zz = zr[m];
+            if (has_z && ok) {
+                const float zz = sm.zs[j][lane];
                 const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
                 const float yc = __builtin_fmaf(Dh, xv, ycs);
-                a.dz[e] = dor[m] * yc * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+                a.dz[e] = sm.dos[j][lane] * yc * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
             }
             accD = __builtin_fmaf(dy, xv, accD);
             accA = __builtin_fmaf(dl * av, s1sum, accA);
@@ -366,7 +404,7 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
                 accBias += dv;
             }
         }
-        lds_barrier();   // the tile's LDS is restaged next
+        lds_barrier();   // the tile's LDS is rewritten next
     }
 
     if (a.dh0) {

@@ -217,10 +217,16 @@ def m1_state(batch, dim, dstate, seed=0, device="cpu"):
 
 
 def bwd_algorithmic_bytes(w: Workload) -> int:
-    """Bytes the Mamba-1 backward must move: the forward's inputs and dout
-    read once, every fp32 gradient written once."""
+    """Bytes the backward must move: the forward's inputs and dout (of the
+    output's dtype) read once, every fp32 gradient written once."""
     s = torch.tensor([], dtype=w.dtype).element_size()
     so = torch.tensor([], dtype=w.out_dtype).element_size()
+    if w.kind == "m2":
+        elem = w.batch * w.seqlen * w.nheads * w.headdim
+        tok = w.batch * w.seqlen * w.nheads
+        bc = w.batch * w.seqlen * w.ngroups * w.dstate
+        return (elem * (2 * s + so) + tok * s + 2 * bc * s + 3 * w.nheads * 4
+                + elem * 2 * 4 + tok * 4 + 2 * bc * 4 + 3 * w.nheads * 4)
     elem = w.batch * w.dim * w.seqlen
     bc = w.batch * w.dstate * w.seqlen
     return (elem * (3 * s + so) + 2 * bc * s + (w.dim * w.dstate + 2 * w.dim) * 4
