@@ -70,27 +70,40 @@ __device__ __forceinline__ float wave_sum(float v) {
     return row_sum(v);
 }
 
-// Sums over the 64 lanes of 16 per-lane values v[0..15].  Returns, in lane l
-// with i = l % 16 < 4, the sum of value 4 (l / 16) + i (other lanes: junk).
-// permlane32 swaps pair value m with m + 8 (lower half keeps m), permlane16
-// swaps pair m with m + 4 (rows 0..3 then hold values 4r .. 4r + 3, each
-// summed over the 4 rows' lanes at the same place), and row sums finish.
-__device__ __forceinline__ float reduce16(const float* v) {
-    float u[8];
+// Sums over the 64 lanes of 32 per-lane values (v[0..15], then u[0..15]),
+// reduce-scattered: each exchange hands half of a lane's values to the
+// partner that keeps the other half and adds what it receives.  permlane32
+// swaps pair value m with m + 16 (lanes 0..31 keep v, 32..63 keep u),
+// permlane16 swaps pair m with m + 8, then within each 16-lane row the
+// partners lane ^ 8 (row rotation by 8), the mirrored lane of the 8-lane
+// half (bit 2 differs), lane ^ 2 and lane ^ 1 (quad permutes).  Lane l ends
+// with the sum of value 8 (l >> 4) + 4 b3 + 2 b2 + b1 (b = bits of l; 0..15
+// from v, 16..31 from u), in lanes l and l ^ 1.
+constexpr int kHalfMirror = 0x141;
+__device__ __forceinline__ float pick(bool hi, float a, float b) { return hi ? b : a; }
+__device__ __forceinline__ float reduce32(const float* v, const float* u) {
+    float x[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(u[m]), false, false);
+        x[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+    float y[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 8]), false, false);
-        u[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[m]), __float_as_uint(x[m + 8]), false, false);
+        y[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
     }
-    float x[4];
+    const int l = threadIdx.x & 63;
+    const bool b3 = l & 8, b2 = l & 4, b1 = l & 2;
+    float z[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[m]), __float_as_uint(u[m + 4]), false, false);
-        x[m] = row_sum(__uint_as_float(s[0]) + __uint_as_float(s[1]));
-    }
-    const int i = threadIdx.x & 3;
-    const float lo = (i & 1) ? x[1] : x[0], hi = (i & 1) ? x[3] : x[2];
-    return (i & 2) ? hi : lo;
+    for (int m = 0; m < 4; ++m) z[m] = pick(b3, y[m], y[m + 4]) + dpp<kRor8>(pick(b3, y[m + 4], y[m]));
+    float w[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) w[m] = pick(b2, z[m], z[m + 2]) + dpp<kHalfMirror>(pick(b2, z[m + 2], z[m]));
+    const float r = pick(b1, w[0], w[1]) + dpp<kQuadX2>(pick(b1, w[1], w[0]));
+    return r + dpp<kQuadX1>(r);
 }
 
 __device__ __forceinline__ void lds_barrier() {
@@ -361,12 +374,11 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
             }
             sm.dxp[w][j][lane] = dxs;
             sm.s1p[w][j][lane] = s1;
-            const float sB = reduce16(vB);
-            const float sC = reduce16(vC);
-            if ((lane & 15) < 4 && t < a.L) {
-                const int64_t o = (bh * a.L + t) * N + 16 * w + 4 * (lane >> 4) + (lane & 3);
-                a.pB[o] = sB;
-                a.pC[o] = sC;
+            const float sBC = reduce32(vB, vC);
+            if ((lane & 1) == 0 && t < a.L) {
+                const int r = lane >> 4;   // rows 0, 1: dB; rows 2, 3: dC
+                const int64_t o = (bh * a.L + t) * N + 16 * w + 8 * (r & 1) + ((lane >> 1) & 7);
+                (r < 2 ? a.pB : a.pC)[o] = sBC;
             }
         }
         lds_barrier();
