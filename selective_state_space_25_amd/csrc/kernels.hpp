@@ -141,7 +141,7 @@ struct M2BwdArgs {
     const float* h0;
     const void* dout;
     float *dx, *ddt, *dA, *dB, *dC, *dD, *dz, *ddt_bias, *dh0;
-    float* ck;        // [batch*H, tiles, N/16, 64, 16] states entering each 8-token tile
+    float* ck;        // [batch*H, tiles, N/16, 4, 64, 4] states entering each 8-token tile
     float* pB;        // [batch*H, L, N] per-head dB
     float* pC;        // [batch*H, L, N] per-head dC
     float *pA, *pD, *pbias;   // [batch*H] per-(batch, head) sums

@@ -216,17 +216,21 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_ck_kernel(M2BwdArgs a) {
             }
         }
     };
-    TileRegs<NW> nx;
-    load_tile<Tin, Tin, NW, false>(a, b, h, g, 0, nx);
-    put(nx, 0, 0);
+    // two register sets, each loaded two tiles ahead of its use: the
+    // tile's arithmetic alone (8 tokens) is shorter than a load's latency
+    TileRegs<NW> ra, rb;
+    load_tile<Tin, Tin, NW, false>(a, b, h, g, 0, ra);
+    if (ntiles > 1) load_tile<Tin, Tin, NW, false>(a, b, h, g, kT2, rb);
+    put(ra, 0, 0);
     lds_barrier();
-    for (int64_t k = 0; k < ntiles; ++k) {
+    auto step = [&](int64_t k, TileRegs<NW>& mine, TileRegs<NW>& other) {
         const int buf = (int)(k & 1);
-        // the next tile's loads stay in flight over this tile's arithmetic
-        if (k + 1 < ntiles) load_tile<Tin, Tin, NW, false>(a, b, h, g, (k + 1) * kT2, nx);
-        float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16) + lane * 16);
+        if (k + 2 < ntiles) load_tile<Tin, Tin, NW, false>(a, b, h, g, (k + 2) * kT2, mine);
+        // checkpoint record of (tile, wave): piece q of every lane's 16 states
+        // together, so that each store covers 1 KB of consecutive bytes
+        float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16)) + lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = make_float4(hs[4 * q], hs[4 * q + 1], hs[4 * q + 2], hs[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) dst[64 * q] = make_float4(hs[4 * q], hs[4 * q + 1], hs[4 * q + 2], hs[4 * q + 3]);
 #pragma unroll
         for (int j = 0; j < kT2; ++j) {
             const float xw = xws[buf][j][lane], av = Aa[buf][j];
@@ -241,8 +245,12 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_ck_kernel(M2BwdArgs a) {
             }
         }
         // buffer buf ^ 1 was last read in iteration k - 1, before its barrier
-        if (k + 1 < ntiles) put(nx, (k + 1) * kT2, buf ^ 1);
+        if (k + 1 < ntiles) put(other, (k + 1) * kT2, buf ^ 1);
         lds_barrier();
+    };
+    for (int64_t k = 0; k < ntiles; k += 2) {
+        step(k, ra, rb);          // tile k: ra (tile k's data) is free for tile k + 2
+        if (k + 1 < ntiles) step(k + 1, rb, ra);
     }
 }
 
@@ -279,9 +287,9 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
     float4 ckn[4];
     auto load_ck = [&](int64_t k) {
         const float4* src =
-            reinterpret_cast<const float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16) + lane * 16);
+            reinterpret_cast<const float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16)) + lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ckn[q] = src[q];
+        for (int q = 0; q < 4; ++q) ckn[q] = src[64 * q];
     };
     load_tile<Tin, Tout, NW, true>(a, b, h, g, (ntiles - 1) * kT2, nx);
 
