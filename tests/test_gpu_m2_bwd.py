@@ -125,3 +125,19 @@ def test_full_size_sampled(gpu):
         got = {"dx": g["dx"][b:b + 1, :, heads], "ddt": g["ddt"][b:b + 1, :, heads], "dz": g["dz"][b:b + 1, :, heads],
                "dB": g["dB"][b:b + 1], "dC": g["dC"][b:b + 1]}
         _check(got, r, names=("dx", "ddt", "dz", "dB", "dC"))
+
+
+def test_caller_workspace(gpu):
+    """A caller-provided workspace gives the same gradients bit for bit; one
+    byte too small is refused."""
+    m, dout, _ = _case(1, 100, 4, 2, 64, torch.bfloat16, seed=17)
+    args = (m["x"], m["dt"], m["A"], m["B"], m["C"], m["D"], m["z"], m["dt_bias"], dout)
+    n = ss.mamba2_bwd_workspace_bytes(1, 100, 4, 64, 2, 64, ss.BF16, ss.F32)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    a = ss.mamba2_bwd(*args)
+    b = ss.mamba2_bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    with pytest.raises(ss.SelscanError):
+        ss.mamba2_bwd(*args, workspace=ws[:n - 1])
