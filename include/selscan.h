@@ -259,7 +259,9 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* shape,
 
 /* Bytes of workspace selscan_mamba2_bwd needs for `shape` (0 on a bad
  * shape): per (batch, head) the state entering every 8-token tile
- * (64 x N fp32 each) and the head's share of dB and dC (2 x L x N fp32). */
+ * (64 x N fp32 each, i.e. 4 KiB per token and head at N = 128) and the
+ * head's share of dB and dC (2 x L x N fp32).  It grows with
+ * batch x seqlen x nheads: 5.4 GB for batch 8, seqlen 4096, 32 heads. */
 size_t selscan_mamba2_bwd_workspace_bytes(const selscan_m2_shape_t* shape);
 
 /*
@@ -285,7 +287,9 @@ size_t selscan_mamba2_bwd_workspace_bytes(const selscan_m2_shape_t* shape);
  *                                         is NULL)
  *   dh0         [B, H, P, N]  fp32        (written; NULL = skip)
  * headdim P = 64 only (SELSCAN_ERR_UNSUPPORTED otherwise); N in
- * {16, 32, 64, 128}.  Gradients must not alias inputs or each other.  Sums
+ * {16, 32, 64, 128}.  One workgroup per (batch, head) walks the whole
+ * sequence: time is not split, so few (batch, head) units leave most of the
+ * GPU idle.  Gradients must not alias inputs or each other.  Sums
  * over heads, channels, batches and time run in a fixed order: results are
  * reproducible bit for bit.  shape->workspace as for selscan_mamba2_fwd,
  * sized by selscan_mamba2_bwd_workspace_bytes.  Errors as for
