@@ -148,10 +148,12 @@ struct M2BwdArgs {
     int64_t batch, L, H, G, N;
     int softplus;
     int in_bf16;
+    int ck_shift;     // checkpoint records every 2^ck_shift 8-token tiles
 };
 size_t m2_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t N);
 void m2_bwd_carve(M2BwdArgs& a, void* ws);
-hipError_t launch_m2_bwd(const M2BwdArgs& a, int in_bf16, int out_bf16, hipStream_t stream);
+// ssd: the chunked matrix form (N in {32, 64, 128}; N = 16 always takes the recurrent form)
+hipError_t launch_m2_bwd(const M2BwdArgs& a, int in_bf16, int out_bf16, int ssd, hipStream_t stream);
 
 // One-token state update (decoding), both variants.  Mamba-1: u, delta, z, y
 // [batch, dim]; B, C [batch, N]; A [dim, N]; D, bias [dim]; state

@@ -227,10 +227,15 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_ck_kernel(M2BwdArgs a) {
         const int buf = (int)(k & 1);
         if (k + 2 < ntiles) load_tile<Tin, Tin, NW, false>(a, b, h, g, (k + 2) * kT2, mine);
         // checkpoint record of (tile, wave): piece q of every lane's 16 states
-        // together, so that each store covers 1 KB of consecutive bytes
-        float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16)) + lane;
+        // together, so that each store covers 1 KB of consecutive bytes; one
+        // record every 2^ck_shift tiles
+        if ((k & ((1 << a.ck_shift) - 1)) == 0) {
+            const int64_t rec = k >> a.ck_shift, nrec = ((ntiles - 1) >> a.ck_shift) + 1;
+            float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * nrec + rec) * NW + w) * (kP * 16)) + lane;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dst[64 * q] = make_float4(hs[4 * q], hs[4 * q + 1], hs[4 * q + 2], hs[4 * q + 3]);
+            for (int q = 0; q < 4; ++q)
+                dst[64 * q] = make_float4(hs[4 * q], hs[4 * q + 1], hs[4 * q + 2], hs[4 * q + 3]);
+        }
 #pragma unroll
         for (int j = 0; j < kT2; ++j) {
             const float xw = xws[buf][j][lane], av = Aa[buf][j];
@@ -447,6 +452,439 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_kernel(M2BwdArgs a) {
     }
 }
 
+// ---------------- chunked matrix form ---------------------------------------
+// The same gradients regrouped over 32-token chunks as matrix products (the
+// state-space-duality form the README's Mamba-2 section names), on the
+// matrix cores.  With, inside a chunk, cum_t = A sum_{s <= t} Delta_s,
+// F[t,s] = exp(cum_t - cum_s) Delta_s (s <= t, else 0), G = C B^T,
+// M = G o F, W_s = exp(cum_last - cum_s) Delta_s, S_in the state entering
+// the chunk (a checkpoint) and dS the adjoint of the state leaving it:
+//   y       = M X + exp(cum) o (C S_in^T) + D X
+//   dX      = M^T dY + W o (B dS^T) + D dY
+//   dC      = (dM o F) B + (exp(cum) o dY) S_in,      dM = dY X^T
+//   dB      = (dM o F)^T C + W o (X dS)
+//   dS_in   = exp(cum_last) dS + (exp(cum) o dY)^T C
+// and the scalar paths through F, exp(cum) and W collect into dcum_t and
+// the direct dDelta_s; dDelta_s += A sum_{t >= s} dcum_t.  Every product is
+// a v_mfma_f32_16x16x32_bf16 contraction.  Operands sit in LDS as bf16
+// planes, row-major: x, B and C (bf16 inputs) exactly, the fp32 ones (dY,
+// exp(cum) o dY, S_in, dS, M, dM o F) as hi + lo planes (hi*hi + hi*lo +
+// lo*hi, relative error near 2^-16).  A fragment whose k runs along a row
+// is one 16-byte read; one whose k runs down a column comes from two
+// transposing reads (ds_read_b64_tr_b16).  bf16 inputs only.
+constexpr int kQs = 32;    // tokens per chunk (4 checkpoint tiles)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
+
+__device__ __forceinline__ uint16_t bfbits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ float bfval(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// v as a bf16 pair hi + lo
+__device__ __forceinline__ void put2(uint16_t* hi, uint16_t* lo, float v) {
+    const uint16_t hb = bfbits(v);
+    *hi = hb;
+    *lo = bfbits(v - bfval(hb));
+}
+
+// fragment of 8 consecutive k from a row (16-byte aligned)
+__device__ __forceinline__ bf16x8_t frag_row(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+// lane (g, i) of the wave: k = r0 + 8 g .. + 7 down column c0 + i of a
+// row-major plane with row stride rs (two transposing reads)
+__device__ __forceinline__ bf16x8_t frag_col(const uint16_t* m, int rs, int r0, int c0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, a = lane & 15;
+    const uint16_t* p = m + (r0 + 8 * g + (a >> 2)) * rs + c0 + 4 * (a & 3);
+    const s16x4_t u = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p));
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p + 4 * rs));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(u, v, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// An MFMA operand in LDS: hi (and lo) planes, row stride rs; kc: k runs
+// along the plane's rows (A: plane[row][k], B: plane[col][k]), else down
+// its columns (A: plane[k][row], B: plane[k][col]).
+struct Op {
+    const uint16_t* hi;
+    const uint16_t* lo;   // nullptr: exact in bf16
+    int rs;
+    bool kc;
+};
+__device__ __forceinline__ bf16x8_t frag(const Op& o, const uint16_t* plane, int idx0, int k0) {
+    const int lane = threadIdx.x & 63;
+    return o.kc ? frag_row(plane + (idx0 + (lane & 15)) * o.rs + k0 + 8 * (lane >> 4)) : frag_col(plane, o.rs, k0, idx0);
+}
+// acc += A[16 rows from r0] x B[16 cols from c0] over k = k0 .. k0 + K - 1
+template <int K>
+__device__ __forceinline__ f32x4_t mma(f32x4_t acc, const Op& A, int r0, const Op& B, int c0, int ka = 0, int kb = 0) {
+#pragma unroll
+    for (int kk = 0; kk < K; kk += 32) {
+        const bf16x8_t ah = frag(A, A.hi, r0, ka + kk), bh = frag(B, B.hi, c0, kb + kk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        if (B.lo) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, frag(B, B.lo, c0, kb + kk), acc, 0, 0, 0);
+        if (A.lo) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag(A, A.lo, r0, ka + kk), bh, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <int N>
+struct SsdSmem {
+    static constexpr int RP = kP + 8, RN = N + 16, RQ = kQs + 8;   // padded row strides (elements)
+    alignas(16) uint16_t Xh[kQs][RP];
+    alignas(16) uint16_t DYh[kQs][RP], DYl[kQs][RP];
+    alignas(16) uint16_t EYh[kQs][RP], EYl[kQs][RP];       // exp(cum) o dY
+    alignas(16) uint16_t Bh[kQs][RN], Ch[kQs][RN];
+    alignas(16) uint16_t S0h[kP][RN], S0l[kP][RN];
+    alignas(16) uint16_t dSh[kP][RN], dSl[kP][RN];
+    alignas(16) uint16_t Mh[kQs][RQ], Ml[kQs][RQ];
+    alignas(16) uint16_t Kh[kQs][RQ], Kl[kQs][RQ];         // dM o F
+    float Gm[kQs][kQs + 1], dM[kQs][kQs + 1];
+    float dl[kQs], cum[kQs], ecum[kQs], Wv[kQs], em[kQs], dv[kQs];
+    float Zf[kQs][kP];   // dout sigma(z) (1 + z (1 - sigma(z))): dz = Zf o (gate's input)
+    float dDl[kQs], colMM[kQs], rowMM[kQs];
+    float dWp[N / 16][kQs], yyp[kP / 16][kQs];
+    float red[8];
+};
+
+template <typename Tout, int N, bool SP>
+__global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
+    constexpr int NW = N / 16, RP = SsdSmem<N>::RP, RN = SsdSmem<N>::RN, RQ = SsdSmem<N>::RQ;
+    constexpr int TND = N / 16;                     // column tiles of the 64 x N state
+    __shared__ SsdSmem<N> sm;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, gq = lane >> 4, li = lane & 15;
+    const int64_t bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
+    const float Ah = a.A[h], biash = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    const bool has_z = a.z != nullptr;
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
+    const uint16_t* Zp = reinterpret_cast<const uint16_t*>(a.z);
+    const uint16_t* DT = reinterpret_cast<const uint16_t*>(a.dt);
+    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(a.B);
+    const uint16_t* Cp = reinterpret_cast<const uint16_t*>(a.C);
+    const Tout* DO = reinterpret_cast<const Tout*>(a.dout);
+    const int64_t nch = (a.L + kQs - 1) / kQs;
+
+    const Op opX{&sm.Xh[0][0], nullptr, RP, true}, opXt{&sm.Xh[0][0], nullptr, RP, false};
+    const Op opDYt{&sm.DYh[0][0], &sm.DYl[0][0], RP, false}, opDY{&sm.DYh[0][0], &sm.DYl[0][0], RP, true};
+    const Op opEY{&sm.EYh[0][0], &sm.EYl[0][0], RP, true}, opEYt{&sm.EYh[0][0], &sm.EYl[0][0], RP, false};
+    const Op opB{&sm.Bh[0][0], nullptr, RN, true}, opBt{&sm.Bh[0][0], nullptr, RN, false};
+    const Op opC{&sm.Ch[0][0], nullptr, RN, true}, opCt{&sm.Ch[0][0], nullptr, RN, false};
+    const Op opS0{&sm.S0h[0][0], &sm.S0l[0][0], RN, true}, opS0t{&sm.S0h[0][0], &sm.S0l[0][0], RN, false};
+    const Op opdS{&sm.dSh[0][0], &sm.dSl[0][0], RN, true}, opdSt{&sm.dSh[0][0], &sm.dSl[0][0], RN, false};
+    const Op opM{&sm.Mh[0][0], &sm.Ml[0][0], RQ, true}, opMt{&sm.Mh[0][0], &sm.Ml[0][0], RQ, false};
+    const Op opK{&sm.Kh[0][0], &sm.Kl[0][0], RQ, true}, opKt{&sm.Kh[0][0], &sm.Kl[0][0], RQ, false};
+
+    // the adjoint of the state leaving the current chunk: this wave's tiles
+    // (tile wv + 4 j of the 4 x TND tiles of 16 x 16) in registers
+    f32x4_t dSr[TND];
+#pragma unroll
+    for (int j = 0; j < TND; ++j) dSr[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int e = tid; e < kP * RN; e += 256) {
+        (&sm.dSh[0][0])[e] = 0;
+        (&sm.dSl[0][0])[e] = 0;
+    }
+    float accD = 0.0f, accA = 0.0f, accBias = 0.0f;
+
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t t0 = c * kQs;
+        // ---- stage: every global read of the chunk is issued up front as
+        //      16-byte loads (one latency per chunk), then x, B, C (exact),
+        //      dY and S_in go to their planes and dout's gate factor to Zf
+        const int st = tid >> 3, sq = tid & 7;   // token, 8-channel segment
+        const bool sok = t0 + st < a.L;
+        const int64_t sgi = ((b * a.L + t0 + st) * a.H + h) * kP + 8 * sq;
+        uint4 xr = {0u, 0u, 0u, 0u}, zr = {0u, 0u, 0u, 0u};
+        float dov[8];
+        if constexpr (sizeof(Tout) == 4) {
+            float4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
+            if (sok) {
+                d0 = *reinterpret_cast<const float4*>(DO + sgi);
+                d1 = *reinterpret_cast<const float4*>(DO + sgi + 4);
+            }
+            dov[0] = d0.x; dov[1] = d0.y; dov[2] = d0.z; dov[3] = d0.w;
+            dov[4] = d1.x; dov[5] = d1.y; dov[6] = d1.z; dov[7] = d1.w;
+        } else {
+            uint4 dr = {0u, 0u, 0u, 0u};
+            if (sok) dr = *reinterpret_cast<const uint4*>(DO + sgi);
+            const uint32_t w4[4] = {dr.x, dr.y, dr.z, dr.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dov[2 * i] = __uint_as_float(w4[i] << 16);
+                dov[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+            }
+        }
+        if (sok) {
+            xr = *reinterpret_cast<const uint4*>(X + sgi);
+            if (has_z) zr = *reinterpret_cast<const uint4*>(Zp + sgi);
+        }
+        constexpr int SEG = N / 8, NBC = (kQs * SEG + 255) / 256;
+        uint4 br[NBC], cr[NBC];
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) {
+            const int e = tid + 256 * i, t = e / SEG, sg8 = e - t * SEG;
+            br[i] = cr[i] = uint4{0u, 0u, 0u, 0u};
+            if (e < kQs * SEG && t0 + t < a.L) {
+                const int64_t gi = ((b * a.L + t0 + t) * a.G + g) * N + 8 * sg8;
+                br[i] = *reinterpret_cast<const uint4*>(Bp + gi);
+                cr[i] = *reinterpret_cast<const uint4*>(Cp + gi);
+            }
+        }
+        float4 ckr[NW];
+        {
+            const float4* src = reinterpret_cast<const float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
+#pragma unroll
+            for (int w = 0; w < NW; ++w) ckr[w] = src[256 * w + tid];
+        }
+        float dtv = 0.0f;
+        if (wv == 0 && lane < kQs && t0 + lane < a.L) dtv = bfval(DT[(b * a.L + t0 + lane) * a.H + h]);
+
+        *reinterpret_cast<uint4*>(&sm.Xh[st][8 * sq]) = xr;
+        {
+            const uint32_t zw[4] = {zr.x, zr.y, zr.z, zr.w};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hp = 0u, lp = 0u;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int j = 2 * i + k;
+                    float dy = dov[j];
+                    if (has_z) {
+                        const float zz = __uint_as_float(k ? (zw[i] & 0xffff0000u) : (zw[i] << 16));
+                        const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+                        sm.Zf[st][8 * sq + j] = dov[j] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+                        dy = dov[j] * zz * sg;
+                    }
+                    const uint16_t hb = bfbits(dy), lb = bfbits(dy - bfval(hb));
+                    hp |= (uint32_t)hb << (16 * k);
+                    lp |= (uint32_t)lb << (16 * k);
+                }
+                hw[i] = hp;
+                lw[i] = lp;
+            }
+            *reinterpret_cast<uint4*>(&sm.DYh[st][8 * sq]) = uint4{hw[0], hw[1], hw[2], hw[3]};
+            *reinterpret_cast<uint4*>(&sm.DYl[st][8 * sq]) = uint4{lw[0], lw[1], lw[2], lw[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) {
+            const int e = tid + 256 * i, t = e / SEG, sg8 = e - t * SEG;
+            if (e < kQs * SEG) {
+                *reinterpret_cast<uint4*>(&sm.Bh[t][8 * sg8]) = br[i];
+                *reinterpret_cast<uint4*>(&sm.Ch[t][8 * sg8]) = cr[i];
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            // record float4 (w, q, p): state row p, columns 16 w + 4 q .. + 3
+            const int q = tid >> 6, p = tid & 63, n = 16 * w + 4 * q;
+            const float v[4] = {ckr[w].x, ckr[w].y, ckr[w].z, ckr[w].w};
+            uint32_t hw[2], lw[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint16_t h0b = bfbits(v[2 * i]), h1b = bfbits(v[2 * i + 1]);
+                hw[i] = (uint32_t)h0b | ((uint32_t)h1b << 16);
+                lw[i] = (uint32_t)bfbits(v[2 * i] - bfval(h0b)) | ((uint32_t)bfbits(v[2 * i + 1] - bfval(h1b)) << 16);
+            }
+            *reinterpret_cast<uint2*>(&sm.S0h[p][n]) = uint2{hw[0], hw[1]};
+            *reinterpret_cast<uint2*>(&sm.S0l[p][n]) = uint2{lw[0], lw[1]};
+        }
+        if (wv == 0 && lane < kQs) {
+            float dl, av, dvv;
+            const bool ok = t0 + lane < a.L;
+            tok_consts<SP>(dtv, ok, Ah, biash, dl, av, dvv);
+            float cs = dl * Ah;   // inclusive prefix of Delta A over the chunk
+#pragma unroll
+            for (int o = 1; o < kQs; o <<= 1) {
+                const float up = __shfl_up(cs, o, 64);
+                if (lane >= o) cs += up;
+            }
+            const float cl = __shfl(cs, kQs - 1, 64);
+            sm.dl[lane] = dl;
+            sm.cum[lane] = cs;
+            sm.ecum[lane] = __expf(cs);
+            sm.em[lane] = __expf(cl - cs);
+            sm.Wv[lane] = __expf(cl - cs) * dl;
+            sm.dv[lane] = dvv;
+        }
+        lds_barrier();
+
+        auto F = [&](int t, int s) { return s <= t ? __expf(sm.cum[t] - sm.cum[s]) * sm.dl[s] : 0.0f; };
+        // ---- G = C B^T, M = G o F (tiles 0..3); dM = dY X^T (tiles 4..7); exp(cum) o dY
+        for (int tile = wv; tile < 8; tile += 4) {
+            const int tm = (tile >> 1) & 1, tn = tile & 1;
+            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (tile < 4) {
+                acc = mma<N>(acc, opC, 16 * tm, opB, 16 * tn);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tm + 4 * gq + r, s = 16 * tn + li;
+                    sm.Gm[t][s] = acc[r];
+                    put2(&sm.Mh[t][s], &sm.Ml[t][s], acc[r] * F(t, s));
+                }
+            } else {
+                acc = mma<kP>(acc, opDY, 16 * tm, opX, 16 * tn);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.dM[16 * tm + 4 * gq + r][16 * tn + li] = acc[r];
+            }
+        }
+        for (int e = tid; e < kQs * kP; e += 256) {
+            const int t = e >> 6, p = e & 63;
+            put2(&sm.EYh[t][p], &sm.EYl[t][p], sm.ecum[t] * (bfval(sm.DYh[t][p]) + bfval(sm.DYl[t][p])));
+        }
+        lds_barrier();
+
+        // ---- y (for dz) = M X + exp(cum) o (C S_in^T) + D x, with its dY . Yint row sums;
+        //      dX = M^T dY + W o (B dS^T) + D dY;   dM o F;   scalar sums
+        for (int tile = wv; tile < 8; tile += 4) {
+            const int tm = tile >> 2, tn = tile & 3;
+            f32x4_t yi = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opM, 16 * tm, opXt, 16 * tn);
+            f32x4_t y0 = mma<N>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opC, 16 * tm, opS0, 16 * tn);
+            f32x4_t d1 = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opMt, 16 * tm, opDYt, 16 * tn);
+            f32x4_t d2 = mma<N>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opB, 16 * tm, opdS, 16 * tn);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tm + 4 * gq + r, p = 16 * tn + li;
+                const bool ok = t0 + t < a.L;
+                const int64_t gi = ((b * a.L + t0 + t) * a.H + h) * kP + p;
+                const float xv = bfval(sm.Xh[t][p]), dy = bfval(sm.DYh[t][p]) + bfval(sm.DYl[t][p]);
+                const float yint = sm.ecum[t] * y0[r];
+                if (has_z && ok) a.dz[gi] = sm.Zf[t][p] * (yi[r] + yint + Dh * xv);
+                if (ok) accD = __builtin_fmaf(dy, xv, accD);
+                if (ok) a.dx[gi] = d1[r] + sm.Wv[t] * d2[r] + Dh * dy;
+                const float yy = row_sum(dy * yint);
+                if (li == 0) sm.yyp[tn][t] = yy;
+            }
+        }
+        for (int e = tid; e < kQs * kQs; e += 256) {
+            const int t = e >> 5, s = e & 31;
+            put2(&sm.Kh[t][s], &sm.Kl[t][s], sm.dM[t][s] * F(t, s));
+        }
+        if (tid < kQs) {
+            const int s = tid;
+            float d1 = 0.0f, cm = 0.0f;
+            for (int t = s; t < kQs; ++t) {
+                const float e = __expf(sm.cum[t] - sm.cum[s]);
+                const float dm = sm.dM[t][s];
+                d1 += dm * sm.Gm[t][s] * e;
+                cm += dm * sm.Gm[t][s] * e * sm.dl[s];
+            }
+            sm.dDl[s] = d1;
+            sm.colMM[s] = cm;
+        } else if (tid < 2 * kQs) {
+            const int t = tid - kQs;
+            float rm = 0.0f;
+            for (int s = 0; s <= t; ++s) rm += sm.dM[t][s] * sm.Gm[t][s] * F(t, s);
+            sm.rowMM[t] = rm;
+        }
+        lds_barrier();
+
+        // ---- dC = (dM o F) B + (exp(cum) o dY) S_in;  dB = (dM o F)^T C + W o (X dS), dW
+        for (int tile = wv; tile < 2 * TND; tile += 4) {
+            const int tm = tile / TND, tn = tile - tm * TND;
+            f32x4_t dc = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opK, 16 * tm, opBt, 16 * tn);
+            dc = mma<kP>(dc, opEY, 16 * tm, opS0t, 16 * tn);
+            const f32x4_t db = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opKt, 16 * tm, opCt, 16 * tn);
+            const f32x4_t xd = mma<kP>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opX, 16 * tm, opdSt, 16 * tn);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 16 * tm + 4 * gq + r, n = 16 * tn + li;
+                if (t0 + s < a.L) {
+                    a.pC[(bh * a.L + t0 + s) * N + n] = dc[r];
+                    a.pB[(bh * a.L + t0 + s) * N + n] = db[r] + sm.Wv[s] * xd[r];
+                }
+                const float part = row_sum(xd[r] * bfval(sm.Bh[s][n]));
+                if (li == 0) sm.dWp[tn][s] = part;
+            }
+        }
+        // sum_{p,n} dS o S_in (the exp(cum_last) path), this wave's tiles
+        float sds = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TND; ++j) {
+            const int tile = wv + 4 * j, tm = tile / TND, tn = tile - tm * TND;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = 16 * tm + 4 * gq + r, n = 16 * tn + li;
+                sds += dSr[j][r] * (bfval(sm.S0h[p][n]) + bfval(sm.S0l[p][n]));
+            }
+        }
+        sds = wave_sum(sds);
+        if (lane == 0) sm.red[wv] = sds;
+        lds_barrier();
+
+        // ---- dS_in = exp(cum_last) dS + (exp(cum) o dY)^T C, into registers and the planes
+        {
+            const float ecl = sm.ecum[kQs - 1];
+#pragma unroll
+            for (int j = 0; j < TND; ++j) {
+                const int tile = wv + 4 * j, tm = tile / TND, tn = tile - tm * TND;
+                const f32x4_t u = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opEYt, 16 * tm, opCt, 16 * tn);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    dSr[j][r] = __builtin_fmaf(ecl, dSr[j][r], u[r]);
+                    const int p = 16 * tm + 4 * gq + r, n = 16 * tn + li;
+                    put2(&sm.dSh[p][n], &sm.dSl[p][n], dSr[j][r]);
+                }
+            }
+        }
+        // ---- per token: dcum, dDelta, ddt, and the chunk's share of dA, dbias, dD
+        if (wv == 0) {
+            const int t = lane;
+            float dW = 0.0f, dc = 0.0f;
+            if (t < kQs) {
+                float yy = 0.0f;
+                for (int tn = 0; tn < kP / 16; ++tn) yy += sm.yyp[tn][t];
+                for (int tn = 0; tn < N / 16; ++tn) dW += sm.dWp[tn][t];
+                dc = sm.rowMM[t] - sm.colMM[t] + yy - dW * sm.Wv[t];
+            }
+            // the last token also carries exp(cum_last)'s paths: sum_s dW_s W_s
+            // and exp(cum_last) sum dS o S_in
+            const float dwW = wave_sum(t < kQs ? dW * sm.Wv[t] : 0.0f);
+            const float sds_all = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+            if (t == kQs - 1) dc += dwW + sm.ecum[kQs - 1] * sds_all;
+            // rc_t = sum_{t' >= t} dcum_t' (a reversed inclusive scan over the lanes)
+            float rc = t < kQs ? dc : 0.0f;
+#pragma unroll
+            for (int o = 1; o < kQs; o <<= 1) {
+                const float dn = __shfl_down(rc, o, 64);
+                if (t + o < kQs) rc += dn;
+            }
+            if (t < kQs && t0 + t < a.L) {
+                const float dD = sm.dDl[t] + dW * sm.em[t] + Ah * rc;
+                const float dvt = dD * sm.dv[t];
+                a.ddt[(b * a.L + t0 + t) * a.H + h] = dvt;
+                accBias += dvt;
+                accA = __builtin_fmaf(sm.dl[t], rc, accA);
+            }
+        }
+        lds_barrier();
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int j = 0; j < TND; ++j) {
+            const int tile = wv + 4 * j, tm = tile / TND, tn = tile - tm * TND;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                a.dh0[(bh * kP + 16 * tm + 4 * gq + r) * N + 16 * tn + li] = dSr[j][r];
+        }
+    }
+    // dD = sum dY o x: every wave holds a share
+    accD = wave_sum(accD);
+    if (lane == 0) sm.red[wv] = accD;
+    lds_barrier();
+    if (wv == 0) {
+        accD = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+        accA = wave_sum(accA);
+        accBias = wave_sum(accBias);
+        if (lane == 0) {
+            a.pD[bh] = accD;
+            a.pA[bh] = accA;
+            a.pbias[bh] = accBias;
+        }
+    }
+}
+
 // dB, dC: sums of the per-head partials over the heads of each group, one
 // thread per (batch, token, group, n).
 __global__ __launch_bounds__(256) void m2_bwd_bc_reduce_kernel(M2BwdArgs a) {
@@ -481,14 +919,28 @@ __global__ __launch_bounds__(64) void m2_bwd_param_reduce_kernel(M2BwdArgs a) {
 }
 
 template <typename Tin, typename Tout, int NW>
-hipError_t launch_nw(const M2BwdArgs& a, hipStream_t stream) {
+hipError_t launch_nw(M2BwdArgs a, bool ssd, hipStream_t stream) {
     const dim3 grid((unsigned)(a.batch * a.H)), block(64 * NW);
+    // the chunked form takes bf16 inputs, N >= 32 and 16-byte aligned x, z, dout, B, C
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    ssd = ssd && NW >= 2 && sizeof(Tin) == 2 && al16(a.x) && al16(a.z) && al16(a.dout) && al16(a.B) && al16(a.C);
+    a.ck_shift = ssd ? 2 : 0;   // it needs the state entering each 32-token chunk
     {
         KTime kt("m2_bwd_checkpoint", stream);
         if (a.softplus)
             hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, true>), grid, block, 0, stream, a);
         else
             hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, false>), grid, block, 0, stream, a);
+    }
+    if constexpr (NW >= 2 && sizeof(Tin) == 2) {
+        if (ssd) {
+            KTime kt("m2_bwd_ssd", stream);
+            if (a.softplus)
+                hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, true>), grid, dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, false>), grid, dim3(256), 0, stream, a);
+            return hipGetLastError();
+        }
     }
     {
         KTime kt("m2_bwd_adjoint", stream);
@@ -501,12 +953,12 @@ hipError_t launch_nw(const M2BwdArgs& a, hipStream_t stream) {
 }
 
 template <typename Tin, typename Tout>
-hipError_t launch_dt(const M2BwdArgs& a, hipStream_t stream) {
+hipError_t launch_dt(const M2BwdArgs& a, bool ssd, hipStream_t stream) {
     switch (a.N) {
-        case 16: return launch_nw<Tin, Tout, 1>(a, stream);
-        case 32: return launch_nw<Tin, Tout, 2>(a, stream);
-        case 64: return launch_nw<Tin, Tout, 4>(a, stream);
-        default: return launch_nw<Tin, Tout, 8>(a, stream);
+        case 16: return launch_nw<Tin, Tout, 1>(a, false, stream);
+        case 32: return launch_nw<Tin, Tout, 2>(a, ssd, stream);
+        case 64: return launch_nw<Tin, Tout, 4>(a, ssd, stream);
+        default: return launch_nw<Tin, Tout, 8>(a, ssd, stream);
     }
 }
 
@@ -534,12 +986,12 @@ void m2_bwd_carve(M2BwdArgs& a, void* ws) {
     a.pbias = p + 2 * a.batch * a.H;
 }
 
-hipError_t launch_m2_bwd(const M2BwdArgs& a, int in_bf16, int out_bf16, hipStream_t stream) {
+hipError_t launch_m2_bwd(const M2BwdArgs& a, int in_bf16, int out_bf16, int ssd, hipStream_t stream) {
     hipError_t e;
     if (in_bf16)
-        e = out_bf16 ? launch_dt<uint16_t, uint16_t>(a, stream) : launch_dt<uint16_t, float>(a, stream);
+        e = out_bf16 ? launch_dt<uint16_t, uint16_t>(a, ssd, stream) : launch_dt<uint16_t, float>(a, ssd, stream);
     else
-        e = out_bf16 ? launch_dt<float, uint16_t>(a, stream) : launch_dt<float, float>(a, stream);
+        e = out_bf16 ? launch_dt<float, uint16_t>(a, ssd, stream) : launch_dt<float, float>(a, ssd, stream);
     if (e != hipSuccess) return e;
     {
         KTime kt("m2_bwd_bc_reduce", stream);

@@ -141,3 +141,38 @@ def test_caller_workspace(gpu):
         assert torch.equal(a[k], b[k]), k
     with pytest.raises(ss.SelscanError):
         ss.mamba2_bwd(*args, workspace=ws[:n - 1])
+
+
+# ---- the chunked matrix form (SELSCAN_M2_BWD_SSD=1) -----------------------
+
+@pytest.mark.parametrize("L", [1, 7, 31, 32, 33, 100, 301])
+def test_chunked_form_lengths(gpu, monkeypatch, L):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+    m, dout, _ = _case(1, L, 4, 2, 32, torch.bfloat16, seed=100 + L)
+    _check(*_run(m, dout))
+
+
+@pytest.mark.parametrize("N", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_chunked_form_state_sizes(gpu, monkeypatch, N, dtype):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+    m, dout, _ = _case(2, 77, 4, 1, N, dtype, seed=N + 1)
+    _check(*_run(m, dout))
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_chunked_form_h0_softplus(gpu, monkeypatch, softplus):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+    m, dout, h0 = _case(1, 70, 2, 1, 64, torch.float32, seed=7 + int(softplus), h0=True)
+    if not softplus:
+        m["dt"] = (m["dt"].abs() * 0.1).contiguous()
+        m["dt_bias"] = None
+    _check(*_run(m, dout, softplus=softplus, h0=h0))
+
+
+def test_chunked_form_groups_no_gate(gpu, monkeypatch):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+    m, dout, _ = _case(2, 50, 8, 4, 32, torch.bfloat16, seed=21)
+    _check(*_run(m, dout))
+    m, dout, _ = _case(1, 40, 2, 1, 64, torch.bfloat16, seed=22, gate=False, skip=False, bias=False)
+    _check(*_run(m, dout))
