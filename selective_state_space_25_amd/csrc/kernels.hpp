@@ -142,17 +142,18 @@ struct M2BwdArgs {
     const void* dout;
     float *dx, *ddt, *dA, *dB, *dC, *dD, *dz, *ddt_bias, *dh0;
     float* ck;        // [batch*H, tiles, N/16, 4, 64, 4] states entering each 8-token tile
+                      // (the chunked form: each 32-token chunk)
     float* pB;        // [batch*H, L, N] per-head dB
     float* pC;        // [batch*H, L, N] per-head dC
     float *pA, *pD, *pbias;   // [batch*H] per-(batch, head) sums
     int64_t batch, L, H, G, N;
     int softplus;
     int in_bf16;
-    int ck_shift;     // checkpoint records every 2^ck_shift 8-token tiles
 };
 size_t m2_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t N);
 void m2_bwd_carve(M2BwdArgs& a, void* ws);
-// ssd: the chunked matrix form (N in {32, 64, 128}; N = 16 always takes the recurrent form)
+// ssd: the chunked matrix form (bf16 inputs, N in {32, 64, 128}, 16-byte aligned
+// x, z, dout, B, C); otherwise the recurrent form
 hipError_t launch_m2_bwd(const M2BwdArgs& a, int in_bf16, int out_bf16, int ssd, hipStream_t stream);
 
 // One-token state update (decoding), both variants.  Mamba-1: u, delta, z, y

@@ -227,11 +227,9 @@ __global__ __launch_bounds__(64 * NW) void m2_bwd_ck_kernel(M2BwdArgs a) {
         const int buf = (int)(k & 1);
         if (k + 2 < ntiles) load_tile<Tin, Tin, NW, false>(a, b, h, g, (k + 2) * kT2, mine);
         // checkpoint record of (tile, wave): piece q of every lane's 16 states
-        // together, so that each store covers 1 KB of consecutive bytes; one
-        // record every 2^ck_shift tiles
-        if ((k & ((1 << a.ck_shift) - 1)) == 0) {
-            const int64_t rec = k >> a.ck_shift, nrec = ((ntiles - 1) >> a.ck_shift) + 1;
-            float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * nrec + rec) * NW + w) * (kP * 16)) + lane;
+        // together, so that each store covers 1 KB of consecutive bytes
+        {
+            float4* dst = reinterpret_cast<float4*>(a.ck + ((bh * ntiles + k) * NW + w) * (kP * 16)) + lane;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 dst[64 * q] = make_float4(hs[4 * q], hs[4 * q + 1], hs[4 * q + 2], hs[4 * q + 3]);
@@ -885,6 +883,113 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     }
 }
 
+// ---------------- chunk-entry states on the matrix cores --------------------
+// The chunked form needs only the state entering each chunk, and each
+// follows from the one before by a single product:
+//   S_out = exp(cum_last) S_in + (W o X)^T B,   W_s = exp(cum_last - cum_s) Delta_s.
+// The state is held transposed, S^T[n][p] = B^T (W o X) + ..., as MFMA
+// accumulators (rows n, columns p): a lane's four rows are then the four
+// consecutive n of one checkpoint float4.  Wave w owns the columns
+// p = 16 w .. 16 w + 15.  The next chunk's inputs are loaded while this one
+// is multiplied, and the LDS operands are double-buffered so that one
+// chunk's writes never meet the other's reads.
+template <int N, bool SP>
+__global__ __launch_bounds__(256) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
+    constexpr int NW = N / 16, SEG = N / 8, NBC = (kQs * SEG + 255) / 256;
+    constexpr int RP = kP + 8, RN = N + 16;
+    __shared__ alignas(16) uint16_t Bh[2][kQs][RN];
+    __shared__ alignas(16) uint16_t XWh[2][kQs][RP];
+    __shared__ alignas(16) uint16_t XWl[2][kQs][RP];
+    __shared__ float Ws[2][kQs], Es[2];
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, gq = lane >> 4, li = lane & 15;
+    const int64_t bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
+    const float Ah = a.A[h], biash = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
+    const uint16_t* Bp = reinterpret_cast<const uint16_t*>(a.B);
+    const uint16_t* DT = reinterpret_cast<const uint16_t*>(a.dt);
+    const int64_t nch = (a.L + kQs - 1) / kQs;
+    const int st = tid >> 3, sq = tid & 7;   // token, 8-channel segment of x
+
+    f32x4_t acc[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc[j][r] = a.h0 ? a.h0[(bh * kP + 16 * wv + li) * N + 16 * j + 4 * gq + r] : 0.0f;
+
+    uint4 xr, br[NBC];
+    float dtv;
+    auto load = [&](int64_t c) {
+        const int64_t t0 = c * kQs;
+        xr = uint4{0u, 0u, 0u, 0u};
+        if (t0 + st < a.L) xr = *reinterpret_cast<const uint4*>(X + ((b * a.L + t0 + st) * a.H + h) * kP + 8 * sq);
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) {
+            const int e = tid + 256 * i, t = e / SEG, s8 = e - t * SEG;
+            br[i] = uint4{0u, 0u, 0u, 0u};
+            if (e < kQs * SEG && t0 + t < a.L)
+                br[i] = *reinterpret_cast<const uint4*>(Bp + ((b * a.L + t0 + t) * a.G + g) * N + 8 * s8);
+        }
+        dtv = 0.0f;
+        if (wv == 0 && lane < kQs && t0 + lane < a.L) dtv = bfval(DT[(b * a.L + t0 + lane) * a.H + h]);
+    };
+    if (nch > 1) load(0);
+    for (int64_t c = 0; c < nch; ++c) {
+        float4* dst = reinterpret_cast<float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            dst[256 * j + 64 * gq + 16 * wv + li] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        if (c + 1 == nch) break;
+        const int buf = (int)(c & 1);
+        if (wv == 0 && lane < kQs) {
+            float dl, av, dvv;
+            tok_consts<SP>(dtv, c * kQs + lane < a.L, Ah, biash, dl, av, dvv);
+            float cs = dl * Ah;   // inclusive prefix of Delta A over the chunk
+#pragma unroll
+            for (int o = 1; o < kQs; o <<= 1) {
+                const float up = __shfl_up(cs, o, 64);
+                if (lane >= o) cs += up;
+            }
+            const float cl = __shfl(cs, kQs - 1, 64);
+            Ws[buf][lane] = __expf(cl - cs) * dl;
+            if (lane == 0) Es[buf] = __expf(cl);
+        }
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) {
+            const int e = tid + 256 * i, t = e / SEG, s8 = e - t * SEG;
+            if (e < kQs * SEG) *reinterpret_cast<uint4*>(&Bh[buf][t][8 * s8]) = br[i];
+        }
+        const uint4 xc = xr;
+        if (c + 2 < nch) load(c + 1);   // the last chunk never updates the state
+        lds_barrier();
+        {
+            const float wt = Ws[buf][st];
+            const uint32_t xw4[4] = {xc.x, xc.y, xc.z, xc.w};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v0 = wt * __uint_as_float(xw4[i] << 16), v1 = wt * __uint_as_float(xw4[i] & 0xffff0000u);
+                const uint16_t h0b = bfbits(v0), h1b = bfbits(v1);
+                hw[i] = (uint32_t)h0b | ((uint32_t)h1b << 16);
+                lw[i] = (uint32_t)bfbits(v0 - bfval(h0b)) | ((uint32_t)bfbits(v1 - bfval(h1b)) << 16);
+            }
+            *reinterpret_cast<uint4*>(&XWh[buf][st][8 * sq]) = uint4{hw[0], hw[1], hw[2], hw[3]};
+            *reinterpret_cast<uint4*>(&XWl[buf][st][8 * sq]) = uint4{lw[0], lw[1], lw[2], lw[3]};
+        }
+        lds_barrier();
+        const float ecl = Es[buf];
+        const bf16x8_t xh = frag_col(&XWh[buf][0][0], RP, 0, 16 * wv);
+        const bf16x8_t xl = frag_col(&XWl[buf][0][0], RP, 0, 16 * wv);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const bf16x8_t bf = frag_col(&Bh[buf][0][0], RN, 0, 16 * j);
+            f32x4_t s = acc[j] * ecl;
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xh, s, 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xl, s, 0, 0, 0);
+        }
+    }
+}
+
 // dB, dC: sums of the per-head partials over the heads of each group, one
 // thread per (batch, token, group, n).
 __global__ __launch_bounds__(256) void m2_bwd_bc_reduce_kernel(M2BwdArgs a) {
@@ -924,16 +1029,15 @@ hipError_t launch_nw(M2BwdArgs a, bool ssd, hipStream_t stream) {
     // the chunked form takes bf16 inputs, N >= 32 and 16-byte aligned x, z, dout, B, C
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     ssd = ssd && NW >= 2 && sizeof(Tin) == 2 && al16(a.x) && al16(a.z) && al16(a.dout) && al16(a.B) && al16(a.C);
-    a.ck_shift = ssd ? 2 : 0;   // it needs the state entering each 32-token chunk
-    {
-        KTime kt("m2_bwd_checkpoint", stream);
-        if (a.softplus)
-            hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, true>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, false>), grid, block, 0, stream, a);
-    }
     if constexpr (NW >= 2 && sizeof(Tin) == 2) {
         if (ssd) {
+            {
+                KTime kt("m2_bwd_chunk_state", stream);
+                if (a.softplus)
+                    hipLaunchKernelGGL((m2_bwd_chunk_state_kernel<16 * NW, true>), grid, dim3(256), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((m2_bwd_chunk_state_kernel<16 * NW, false>), grid, dim3(256), 0, stream, a);
+            }
             KTime kt("m2_bwd_ssd", stream);
             if (a.softplus)
                 hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, true>), grid, dim3(256), 0, stream, a);
@@ -941,6 +1045,13 @@ hipError_t launch_nw(M2BwdArgs a, bool ssd, hipStream_t stream) {
                 hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, false>), grid, dim3(256), 0, stream, a);
             return hipGetLastError();
         }
+    }
+    {
+        KTime kt("m2_bwd_checkpoint", stream);
+        if (a.softplus)
+            hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((m2_bwd_ck_kernel<Tin, NW, false>), grid, block, 0, stream, a);
     }
     {
         KTime kt("m2_bwd_adjoint", stream);

@@ -578,7 +578,7 @@ selscan_status_t selscan_mamba2_bwd(const selscan_m2_shape_t* s, const void* x, 
                          (long long)s->seqlen, (long long)s->nheads, (long long)s->ngroups, (long long)s->dstate,
                          selscan::m2_bwd_workspace_bytes(s->batch, s->seqlen, s->nheads, s->dstate));
         hipError_t e = selscan::launch_m2_bwd(a, a.in_bf16, s->out_dtype == SELSCAN_BF16,
-                                              env_int("SELSCAN_M2_BWD_SSD", 0) != 0, hs);
+                                              env_int("SELSCAN_M2_BWD_SSD", 1) != 0, hs);
         ws.release();
         if (e != hipSuccess) return fail(SELSCAN_ERR_LAUNCH, std::string("kernel launch failed: ") + hipGetErrorString(e));
         return ok();

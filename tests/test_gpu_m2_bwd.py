@@ -9,7 +9,10 @@ batch x L x headdim (dA, dD, dt_bias), heads x headdim (dB, dC), headdim x N
 is bounded by the decay; with unit roundoff 2^-24 and at most ~1e5
 accumulated roundings the error stays below ~1e-3 of the typical size (rms)
 of that gradient where its terms cancel, and below 1e-4 relative where
-they do not: |gpu - ref| <= 1e-3 rms(ref) + 1e-4 |ref| per element."""
+they do not: |gpu - ref| <= 1e-3 rms(ref) + 1e-4 |ref| per element.  The
+chunked matrix form (the default for bf16 inputs and N >= 32) multiplies
+fp32 operands as bf16 hi + lo pairs, whose products carry a relative error
+near 2^-16 (1.5e-5), inside the same bound."""
 import numpy as np
 import pytest
 import torch
@@ -53,9 +56,9 @@ def _run(m, dout, softplus=True, h0=None):
     return g, r
 
 
-@pytest.mark.parametrize("L", [1, 7, 8, 9, 64, 301])
+@pytest.mark.parametrize("L", [1, 7, 8, 9, 31, 32, 33, 64, 100, 301])
 def test_lengths(gpu, L):
-    m, dout, _ = _case(1, L, 4, 2, 16, torch.bfloat16, seed=L)
+    m, dout, _ = _case(1, L, 4, 2, 32, torch.bfloat16, seed=L)
     _check(*_run(m, dout))
 
 
@@ -104,6 +107,16 @@ def test_reproducible_bitwise(gpu):
         assert torch.equal(a[k], b[k]), k
 
 
+def test_unaligned_tensors(gpu):
+    """An x that is not 16-byte aligned takes the recurrent form: same results."""
+    m, dout, _ = _case(1, 70, 2, 1, 64, torch.bfloat16, seed=31)
+    buf = torch.empty(m["x"].numel() + 1, dtype=m["x"].dtype, device=DEV)
+    xs = buf[1:].view(m["x"].shape)
+    xs.copy_(m["x"])
+    m["x"] = xs
+    _check(*_run(m, dout))
+
+
 def test_full_size_sampled(gpu):
     """The Mamba-2 multi-head workload (batch 8, L 4096, 32 heads x 64, N 128,
     one group): per-(batch, head) gradients of two heads in two batch
@@ -143,26 +156,27 @@ def test_caller_workspace(gpu):
         ss.mamba2_bwd(*args, workspace=ws[:n - 1])
 
 
-# ---- the chunked matrix form (SELSCAN_M2_BWD_SSD=1) -----------------------
+# ---- the recurrent form (SELSCAN_M2_BWD_SSD=0), which the tests above reach
+# only for fp32 inputs and N = 16 --------------------------------------------
 
 @pytest.mark.parametrize("L", [1, 7, 31, 32, 33, 100, 301])
-def test_chunked_form_lengths(gpu, monkeypatch, L):
-    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+def test_recurrent_form_lengths(gpu, monkeypatch, L):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "0")
     m, dout, _ = _case(1, L, 4, 2, 32, torch.bfloat16, seed=100 + L)
     _check(*_run(m, dout))
 
 
 @pytest.mark.parametrize("N", [32, 64, 128])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_chunked_form_state_sizes(gpu, monkeypatch, N, dtype):
-    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+def test_recurrent_form_state_sizes(gpu, monkeypatch, N, dtype):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "0")
     m, dout, _ = _case(2, 77, 4, 1, N, dtype, seed=N + 1)
     _check(*_run(m, dout))
 
 
 @pytest.mark.parametrize("softplus", [True, False])
-def test_chunked_form_h0_softplus(gpu, monkeypatch, softplus):
-    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+def test_recurrent_form_h0_softplus(gpu, monkeypatch, softplus):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "0")
     m, dout, h0 = _case(1, 70, 2, 1, 64, torch.float32, seed=7 + int(softplus), h0=True)
     if not softplus:
         m["dt"] = (m["dt"].abs() * 0.1).contiguous()
@@ -170,8 +184,8 @@ def test_chunked_form_h0_softplus(gpu, monkeypatch, softplus):
     _check(*_run(m, dout, softplus=softplus, h0=h0))
 
 
-def test_chunked_form_groups_no_gate(gpu, monkeypatch):
-    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "1")
+def test_recurrent_form_groups_no_gate(gpu, monkeypatch):
+    monkeypatch.setenv("SELSCAN_M2_BWD_SSD", "0")
     m, dout, _ = _case(2, 50, 8, 4, 32, torch.bfloat16, seed=21)
     _check(*_run(m, dout))
     m, dout, _ = _case(1, 40, 2, 1, 64, torch.bfloat16, seed=22, gate=False, skip=False, bias=False)
