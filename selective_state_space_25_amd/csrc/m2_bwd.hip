@@ -541,7 +541,7 @@ struct SsdSmem {
     float Gm[kQs][kQs + 1], dM[kQs][kQs + 1];
     float dl[kQs], cum[kQs], ecum[kQs], Wv[kQs], em[kQs], dv[kQs];
     float Zf[kQs][kP];   // dout sigma(z) (1 + z (1 - sigma(z))): dz = Zf o (gate's input)
-    float dDl[kQs], colMM[kQs], rowMM[kQs];
+    float colp[4][kQs], rowMM[kQs];   // per-wave column sums of V; row sums
     float dWp[N / 16][kQs], yyp[kP / 16][kQs];
     float red[8];
 };
@@ -585,16 +585,18 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     }
     float accD = 0.0f, accA = 0.0f, accBias = 0.0f;
 
-    for (int64_t c = nch - 1; c >= 0; --c) {
+    // a chunk's global inputs as 16-byte loads into registers, fetched while
+    // the chunk after it (the one before in this reverse walk) is computed
+    constexpr int SEG = N / 8, NBC = (kQs * SEG + 255) / 256;
+    const int st = tid >> 3, sq = tid & 7;   // token, 8-channel segment
+    uint4 xr, zr, br[NBC], cr[NBC];
+    float dov[8], dtv;
+    float4 ckr[NW];
+    auto fetch = [&](int64_t c) {
         const int64_t t0 = c * kQs;
-        // ---- stage: every global read of the chunk is issued up front as
-        //      16-byte loads (one latency per chunk), then x, B, C (exact),
-        //      dY and S_in go to their planes and dout's gate factor to Zf
-        const int st = tid >> 3, sq = tid & 7;   // token, 8-channel segment
         const bool sok = t0 + st < a.L;
         const int64_t sgi = ((b * a.L + t0 + st) * a.H + h) * kP + 8 * sq;
-        uint4 xr = {0u, 0u, 0u, 0u}, zr = {0u, 0u, 0u, 0u};
-        float dov[8];
+        xr = zr = uint4{0u, 0u, 0u, 0u};
         if constexpr (sizeof(Tout) == 4) {
             float4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
             if (sok) {
@@ -617,8 +619,6 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             xr = *reinterpret_cast<const uint4*>(X + sgi);
             if (has_z) zr = *reinterpret_cast<const uint4*>(Zp + sgi);
         }
-        constexpr int SEG = N / 8, NBC = (kQs * SEG + 255) / 256;
-        uint4 br[NBC], cr[NBC];
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
             const int e = tid + 256 * i, t = e / SEG, sg8 = e - t * SEG;
@@ -629,15 +629,18 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 cr[i] = *reinterpret_cast<const uint4*>(Cp + gi);
             }
         }
-        float4 ckr[NW];
-        {
-            const float4* src = reinterpret_cast<const float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
+        const float4* src = reinterpret_cast<const float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
 #pragma unroll
-            for (int w = 0; w < NW; ++w) ckr[w] = src[256 * w + tid];
-        }
-        float dtv = 0.0f;
+        for (int w = 0; w < NW; ++w) ckr[w] = src[256 * w + tid];
+        dtv = 0.0f;
         if (wv == 0 && lane < kQs && t0 + lane < a.L) dtv = bfval(DT[(b * a.L + t0 + lane) * a.H + h]);
+    };
+    fetch(nch - 1);
 
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t t0 = c * kQs;
+        // ---- stage: x, B, C (exact), dY and S_in to their planes, dout's
+        //      gate factor to Zf, from the registers fetched during the chunk after
         *reinterpret_cast<uint4*>(&sm.Xh[st][8 * sq]) = xr;
         {
             const uint32_t zw[4] = {zr.x, zr.y, zr.z, zr.w};
@@ -706,6 +709,7 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             sm.Wv[lane] = __expf(cl - cs) * dl;
             sm.dv[lane] = dvv;
         }
+        if (c > 0) fetch(c - 1);
         lds_barrier();
 
         auto F = [&](int t, int s) { return s <= t ? __expf(sm.cum[t] - sm.cum[s]) * sm.dl[s] : 0.0f; };
@@ -755,26 +759,38 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 if (li == 0) sm.yyp[tn][t] = yy;
             }
         }
-        for (int e = tid; e < kQs * kQs; e += 256) {
-            const int t = e >> 5, s = e & 31;
-            put2(&sm.Kh[t][s], &sm.Kl[t][s], sm.dM[t][s] * F(t, s));
-        }
-        if (tid < kQs) {
-            const int s = tid;
-            float d1 = 0.0f, cm = 0.0f;
-            for (int t = s; t < kQs; ++t) {
-                const float e = __expf(sm.cum[t] - sm.cum[s]);
+        // dM o F into its planes, and the sums over V = dM o G o exp(cum_t - cum_s)
+        // below the diagonal (s < t): rowMM_t = sum_s V Delta_s here, the column
+        // sums sum_t V as one partial per wave.  The diagonal enters dcum_t
+        // twice with opposite signs and is left out of both; the direct
+        // dDelta_s adds it back.  Thread: token t, columns 4 sb .. 4 sb + 3.
+        {
+            const int t = tid >> 3, sb = tid & 7;
+            const float ct = sm.cum[t];
+            float vs[4], row = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int s = 4 * sb + k;
+                const float e = s <= t ? __expf(ct - sm.cum[s]) : 0.0f;
                 const float dm = sm.dM[t][s];
-                d1 += dm * sm.Gm[t][s] * e;
-                cm += dm * sm.Gm[t][s] * e * sm.dl[s];
+                put2(&sm.Kh[t][s], &sm.Kl[t][s], dm * e * sm.dl[s]);
+                vs[k] = s < t ? dm * sm.Gm[t][s] * e : 0.0f;
+                row = __builtin_fmaf(vs[k], sm.dl[s], row);
             }
-            sm.dDl[s] = d1;
-            sm.colMM[s] = cm;
-        } else if (tid < 2 * kQs) {
-            const int t = tid - kQs;
-            float rm = 0.0f;
-            for (int s = 0; s <= t; ++s) rm += sm.dM[t][s] * sm.Gm[t][s] * F(t, s);
-            sm.rowMM[t] = rm;
+            row += __shfl_xor(row, 1, 64);
+            row += __shfl_xor(row, 2, 64);
+            row += __shfl_xor(row, 4, 64);
+            if (sb == 0) sm.rowMM[t] = row;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {   // over the wave's 8 tokens
+                vs[k] += __shfl_xor(vs[k], 8, 64);
+                vs[k] += __shfl_xor(vs[k], 16, 64);
+                vs[k] += __shfl_xor(vs[k], 32, 64);
+            }
+            if (lane < 8) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) sm.colp[wv][4 * lane + k] = vs[k];
+            }
         }
         lds_barrier();
 
@@ -829,12 +845,14 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         // ---- per token: dcum, dDelta, ddt, and the chunk's share of dA, dbias, dD
         if (wv == 0) {
             const int t = lane;
-            float dW = 0.0f, dc = 0.0f;
+            float dW = 0.0f, dc = 0.0f, dDl = 0.0f;
             if (t < kQs) {
                 float yy = 0.0f;
                 for (int tn = 0; tn < kP / 16; ++tn) yy += sm.yyp[tn][t];
                 for (int tn = 0; tn < N / 16; ++tn) dW += sm.dWp[tn][t];
-                dc = sm.rowMM[t] - sm.colMM[t] + yy - dW * sm.Wv[t];
+                const float col = sm.colp[0][t] + sm.colp[1][t] + sm.colp[2][t] + sm.colp[3][t];
+                dDl = col + sm.dM[t][t] * sm.Gm[t][t];
+                dc = sm.rowMM[t] - sm.dl[t] * col + yy - dW * sm.Wv[t];
             }
             // the last token also carries exp(cum_last)'s paths: sum_s dW_s W_s
             // and exp(cum_last) sum dS o S_in
@@ -849,7 +867,7 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 if (t + o < kQs) rc += dn;
             }
             if (t < kQs && t0 + t < a.L) {
-                const float dD = sm.dDl[t] + dW * sm.em[t] + Ah * rc;
+                const float dD = dDl + dW * sm.em[t] + Ah * rc;
                 const float dvt = dD * sm.dv[t];
                 a.ddt[(b * a.L + t0 + t) * a.H + h] = dvt;
                 accBias += dvt;
