@@ -527,6 +527,8 @@ __device__ __forceinline__ f32x4_t mma(f32x4_t acc, const Op& A, int r0, const O
     return acc;
 }
 
+constexpr int kSsdThreads = 512;   // 8 waves: two per SIMD
+
 template <int N>
 struct SsdSmem {
     static constexpr int RP = kP + 8, RN = N + 16, RQ = kQs + 8;   // padded row strides (elements)
@@ -541,15 +543,17 @@ struct SsdSmem {
     float Gm[kQs][kQs + 1], dM[kQs][kQs + 1];
     float dl[kQs], cum[kQs], ecum[kQs], Wv[kQs], em[kQs], dv[kQs];
     float Zf[kQs][kP];   // dout sigma(z) (1 + z (1 - sigma(z))): dz = Zf o (gate's input)
-    float colp[4][kQs], rowMM[kQs];   // per-wave column sums of V; row sums
+    float colp[kSsdThreads / 64][kQs], rowMM[kQs];   // per-wave column sums of V; row sums
     float dWp[N / 16][kQs], yyp[kP / 16][kQs];
     float red[8];
 };
 
 template <typename Tout, int N, bool SP>
-__global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
+__global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     constexpr int NW = N / 16, RP = SsdSmem<N>::RP, RN = SsdSmem<N>::RN, RQ = SsdSmem<N>::RQ;
     constexpr int TND = N / 16;                     // column tiles of the 64 x N state
+    constexpr int NT = kSsdThreads, NWV = NT / 64;   // threads, waves
+    constexpr int TPW = 4 * TND / NWV;              // state tiles per wave
     __shared__ SsdSmem<N> sm;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, gq = lane >> 4, li = lane & 15;
     const int64_t bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
@@ -575,11 +579,11 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     const Op opK{&sm.Kh[0][0], &sm.Kl[0][0], RQ, true}, opKt{&sm.Kh[0][0], &sm.Kl[0][0], RQ, false};
 
     // the adjoint of the state leaving the current chunk: this wave's tiles
-    // (tile wv + 4 j of the 4 x TND tiles of 16 x 16) in registers
-    f32x4_t dSr[TND];
+    // (tile wv + NWV j of the 4 x TND tiles of 16 x 16) in registers
+    f32x4_t dSr[TPW];
 #pragma unroll
-    for (int j = 0; j < TND; ++j) dSr[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int e = tid; e < kP * RN; e += 256) {
+    for (int j = 0; j < TPW; ++j) dSr[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int e = tid; e < kP * RN; e += NT) {
         (&sm.dSh[0][0])[e] = 0;
         (&sm.dSl[0][0])[e] = 0;
     }
@@ -587,41 +591,38 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 
     // a chunk's global inputs as 16-byte loads into registers, fetched while
     // the chunk after it (the one before in this reverse walk) is computed
-    constexpr int SEG = N / 8, NBC = (kQs * SEG + 255) / 256;
-    const int st = tid >> 3, sq = tid & 7;   // token, 8-channel segment
-    uint4 xr, zr, br[NBC], cr[NBC];
-    float dov[8], dtv;
-    float4 ckr[NW];
+    constexpr int SEG = N / 8, NBC = (kQs * SEG + NT - 1) / NT;
+    const int st = tid >> 4, sq = tid & 15;   // token, 4-channel segment
+    uint2 xr, zr;
+    uint4 br[NBC], cr[NBC];
+    float dov[4], dtv;
+    float4 ckr[NW / 2];
     auto fetch = [&](int64_t c) {
         const int64_t t0 = c * kQs;
         const bool sok = t0 + st < a.L;
-        const int64_t sgi = ((b * a.L + t0 + st) * a.H + h) * kP + 8 * sq;
-        xr = zr = uint4{0u, 0u, 0u, 0u};
+        const int64_t sgi = ((b * a.L + t0 + st) * a.H + h) * kP + 4 * sq;
+        xr = zr = uint2{0u, 0u};
         if constexpr (sizeof(Tout) == 4) {
-            float4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0;
-            if (sok) {
-                d0 = *reinterpret_cast<const float4*>(DO + sgi);
-                d1 = *reinterpret_cast<const float4*>(DO + sgi + 4);
-            }
+            float4 d0 = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (sok) d0 = *reinterpret_cast<const float4*>(DO + sgi);
             dov[0] = d0.x; dov[1] = d0.y; dov[2] = d0.z; dov[3] = d0.w;
-            dov[4] = d1.x; dov[5] = d1.y; dov[6] = d1.z; dov[7] = d1.w;
         } else {
-            uint4 dr = {0u, 0u, 0u, 0u};
-            if (sok) dr = *reinterpret_cast<const uint4*>(DO + sgi);
-            const uint32_t w4[4] = {dr.x, dr.y, dr.z, dr.w};
+            uint2 dr = {0u, 0u};
+            if (sok) dr = *reinterpret_cast<const uint2*>(DO + sgi);
+            const uint32_t w2[2] = {dr.x, dr.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dov[2 * i] = __uint_as_float(w4[i] << 16);
-                dov[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+            for (int i = 0; i < 2; ++i) {
+                dov[2 * i] = __uint_as_float(w2[i] << 16);
+                dov[2 * i + 1] = __uint_as_float(w2[i] & 0xffff0000u);
             }
         }
         if (sok) {
-            xr = *reinterpret_cast<const uint4*>(X + sgi);
-            if (has_z) zr = *reinterpret_cast<const uint4*>(Zp + sgi);
+            xr = *reinterpret_cast<const uint2*>(X + sgi);
+            if (has_z) zr = *reinterpret_cast<const uint2*>(Zp + sgi);
         }
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
-            const int e = tid + 256 * i, t = e / SEG, sg8 = e - t * SEG;
+            const int e = tid + NT * i, t = e / SEG, sg8 = e - t * SEG;
             br[i] = cr[i] = uint4{0u, 0u, 0u, 0u};
             if (e < kQs * SEG && t0 + t < a.L) {
                 const int64_t gi = ((b * a.L + t0 + t) * a.G + g) * N + 8 * sg8;
@@ -631,7 +632,7 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         }
         const float4* src = reinterpret_cast<const float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
 #pragma unroll
-        for (int w = 0; w < NW; ++w) ckr[w] = src[256 * w + tid];
+        for (int i = 0; i < NW / 2; ++i) ckr[i] = src[NT * i + tid];
         dtv = 0.0f;
         if (wv == 0 && lane < kQs && t0 + lane < a.L) dtv = bfval(DT[(b * a.L + t0 + lane) * a.H + h]);
     };
@@ -641,12 +642,12 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         const int64_t t0 = c * kQs;
         // ---- stage: x, B, C (exact), dY and S_in to their planes, dout's
         //      gate factor to Zf, from the registers fetched during the chunk after
-        *reinterpret_cast<uint4*>(&sm.Xh[st][8 * sq]) = xr;
+        *reinterpret_cast<uint2*>(&sm.Xh[st][4 * sq]) = xr;
         {
-            const uint32_t zw[4] = {zr.x, zr.y, zr.z, zr.w};
-            uint32_t hw[4], lw[4];
+            const uint32_t zw[2] = {zr.x, zr.y};
+            uint32_t hw[2], lw[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 2; ++i) {
                 uint32_t hp = 0u, lp = 0u;
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
@@ -655,7 +656,7 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                     if (has_z) {
                         const float zz = __uint_as_float(k ? (zw[i] & 0xffff0000u) : (zw[i] << 16));
                         const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
-                        sm.Zf[st][8 * sq + j] = dov[j] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+                        sm.Zf[st][4 * sq + j] = dov[j] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
                         dy = dov[j] * zz * sg;
                     }
                     const uint16_t hb = bfbits(dy), lb = bfbits(dy - bfval(hb));
@@ -665,22 +666,22 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 hw[i] = hp;
                 lw[i] = lp;
             }
-            *reinterpret_cast<uint4*>(&sm.DYh[st][8 * sq]) = uint4{hw[0], hw[1], hw[2], hw[3]};
-            *reinterpret_cast<uint4*>(&sm.DYl[st][8 * sq]) = uint4{lw[0], lw[1], lw[2], lw[3]};
+            *reinterpret_cast<uint2*>(&sm.DYh[st][4 * sq]) = uint2{hw[0], hw[1]};
+            *reinterpret_cast<uint2*>(&sm.DYl[st][4 * sq]) = uint2{lw[0], lw[1]};
         }
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
-            const int e = tid + 256 * i, t = e / SEG, sg8 = e - t * SEG;
+            const int e = tid + NT * i, t = e / SEG, sg8 = e - t * SEG;
             if (e < kQs * SEG) {
                 *reinterpret_cast<uint4*>(&sm.Bh[t][8 * sg8]) = br[i];
                 *reinterpret_cast<uint4*>(&sm.Ch[t][8 * sg8]) = cr[i];
             }
         }
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
+        for (int i = 0; i < NW / 2; ++i) {
             // record float4 (w, q, p): state row p, columns 16 w + 4 q .. + 3
-            const int q = tid >> 6, p = tid & 63, n = 16 * w + 4 * q;
-            const float v[4] = {ckr[w].x, ckr[w].y, ckr[w].z, ckr[w].w};
+            const int e4 = NT * i + tid, w = e4 >> 8, q = (e4 >> 6) & 3, p = e4 & 63, n = 16 * w + 4 * q;
+            const float v[4] = {ckr[i].x, ckr[i].y, ckr[i].z, ckr[i].w};
             uint32_t hw[2], lw[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 
         auto F = [&](int t, int s) { return s <= t ? __expf(sm.cum[t] - sm.cum[s]) * sm.dl[s] : 0.0f; };
         // ---- G = C B^T, M = G o F (tiles 0..3); dM = dY X^T (tiles 4..7); exp(cum) o dY
-        for (int tile = wv; tile < 8; tile += 4) {
+        for (int tile = wv; tile < 8; tile += NWV) {
             const int tm = (tile >> 1) & 1, tn = tile & 1;
             f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
             if (tile < 4) {
@@ -731,7 +732,7 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 for (int r = 0; r < 4; ++r) sm.dM[16 * tm + 4 * gq + r][16 * tn + li] = acc[r];
             }
         }
-        for (int e = tid; e < kQs * kP; e += 256) {
+        for (int e = tid; e < kQs * kP; e += NT) {
             const int t = e >> 6, p = e & 63;
             put2(&sm.EYh[t][p], &sm.EYl[t][p], sm.ecum[t] * (bfval(sm.DYh[t][p]) + bfval(sm.DYl[t][p])));
         }
@@ -739,7 +740,7 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 
         // ---- y (for dz) = M X + exp(cum) o (C S_in^T) + D x, with its dY . Yint row sums;
         //      dX = M^T dY + W o (B dS^T) + D dY;   dM o F;   scalar sums
-        for (int tile = wv; tile < 8; tile += 4) {
+        for (int tile = wv; tile < 8; tile += NWV) {
             const int tm = tile >> 2, tn = tile & 3;
             f32x4_t yi = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opM, 16 * tm, opXt, 16 * tn);
             f32x4_t y0 = mma<N>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opC, 16 * tm, opS0, 16 * tn);
@@ -763,14 +764,14 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         // below the diagonal (s < t): rowMM_t = sum_s V Delta_s here, the column
         // sums sum_t V as one partial per wave.  The diagonal enters dcum_t
         // twice with opposite signs and is left out of both; the direct
-        // dDelta_s adds it back.  Thread: token t, columns 4 sb .. 4 sb + 3.
+        // dDelta_s adds it back.  Thread: token t, columns 2 sb, 2 sb + 1.
         {
-            const int t = tid >> 3, sb = tid & 7;
+            const int t = tid >> 4, sb = tid & 15;
             const float ct = sm.cum[t];
-            float vs[4], row = 0.0f;
+            float vs[2], row = 0.0f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int s = 4 * sb + k;
+            for (int k = 0; k < 2; ++k) {
+                const int s = 2 * sb + k;
                 const float e = s <= t ? __expf(ct - sm.cum[s]) : 0.0f;
                 const float dm = sm.dM[t][s];
                 put2(&sm.Kh[t][s], &sm.Kl[t][s], dm * e * sm.dl[s]);
@@ -780,22 +781,22 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             row += __shfl_xor(row, 1, 64);
             row += __shfl_xor(row, 2, 64);
             row += __shfl_xor(row, 4, 64);
+            row += __shfl_xor(row, 8, 64);
             if (sb == 0) sm.rowMM[t] = row;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {   // over the wave's 8 tokens
-                vs[k] += __shfl_xor(vs[k], 8, 64);
+            for (int k = 0; k < 2; ++k) {   // over the wave's 4 tokens
                 vs[k] += __shfl_xor(vs[k], 16, 64);
                 vs[k] += __shfl_xor(vs[k], 32, 64);
             }
-            if (lane < 8) {
+            if (lane < 16) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) sm.colp[wv][4 * lane + k] = vs[k];
+                for (int k = 0; k < 2; ++k) sm.colp[wv][2 * lane + k] = vs[k];
             }
         }
         lds_barrier();
 
         // ---- dC = (dM o F) B + (exp(cum) o dY) S_in;  dB = (dM o F)^T C + W o (X dS), dW
-        for (int tile = wv; tile < 2 * TND; tile += 4) {
+        for (int tile = wv; tile < 2 * TND; tile += NWV) {
             const int tm = tile / TND, tn = tile - tm * TND;
             f32x4_t dc = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opK, 16 * tm, opBt, 16 * tn);
             dc = mma<kP>(dc, opEY, 16 * tm, opS0t, 16 * tn);
@@ -815,8 +816,8 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         // sum_{p,n} dS o S_in (the exp(cum_last) path), this wave's tiles
         float sds = 0.0f;
 #pragma unroll
-        for (int j = 0; j < TND; ++j) {
-            const int tile = wv + 4 * j, tm = tile / TND, tn = tile - tm * TND;
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wv + NWV * j, tm = tile / TND, tn = tile - tm * TND;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int p = 16 * tm + 4 * gq + r, n = 16 * tn + li;
@@ -831,8 +832,8 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         {
             const float ecl = sm.ecum[kQs - 1];
 #pragma unroll
-            for (int j = 0; j < TND; ++j) {
-                const int tile = wv + 4 * j, tm = tile / TND, tn = tile - tm * TND;
+            for (int j = 0; j < TPW; ++j) {
+                const int tile = wv + NWV * j, tm = tile / TND, tn = tile - tm * TND;
                 const f32x4_t u = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opEYt, 16 * tm, opCt, 16 * tn);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -850,14 +851,18 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 float yy = 0.0f;
                 for (int tn = 0; tn < kP / 16; ++tn) yy += sm.yyp[tn][t];
                 for (int tn = 0; tn < N / 16; ++tn) dW += sm.dWp[tn][t];
-                const float col = sm.colp[0][t] + sm.colp[1][t] + sm.colp[2][t] + sm.colp[3][t];
+                float col = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NWV; ++w) col += sm.colp[w][t];
                 dDl = col + sm.dM[t][t] * sm.Gm[t][t];
                 dc = sm.rowMM[t] - sm.dl[t] * col + yy - dW * sm.Wv[t];
             }
             // the last token also carries exp(cum_last)'s paths: sum_s dW_s W_s
             // and exp(cum_last) sum dS o S_in
             const float dwW = wave_sum(t < kQs ? dW * sm.Wv[t] : 0.0f);
-            const float sds_all = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+            float sds_all = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) sds_all += sm.red[w];
             if (t == kQs - 1) dc += dwW + sm.ecum[kQs - 1] * sds_all;
             // rc_t = sum_{t' >= t} dcum_t' (a reversed inclusive scan over the lanes)
             float rc = t < kQs ? dc : 0.0f;
@@ -878,8 +883,8 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     }
     if (a.dh0) {
 #pragma unroll
-        for (int j = 0; j < TND; ++j) {
-            const int tile = wv + 4 * j, tm = tile / TND, tn = tile - tm * TND;
+        for (int j = 0; j < TPW; ++j) {
+            const int tile = wv + NWV * j, tm = tile / TND, tn = tile - tm * TND;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 a.dh0[(bh * kP + 16 * tm + 4 * gq + r) * N + 16 * tn + li] = dSr[j][r];
@@ -890,7 +895,9 @@ __global__ __launch_bounds__(256) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     if (lane == 0) sm.red[wv] = accD;
     lds_barrier();
     if (wv == 0) {
-        accD = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+        accD = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) accD += sm.red[w];
         accA = wave_sum(accA);
         accBias = wave_sum(accBias);
         if (lane == 0) {
@@ -1058,9 +1065,9 @@ hipError_t launch_nw(M2BwdArgs a, bool ssd, hipStream_t stream) {
             }
             KTime kt("m2_bwd_ssd", stream);
             if (a.softplus)
-                hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, true>), grid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, true>), grid, dim3(kSsdThreads), 0, stream, a);
             else
-                hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, false>), grid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((m2_bwd_ssd_kernel<Tout, 16 * NW, false>), grid, dim3(kSsdThreads), 0, stream, a);
             return hipGetLastError();
         }
     }
