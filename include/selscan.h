@@ -259,9 +259,10 @@ selscan_status_t selscan_mamba2_fwd_h0(const selscan_m2_shape_t* shape,
 
 /* Bytes of workspace selscan_mamba2_bwd needs for `shape` (0 on a bad
  * shape): per (batch, head) the state entering every 8-token tile
- * (64 x N fp32 each, i.e. 4 KiB per token and head at N = 128) and the
- * head's share of dB and dC (2 x L x N fp32).  It grows with
- * batch x seqlen x nheads: 5.4 GB for batch 8, seqlen 4096, 32 heads. */
+ * (64 x N fp32 each, i.e. 4 KiB per token and head at N = 128; the chunked
+ * form below uses one state per 32 tokens of this space) and the head's
+ * share of dB and dC (2 x L x N fp32).  It grows with batch x seqlen x
+ * nheads: 5.4 GB for batch 8, seqlen 4096, 32 heads. */
 size_t selscan_mamba2_bwd_workspace_bytes(const selscan_m2_shape_t* shape);
 
 /*
@@ -270,8 +271,12 @@ size_t selscan_mamba2_bwd_workspace_bytes(const selscan_m2_shape_t* shape);
  * per token and head, B and C shared by the heads of a group).  For
  * out = selscan_mamba2_fwd_h0(...) and dout = d loss / d out, writes the
  * gradient of the loss with respect to every input; the states are
- * recomputed from the inputs (the recurrence in fp32, states entering every
- * 8-token tile kept in the workspace).
+ * recomputed from the inputs.  bf16 inputs with N >= 32 and 16-byte aligned
+ * x, z, dout, B, C take the chunked matrix form (32-token chunks, products
+ * on the matrix cores with fp32 operands split into bf16 hi + lo pairs, the
+ * state entering each chunk kept in the workspace; the environment variable
+ * SELSCAN_M2_BWD_SSD=0 turns it off); other calls take the recurrent form
+ * (fp32, the state entering every 8-token tile kept).
  *   x .. softplus, h0   as for selscan_mamba2_fwd_h0 (h0 NULL = zero state)
  *   dout        [B, L, H, P]  out_dtype   gradient of the output
  *   dx          [B, L, H, P]  fp32        (written)
