@@ -914,13 +914,13 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 //   S_out = exp(cum_last) S_in + (W o X)^T B,   W_s = exp(cum_last - cum_s) Delta_s.
 // The state is held transposed, S^T[n][p] = B^T (W o X) + ..., as MFMA
 // accumulators (rows n, columns p): a lane's four rows are then the four
-// consecutive n of one checkpoint float4.  Wave w owns the columns
-// p = 16 w .. 16 w + 15.  The next chunk's inputs are loaded while this one
+// consecutive n of one checkpoint float4.  Eight waves (two per SIMD):
+// wave w owns the columns p = 16 (w & 3) .. + 15 and half of the rows n.  The next chunk's inputs are loaded while this one
 // is multiplied, and the LDS operands are double-buffered so that one
 // chunk's writes never meet the other's reads.
 template <int N, bool SP>
-__global__ __launch_bounds__(256) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
-    constexpr int NW = N / 16, SEG = N / 8, NBC = (kQs * SEG + 255) / 256;
+__global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
+    constexpr int NW = N / 16, SEG = N / 8, NT = 512, NBC = (kQs * SEG + NT - 1) / NT, NJ = NW / 2;
     constexpr int RP = kP + 8, RN = N + 16;
     __shared__ alignas(16) uint16_t Bh[2][kQs][RN];
     __shared__ alignas(16) uint16_t XWh[2][kQs][RP];
@@ -933,24 +933,26 @@ __global__ __launch_bounds__(256) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
     const uint16_t* Bp = reinterpret_cast<const uint16_t*>(a.B);
     const uint16_t* DT = reinterpret_cast<const uint16_t*>(a.dt);
     const int64_t nch = (a.L + kQs - 1) / kQs;
-    const int st = tid >> 3, sq = tid & 7;   // token, 8-channel segment of x
+    const int st = tid >> 4, sq = tid & 15;   // token, 4-channel segment of x
+    const int pb = wv & 3, j0 = (wv >> 2) * NJ;   // this wave's column block, first row block
 
-    f32x4_t acc[NW];
+    f32x4_t acc[NJ];
 #pragma unroll
-    for (int j = 0; j < NW; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            acc[j][r] = a.h0 ? a.h0[(bh * kP + 16 * wv + li) * N + 16 * j + 4 * gq + r] : 0.0f;
+            acc[j][r] = a.h0 ? a.h0[(bh * kP + 16 * pb + li) * N + 16 * (j0 + j) + 4 * gq + r] : 0.0f;
 
-    uint4 xr, br[NBC];
+    uint2 xr;
+    uint4 br[NBC];
     float dtv;
     auto load = [&](int64_t c) {
         const int64_t t0 = c * kQs;
-        xr = uint4{0u, 0u, 0u, 0u};
-        if (t0 + st < a.L) xr = *reinterpret_cast<const uint4*>(X + ((b * a.L + t0 + st) * a.H + h) * kP + 8 * sq);
+        xr = uint2{0u, 0u};
+        if (t0 + st < a.L) xr = *reinterpret_cast<const uint2*>(X + ((b * a.L + t0 + st) * a.H + h) * kP + 4 * sq);
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
-            const int e = tid + 256 * i, t = e / SEG, s8 = e - t * SEG;
+            const int e = tid + NT * i, t = e / SEG, s8 = e - t * SEG;
             br[i] = uint4{0u, 0u, 0u, 0u};
             if (e < kQs * SEG && t0 + t < a.L)
                 br[i] = *reinterpret_cast<const uint4*>(Bp + ((b * a.L + t0 + t) * a.G + g) * N + 8 * s8);
@@ -962,8 +964,8 @@ __global__ __launch_bounds__(256) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
     for (int64_t c = 0; c < nch; ++c) {
         float4* dst = reinterpret_cast<float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
 #pragma unroll
-        for (int j = 0; j < NW; ++j)
-            dst[256 * j + 64 * gq + 16 * wv + li] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        for (int j = 0; j < NJ; ++j)
+            dst[256 * (j0 + j) + 64 * gq + 16 * pb + li] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         if (c + 1 == nch) break;
         const int buf = (int)(c & 1);
         if (wv == 0 && lane < kQs) {
@@ -981,33 +983,33 @@ __global__ __launch_bounds__(256) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
-            const int e = tid + 256 * i, t = e / SEG, s8 = e - t * SEG;
+            const int e = tid + NT * i, t = e / SEG, s8 = e - t * SEG;
             if (e < kQs * SEG) *reinterpret_cast<uint4*>(&Bh[buf][t][8 * s8]) = br[i];
         }
-        const uint4 xc = xr;
+        const uint2 xc = xr;
         if (c + 2 < nch) load(c + 1);   // the last chunk never updates the state
         lds_barrier();
         {
             const float wt = Ws[buf][st];
-            const uint32_t xw4[4] = {xc.x, xc.y, xc.z, xc.w};
-            uint32_t hw[4], lw[4];
+            const uint32_t xw4[2] = {xc.x, xc.y};
+            uint32_t hw[2], lw[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 2; ++i) {
                 const float v0 = wt * __uint_as_float(xw4[i] << 16), v1 = wt * __uint_as_float(xw4[i] & 0xffff0000u);
                 const uint16_t h0b = bfbits(v0), h1b = bfbits(v1);
                 hw[i] = (uint32_t)h0b | ((uint32_t)h1b << 16);
                 lw[i] = (uint32_t)bfbits(v0 - bfval(h0b)) | ((uint32_t)bfbits(v1 - bfval(h1b)) << 16);
             }
-            *reinterpret_cast<uint4*>(&XWh[buf][st][8 * sq]) = uint4{hw[0], hw[1], hw[2], hw[3]};
-            *reinterpret_cast<uint4*>(&XWl[buf][st][8 * sq]) = uint4{lw[0], lw[1], lw[2], lw[3]};
+            *reinterpret_cast<uint2*>(&XWh[buf][st][4 * sq]) = uint2{hw[0], hw[1]};
+            *reinterpret_cast<uint2*>(&XWl[buf][st][4 * sq]) = uint2{lw[0], lw[1]};
         }
         lds_barrier();
         const float ecl = Es[buf];
-        const bf16x8_t xh = frag_col(&XWh[buf][0][0], RP, 0, 16 * wv);
-        const bf16x8_t xl = frag_col(&XWl[buf][0][0], RP, 0, 16 * wv);
+        const bf16x8_t xh = frag_col(&XWh[buf][0][0], RP, 0, 16 * pb);
+        const bf16x8_t xl = frag_col(&XWl[buf][0][0], RP, 0, 16 * pb);
 #pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            const bf16x8_t bf = frag_col(&Bh[buf][0][0], RN, 0, 16 * j);
+        for (int j = 0; j < NJ; ++j) {
+            const bf16x8_t bf = frag_col(&Bh[buf][0][0], RN, 0, 16 * (j0 + j));
             f32x4_t s = acc[j] * ecl;
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xh, s, 0, 0, 0);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xl, s, 0, 0, 0);
@@ -1059,9 +1061,9 @@ hipError_t launch_nw(M2BwdArgs a, bool ssd, hipStream_t stream) {
             {
                 KTime kt("m2_bwd_chunk_state", stream);
                 if (a.softplus)
-                    hipLaunchKernelGGL((m2_bwd_chunk_state_kernel<16 * NW, true>), grid, dim3(256), 0, stream, a);
+                    hipLaunchKernelGGL((m2_bwd_chunk_state_kernel<16 * NW, true>), grid, dim3(512), 0, stream, a);
                 else
-                    hipLaunchKernelGGL((m2_bwd_chunk_state_kernel<16 * NW, false>), grid, dim3(256), 0, stream, a);
+                    hipLaunchKernelGGL((m2_bwd_chunk_state_kernel<16 * NW, false>), grid, dim3(512), 0, stream, a);
             }
             KTime kt("m2_bwd_ssd", stream);
             if (a.softplus)
