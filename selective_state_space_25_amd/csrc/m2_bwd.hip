@@ -537,11 +537,13 @@ struct SsdSmem {
     alignas(16) uint16_t EYh[kQs][RP], EYl[kQs][RP];       // exp(cum) o dY
     alignas(16) uint16_t Bh[kQs][RN], Ch[kQs][RN];
     alignas(16) uint16_t S0h[kP][RN], S0l[kP][RN];
-    alignas(16) uint16_t dSh[kP][RN], dSl[kP][RN];
+    alignas(16) uint16_t dSh[N][RP], dSl[N][RP];            // transposed: dS^T[n][p]
     alignas(16) uint16_t Mh[kQs][RQ], Ml[kQs][RQ];
     alignas(16) uint16_t Kh[kQs][RQ], Kl[kQs][RQ];         // dM o F
     float Gm[kQs][kQs + 1], dM[kQs][kQs + 1];
-    float dl[kQs], cum[kQs], ecum[kQs], Wv[kQs], em[kQs], dv[kQs];
+    float dl[kQs], cum[kQs], em[kQs], dv[kQs];
+    alignas(16) float ecum[kQs];
+    alignas(16) float Wv[kQs];
     float Zf[kQs][kP];   // dout sigma(z) (1 + z (1 - sigma(z))): dz = Zf o (gate's input)
     float colp[kSsdThreads / 64][kQs], rowMM[kQs];   // per-wave column sums of V; row sums
     float dWp[N / 16][kQs], yyp[kP / 16][kQs];
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     const Op opB{&sm.Bh[0][0], nullptr, RN, true}, opBt{&sm.Bh[0][0], nullptr, RN, false};
     const Op opC{&sm.Ch[0][0], nullptr, RN, true}, opCt{&sm.Ch[0][0], nullptr, RN, false};
     const Op opS0{&sm.S0h[0][0], &sm.S0l[0][0], RN, true}, opS0t{&sm.S0h[0][0], &sm.S0l[0][0], RN, false};
-    const Op opdS{&sm.dSh[0][0], &sm.dSl[0][0], RN, true}, opdSt{&sm.dSh[0][0], &sm.dSl[0][0], RN, false};
+    const Op opdS{&sm.dSh[0][0], &sm.dSl[0][0], RP, false}, opdSt{&sm.dSh[0][0], &sm.dSl[0][0], RP, true};
     const Op opM{&sm.Mh[0][0], &sm.Ml[0][0], RQ, true}, opMt{&sm.Mh[0][0], &sm.Ml[0][0], RQ, false};
     const Op opK{&sm.Kh[0][0], &sm.Kl[0][0], RQ, true}, opKt{&sm.Kh[0][0], &sm.Kl[0][0], RQ, false};
 
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     f32x4_t dSr[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) dSr[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int e = tid; e < kP * RN; e += NT) {
+    for (int e = tid; e < N * RP; e += NT) {
         (&sm.dSh[0][0])[e] = 0;
         (&sm.dSl[0][0])[e] = 0;
     }
@@ -732,9 +734,23 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 for (int r = 0; r < 4; ++r) sm.dM[16 * tm + 4 * gq + r][16 * tn + li] = acc[r];
             }
         }
-        for (int e = tid; e < kQs * kP; e += NT) {
-            const int t = e >> 6, p = e & 63;
-            put2(&sm.EYh[t][p], &sm.EYl[t][p], sm.ecum[t] * (bfval(sm.DYh[t][p]) + bfval(sm.DYl[t][p])));
+        for (int e = tid; e < kQs * kP / 4; e += NT) {   // 4 channels of one token per thread
+            const int t = e >> 4, p = 4 * (e & 15);
+            const uint2 hv = *reinterpret_cast<const uint2*>(&sm.DYh[t][p]);
+            const uint2 lv = *reinterpret_cast<const uint2*>(&sm.DYl[t][p]);
+            const float ec = sm.ecum[t];
+            const uint32_t hw[2] = {hv.x, hv.y}, lw[2] = {lv.x, lv.y};
+            uint32_t oh[2], ol[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float v0 = ec * (__uint_as_float(hw[i] << 16) + __uint_as_float(lw[i] << 16));
+                const float v1 = ec * (__uint_as_float(hw[i] & 0xffff0000u) + __uint_as_float(lw[i] & 0xffff0000u));
+                const uint16_t h0b = bfbits(v0), h1b = bfbits(v1);
+                oh[i] = (uint32_t)h0b | ((uint32_t)h1b << 16);
+                ol[i] = (uint32_t)bfbits(v0 - bfval(h0b)) | ((uint32_t)bfbits(v1 - bfval(h1b)) << 16);
+            }
+            *reinterpret_cast<uint2*>(&sm.EYh[t][p]) = uint2{oh[0], oh[1]};
+            *reinterpret_cast<uint2*>(&sm.EYl[t][p]) = uint2{ol[0], ol[1]};
         }
         lds_barrier();
 
@@ -746,16 +762,19 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             f32x4_t y0 = mma<N>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opC, 16 * tm, opS0, 16 * tn);
             f32x4_t d1 = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opMt, 16 * tm, opDYt, 16 * tn);
             f32x4_t d2 = mma<N>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opB, 16 * tm, opdS, 16 * tn);
+            const float4 ec4 = *reinterpret_cast<const float4*>(&sm.ecum[16 * tm + 4 * gq]);
+            const float4 wv4 = *reinterpret_cast<const float4*>(&sm.Wv[16 * tm + 4 * gq]);
+            const float ecr[4] = {ec4.x, ec4.y, ec4.z, ec4.w}, wvr[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tm + 4 * gq + r, p = 16 * tn + li;
                 const bool ok = t0 + t < a.L;
                 const int64_t gi = ((b * a.L + t0 + t) * a.H + h) * kP + p;
                 const float xv = bfval(sm.Xh[t][p]), dy = bfval(sm.DYh[t][p]) + bfval(sm.DYl[t][p]);
-                const float yint = sm.ecum[t] * y0[r];
+                const float yint = ecr[r] * y0[r];
                 if (has_z && ok) a.dz[gi] = sm.Zf[t][p] * (yi[r] + yint + Dh * xv);
                 if (ok) accD = __builtin_fmaf(dy, xv, accD);
-                if (ok) a.dx[gi] = d1[r] + sm.Wv[t] * d2[r] + Dh * dy;
+                if (ok) a.dx[gi] = d1[r] + wvr[r] * d2[r] + Dh * dy;
                 const float yy = row_sum(dy * yint);
                 if (li == 0) sm.yyp[tn][t] = yy;
             }
@@ -802,12 +821,14 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             dc = mma<kP>(dc, opEY, 16 * tm, opS0t, 16 * tn);
             const f32x4_t db = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opKt, 16 * tm, opCt, 16 * tn);
             const f32x4_t xd = mma<kP>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opX, 16 * tm, opdSt, 16 * tn);
+            const float4 wv4 = *reinterpret_cast<const float4*>(&sm.Wv[16 * tm + 4 * gq]);
+            const float wvr[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * tm + 4 * gq + r, n = 16 * tn + li;
                 if (t0 + s < a.L) {
                     a.pC[(bh * a.L + t0 + s) * N + n] = dc[r];
-                    a.pB[(bh * a.L + t0 + s) * N + n] = db[r] + sm.Wv[s] * xd[r];
+                    a.pB[(bh * a.L + t0 + s) * N + n] = db[r] + wvr[r] * xd[r];
                 }
                 const float part = row_sum(xd[r] * bfval(sm.Bh[s][n]));
                 if (li == 0) sm.dWp[tn][s] = part;
@@ -835,12 +856,19 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             for (int j = 0; j < TPW; ++j) {
                 const int tile = wv + NWV * j, tm = tile / TND, tn = tile - tm * TND;
                 const f32x4_t u = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opEYt, 16 * tm, opCt, 16 * tn);
+                uint16_t hb[4], lb[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     dSr[j][r] = __builtin_fmaf(ecl, dSr[j][r], u[r]);
-                    const int p = 16 * tm + 4 * gq + r, n = 16 * tn + li;
-                    put2(&sm.dSh[p][n], &sm.dSl[p][n], dSr[j][r]);
+                    hb[r] = bfbits(dSr[j][r]);
+                    lb[r] = bfbits(dSr[j][r] - bfval(hb[r]));
                 }
+                // rows p = 16 tm + 4 gq .. + 3 of column n: four consecutive p of dS^T
+                const int p = 16 * tm + 4 * gq, n = 16 * tn + li;
+                *reinterpret_cast<uint2*>(&sm.dSh[n][p]) =
+                    uint2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+                *reinterpret_cast<uint2*>(&sm.dSl[n][p]) =
+                    uint2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
             }
         }
         // ---- per token: dcum, dDelta, ddt, and the chunk's share of dA, dbias, dD
