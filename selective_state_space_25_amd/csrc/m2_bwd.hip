@@ -597,7 +597,8 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     const int st = tid >> 4, sq = tid & 15;   // token, 4-channel segment
     uint2 xr, zr;
     uint4 br[NBC], cr[NBC];
-    float dov[4], dtv;
+    float dov[4];
+    uint32_t dtr;   // dt's bf16 bits
     float4 ckr[NW / 2];
     auto fetch = [&](int64_t c) {
         const int64_t t0 = c * kQs;
@@ -635,8 +636,9 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         const float4* src = reinterpret_cast<const float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
 #pragma unroll
         for (int i = 0; i < NW / 2; ++i) ckr[i] = src[NT * i + tid];
-        dtv = 0.0f;
-        if (wv == 0 && lane < kQs && t0 + lane < a.L) dtv = bfval(DT[(b * a.L + t0 + lane) * a.H + h]);
+        // raw bits: converting here would make the wave wait for the load at once
+        dtr = 0u;
+        if (wv == 0 && lane < kQs && t0 + lane < a.L) dtr = DT[(b * a.L + t0 + lane) * a.H + h];
     };
     fetch(nch - 1);
 
@@ -697,7 +699,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         if (wv == 0 && lane < kQs) {
             float dl, av, dvv;
             const bool ok = t0 + lane < a.L;
-            tok_consts<SP>(dtv, ok, Ah, biash, dl, av, dvv);
+            tok_consts<SP>(__uint_as_float(dtr << 16), ok, Ah, biash, dl, av, dvv);
             float cs = dl * Ah;   // inclusive prefix of Delta A over the chunk
 #pragma unroll
             for (int o = 1; o < kQs; o <<= 1) {
@@ -973,7 +975,7 @@ __global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
 
     uint2 xr;
     uint4 br[NBC];
-    float dtv;
+    uint32_t dtr;   // dt's bf16 bits
     auto load = [&](int64_t c) {
         const int64_t t0 = c * kQs;
         xr = uint2{0u, 0u};
@@ -985,8 +987,9 @@ __global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
             if (e < kQs * SEG && t0 + t < a.L)
                 br[i] = *reinterpret_cast<const uint4*>(Bp + ((b * a.L + t0 + t) * a.G + g) * N + 8 * s8);
         }
-        dtv = 0.0f;
-        if (wv == 0 && lane < kQs && t0 + lane < a.L) dtv = bfval(DT[(b * a.L + t0 + lane) * a.H + h]);
+        // raw bits: converting here would make the wave wait for the load at once
+        dtr = 0u;
+        if (wv == 0 && lane < kQs && t0 + lane < a.L) dtr = DT[(b * a.L + t0 + lane) * a.H + h];
     };
     if (nch > 1) load(0);
     for (int64_t c = 0; c < nch; ++c) {
@@ -998,7 +1001,7 @@ __global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
         const int buf = (int)(c & 1);
         if (wv == 0 && lane < kQs) {
             float dl, av, dvv;
-            tok_consts<SP>(dtv, c * kQs + lane < a.L, Ah, biash, dl, av, dvv);
+            tok_consts<SP>(__uint_as_float(dtr << 16), c * kQs + lane < a.L, Ah, biash, dl, av, dvv);
             float cs = dl * Ah;   // inclusive prefix of Delta A over the chunk
 #pragma unroll
             for (int o = 1; o < kQs; o <<= 1) {
