@@ -541,9 +541,10 @@ struct SsdSmem {
     alignas(16) uint16_t Mh[kQs][RQ], Ml[kQs][RQ];
     alignas(16) uint16_t Kh[kQs][RQ], Kl[kQs][RQ];         // dM o F
     float Gm[kQs][kQs + 1], dM[kQs][kQs + 1];
-    float dl[kQs], cum[kQs], em[kQs], dv[kQs];
-    alignas(16) float ecum[kQs];
-    alignas(16) float Wv[kQs];
+    // token constants, double-buffered by chunk parity
+    float dl[2][kQs], cum[2][kQs], em[2][kQs], dv[2][kQs];
+    alignas(16) float ecum[2][kQs];
+    alignas(16) float Wv[2][kQs];
     float Zf[kQs][kP];   // dout sigma(z) (1 + z (1 - sigma(z))): dz = Zf o (gate's input)
     float colp[kSsdThreads / 64][kQs], rowMM[kQs];   // per-wave column sums of V; row sums
     float dWp[N / 16][kQs], yyp[kP / 16][kQs];
@@ -638,12 +639,13 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         for (int i = 0; i < NW / 2; ++i) ckr[i] = src[NT * i + tid];
         // raw bits: converting here would make the wave wait for the load at once
         dtr = 0u;
-        if (wv == 0 && lane < kQs && t0 + lane < a.L) dtr = DT[(b * a.L + t0 + lane) * a.H + h];
+        if (wv == 1 && lane < kQs && t0 + lane < a.L) dtr = DT[(b * a.L + t0 + lane) * a.H + h];
     };
     fetch(nch - 1);
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t t0 = c * kQs;
+        const int tb = (int)(c & 1);   // this chunk's token constants
         // ---- stage: x, B, C (exact), dY and S_in to their planes, dout's
         //      gate factor to Zf, from the registers fetched during the chunk after
         *reinterpret_cast<uint2*>(&sm.Xh[st][4 * sq]) = xr;
@@ -696,7 +698,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             *reinterpret_cast<uint2*>(&sm.S0h[p][n]) = uint2{hw[0], hw[1]};
             *reinterpret_cast<uint2*>(&sm.S0l[p][n]) = uint2{lw[0], lw[1]};
         }
-        if (wv == 0 && lane < kQs) {
+        if (wv == 1 && lane < kQs) {   // wave 0 may still be on the chunk after's scalars
             float dl, av, dvv;
             const bool ok = t0 + lane < a.L;
             tok_consts<SP>(__uint_as_float(dtr << 16), ok, Ah, biash, dl, av, dvv);
@@ -707,17 +709,17 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 if (lane >= o) cs += up;
             }
             const float cl = __shfl(cs, kQs - 1, 64);
-            sm.dl[lane] = dl;
-            sm.cum[lane] = cs;
-            sm.ecum[lane] = __expf(cs);
-            sm.em[lane] = __expf(cl - cs);
-            sm.Wv[lane] = __expf(cl - cs) * dl;
-            sm.dv[lane] = dvv;
+            sm.dl[tb][lane] = dl;
+            sm.cum[tb][lane] = cs;
+            sm.ecum[tb][lane] = __expf(cs);
+            sm.em[tb][lane] = __expf(cl - cs);
+            sm.Wv[tb][lane] = __expf(cl - cs) * dl;
+            sm.dv[tb][lane] = dvv;
         }
         if (c > 0) fetch(c - 1);
         lds_barrier();
 
-        auto F = [&](int t, int s) { return s <= t ? __expf(sm.cum[t] - sm.cum[s]) * sm.dl[s] : 0.0f; };
+        auto F = [&](int t, int s) { return s <= t ? __expf(sm.cum[tb][t] - sm.cum[tb][s]) * sm.dl[tb][s] : 0.0f; };
         // ---- G = C B^T, M = G o F (tiles 0..3); dM = dY X^T (tiles 4..7); exp(cum) o dY
         for (int tile = wv; tile < 8; tile += NWV) {
             const int tm = (tile >> 1) & 1, tn = tile & 1;
@@ -740,7 +742,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             const int t = e >> 4, p = 4 * (e & 15);
             const uint2 hv = *reinterpret_cast<const uint2*>(&sm.DYh[t][p]);
             const uint2 lv = *reinterpret_cast<const uint2*>(&sm.DYl[t][p]);
-            const float ec = sm.ecum[t];
+            const float ec = sm.ecum[tb][t];
             const uint32_t hw[2] = {hv.x, hv.y}, lw[2] = {lv.x, lv.y};
             uint32_t oh[2], ol[2];
 #pragma unroll
@@ -764,8 +766,8 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             f32x4_t y0 = mma<N>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opC, 16 * tm, opS0, 16 * tn);
             f32x4_t d1 = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opMt, 16 * tm, opDYt, 16 * tn);
             f32x4_t d2 = mma<N>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opB, 16 * tm, opdS, 16 * tn);
-            const float4 ec4 = *reinterpret_cast<const float4*>(&sm.ecum[16 * tm + 4 * gq]);
-            const float4 wv4 = *reinterpret_cast<const float4*>(&sm.Wv[16 * tm + 4 * gq]);
+            const float4 ec4 = *reinterpret_cast<const float4*>(&sm.ecum[tb][16 * tm + 4 * gq]);
+            const float4 wv4 = *reinterpret_cast<const float4*>(&sm.Wv[tb][16 * tm + 4 * gq]);
             const float ecr[4] = {ec4.x, ec4.y, ec4.z, ec4.w}, wvr[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -788,16 +790,16 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         // dDelta_s adds it back.  Thread: token t, columns 2 sb, 2 sb + 1.
         {
             const int t = tid >> 4, sb = tid & 15;
-            const float ct = sm.cum[t];
+            const float ct = sm.cum[tb][t];
             float vs[2], row = 0.0f;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int s = 2 * sb + k;
-                const float e = s <= t ? __expf(ct - sm.cum[s]) : 0.0f;
+                const float e = s <= t ? __expf(ct - sm.cum[tb][s]) : 0.0f;
                 const float dm = sm.dM[t][s];
-                put2(&sm.Kh[t][s], &sm.Kl[t][s], dm * e * sm.dl[s]);
+                put2(&sm.Kh[t][s], &sm.Kl[t][s], dm * e * sm.dl[tb][s]);
                 vs[k] = s < t ? dm * sm.Gm[t][s] * e : 0.0f;
-                row = __builtin_fmaf(vs[k], sm.dl[s], row);
+                row = __builtin_fmaf(vs[k], sm.dl[tb][s], row);
             }
             row += __shfl_xor(row, 1, 64);
             row += __shfl_xor(row, 2, 64);
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
             dc = mma<kP>(dc, opEY, 16 * tm, opS0t, 16 * tn);
             const f32x4_t db = mma<kQs>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opKt, 16 * tm, opCt, 16 * tn);
             const f32x4_t xd = mma<kP>(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, opX, 16 * tm, opdSt, 16 * tn);
-            const float4 wv4 = *reinterpret_cast<const float4*>(&sm.Wv[16 * tm + 4 * gq]);
+            const float4 wv4 = *reinterpret_cast<const float4*>(&sm.Wv[tb][16 * tm + 4 * gq]);
             const float wvr[4] = {wv4.x, wv4.y, wv4.z, wv4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -853,7 +855,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 
         // ---- dS_in = exp(cum_last) dS + (exp(cum) o dY)^T C, into registers and the planes
         {
-            const float ecl = sm.ecum[kQs - 1];
+            const float ecl = sm.ecum[tb][kQs - 1];
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
                 const int tile = wv + NWV * j, tm = tile / TND, tn = tile - tm * TND;
@@ -873,7 +875,10 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                     uint2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
             }
         }
+        lds_barrier();
         // ---- per token: dcum, dDelta, ddt, and the chunk's share of dA, dbias, dD
+        //      (wave 0, while the others stage the next chunk: nothing it reads
+        //      is written before the next chunk's first barrier)
         if (wv == 0) {
             const int t = lane;
             float dW = 0.0f, dc = 0.0f, dDl = 0.0f;
@@ -885,15 +890,15 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 #pragma unroll
                 for (int w = 0; w < NWV; ++w) col += sm.colp[w][t];
                 dDl = col + sm.dM[t][t] * sm.Gm[t][t];
-                dc = sm.rowMM[t] - sm.dl[t] * col + yy - dW * sm.Wv[t];
+                dc = sm.rowMM[t] - sm.dl[tb][t] * col + yy - dW * sm.Wv[tb][t];
             }
             // the last token also carries exp(cum_last)'s paths: sum_s dW_s W_s
             // and exp(cum_last) sum dS o S_in
-            const float dwW = wave_sum(t < kQs ? dW * sm.Wv[t] : 0.0f);
+            const float dwW = wave_sum(t < kQs ? dW * sm.Wv[tb][t] : 0.0f);
             float sds_all = 0.0f;
 #pragma unroll
             for (int w = 0; w < NWV; ++w) sds_all += sm.red[w];
-            if (t == kQs - 1) dc += dwW + sm.ecum[kQs - 1] * sds_all;
+            if (t == kQs - 1) dc += dwW + sm.ecum[tb][kQs - 1] * sds_all;
             // rc_t = sum_{t' >= t} dcum_t' (a reversed inclusive scan over the lanes)
             float rc = t < kQs ? dc : 0.0f;
 #pragma unroll
@@ -902,15 +907,15 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 if (t + o < kQs) rc += dn;
             }
             if (t < kQs && t0 + t < a.L) {
-                const float dD = dDl + dW * sm.em[t] + Ah * rc;
-                const float dvt = dD * sm.dv[t];
+                const float dD = dDl + dW * sm.em[tb][t] + Ah * rc;
+                const float dvt = dD * sm.dv[tb][t];
                 a.ddt[(b * a.L + t0 + t) * a.H + h] = dvt;
                 accBias += dvt;
-                accA = __builtin_fmaf(sm.dl[t], rc, accA);
+                accA = __builtin_fmaf(sm.dl[tb][t], rc, accA);
             }
         }
-        lds_barrier();
     }
+    lds_barrier();   // wave 0 reads red above
     if (a.dh0) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
