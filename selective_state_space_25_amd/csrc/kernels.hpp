@@ -142,7 +142,9 @@ struct M2BwdArgs {
     const void* dout;
     float *dx, *ddt, *dA, *dB, *dC, *dD, *dz, *ddt_bias, *dh0;
     float* ck;        // [batch*H, tiles, N/16, 4, 64, 4] states entering each 8-token tile
-                      // (the chunked form: each 32-token chunk)
+                      // (the chunked form: each 32-token chunk, as
+                      // [batch*H, chunks, N/16, 4, 4, 16, 4]: n block, p block,
+                      // p quad, n in block, 4 consecutive p)
     float* pB;        // [batch*H, L, N] per-head dB
     float* pC;        // [batch*H, L, N] per-head dC
     float *pA, *pD, *pbias;   // [batch*H] per-(batch, head) sums

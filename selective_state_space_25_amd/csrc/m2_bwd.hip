@@ -536,7 +536,7 @@ struct SsdSmem {
     alignas(16) uint16_t DYh[kQs][RP], DYl[kQs][RP];
     alignas(16) uint16_t EYh[kQs][RP], EYl[kQs][RP];       // exp(cum) o dY
     alignas(16) uint16_t Bh[kQs][RN], Ch[kQs][RN];
-    alignas(16) uint16_t S0h[kP][RN], S0l[kP][RN];
+    alignas(16) uint16_t S0h[N][RP], S0l[N][RP];            // transposed: S_in^T[n][p]
     alignas(16) uint16_t dSh[N][RP], dSl[N][RP];            // transposed: dS^T[n][p]
     alignas(16) uint16_t Mh[kQs][RQ], Ml[kQs][RQ];
     alignas(16) uint16_t Kh[kQs][RQ], Kl[kQs][RQ];         // dM o F
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
     const Op opEY{&sm.EYh[0][0], &sm.EYl[0][0], RP, true}, opEYt{&sm.EYh[0][0], &sm.EYl[0][0], RP, false};
     const Op opB{&sm.Bh[0][0], nullptr, RN, true}, opBt{&sm.Bh[0][0], nullptr, RN, false};
     const Op opC{&sm.Ch[0][0], nullptr, RN, true}, opCt{&sm.Ch[0][0], nullptr, RN, false};
-    const Op opS0{&sm.S0h[0][0], &sm.S0l[0][0], RN, true}, opS0t{&sm.S0h[0][0], &sm.S0l[0][0], RN, false};
+    const Op opS0{&sm.S0h[0][0], &sm.S0l[0][0], RP, false}, opS0t{&sm.S0h[0][0], &sm.S0l[0][0], RP, true};
     const Op opdS{&sm.dSh[0][0], &sm.dSl[0][0], RP, false}, opdSt{&sm.dSh[0][0], &sm.dSl[0][0], RP, true};
     const Op opM{&sm.Mh[0][0], &sm.Ml[0][0], RQ, true}, opMt{&sm.Mh[0][0], &sm.Ml[0][0], RQ, false};
     const Op opK{&sm.Kh[0][0], &sm.Kl[0][0], RQ, true}, opKt{&sm.Kh[0][0], &sm.Kl[0][0], RQ, false};
@@ -685,8 +685,9 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < NW / 2; ++i) {
-            // record float4 (w, q, p): state row p, columns 16 w + 4 q .. + 3
-            const int e4 = NT * i + tid, w = e4 >> 8, q = (e4 >> 6) & 3, p = e4 & 63, n = 16 * w + 4 * q;
+            // record float4 (n block, p block, q, i): rows p = 16 p block + 4 q .. + 3
+            // of the state's column n = 16 n block + i
+            const int e4 = NT * i + tid, n = 16 * (e4 >> 8) + (e4 & 15), p = 16 * ((e4 >> 6) & 3) + 4 * ((e4 >> 4) & 3);
             const float v[4] = {ckr[i].x, ckr[i].y, ckr[i].z, ckr[i].w};
             uint32_t hw[2], lw[2];
 #pragma unroll
@@ -695,8 +696,8 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
                 hw[i] = (uint32_t)h0b | ((uint32_t)h1b << 16);
                 lw[i] = (uint32_t)bfbits(v[2 * i] - bfval(h0b)) | ((uint32_t)bfbits(v[2 * i + 1] - bfval(h1b)) << 16);
             }
-            *reinterpret_cast<uint2*>(&sm.S0h[p][n]) = uint2{hw[0], hw[1]};
-            *reinterpret_cast<uint2*>(&sm.S0l[p][n]) = uint2{lw[0], lw[1]};
+            *reinterpret_cast<uint2*>(&sm.S0h[n][p]) = uint2{hw[0], hw[1]};
+            *reinterpret_cast<uint2*>(&sm.S0l[n][p]) = uint2{lw[0], lw[1]};
         }
         if (wv == 1 && lane < kQs) {   // wave 0 may still be on the chunk after's scalars
             float dl, av, dvv;
@@ -843,10 +844,15 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int tile = wv + NWV * j, tm = tile / TND, tn = tile - tm * TND;
+            const int p = 16 * tm + 4 * gq, n = 16 * tn + li;   // rows p .. p + 3 of column n
+            const uint2 h2 = *reinterpret_cast<const uint2*>(&sm.S0h[n][p]);
+            const uint2 l2 = *reinterpret_cast<const uint2*>(&sm.S0l[n][p]);
+            const uint32_t hw[2] = {h2.x, h2.y}, lw[2] = {l2.x, l2.y};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int p = 16 * tm + 4 * gq + r, n = 16 * tn + li;
-                sds += dSr[j][r] * (bfval(sm.S0h[p][n]) + bfval(sm.S0l[p][n]));
+                const uint32_t hb = (r & 1) ? (hw[r >> 1] & 0xffff0000u) : (hw[r >> 1] << 16);
+                const uint32_t lb = (r & 1) ? (lw[r >> 1] & 0xffff0000u) : (lw[r >> 1] << 16);
+                sds += dSr[j][r] * (__uint_as_float(hb) + __uint_as_float(lb));
             }
         }
         sds = wave_sum(sds);
@@ -947,12 +953,13 @@ __global__ __launch_bounds__(kSsdThreads) void m2_bwd_ssd_kernel(M2BwdArgs a) {
 // The chunked form needs only the state entering each chunk, and each
 // follows from the one before by a single product:
 //   S_out = exp(cum_last) S_in + (W o X)^T B,   W_s = exp(cum_last - cum_s) Delta_s.
-// The state is held transposed, S^T[n][p] = B^T (W o X) + ..., as MFMA
-// accumulators (rows n, columns p): a lane's four rows are then the four
-// consecutive n of one checkpoint float4.  Eight waves (two per SIMD):
-// wave w owns the columns p = 16 (w & 3) .. + 15 and half of the rows n.  The next chunk's inputs are loaded while this one
-// is multiplied, and the LDS operands are double-buffered so that one
-// chunk's writes never meet the other's reads.
+// The state S[p][n] is held as MFMA accumulators (rows p, columns n): a
+// lane's four rows are four consecutive p of one n, which is one float4 of
+// the record and, transposed, one 8-byte row piece of the consumer's
+// S_in^T planes.  Eight waves (two per SIMD): wave w owns the rows
+// p = 16 (w & 3) .. + 15 and half of the columns n.  The next chunk's
+// inputs are loaded while this one is multiplied, and the LDS operands are
+// double-buffered so that one chunk's writes never meet the other's reads.
 template <int N, bool SP>
 __global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
     constexpr int NW = N / 16, SEG = N / 8, NT = 512, NBC = (kQs * SEG + NT - 1) / NT, NJ = NW / 2;
@@ -976,7 +983,7 @@ __global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            acc[j][r] = a.h0 ? a.h0[(bh * kP + 16 * pb + li) * N + 16 * (j0 + j) + 4 * gq + r] : 0.0f;
+            acc[j][r] = a.h0 ? a.h0[(bh * kP + 16 * pb + 4 * gq + r) * N + 16 * (j0 + j) + li] : 0.0f;
 
     uint2 xr;
     uint4 br[NBC];
@@ -1001,7 +1008,7 @@ __global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
         float4* dst = reinterpret_cast<float4*>(a.ck + (bh * nch + c) * (int64_t)(NW * kP * 16));
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-            dst[256 * (j0 + j) + 64 * gq + 16 * pb + li] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+            dst[256 * (j0 + j) + 64 * pb + 16 * gq + li] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         if (c + 1 == nch) break;
         const int buf = (int)(c & 1);
         if (wv == 0 && lane < kQs) {
@@ -1047,8 +1054,8 @@ __global__ __launch_bounds__(512) void m2_bwd_chunk_state_kernel(M2BwdArgs a) {
         for (int j = 0; j < NJ; ++j) {
             const bf16x8_t bf = frag_col(&Bh[buf][0][0], RN, 0, 16 * (j0 + j));
             f32x4_t s = acc[j] * ecl;
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xh, s, 0, 0, 0);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, xl, s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bf, s, 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bf, s, 0, 0, 0);
         }
     }
 }
